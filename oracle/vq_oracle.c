@@ -1,0 +1,379 @@
+/*
+ * CPU oracle for the VQ dequantize-and-multiply path.  TEST INFRASTRUCTURE ONLY (see
+ * vq_oracle.h): slow, plain and independent of the HIP library.  Built with
+ *   gcc -O2 -std=c11 -fno-fast-math -ffp-contract=off
+ * so that every float operation below is one IEEE operation rounded to nearest-even,
+ * with subnormals kept.
+ *
+ * Sources on the pages this follows:
+ *   - VPTQ guide (aifetchly), "The Information-Theoretic Superiority of Vector
+ *     Quantization": a vector of v adjacent weights is replaced by a centroid of a
+ *     K-entry codebook, its index costs log2(K) bits.
+ *   - VPTQ guide, "2. Multi-Stage Residual Vector Quantization (RVQ)": the decoded
+ *     vector is the main centroid plus the residual centroid.
+ *   - VPTQ guide, "Step 2" (dequantize: gather both books, add, view as [out, in])
+ *     and "Step 3" (forward: y = x W^T + bias).
+ *   - Production-VQ post (llms.blog), QuIP# "per-channel scaling": a scale per output
+ *     channel multiplies the rebuilt vector.
+ */
+#define _POSIX_C_SOURCE 200809L
+#include "vq_oracle.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+#include <unistd.h>
+
+/* ---------------------------------------------------------------- number formats */
+
+/* binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+double oracle_f16_to_f64(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int e = (h >> 10) & 0x1f;
+  int f = h & 0x3ff;
+  double val;
+  if (e == 0) {
+    val = ldexp((double)f, -24); /* subnormal: f * 2^-14 / 2^10 */
+  } else if (e == 31) {
+    val = f ? NAN : INFINITY;
+  } else {
+    val = ldexp((double)(1024 + f), e - 15 - 10); /* (1 + f/2^10) * 2^(e-15) */
+  }
+  return sign ? -val : val;
+}
+
+/* bfloat16: 1 sign bit, 8 exponent bits (bias 127), 7 fraction bits. */
+double oracle_bf16_to_f64(uint16_t b) {
+  int sign = (b >> 15) & 1;
+  int e = (b >> 7) & 0xff;
+  int f = b & 0x7f;
+  double val;
+  if (e == 0) {
+    val = ldexp((double)f, -126 - 7);
+  } else if (e == 255) {
+    val = f ? NAN : INFINITY;
+  } else {
+    val = ldexp((double)(128 + f), e - 127 - 7);
+  }
+  return sign ? -val : val;
+}
+
+/* Round |a| to a multiple of the quantum q, ties to an even multiple.  a/q is exact
+ * because a carries at most 24 significant bits and q is a power of two. */
+static double round_to_quantum_even(double a, double q) {
+  double n = a / q;
+  double fl = floor(n);
+  double fr = n - fl;
+  double r;
+  if (fr > 0.5) {
+    r = fl + 1.0;
+  } else if (fr < 0.5) {
+    r = fl;
+  } else {
+    r = (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;
+  }
+  return r * q;
+}
+
+/* Generic RNE to a binary format with `mbits` fraction bits and exponent range
+ * [emin, emax] (normal numbers), then encoded. */
+static uint16_t encode_rne(double x, int mbits, int emin, int emax, int ebias, int ebits) {
+  uint16_t sign = signbit(x) ? (uint16_t)0x8000 : (uint16_t)0;
+  uint16_t exp_all_ones = (uint16_t)(((1 << ebits) - 1) << mbits);
+  if (isnan(x)) return (uint16_t)(exp_all_ones | (1u << (mbits - 1)));
+  double a = fabs(x);
+  double maxfin = ldexp(2.0 - ldexp(1.0, -mbits), emax);
+  double overflow_mid = ldexp(2.0 - ldexp(1.0, -mbits - 1), emax);
+  if (a >= overflow_mid) return (uint16_t)(sign | exp_all_ones); /* tie goes to even = infinity */
+  double q;
+  if (a < ldexp(1.0, emin)) {
+    q = ldexp(1.0, emin - mbits);
+  } else {
+    int e2;
+    frexp(a, &e2); /* a in [2^(e2-1), 2^e2) */
+    q = ldexp(1.0, (e2 - 1) - mbits);
+  }
+  double r = round_to_quantum_even(a, q);
+  if (r > maxfin) return (uint16_t)(sign | exp_all_ones);
+  if (r == 0.0) return sign;
+  if (r < ldexp(1.0, emin)) {
+    return (uint16_t)(sign | (uint16_t)(r / ldexp(1.0, emin - mbits)));
+  }
+  int e2;
+  double fr = frexp(r, &e2); /* r = fr * 2^e2, fr in [0.5, 1) */
+  int E = e2 - 1;
+  uint16_t mant = (uint16_t)((fr * 2.0 - 1.0) * ldexp(1.0, mbits));
+  return (uint16_t)(sign | (uint16_t)((E + ebias) << mbits) | mant);
+}
+
+uint16_t oracle_f64_to_f16_rne(double x) { return encode_rne(x, 10, -14, 15, 15, 5); }
+uint16_t oracle_f64_to_bf16_rne(double x) { return encode_rne(x, 7, -126, 127, 127, 8); }
+
+/* ---------------------------------------------------------------- layout */
+
+static int valid_desc(int64_t n, int64_t in_features, int v, int bits1, int bits2) {
+  if (n < 0 || in_features < 0) return 0;
+  if (v < 1 || v > 16) return 0;
+  if (bits1 < 1 || bits1 > 16) return 0;
+  if (bits2 < 0 || bits2 > 16) return 0;
+  return 1;
+}
+
+static int64_t num_vectors(int64_t in_features, int v) { return (in_features + v - 1) / v; }
+
+int64_t oracle_row_stride(int64_t in_features, int v, int bits) {
+  if (bits == 0) return 0;
+  int64_t bits_per_row = num_vectors(in_features, v) * (int64_t)bits;
+  return 16 * ((bits_per_row + 127) / 128);
+}
+
+int64_t oracle_packed_bytes(int64_t n, int64_t in_features, int v, int bits1, int bits2) {
+  if (!valid_desc(n, in_features, v, bits1, bits2)) return -1;
+  return n * (oracle_row_stride(in_features, v, bits1) + oracle_row_stride(in_features, v, bits2));
+}
+
+/* Bit k of a row is bit (k mod 8) of byte floor(k/8). */
+static int get_bit(const uint8_t* row, int64_t k) { return (row[k >> 3] >> (k & 7)) & 1; }
+static void set_bit(uint8_t* row, int64_t k) { row[k >> 3] = (uint8_t)(row[k >> 3] | (1u << (k & 7))); }
+
+/* Field j (B bits, LSB first) of a row, read one bit at a time. */
+static uint32_t read_field(const uint8_t* row, int64_t j, int bits) {
+  uint32_t val = 0;
+  for (int q = 0; q < bits; ++q) {
+    if (get_bit(row, j * bits + q)) val |= (uint32_t)1 << q;
+  }
+  return val;
+}
+
+int oracle_pack(int64_t n, int64_t in_features, int v, int bits1, int bits2, const uint32_t* idx1,
+                const uint32_t* idx2, uint8_t* out, int64_t out_bytes) {
+  if (!valid_desc(n, in_features, v, bits1, bits2)) return ORACLE_BAD_ARGS;
+  if ((n > 0 && in_features > 0) && (!idx1 || (bits2 > 0 && !idx2) || !out)) return ORACLE_BAD_ARGS;
+  int64_t need = oracle_packed_bytes(n, in_features, v, bits1, bits2);
+  if (out_bytes < need) return ORACLE_BUFFER_SMALL;
+  int64_t nv = num_vectors(in_features, v);
+  for (int stream = 1; stream <= 2; ++stream) {
+    int bits = stream == 1 ? bits1 : bits2;
+    if (bits == 0) continue;
+    const uint32_t* idx = stream == 1 ? idx1 : idx2;
+    for (int64_t i = 0; i < n * nv; ++i)
+      if (idx[i] >> bits) return ORACLE_INDEX_RANGE;
+  }
+  memset(out, 0, (size_t)need);
+  int64_t s1 = oracle_row_stride(in_features, v, bits1);
+  int64_t s2 = oracle_row_stride(in_features, v, bits2);
+  for (int stream = 1; stream <= 2; ++stream) {
+    int bits = stream == 1 ? bits1 : bits2;
+    if (bits == 0) continue;
+    const uint32_t* idx = stream == 1 ? idx1 : idx2;
+    for (int64_t o = 0; o < n; ++o) {
+      uint8_t* row = stream == 1 ? out + o * s1 : out + n * s1 + o * s2;
+      for (int64_t j = 0; j < nv; ++j) {
+        uint32_t val = idx[o * nv + j];
+        for (int q = 0; q < bits; ++q)
+          if ((val >> q) & 1u) set_bit(row, j * bits + q);
+      }
+    }
+  }
+  return ORACLE_OK;
+}
+
+int oracle_unpack(int64_t n, int64_t in_features, int v, int bits1, int bits2, const uint8_t* packed,
+                  uint32_t* idx1, uint32_t* idx2) {
+  if (!valid_desc(n, in_features, v, bits1, bits2)) return ORACLE_BAD_ARGS;
+  int64_t nv = num_vectors(in_features, v);
+  int64_t s1 = oracle_row_stride(in_features, v, bits1);
+  int64_t s2 = oracle_row_stride(in_features, v, bits2);
+  int pad_set = 0;
+  for (int stream = 1; stream <= 2; ++stream) {
+    int bits = stream == 1 ? bits1 : bits2;
+    if (bits == 0) continue;
+    uint32_t* idx = stream == 1 ? idx1 : idx2;
+    int64_t stride = stream == 1 ? s1 : s2;
+    for (int64_t o = 0; o < n; ++o) {
+      const uint8_t* row = stream == 1 ? packed + o * s1 : packed + n * s1 + o * s2;
+      for (int64_t j = 0; j < nv; ++j) idx[o * nv + j] = read_field(row, j, bits);
+      for (int64_t k = nv * bits; k < stride * 8; ++k)
+        if (get_bit(row, k)) pad_set = 1;
+    }
+  }
+  return pad_set ? ORACLE_PAD_NONZERO : ORACLE_OK;
+}
+
+/* ---------------------------------------------------------------- dequant + product */
+
+typedef struct {
+  int64_t n, in_features;
+  int v, bits1, bits2;
+  const uint8_t* packed;
+  const uint16_t* cb1;
+  const uint16_t* cb2;
+  const uint16_t* scale;
+  const uint16_t* bias;
+  const double* xd; /* [M][in] decoded activations, NULL for dequant-only */
+  int64_t M;
+  const int64_t* rows;
+  int64_t nrows;
+  float* w_out;  /* dequant-only: [nrows][in] */
+  double* y_out; /* forward: [M][nrows] */
+  int64_t begin, end;
+} job_t;
+
+/* One row of W in fp32, following the decode order: sum the two centroids in fp32,
+ * then multiply by the channel scale in fp32. */
+static void dequant_row(const job_t* jb, int64_t o, float* wrow) {
+  int64_t nv = num_vectors(jb->in_features, jb->v);
+  int64_t s1 = oracle_row_stride(jb->in_features, jb->v, jb->bits1);
+  int64_t s2 = oracle_row_stride(jb->in_features, jb->v, jb->bits2);
+  const uint8_t* row1 = jb->packed + o * s1;
+  const uint8_t* row2 = jb->packed + jb->n * s1 + o * s2;
+  float s = jb->scale ? (float)oracle_f16_to_f64(jb->scale[o]) : 1.0f;
+  for (int64_t j = 0; j < nv; ++j) {
+    uint32_t i1 = read_field(row1, j, jb->bits1);
+    uint32_t i2 = jb->bits2 ? read_field(row2, j, jb->bits2) : 0;
+    for (int t = 0; t < jb->v; ++t) {
+      int64_t col = j * jb->v + t;
+      if (col >= jb->in_features) break; /* tail lanes of the last vector are dropped */
+      float c1 = (float)oracle_f16_to_f64(jb->cb1[(int64_t)i1 * jb->v + t]);
+      float w;
+      if (jb->bits2) {
+        float c2 = (float)oracle_f16_to_f64(jb->cb2[(int64_t)i2 * jb->v + t]);
+        w = c1 + c2;
+      } else {
+        w = c1; /* no residual: no add, so a -0 centroid stays -0 */
+      }
+      if (jb->scale) w = w * s;
+      wrow[col] = w;
+    }
+  }
+}
+
+static void* worker(void* arg) {
+  job_t* jb = (job_t*)arg;
+  float* wrow = NULL;
+  if (jb->y_out) {
+    wrow = (float*)malloc(sizeof(float) * (size_t)(jb->in_features > 0 ? jb->in_features : 1));
+    if (!wrow) return (void*)1;
+  }
+  for (int64_t r = jb->begin; r < jb->end; ++r) {
+    int64_t o = jb->rows ? jb->rows[r] : r;
+    if (!jb->y_out) {
+      dequant_row(jb, o, jb->w_out + r * jb->in_features);
+      continue;
+    }
+    dequant_row(jb, o, wrow);
+    double b = jb->bias ? oracle_f16_to_f64(jb->bias[o]) : 0.0;
+    for (int64_t m = 0; m < jb->M; ++m) {
+      const double* xm = jb->xd + m * jb->in_features;
+      double acc = 0.0;
+      for (int64_t col = 0; col < jb->in_features; ++col) acc += xm[col] * (double)wrow[col];
+      jb->y_out[m * jb->nrows + r] = acc + b;
+    }
+  }
+  free(wrow);
+  return NULL;
+}
+
+static int run_jobs(job_t* proto, int nthreads) {
+  if (nthreads <= 0) {
+    long c = sysconf(_SC_NPROCESSORS_ONLN);
+    nthreads = c > 0 ? (int)c : 1;
+  }
+  if (nthreads > 256) nthreads = 256;
+  if ((int64_t)nthreads > proto->nrows) nthreads = proto->nrows > 0 ? (int)proto->nrows : 1;
+  job_t jobs[256];
+  pthread_t th[256];
+  int started[256];
+  int64_t per = (proto->nrows + nthreads - 1) / nthreads;
+  int rc = ORACLE_OK;
+  for (int t = 0; t < nthreads; ++t) {
+    jobs[t] = *proto;
+    jobs[t].begin = t * per;
+    jobs[t].end = (t + 1) * per < proto->nrows ? (t + 1) * per : proto->nrows;
+    started[t] = 0;
+    if (jobs[t].begin >= jobs[t].end) continue;
+    if (nthreads == 1) {
+      if (worker(&jobs[t])) rc = ORACLE_BAD_ARGS;
+    } else if (pthread_create(&th[t], NULL, worker, &jobs[t]) == 0) {
+      started[t] = 1;
+    } else if (worker(&jobs[t])) {
+      rc = ORACLE_BAD_ARGS;
+    }
+  }
+  for (int t = 0; t < nthreads; ++t) {
+    if (!started[t]) continue;
+    void* ret = NULL;
+    pthread_join(th[t], &ret);
+    if (ret) rc = ORACLE_BAD_ARGS;
+  }
+  return rc;
+}
+
+static int check_rows(int64_t n, const int64_t* rows, int64_t nrows) {
+  if (!rows) return nrows == n;
+  for (int64_t r = 0; r < nrows; ++r)
+    if (rows[r] < 0 || rows[r] >= n) return 0;
+  return 1;
+}
+
+int oracle_dequant_rows(int64_t n, int64_t in_features, int v, int bits1, int bits2, const uint8_t* packed,
+                        const uint16_t* cb1, const uint16_t* cb2, const uint16_t* scale, const int64_t* rows,
+                        int64_t nrows, float* w, int nthreads) {
+  if (!valid_desc(n, in_features, v, bits1, bits2)) return ORACLE_BAD_ARGS;
+  if (!rows) nrows = n;
+  if (!check_rows(n, rows, nrows)) return ORACLE_BAD_ARGS;
+  if (nrows == 0 || in_features == 0) return ORACLE_OK;
+  if (!packed || !cb1 || (bits2 && !cb2) || !w) return ORACLE_BAD_ARGS;
+  job_t proto;
+  memset(&proto, 0, sizeof proto);
+  proto.n = n;
+  proto.in_features = in_features;
+  proto.v = v;
+  proto.bits1 = bits1;
+  proto.bits2 = bits2;
+  proto.packed = packed;
+  proto.cb1 = cb1;
+  proto.cb2 = cb2;
+  proto.scale = scale;
+  proto.rows = rows;
+  proto.nrows = nrows;
+  proto.w_out = w;
+  return run_jobs(&proto, nthreads);
+}
+
+int oracle_forward_rows(int64_t n, int64_t in_features, int v, int bits1, int bits2, const uint8_t* packed,
+                        const uint16_t* cb1, const uint16_t* cb2, const uint16_t* scale, const uint16_t* bias,
+                        const uint16_t* x, int x_is_bf16, int64_t M, const int64_t* rows, int64_t nrows,
+                        double* y, int nthreads) {
+  if (!valid_desc(n, in_features, v, bits1, bits2) || M < 0) return ORACLE_BAD_ARGS;
+  if (!rows) nrows = n;
+  if (!check_rows(n, rows, nrows)) return ORACLE_BAD_ARGS;
+  if (nrows == 0 || M == 0) return ORACLE_OK;
+  if (!y) return ORACLE_BAD_ARGS;
+  if (in_features > 0 && (!packed || !cb1 || (bits2 && !cb2) || !x)) return ORACLE_BAD_ARGS;
+  double* xd = (double*)malloc(sizeof(double) * (size_t)(M * in_features > 0 ? M * in_features : 1));
+  if (!xd) return ORACLE_BAD_ARGS;
+  for (int64_t i = 0; i < M * in_features; ++i)
+    xd[i] = x_is_bf16 ? oracle_bf16_to_f64(x[i]) : oracle_f16_to_f64(x[i]);
+  job_t proto;
+  memset(&proto, 0, sizeof proto);
+  proto.n = n;
+  proto.in_features = in_features;
+  proto.v = v;
+  proto.bits1 = bits1;
+  proto.bits2 = bits2;
+  proto.packed = packed;
+  proto.cb1 = cb1;
+  proto.cb2 = cb2;
+  proto.scale = scale;
+  proto.bias = bias;
+  proto.xd = xd;
+  proto.M = M;
+  proto.rows = rows;
+  proto.nrows = nrows;
+  proto.y_out = y;
+  int rc = run_jobs(&proto, nthreads);
+  free(xd);
+  return rc;
+}

@@ -1,0 +1,77 @@
+/*
+ * CPU oracle for the VQ dequantize-and-multiply path.  TEST INFRASTRUCTURE ONLY:
+ * nothing on the product path may include, link or call this; only tests, the
+ * smoke check and the CPU-baseline leg of the benchmark use it.  It shares no code,
+ * header, table or constant with the HIP library.
+ *
+ * What it computes (plain definitions, written out slowly):
+ *   - index layout: per output row, each codebook's indices form one LSB-first
+ *     bitstream of nv = ceil(in/v) fields of B bits, the row padded with zero bits
+ *     to a multiple of 16 bytes; the main stream for all rows comes first, the
+ *     residual stream (if any) after it.  The pages are silent on packing (the VPTQ
+ *     guide stores whole uint8/int16 tensors, the production-VQ post speaks only of
+ *     "a 16-bit uint per 8 weights"); this bit order is the reading taken.
+ *   - dequant (VPTQ guide, "Step 2 ... dequantize" and the residual-decode formula
+ *     of "2. Multi-Stage Residual Vector Quantization"): w = C1[i1] + C2[i2], summed in
+ *     fp32, then times the per-output-channel scale in fp32.
+ *   - product (VPTQ guide, "Step 3: Fused Low-Bit VPTQ Linear Layer"): y = x W^T (+ bias),
+ *     accumulated in fp64 in ascending column order.
+ */
+#ifndef VQ_ORACLE_H
+#define VQ_ORACLE_H
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define ORACLE_OK 0
+#define ORACLE_BAD_ARGS (-1)
+#define ORACLE_BUFFER_SMALL (-2)
+#define ORACLE_INDEX_RANGE (-3)
+#define ORACLE_PAD_NONZERO 1 /* unpack: a pad bit was set (indices are still written) */
+
+/* Exact decode of IEEE binary16 / bfloat16 bit patterns (values returned in double). */
+double oracle_f16_to_f64(uint16_t h);
+double oracle_bf16_to_f64(uint16_t b);
+/* Round-to-nearest-even of a finite double holding an fp32 value to binary16 / bfloat16 bits. */
+uint16_t oracle_f64_to_f16_rne(double x);
+uint16_t oracle_f64_to_bf16_rne(double x);
+
+/* Bytes of one row's bitstream for nv fields of `bits` bits (0 if bits == 0). */
+int64_t oracle_row_stride(int64_t in_features, int v, int bits);
+/* Total packed bytes; -1 on invalid arguments. */
+int64_t oracle_packed_bytes(int64_t n, int64_t in_features, int v, int bits1, int bits2);
+
+/* Pack idx1 [n][nv] (and idx2 when bits2 > 0) bit by bit. */
+int oracle_pack(int64_t n, int64_t in_features, int v, int bits1, int bits2, const uint32_t* idx1,
+                const uint32_t* idx2, uint8_t* out, int64_t out_bytes);
+/* Unpack bit by bit; returns ORACLE_PAD_NONZERO when any pad bit is 1. */
+int oracle_unpack(int64_t n, int64_t in_features, int v, int bits1, int bits2, const uint8_t* packed,
+                  uint32_t* idx1, uint32_t* idx2);
+
+/*
+ * Dequantize rows (rows == NULL: all n rows, in order) into w[nrows][in_features] fp32.
+ * cb1: fp16 bits [2^bits1][v]; cb2: fp16 bits [2^bits2][v] or NULL when bits2 == 0;
+ * scale: fp16 bits [n] or NULL (scale 1, multiply skipped).
+ */
+int oracle_dequant_rows(int64_t n, int64_t in_features, int v, int bits1, int bits2, const uint8_t* packed,
+                        const uint16_t* cb1, const uint16_t* cb2, const uint16_t* scale, const int64_t* rows,
+                        int64_t nrows, float* w, int nthreads);
+
+/*
+ * y[m][r] (fp64, [M][nrows]) = sum_col x[m][col] * w[row_r][col] (+ bias[row_r]).
+ * x: [M][in_features] fp16 bits (x_is_bf16 == 0) or bf16 bits (x_is_bf16 == 1);
+ * bias: fp16 bits [n] or NULL.
+ */
+int oracle_forward_rows(int64_t n, int64_t in_features, int v, int bits1, int bits2, const uint8_t* packed,
+                        const uint16_t* cb1, const uint16_t* cb2, const uint16_t* scale, const uint16_t* bias,
+                        const uint16_t* x, int x_is_bf16, int64_t M, const int64_t* rows, int64_t nrows,
+                        double* y, int nthreads);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,128 @@
+"""Seeded synthetic inputs for the VQ dequantize-and-multiply path.
+
+This module only draws random numbers and rounds them to the storage formats; it holds
+none of the method's arithmetic (no packing, no decode, no product).  Both the CPU
+oracle and the HIP library are fed from here.
+
+Workloads (shapes from the pages' 8B / 70B-class layers; the pages print no layer
+dimensions, so the sizes are the usual LLaMA-3 ones):
+
+  tiny       256 x 256,            v=8, K1=256                 (1 bit/weight), M=1,   x fp16
+  dec4k      4096 x 4096,          v=8, K1=65536               (2 bits),       M=1,   x fp16
+  dec4k_res  4096 x 4096,          v=8, K1=65536 + K2=256      (3 bits),       M in {1,4,16}, fp16
+  mlp8b      up 14336x4096 / down 4096x14336, v=6, K1=K2=4096  (4 bits),       M in {1,4,16}, fp16
+  l70b       up 28672x8192 / down 8192x28672, v=8, K1=65536 + K2=256 (3 bits), M in {1,8,32,128,256}, bf16
+
+Distributions: main centroids 0.02*N(0,1) (the weight scale of the VPTQ guide's
+verification harness), residual centroids 0.005*N(0,1), both rounded to fp16;
+indices uniform on [0, 2^B); per-channel scale U(0.5, 1.5) in fp16; x ~ N(0,1) in
+fp16 or bf16 (round-to-nearest-even).  Seeds: numpy PCG64 seeded with
+[42, workload, layer, copy, tensor], tensor ids 0 c1, 1 c2, 2 idx1, 3 idx2, 4 scale,
+5 x, 6 bias.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+SEED = 42
+T_C1, T_C2, T_IDX1, T_IDX2, T_SCALE, T_X, T_BIAS = range(7)
+
+
+@dataclass(frozen=True)
+class Workload:
+    key: str
+    wid: int
+    layers: tuple  # ((N, IN), ...)
+    v: int
+    bits1: int
+    bits2: int
+    ms: tuple
+    x_dtype: str  # "f16" | "bf16"
+    sigma1: float = 0.02
+    sigma2: float = 0.005
+    labels: tuple = field(default=("layer",))
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 0, ((256, 256),), 8, 8, 0, (1,), "f16"),
+    "dec4k": Workload("dec4k", 1, ((4096, 4096),), 8, 16, 0, (1,), "f16"),
+    "dec4k_res": Workload("dec4k_res", 2, ((4096, 4096),), 8, 16, 8, (1, 4, 16), "f16"),
+    "mlp8b": Workload("mlp8b", 3, ((14336, 4096), (4096, 14336)), 6, 12, 12, (1, 4, 16), "f16",
+                      labels=("up", "down")),
+    "l70b": Workload("l70b", 4, ((28672, 8192), (8192, 28672)), 8, 16, 8, (1, 8, 32, 128, 256), "bf16",
+                     labels=("up", "down")),
+}
+
+
+def rng(workload: int, layer: int, copy: int, tensor: int) -> np.random.Generator:
+    return np.random.default_rng([SEED, workload, layer, copy, tensor])
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); returns uint16 bits."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def f16_bits(a: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def num_vectors(in_features: int, v: int) -> int:
+    return (in_features + v - 1) // v
+
+
+def codebook(g: np.random.Generator, k: int, v: int, sigma: float) -> np.ndarray:
+    """fp16 bits [k, v]."""
+    return f16_bits(g.standard_normal((k, v), dtype=np.float32) * np.float32(sigma))
+
+
+def indices(g: np.random.Generator, n: int, nv: int, bits: int) -> np.ndarray:
+    return g.integers(0, 1 << bits, size=(n, nv), dtype=np.uint32)
+
+
+def scales(g: np.random.Generator, n: int) -> np.ndarray:
+    return f16_bits(g.uniform(0.5, 1.5, size=n).astype(np.float32))
+
+
+def activations(g: np.random.Generator, m: int, in_features: int, dtype: str) -> np.ndarray:
+    """uint16 bits [m, in_features] of fp16 or bf16 N(0,1) samples."""
+    a = g.standard_normal((m, in_features), dtype=np.float32)
+    return f32_to_bf16_bits(a) if dtype == "bf16" else f16_bits(a)
+
+
+def make_layer(n: int, in_features: int, v: int, bits1: int, bits2: int, *, wid: int = 99, layer: int = 0,
+               copy: int = 0, sigma1: float = 0.02, sigma2: float = 0.005, with_scale: bool = True,
+               with_bias: bool = False) -> dict:
+    """One synthetic quantized layer: indices (uint32 [n, nv]), fp16-bit codebooks, scale, bias."""
+    nv = num_vectors(in_features, v)
+    out = {
+        "n": n, "in_features": in_features, "v": v, "bits1": bits1, "bits2": bits2,
+        "cb1": codebook(rng(wid, layer, copy, T_C1), 1 << bits1, v, sigma1),
+        "idx1": indices(rng(wid, layer, copy, T_IDX1), n, nv, bits1),
+        "cb2": None, "idx2": None, "scale": None, "bias": None,
+    }
+    if bits2:
+        out["cb2"] = codebook(rng(wid, layer, copy, T_C2), 1 << bits2, v, sigma2)
+        out["idx2"] = indices(rng(wid, layer, copy, T_IDX2), n, nv, bits2)
+    if with_scale:
+        out["scale"] = scales(rng(wid, layer, copy, T_SCALE), n)
+    if with_bias:
+        out["bias"] = f16_bits(rng(wid, layer, copy, T_BIAS).standard_normal(n).astype(np.float32) * 0.1)
+    return out
+
+
+def workload_layer(key: str, layer: int = 0, copy: int = 0) -> dict:
+    w = WORKLOADS[key]
+    n, in_features = w.layers[layer]
+    return make_layer(n, in_features, w.v, w.bits1, w.bits2, wid=w.wid, layer=layer, copy=copy,
+                      sigma1=w.sigma1, sigma2=w.sigma2)
+
+
+def workload_x(key: str, layer: int, m: int) -> np.ndarray:
+    w = WORKLOADS[key]
+    _, in_features = w.layers[layer]
+    return activations(rng(w.wid, layer, 0, T_X), m, in_features, w.x_dtype)

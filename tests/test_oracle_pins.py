@@ -1,0 +1,394 @@
+"""Pins for the CPU oracle: each test ties it to something other than itself.
+
+- number formats: every fp16 / bf16 bit pattern against numpy / torch decoders, and
+  round-to-nearest-even against numpy / torch converters;
+- the index layout: the pages' bit-rate examples, hand-derived vectors, and numpy's own
+  little-endian ``packbits``;
+- dequant: codebooks that turn the decode into a known matrix (bit, fp16-identity and
+  one-hot books), brute force over every index matrix of a tiny layer, and exact
+  invariants (codebook permutation, commutation of the two books, zero residual);
+- product: an independent numpy matmul, linearity, row-subset and thread-count
+  independence.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ------------------------------------------------------------------ number formats
+
+
+def test_f16_decode_every_pattern(oracle_mod):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = oracle_mod.f16_to_f64(bits)
+    ref = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(ours[~nan]), np.signbit(ref[~nan]))
+
+
+def test_bf16_decode_every_pattern(oracle_mod):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = oracle_mod.bf16_to_f64(bits)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(ours[~nan]), np.signbit(ref[~nan]))
+
+
+def _rounding_probe_values(seed):
+    g = np.random.default_rng(seed)
+    # wide exponent sweep, subnormal and overflow regions, and exact midpoints
+    a = (g.standard_normal(4000) * np.exp2(g.integers(-30, 20, 4000))).astype(np.float32)
+    h = g.integers(0, 0x7BFF, 2000, dtype=np.uint32).astype(np.uint16).view(np.float16).astype(np.float32)
+    ulp = np.spacing(h.astype(np.float16)).astype(np.float32)
+    mids = (h + ulp / np.float32(2)).astype(np.float32)  # exact ties for fp16
+    edges = np.array([65504, 65519.996, 65520, 65535, 70000, 6.1035156e-05, 5.9604645e-08, 2.9802322e-08,
+                      2.9802326e-08, 0.0, -0.0, 1e-30, -3.0e38], dtype=np.float32)
+    vals = np.concatenate([a, mids, -mids, edges]).astype(np.float32)
+    return vals[np.isfinite(vals)]
+
+
+def test_f16_round_nearest_even_matches_numpy(oracle_mod):
+    vals = _rounding_probe_values(1)
+    ours = oracle_mod.f64_to_f16_rne(vals.astype(np.float64))
+    with np.errstate(over="ignore"):
+        ref = vals.astype(np.float16).view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+def test_bf16_round_nearest_even_matches_torch(oracle_mod):
+    g = np.random.default_rng(2)
+    a = (g.standard_normal(4000) * np.exp2(g.integers(-140, 120, 4000))).astype(np.float32)
+    b = g.integers(0, 0x7F7F, 2000, dtype=np.uint32).astype(np.uint16)
+    base = torch.from_numpy(b.view(np.int16).copy()).view(torch.bfloat16).to(torch.float32).numpy()
+    ties = (base.view(np.uint32) | np.uint32(0x8000)).view(np.float32)  # exactly half-way to the next bf16
+    edges = np.array([3.3895314e38, 3.3961776e38, 3.4028235e38, 1.1754944e-38, 1e-45, 0.0, -0.0], dtype=np.float32)
+    vals = np.concatenate([a, ties, -ties, edges])
+    vals = vals[np.isfinite(vals)]
+    ours = oracle_mod.f64_to_bf16_rne(vals.astype(np.float64))
+    ref = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+
+
+# ------------------------------------------------------------------ layout and sizes
+
+
+def test_bitrate_examples_from_pages(oracle_mod):
+    gold = _golden("bitrate_examples.json")
+    for ex in gold["examples"]:
+        v, b1, b2 = ex["v"], ex["bits1"], ex["bits2"]
+        # a layer whose rows hold a whole number of 128-bit units: packed size is exact
+        n, in_features = 64, v * 128
+        nbytes = oracle_mod.packed_bytes(n, in_features, v, b1, b2)
+        assert nbytes * 8 / (n * in_features) == pytest.approx(ex["bits_index"], abs=0), ex["name"]
+        if "overhead_below" in ex:
+            n2, in2 = ex["overhead_layer"]
+            books = (1 << b1) * v * 16 + ((1 << b2) * v * 16 if b2 else 0)
+            overhead = books / (n2 * in2)
+            assert overhead < ex["overhead_below"]
+            beff = oracle_mod.packed_bytes(n2, in2, v, b1, b2) * 8 / (n2 * in2) + overhead
+            assert beff == pytest.approx(ex["bits_index"] + overhead, abs=1e-12)
+    for cb in gold["codebook_bytes"]:
+        assert cb["k"] * cb["v"] * 2 * cb["books"] == cb["bytes"], cb["name"]
+
+
+def test_harness_closed_forms(oracle_mod):
+    h = _golden("bitrate_examples.json")["harness_closed_forms"]
+    n, i, v = h["n"], h["in_features"], h["v"]
+    packed = oracle_mod.packed_bytes(n, i, v, h["bits1"], h["bits2"])
+    books = 2 * (1 << 8) * v * 2
+    assert n * i * 2 == h["fp16_bytes"]
+    assert packed + books == h["quant_bytes"]
+    assert round(h["fp16_bytes"] / h["quant_bytes"], 3) == h["compression"]
+    assert round(h["quant_bytes"] * 8 / (n * i), 4) == h["bits_per_param"]
+
+
+@pytest.mark.parametrize("key,expected", [
+    ("tiny", [8192]), ("dec4k", [4194304]), ("dec4k_res", [6291456]),
+    ("mlp8b", [29818880, 29491200]), ("l70b", [88080384, 88080384]),
+])
+def test_workload_packed_sizes(oracle_mod, key, expected):
+    w = synth.WORKLOADS[key]
+    got = [oracle_mod.packed_bytes(n, i, w.v, w.bits1, w.bits2) for (n, i) in w.layers]
+    assert got == expected
+    for (n, i), nb in zip(w.layers, got):
+        bits = nb * 8 / (n * i)
+        target = (w.bits1 + w.bits2) / w.v
+        assert target <= bits < target * 1.02  # exact when rows fill whole 128-bit units, else padding only
+
+
+def test_pack_hand_vectors(oracle_mod):
+    for vec in _golden("pack_vectors.json")["vectors"]:
+        b, fields = vec["bits"], vec["fields"]
+        nv = len(fields)
+        packed = oracle_mod.pack(1, nv, 1, b, 0, np.array([fields], dtype=np.uint32))
+        want = bytes.fromhex(vec["bytes_hex"])
+        assert len(packed) % 16 == 0
+        assert bytes(packed[: len(want)]) == want, vec
+        assert not packed[len(want):].any()
+        back, _, pad_ok = oracle_mod.unpack(1, nv, 1, b, 0, packed)
+        assert pad_ok and list(back[0]) == fields
+
+
+def _packbits_reference(idx, bits, row_bytes):
+    """Independent construction with numpy: expand every field to its bits, LSB first, then packbits."""
+    n, nv = idx.shape
+    shifts = np.arange(bits, dtype=np.uint32)
+    bitmat = ((idx[:, :, None] >> shifts) & 1).astype(np.uint8).reshape(n, nv * bits)
+    pad = row_bytes * 8 - nv * bits
+    bitmat = np.concatenate([bitmat, np.zeros((n, pad), dtype=np.uint8)], axis=1)
+    return np.packbits(bitmat, axis=1, bitorder="little").reshape(-1)
+
+
+@pytest.mark.parametrize("n,in_features,v,b1,b2", [
+    (3, 40, 8, 16, 8), (5, 37, 6, 12, 12), (2, 100, 3, 5, 0), (4, 64, 8, 8, 0), (1, 7, 1, 13, 3),
+    (7, 200, 16, 16, 16), (2, 13, 4, 1, 2), (3, 96, 6, 12, 0),
+])
+def test_pack_matches_numpy_packbits(oracle_mod, n, in_features, v, b1, b2):
+    g = np.random.default_rng(n * 1000 + in_features)
+    nv = oracle_mod.num_vectors(in_features, v)
+    i1 = g.integers(0, 1 << b1, (n, nv), dtype=np.uint32)
+    i2 = g.integers(0, 1 << b2, (n, nv), dtype=np.uint32) if b2 else None
+    packed = oracle_mod.pack(n, in_features, v, b1, b2, i1, i2)
+    s1 = oracle_mod.row_stride(in_features, v, b1)
+    ref = _packbits_reference(i1, b1, s1)
+    if b2:
+        ref = np.concatenate([ref, _packbits_reference(i2, b2, oracle_mod.row_stride(in_features, v, b2))])
+    assert np.array_equal(packed, ref)
+    a1, a2, pad_ok = oracle_mod.unpack(n, in_features, v, b1, b2, packed)
+    assert pad_ok and np.array_equal(a1, i1)
+    if b2:
+        assert np.array_equal(a2, i2)
+
+
+def test_pack_rejects_out_of_range_and_small_buffer(oracle_mod):
+    lib = oracle_mod._load()
+    idx = np.array([[0, 8]], dtype=np.uint32)
+    out = np.zeros(64, dtype=np.uint8)
+    rc = lib.oracle_pack(1, 2, 1, 3, 0, oracle_mod._ptr(idx), None, oracle_mod._ptr(out), 64)
+    assert rc == oracle_mod.INDEX_RANGE
+    idx = np.array([[0, 7]], dtype=np.uint32)
+    rc = lib.oracle_pack(1, 2, 1, 3, 0, oracle_mod._ptr(idx), None, oracle_mod._ptr(out), 15)
+    assert rc == oracle_mod.BUFFER_SMALL
+
+
+def test_unpack_flags_nonzero_pad(oracle_mod):
+    packed = oracle_mod.pack(1, 3, 1, 4, 0, np.array([[1, 2, 3]], dtype=np.uint32))
+    packed = packed.copy()
+    packed[15] |= 0x80
+    _, _, pad_ok = oracle_mod.unpack(1, 3, 1, 4, 0, packed)
+    assert not pad_ok
+
+
+# ------------------------------------------------------------------ dequant pins
+
+
+def test_bit_codebook_reduces_to_plain_matmul(oracle_mod):
+    """v = 8, K = 256, C[k][t] = bit t of k: W is an arbitrary 0/1 matrix."""
+    n, in_features, v = 24, 256, 8
+    g = np.random.default_rng(7)
+    wbits = g.integers(0, 2, (n, in_features)).astype(np.uint8)
+    idx = np.packbits(wbits.reshape(n, in_features // 8, 8), axis=2, bitorder="little").reshape(n, -1)
+    cb = ((np.arange(256)[:, None] >> np.arange(8)[None, :]) & 1).astype(np.float16)
+    packed = oracle_mod.pack(n, in_features, v, 8, 0, idx.astype(np.uint32))
+    w = oracle_mod.dequant(n, in_features, v, 8, 0, packed, cb)
+    assert np.array_equal(w, wbits.astype(np.float32))
+    x = synth.activations(g, 3, in_features, "f16")
+    y = oracle_mod.forward(n, in_features, v, 8, 0, packed, cb, None, None, None, x, False, 3)
+    ref = x.view(np.float16).astype(np.float64) @ wbits.T.astype(np.float64)
+    assert np.array_equal(y, ref)  # sums of fp16 values in fp64 are exact here
+
+
+def test_fp16_identity_codebook_reproduces_any_matrix(oracle_mod):
+    """v = 1, K = 65536, C[k] = the fp16 number with bit pattern k."""
+    n, in_features = 16, 96
+    g = np.random.default_rng(8)
+    wbits = g.integers(0, 65536, (n, in_features), dtype=np.uint32).astype(np.uint16)
+    finite = np.isfinite(wbits.view(np.float16))
+    wbits[~finite] = 0x3C00
+    cb = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(65536, 1)
+    packed = oracle_mod.pack(n, in_features, 1, 16, 0, wbits.astype(np.uint32))
+    w = oracle_mod.dequant(n, in_features, 1, 16, 0, packed, cb)
+    want = wbits.view(np.float16).astype(np.float32)
+    assert np.array_equal(w.view(np.uint32), want.view(np.uint32))  # bit-exact, -0 included
+    x = synth.activations(g, 2, in_features, "bf16")
+    xf = torch.from_numpy(x.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    y = oracle_mod.forward(n, in_features, 1, 16, 0, packed, cb, None, None, None, x, True, 2)
+    ref = xf @ want.astype(np.float64).T
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
+def test_one_hot_codebook_with_scale(oracle_mod):
+    """K = v = 8 (B = 3), C[k] = e_k: W[o, 8j + t] = scale[o] if idx[o, j] == t else 0."""
+    n, in_features, v = 10, 80, 8
+    g = np.random.default_rng(9)
+    idx = g.integers(0, 8, (n, in_features // 8), dtype=np.uint32)
+    cb = np.eye(8, dtype=np.float16)
+    scale = synth.scales(g, n)
+    packed = oracle_mod.pack(n, in_features, v, 3, 0, idx)
+    w = oracle_mod.dequant(n, in_features, v, 3, 0, packed, cb, None, scale)
+    s = scale.view(np.float16).astype(np.float32)
+    want = np.zeros((n, in_features), dtype=np.float32)
+    for o in range(n):
+        for j in range(in_features // 8):
+            want[o, 8 * j + idx[o, j]] = s[o]
+    assert np.array_equal(w, want)
+
+
+def test_brute_force_every_index_matrix_tiny_layer(oracle_mod):
+    """N = 2, IN = 4, v = 2, B1 = 2, B2 = 1: all 4^4 * 2^4 index matrices."""
+    n, in_features, v = 2, 4, 2
+    g = np.random.default_rng(10)
+    cb1 = synth.codebook(g, 4, 2, 0.5)
+    cb2 = synth.codebook(g, 2, 2, 0.1)
+    scale = synth.scales(g, n)
+    bias = synth.f16_bits(g.standard_normal(n).astype(np.float32))
+    x = synth.activations(g, 3, in_features, "f16")
+    c1 = cb1.view(np.float16).astype(np.float32)
+    c2 = cb2.view(np.float16).astype(np.float32)
+    s = scale.view(np.float16).astype(np.float32)
+    xf = x.view(np.float16).astype(np.float64)
+    bf = bias.view(np.float16).astype(np.float64)
+    count = 0
+    for a in range(4 ** 4):
+        i1 = np.array([(a >> (2 * k)) & 3 for k in range(4)], dtype=np.uint32).reshape(2, 2)
+        for b in range(2 ** 4):
+            i2 = np.array([(b >> k) & 1 for k in range(4)], dtype=np.uint32).reshape(2, 2)
+            packed = oracle_mod.pack(n, in_features, v, 2, 1, i1, i2)
+            w = oracle_mod.dequant(n, in_features, v, 2, 1, packed, cb1, cb2, scale)
+            dense = (c1[i1.reshape(-1)] + c2[i2.reshape(-1)]).reshape(n, in_features)  # numpy fp32 adds
+            want = dense * s[:, None]  # numpy fp32 multiply
+            assert np.array_equal(w.view(np.uint32), want.view(np.uint32))
+            if a % 17 == 0:
+                y = oracle_mod.forward(n, in_features, v, 2, 1, packed, cb1, cb2, scale, bias, x, False, 3)
+                ref = xf @ want.astype(np.float64).T + bf[None, :]
+                assert np.allclose(y, ref, rtol=1e-14, atol=1e-15)
+            count += 1
+    assert count == 4096
+
+
+def _random_layer(oracle_mod, seed, n, in_features, v, b1, b2):
+    lay = synth.make_layer(n, in_features, v, b1, b2, wid=50, copy=seed)
+    packed = oracle_mod.pack(n, in_features, v, b1, b2, lay["idx1"], lay["idx2"])
+    return lay, packed
+
+
+def test_codebook_permutation_invariance(oracle_mod):
+    n, in_features, v, b1, b2 = 12, 70, 6, 5, 4
+    lay, packed = _random_layer(oracle_mod, 1, n, in_features, v, b1, b2)
+    w = oracle_mod.dequant(n, in_features, v, b1, b2, packed, lay["cb1"], lay["cb2"], lay["scale"])
+    g = np.random.default_rng(11)
+    p1 = g.permutation(1 << b1)
+    p2 = g.permutation(1 << b2)
+    cb1p = np.empty_like(lay["cb1"]); cb1p[p1] = lay["cb1"]
+    cb2p = np.empty_like(lay["cb2"]); cb2p[p2] = lay["cb2"]
+    packed_p = oracle_mod.pack(n, in_features, v, b1, b2, p1[lay["idx1"]].astype(np.uint32),
+                               p2[lay["idx2"]].astype(np.uint32))
+    wp = oracle_mod.dequant(n, in_features, v, b1, b2, packed_p, cb1p, cb2p, lay["scale"])
+    assert np.array_equal(w.view(np.uint32), wp.view(np.uint32))
+
+
+def test_swapping_books_commutes(oracle_mod):
+    n, in_features, v, b = 9, 64, 8, 6
+    lay, packed = _random_layer(oracle_mod, 2, n, in_features, v, b, b)
+    w = oracle_mod.dequant(n, in_features, v, b, b, packed, lay["cb1"], lay["cb2"], lay["scale"])
+    packed_s = oracle_mod.pack(n, in_features, v, b, b, lay["idx2"], lay["idx1"])
+    ws = oracle_mod.dequant(n, in_features, v, b, b, packed_s, lay["cb2"], lay["cb1"], lay["scale"])
+    assert np.array_equal(w.view(np.uint32), ws.view(np.uint32))
+
+
+def test_zero_residual_equals_no_residual(oracle_mod):
+    n, in_features, v = 8, 48, 8
+    lay, packed = _random_layer(oracle_mod, 3, n, in_features, v, 8, 4)
+    cb1 = lay["cb1"].copy()
+    cb1[:16] = np.uint16(0x8000)  # -0 centroids: the add turns them into +0
+    zero_book = np.zeros_like(lay["cb2"])
+    w_res = oracle_mod.dequant(n, in_features, v, 8, 4, packed, cb1, zero_book, lay["scale"])
+    packed1 = oracle_mod.pack(n, in_features, v, 8, 0, lay["idx1"])
+    w_one = oracle_mod.dequant(n, in_features, v, 8, 0, packed1, cb1, None, lay["scale"])
+    assert np.array_equal(w_res, w_one)
+    neg0 = (w_one == 0) & np.signbit(w_one)
+    assert neg0.any()
+    assert not np.signbit(w_res[neg0]).any()
+    assert np.array_equal(w_res.view(np.uint32)[~neg0], w_one.view(np.uint32)[~neg0])
+
+
+def test_unit_scale_equals_no_scale(oracle_mod):
+    n, in_features, v = 6, 40, 8
+    lay, packed = _random_layer(oracle_mod, 4, n, in_features, v, 7, 3)
+    ones = np.full(n, 0x3C00, dtype=np.uint16)
+    a = oracle_mod.dequant(n, in_features, v, 7, 3, packed, lay["cb1"], lay["cb2"], ones)
+    b = oracle_mod.dequant(n, in_features, v, 7, 3, packed, lay["cb1"], lay["cb2"], None)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_tail_lanes_dropped(oracle_mod):
+    """IN not a multiple of v: the last vector contributes only its first IN mod v lanes."""
+    n, in_features, v = 3, 20, 6  # nv = 4, last vector keeps 2 lanes
+    lay, packed = _random_layer(oracle_mod, 5, n, in_features, v, 4, 0)
+    w = oracle_mod.dequant(n, in_features, v, 4, 0, packed, lay["cb1"], None, None)
+    c = lay["cb1"].view(np.float16).astype(np.float32)
+    full = c[lay["idx1"].reshape(-1)].reshape(n, 4 * v)
+    assert np.array_equal(w, full[:, :in_features])
+
+
+# ------------------------------------------------------------------ product pins
+
+
+def test_forward_matches_numpy_matmul_and_is_linear(oracle_mod):
+    n, in_features, v, b1, b2 = 33, 300, 6, 9, 5
+    lay, packed = _random_layer(oracle_mod, 6, n, in_features, v, b1, b2)
+    w = oracle_mod.dequant(n, in_features, v, b1, b2, packed, lay["cb1"], lay["cb2"], lay["scale"])
+    g = np.random.default_rng(12)
+    x1 = synth.f16_bits(g.integers(-8, 8, (2, in_features)).astype(np.float32))
+    x2 = synth.f16_bits(g.integers(-8, 8, (2, in_features)).astype(np.float32))
+    x12 = synth.f16_bits(x1.view(np.float16).astype(np.float32) + x2.view(np.float16).astype(np.float32))
+    f = lambda xb: oracle_mod.forward(n, in_features, v, b1, b2, packed, lay["cb1"], lay["cb2"], lay["scale"], None,
+                                      xb, False, 2)
+    y1, y2, y12 = f(x1), f(x2), f(x12)
+    ref = x1.view(np.float16).astype(np.float64) @ w.astype(np.float64).T
+    tol = 1e-12 * np.abs(ref).max()
+    assert np.allclose(y1, ref, rtol=0, atol=tol)
+    assert np.allclose(y12, y1 + y2, rtol=0, atol=tol)
+
+
+def test_rows_subset_and_thread_count(oracle_mod):
+    n, in_features, v, b1, b2 = 40, 128, 8, 10, 6
+    lay, packed = _random_layer(oracle_mod, 7, n, in_features, v, b1, b2)
+    x = synth.activations(np.random.default_rng(13), 3, in_features, "bf16")
+    args = (n, in_features, v, b1, b2, packed, lay["cb1"], lay["cb2"], lay["scale"], None, x, True, 3)
+    y_all = oracle_mod.forward(*args, nthreads=1)
+    y_mt = oracle_mod.forward(*args, nthreads=8)
+    assert np.array_equal(y_all, y_mt)
+    rows = np.array([39, 0, 17, 17, 5])
+    y_sub = oracle_mod.forward(*args, rows=rows, nthreads=3)
+    assert np.array_equal(y_sub, y_all[:, rows])
+
+
+def test_bias_and_empty_shapes(oracle_mod):
+    n, in_features, v = 4, 0, 8
+    bias = synth.f16_bits(np.array([1.5, -2.0, 0.25, 0.0], dtype=np.float32))
+    y = oracle_mod.forward(n, in_features, v, 8, 0, np.zeros(0, np.uint8), np.zeros((256, 8), np.uint16), None,
+                           None, bias, np.zeros((2, 0), np.uint16), False, 2)
+    assert np.array_equal(y, np.tile(np.array([1.5, -2.0, 0.25, 0.0]), (2, 1)))
+    assert oracle_mod.packed_bytes(0, 4096, 8, 16, 8) == 0
+    assert oracle_mod.packed_bytes(16, 0, 8, 16, 8) == 0
+    y0 = oracle_mod.forward(0, 64, 8, 8, 0, np.zeros(0, np.uint8), np.zeros((256, 8), np.uint16), None, None, None,
+                            np.zeros((1, 64), np.uint16), False, 1)
+    assert y0.shape == (1, 0)

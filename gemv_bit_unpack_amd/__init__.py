@@ -1,0 +1,230 @@
+"""Python binding of libvq, the gfx950 VQ dequantize-and-multiply library.
+
+Argument marshalling only: every step of the computation runs in the HIP kernels of
+``libvq.so`` behind the C ABI of ``include/vq.h``.  PyTorch provides device memory and
+streams.  If the library is not built, the first call raises: there is no fallback
+path, and nothing here computes.
+
+Calls (same names as the C ABI):
+    packed_bytes(desc) -> int
+    pack(desc, idx1, idx2=None) -> numpy uint8 (host packing, layout of vq.h)
+    dequant(desc, packed, cb1, cb2, scale, w_dtype=torch.float32, out=None) -> W^ [N, IN]
+    gemv(desc, packed, cb1, cb2, scale, bias, x, y_dtype=None, out=None)  # 1 <= M <= 16
+    gemm(desc, packed, cb1, cb2, scale, bias, x, y_dtype=None, out=None)  # any M, MFMA
+and ``VQLinear``, a layer object holding the packed weights that picks gemv or gemm
+by batch size, the analogue of the VPTQ guide's ``VPTQLinear`` module.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libvq.so")
+
+VQ_OK = 0
+VQ_ERR_NULL = -1
+VQ_ERR_SHAPE = -2
+VQ_ERR_BITS = -3
+VQ_ERR_UNSUPPORTED = -4
+VQ_ERR_ALIGN = -5
+VQ_ERR_INDEX_RANGE = -6
+VQ_ERR_BUFFER_SIZE = -7
+VQ_ERR_HIP = -8
+
+VQ_F16, VQ_BF16, VQ_F32 = 0, 1, 2
+LAYOUT_ROWSTREAM = 1
+
+EXPORTED = ("vq_abi_version", "vq_status_string", "vq_packed_bytes", "vq_pack", "vq_dequant", "vq_gemv", "vq_gemm")
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("out_features", ctypes.c_int32), ("in_features", ctypes.c_int32), ("v", ctypes.c_int32),
+                ("bits1", ctypes.c_int32), ("bits2", ctypes.c_int32), ("layout", ctypes.c_int32)]
+
+    def __repr__(self):
+        return "Desc(N=%d, IN=%d, v=%d, bits1=%d, bits2=%d)" % (
+            self.out_features, self.in_features, self.v, self.bits1, self.bits2)
+
+
+def make_desc(out_features, in_features, v, bits1, bits2=0, layout=LAYOUT_ROWSTREAM) -> Desc:
+    return Desc(out_features, in_features, v, bits1, bits2, layout)
+
+
+class VQError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__("%s: %s" % (where, _status_string(status)))
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError("libvq.so is not built (%s); run `python -m gemv_bit_unpack_amd.build`" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    dp = ctypes.POINTER(Desc)
+    lib.vq_abi_version.argtypes = []
+    lib.vq_abi_version.restype = i32
+    lib.vq_status_string.argtypes = [ctypes.c_int]
+    lib.vq_status_string.restype = ctypes.c_char_p
+    lib.vq_packed_bytes.argtypes = [dp, ctypes.POINTER(sz)]
+    lib.vq_packed_bytes.restype = ctypes.c_int
+    lib.vq_pack.argtypes = [dp, vp, vp, vp, sz]
+    lib.vq_pack.restype = ctypes.c_int
+    lib.vq_dequant.argtypes = [dp, vp, vp, vp, vp, vp, ctypes.c_int, vp]
+    lib.vq_dequant.restype = ctypes.c_int
+    for name in ("vq_gemv", "vq_gemm"):
+        f = getattr(lib, name)
+        f.argtypes = [dp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i32, vp, ctypes.c_int, vp]
+        f.restype = ctypes.c_int
+    return lib
+
+
+_lib = None
+
+
+def lib():
+    """The loaded ctypes handle of libvq.so (raw C ABI); raises if it is not built."""
+    global _lib
+    if _lib is None:
+        _lib = _load()
+    return _lib
+
+
+def _status_string(status) -> str:
+    s = lib().vq_status_string(int(status))
+    return s.decode() if s else "unknown"
+
+
+def _check(status, where):
+    if status != VQ_OK:
+        raise VQError(status, where)
+
+
+def abi_version() -> int:
+    return int(lib().vq_abi_version())
+
+
+def packed_bytes(desc: Desc) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().vq_packed_bytes(ctypes.byref(desc), ctypes.byref(n)), "vq_packed_bytes")
+    return int(n.value)
+
+
+def pack(desc: Desc, idx1, idx2=None) -> np.ndarray:
+    """Host packing of uint32 indices [N, nv] into the row-stream layout."""
+    nv = (desc.in_features + desc.v - 1) // desc.v
+    i1 = np.ascontiguousarray(np.asarray(idx1, dtype=np.uint32).reshape(desc.out_features, nv))
+    i2 = None
+    if desc.bits2:
+        i2 = np.ascontiguousarray(np.asarray(idx2, dtype=np.uint32).reshape(desc.out_features, nv))
+    nb = packed_bytes(desc)
+    out = np.zeros(max(nb, 1), dtype=np.uint8)
+    _check(lib().vq_pack(ctypes.byref(desc), i1.ctypes.data_as(ctypes.c_void_p),
+                        None if i2 is None else i2.ctypes.data_as(ctypes.c_void_p),
+                        out.ctypes.data_as(ctypes.c_void_p), nb), "vq_pack")
+    return out[:nb]
+
+
+# ------------------------------------------------------------------ torch marshalling
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(dt) -> int:
+    torch = _torch()
+    if dt == torch.float16:
+        return VQ_F16
+    if dt == torch.bfloat16:
+        return VQ_BF16
+    if dt == torch.float32:
+        return VQ_F32
+    raise TypeError("unsupported dtype %s" % dt)
+
+
+def _dev_ptr(t, what, dtypes=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % what)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % what)
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError("%s has dtype %s, expected one of %s" % (what, t.dtype, dtypes))
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_ptr(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def dequant(desc: Desc, packed, cb1, cb2, scale, w_dtype=None, out=None):
+    torch = _torch()
+    w_dtype = w_dtype or torch.float32
+    if out is None:
+        out = torch.empty((desc.out_features, desc.in_features), dtype=w_dtype, device=packed.device)
+    f16 = (torch.float16,)
+    st = lib().vq_dequant(ctypes.byref(desc), _dev_ptr(packed, "packed"), _dev_ptr(cb1, "cb1", f16),
+                         _dev_ptr(cb2, "cb2", f16) if desc.bits2 else None, _dev_ptr(scale, "scale", f16),
+                         _dev_ptr(out, "out"), _dtype_code(out.dtype), _stream_ptr(packed.device))
+    _check(st, "vq_dequant")
+    return out
+
+
+def _product(fn, name, desc, packed, cb1, cb2, scale, bias, x, y_dtype, out):
+    torch = _torch()
+    if x.dim() != 2 or x.shape[1] != desc.in_features:
+        raise ValueError("x must be [M, %d], got %s" % (desc.in_features, tuple(x.shape)))
+    m = x.shape[0]
+    y_dtype = y_dtype or x.dtype
+    if out is None:
+        out = torch.empty((m, desc.out_features), dtype=y_dtype, device=x.device)
+    f16 = (torch.float16,)
+    st = fn(ctypes.byref(desc), _dev_ptr(packed, "packed"), _dev_ptr(cb1, "cb1", f16),
+            _dev_ptr(cb2, "cb2", f16) if desc.bits2 else None, _dev_ptr(scale, "scale", f16),
+            _dev_ptr(bias, "bias", f16), _dev_ptr(x, "x", (torch.float16, torch.bfloat16)), _dtype_code(x.dtype),
+            m, _dev_ptr(out, "out"), _dtype_code(out.dtype), _stream_ptr(x.device))
+    _check(st, name)
+    return out
+
+
+def gemv(desc, packed, cb1, cb2, scale, bias, x, y_dtype=None, out=None):
+    return _product(lib().vq_gemv, "vq_gemv", desc, packed, cb1, cb2, scale, bias, x, y_dtype, out)
+
+
+def gemm(desc, packed, cb1, cb2, scale, bias, x, y_dtype=None, out=None):
+    return _product(lib().vq_gemm, "vq_gemm", desc, packed, cb1, cb2, scale, bias, x, y_dtype, out)
+
+
+class VQLinear:
+    """A quantized linear layer: packed indices, fp16 codebooks, per-channel scale, bias.
+
+    ``forward(x)`` computes x W^T (+ bias) for x of shape [..., in_features]; batches of
+    up to ``gemv_max_m`` rows take the VALU decode kernel, larger ones the MFMA kernel.
+    """
+
+    def __init__(self, desc: Desc, packed, cb1, cb2=None, scale=None, bias=None, gemv_max_m: int = 16):
+        self.desc = desc
+        self.packed, self.cb1, self.cb2, self.scale, self.bias = packed, cb1, cb2, scale, bias
+        self.gemv_max_m = min(int(gemv_max_m), 16)
+
+    @classmethod
+    def from_indices(cls, desc: Desc, idx1, idx2, cb1, cb2=None, scale=None, bias=None, device="cuda"):
+        torch = _torch()
+        packed = torch.from_numpy(pack(desc, idx1, idx2)).to(device)
+        return cls(desc, packed, cb1, cb2, scale, bias)
+
+    def forward(self, x, y_dtype=None):
+        lead = x.shape[:-1]
+        x2 = x.reshape(-1, x.shape[-1]).contiguous()
+        fn = gemv if x2.shape[0] <= self.gemv_max_m else gemm
+        y = fn(self.desc, self.packed, self.cb1, self.cb2, self.scale, self.bias, x2, y_dtype)
+        return y.reshape(*lead, self.desc.out_features)
+
+    __call__ = forward

@@ -1,0 +1,196 @@
+// Host side of libvq: descriptor and argument validation, the index packer and the
+// exported C entry points.  Everything here runs on the CPU; the kernels live in the
+// .hip units and are reached through the launch_* functions.
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "vq_internal.h"
+
+namespace vqi {
+
+vq_status check_desc(const vq_desc* d) {
+  if (!d) return VQ_ERR_NULL;
+  if (d->v < 1 || d->v > 16) return VQ_ERR_BITS;
+  if (d->bits1 < 1 || d->bits1 > 16) return VQ_ERR_BITS;
+  if (d->bits2 < 0 || d->bits2 > 16) return VQ_ERR_BITS;
+  if (d->out_features < 0 || d->in_features < 0) return VQ_ERR_SHAPE;
+  if (d->layout != VQ_LAYOUT_ROWSTREAM) return VQ_ERR_UNSUPPORTED;
+  return VQ_OK;
+}
+
+static bool valid_x_dtype(vq_dtype t) { return t == VQ_F16 || t == VQ_BF16; }
+static bool valid_out_dtype(vq_dtype t) { return t == VQ_F16 || t == VQ_BF16 || t == VQ_F32; }
+static size_t dtype_size(vq_dtype t) { return t == VQ_F32 ? 4 : 2; }
+
+vq_status prepare_product(const vq_desc* desc, const void* packed, const void* cb1, const void* cb2,
+                          const void* scale, const void* bias, const void* x, vq_dtype x_dtype, int32_t m, void* y,
+                          vq_dtype y_dtype, int32_t max_m, ProductArgs* a) {
+  vq_status st = check_desc(desc);
+  if (st != VQ_OK) return st;
+  if (m < 0 || (max_m > 0 && m > max_m)) return VQ_ERR_SHAPE;
+  if (!valid_x_dtype(x_dtype) || !valid_out_dtype(y_dtype)) return VQ_ERR_UNSUPPORTED;
+  const vq_desc& d = *desc;
+  std::memset(a, 0, sizeof *a);
+  a->n = d.out_features;
+  a->in_features = d.in_features;
+  a->v = d.v;
+  a->bits1 = d.bits1;
+  a->bits2 = d.bits2;
+  a->m = m;
+  a->x_dtype = x_dtype;
+  a->y_dtype = y_dtype;
+  if (d.out_features == 0 || m == 0) return VQ_OK;  // nothing to compute
+  if (!y) return VQ_ERR_NULL;
+  if (!aligned(y, dtype_size(y_dtype))) return VQ_ERR_ALIGN;
+  if (bias && !aligned(bias, 2)) return VQ_ERR_ALIGN;
+  if (scale && !aligned(scale, 2)) return VQ_ERR_ALIGN;
+  if (d.in_features > 0) {
+    if (!packed || !cb1 || !x || (d.bits2 > 0 && !cb2)) return VQ_ERR_NULL;
+    if (!aligned(packed, 4)) return VQ_ERR_ALIGN;
+    if (!aligned(cb1, 2) || !aligned(x, 2) || (d.bits2 > 0 && !aligned(cb2, 2))) return VQ_ERR_ALIGN;
+  }
+  const int64_t s1 = row_stride(d.in_features, d.v, d.bits1);
+  const int64_t s2 = row_stride(d.in_features, d.v, d.bits2);
+  a->nv = (int32_t)num_vectors(d.in_features, d.v);
+  a->s1_words = (int32_t)(s1 / 4);
+  a->s2_words = (int32_t)(s2 / 4);
+  a->packed1 = (const uint32_t*)packed;
+  a->packed2 = d.bits2 > 0 ? (const uint32_t*)((const uint8_t*)packed + (size_t)d.out_features * (size_t)s1) : nullptr;
+  a->cb1 = (const uint16_t*)cb1;
+  a->cb2 = d.bits2 > 0 ? (const uint16_t*)cb2 : nullptr;
+  a->scale = (const uint16_t*)scale;
+  a->bias = (const uint16_t*)bias;
+  a->x = (const uint16_t*)x;
+  a->y = y;
+  return VQ_OK;
+}
+
+// Appends `bits`-bit fields LSB-first into a row of 32-bit little-endian words.
+struct BitWriter {
+  uint8_t* row;
+  uint64_t acc = 0;
+  int nacc = 0;
+  size_t pos = 0;
+  void put(uint32_t value, int bits) {
+    acc |= (uint64_t)value << nacc;
+    nacc += bits;
+    while (nacc >= 8) {
+      row[pos++] = (uint8_t)(acc & 0xFF);
+      acc >>= 8;
+      nacc -= 8;
+    }
+  }
+  void flush() {
+    if (nacc > 0) row[pos++] = (uint8_t)(acc & 0xFF);
+    acc = 0;
+    nacc = 0;
+  }
+};
+
+}  // namespace vqi
+
+using namespace vqi;
+
+extern "C" {
+
+int32_t vq_abi_version(void) { return VQ_ABI_VERSION; }
+
+const char* vq_status_string(vq_status status) {
+  switch (status) {
+    case VQ_OK: return "VQ_OK";
+    case VQ_ERR_NULL: return "VQ_ERR_NULL: a required pointer is NULL";
+    case VQ_ERR_SHAPE: return "VQ_ERR_SHAPE: invalid sizes or M out of range";
+    case VQ_ERR_BITS: return "VQ_ERR_BITS: v or index bit width out of range";
+    case VQ_ERR_UNSUPPORTED: return "VQ_ERR_UNSUPPORTED: combination not supported";
+    case VQ_ERR_ALIGN: return "VQ_ERR_ALIGN: pointer misaligned";
+    case VQ_ERR_INDEX_RANGE: return "VQ_ERR_INDEX_RANGE: index >= 2^bits";
+    case VQ_ERR_BUFFER_SIZE: return "VQ_ERR_BUFFER_SIZE: packed buffer too small";
+    case VQ_ERR_HIP: return "VQ_ERR_HIP: HIP runtime error";
+  }
+  return "unknown vq_status";
+}
+
+vq_status vq_packed_bytes(const vq_desc* desc, size_t* nbytes) {
+  vq_status st = check_desc(desc);
+  if (st != VQ_OK) return st;
+  if (!nbytes) return VQ_ERR_NULL;
+  *nbytes = packed_size(*desc);
+  return VQ_OK;
+}
+
+vq_status vq_pack(const vq_desc* desc, const uint32_t* idx1, const uint32_t* idx2, void* packed, size_t nbytes) {
+  vq_status st = check_desc(desc);
+  if (st != VQ_OK) return st;
+  const vq_desc& d = *desc;
+  const size_t need = packed_size(d);
+  const int64_t nv = num_vectors(d.in_features, d.v);
+  const size_t count = (size_t)d.out_features * (size_t)nv;
+  if (need > 0 || count > 0) {
+    if (!packed || !idx1 || (d.bits2 > 0 && !idx2)) return VQ_ERR_NULL;
+  }
+  if (nbytes < need) return VQ_ERR_BUFFER_SIZE;
+  for (int stream = 0; stream < 2; ++stream) {
+    const int bits = stream == 0 ? d.bits1 : d.bits2;
+    if (bits == 0) continue;
+    const uint32_t* idx = stream == 0 ? idx1 : idx2;
+    const uint32_t limit = (uint32_t)1 << bits;
+    for (size_t i = 0; i < count; ++i)
+      if (idx[i] >= limit) return VQ_ERR_INDEX_RANGE;
+  }
+  if (need == 0) return VQ_OK;
+  uint8_t* out = (uint8_t*)packed;
+  std::memset(out, 0, need);
+  const int64_t s1 = row_stride(d.in_features, d.v, d.bits1);
+  const int64_t s2 = row_stride(d.in_features, d.v, d.bits2);
+  for (int stream = 0; stream < 2; ++stream) {
+    const int bits = stream == 0 ? d.bits1 : d.bits2;
+    if (bits == 0) continue;
+    const uint32_t* idx = stream == 0 ? idx1 : idx2;
+    uint8_t* base = stream == 0 ? out : out + (size_t)d.out_features * (size_t)s1;
+    const int64_t stride = stream == 0 ? s1 : s2;
+    for (int64_t o = 0; o < d.out_features; ++o) {
+      BitWriter w{base + (size_t)o * (size_t)stride};
+      const uint32_t* r = idx + (size_t)o * (size_t)nv;
+      for (int64_t j = 0; j < nv; ++j) w.put(r[j], bits);
+      w.flush();
+    }
+  }
+  return VQ_OK;
+}
+
+vq_status vq_dequant(const vq_desc* desc, const void* packed, const void* cb1, const void* cb2, const void* scale,
+                     void* w, vq_dtype w_dtype, void* stream) {
+  vq_status st = check_desc(desc);
+  if (st != VQ_OK) return st;
+  if (!valid_out_dtype(w_dtype)) return VQ_ERR_UNSUPPORTED;
+  const vq_desc& d = *desc;
+  if (d.out_features == 0 || d.in_features == 0) return VQ_OK;
+  if (!packed || !cb1 || !w || (d.bits2 > 0 && !cb2)) return VQ_ERR_NULL;
+  if (!aligned(packed, 4) || !aligned(cb1, 2) || (d.bits2 > 0 && !aligned(cb2, 2)) || (scale && !aligned(scale, 2)) ||
+      !aligned(w, dtype_size(w_dtype)))
+    return VQ_ERR_ALIGN;
+  return launch_dequant(d, packed, cb1, d.bits2 > 0 ? cb2 : nullptr, scale, w, w_dtype, stream);
+}
+
+vq_status vq_gemv(const vq_desc* desc, const void* packed, const void* cb1, const void* cb2, const void* scale,
+                  const void* bias, const void* x, vq_dtype x_dtype, int32_t M, void* y, vq_dtype y_dtype,
+                  void* stream) {
+  ProductArgs a;
+  vq_status st = prepare_product(desc, packed, cb1, cb2, scale, bias, x, x_dtype, M, y, y_dtype, 16, &a);
+  if (st != VQ_OK) return st;
+  if (a.n == 0 || a.m == 0) return VQ_OK;
+  return launch_gemv(a, stream);
+}
+
+vq_status vq_gemm(const vq_desc* desc, const void* packed, const void* cb1, const void* cb2, const void* scale,
+                  const void* bias, const void* x, vq_dtype x_dtype, int32_t M, void* y, vq_dtype y_dtype,
+                  void* stream) {
+  ProductArgs a;
+  vq_status st = prepare_product(desc, packed, cb1, cb2, scale, bias, x, x_dtype, M, y, y_dtype, 0, &a);
+  if (st != VQ_OK) return st;
+  if (a.n == 0 || a.m == 0) return VQ_OK;
+  return launch_gemm(a, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+// Internal declarations shared by the host and device translation units of libvq.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "vq.h"
+
+namespace vqi {
+
+// Number of v-wide vectors per row; the last one may be partial.
+inline int64_t num_vectors(int64_t in_features, int v) { return (in_features + v - 1) / v; }
+
+// Bytes of one row of an index stream of `bits`-bit fields: 16-byte padded.
+inline int64_t row_stride(int64_t in_features, int v, int bits) {
+  if (bits == 0) return 0;
+  const int64_t nbits = num_vectors(in_features, v) * bits;
+  return 16 * ((nbits + 127) / 128);
+}
+
+// Validates the descriptor fields (not pointers).  VQ_OK or the error code.
+vq_status check_desc(const vq_desc* d);
+
+// Packed size in bytes of a validated descriptor.
+inline size_t packed_size(const vq_desc& d) {
+  return (size_t)d.out_features *
+         (size_t)(row_stride(d.in_features, d.v, d.bits1) + row_stride(d.in_features, d.v, d.bits2));
+}
+
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Arguments of every product launch (gemv and gemm), after validation.
+struct ProductArgs {
+  int32_t n, in_features, v, bits1, bits2, nv;
+  int32_t s1_words, s2_words;  // row strides in 32-bit words
+  const uint32_t* packed1;     // stream 1
+  const uint32_t* packed2;     // stream 2 or nullptr
+  const uint16_t* cb1;         // fp16 bits [K1][v]
+  const uint16_t* cb2;         // fp16 bits [K2][v] or nullptr
+  const uint16_t* scale;       // fp16 bits [n] or nullptr
+  const uint16_t* bias;        // fp16 bits [n] or nullptr
+  const uint16_t* x;           // [M][in] fp16 / bf16 bits
+  void* y;                     // [M][n]
+  int32_t m;
+  vq_dtype x_dtype, y_dtype;
+};
+
+// Validates a product call; on success fills `a`.  `max_m` bounds M (0: unbounded).
+vq_status prepare_product(const vq_desc* desc, const void* packed, const void* cb1, const void* cb2,
+                          const void* scale, const void* bias, const void* x, vq_dtype x_dtype, int32_t m, void* y,
+                          vq_dtype y_dtype, int32_t max_m, ProductArgs* a);
+
+// Launchers (defined in the .hip units).  Return VQ_OK or VQ_ERR_HIP / VQ_ERR_UNSUPPORTED.
+vq_status launch_dequant(const vq_desc& d, const void* packed, const void* cb1, const void* cb2, const void* scale,
+                         void* w, vq_dtype w_dtype, void* stream);
+vq_status launch_gemv(const ProductArgs& a, void* stream);
+vq_status launch_gemm(const ProductArgs& a, void* stream);
+
+}  // namespace vqi

@@ -1,0 +1,127 @@
+/*
+ * vq.h -- C ABI of the MI355X (gfx950) VQ dequantize-and-multiply library, libvq.so.
+ *
+ * The operation (VPTQ guide, aifetchly, "2. Multi-Stage Residual Vector Quantization
+ * (RVQ)" and "Step 3: Fused Low-Bit VPTQ Linear Layer"; per-channel scaling as in the
+ * QuIP# entry of the production-VQ post, llms.blog):
+ *
+ *   W^[o, j*v + t] = scale[o] * ( C1[idx1[o, j]][t] + C2[idx2[o, j]][t] ),  t < v
+ *   y[m, o]        = sum_col x[m, col] * W^[o, col]  (+ bias[o])
+ *
+ * for o < N = out_features, col < IN = in_features, j < nv = ceil(IN / v).  The weight
+ * matrix is never stored: every call rebuilds W^ on the fly from bit-packed indices
+ * into a main codebook C1 of K1 = 2^bits1 fp16 centroids and an optional residual
+ * codebook C2 of K2 = 2^bits2 fp16 centroids, each centroid a row of v fp16 values.
+ *
+ * Packed index layout (VQ_LAYOUT_ROWSTREAM, the only layout):
+ *   - row stride of stream b: S_b = 16 * ceil(nv * bits_b / 128) bytes (0 if bits_b == 0);
+ *   - stream 1 (idx1) for rows 0..N-1 occupies bytes [0, N*S1), stream 2 (idx2) follows
+ *     at [N*S1, N*(S1+S2));
+ *   - index j of row o is the unsigned integer in bits [j*B, (j+1)*B) of its row, where
+ *     bit k is bit (k mod 8) of byte floor(k/8) (LSB-first, little-endian);
+ *   - pad bits are written as zero by vq_pack and ignored by the kernels.
+ * When IN is not a multiple of v, the last vector's lanes t with j*v + t >= IN are
+ * dropped (the centroid is stored in full, its tail is never used).
+ *
+ * Numerics.  vq_dequant is exact: in fp32, w = fp32(C1) + fp32(C2) rounded to nearest
+ * even, then w * fp32(scale[o]); without a residual book the add is skipped, without a
+ * scale the multiply is skipped.  vq_gemv accumulates in fp32 and applies scale[o] once
+ * per output; vq_gemm rounds the rebuilt vector to the activation's 16-bit type
+ * (bf16 activations: as a bf16 hi + lo pair, ~16 significant bits) and accumulates in
+ * fp32 on the matrix cores.  Outputs are rounded to nearest even into y_dtype.
+ *
+ * Ownership and execution.  The caller allocates and owns every buffer.  Pointers given
+ * to vq_dequant / vq_gemv / vq_gemm are DEVICE pointers; `stream` is a hipStream_t
+ * (NULL = the default stream).  These three calls validate on the host, enqueue kernels
+ * on `stream` and return without synchronising: inputs must stay unchanged until the
+ * stream has run them, and y / w must not alias any input.  The library allocates no
+ * memory, keeps no pointer after returning and is safe to call from several threads.
+ * vq_packed_bytes and vq_pack work on HOST memory and are synchronous.
+ *
+ * Errors.  Every argument is checked before anything is enqueued; on error nothing is
+ * launched and no output is written.  A launch failure reported by the runtime maps to
+ * VQ_ERR_HIP.  No C++ exception crosses this interface.
+ */
+#ifndef VQ_H
+#define VQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define VQ_ABI_VERSION 1
+#define VQ_LAYOUT_ROWSTREAM 1
+
+typedef enum vq_status {
+  VQ_OK = 0,
+  VQ_ERR_NULL = -1,         /* a required pointer is NULL */
+  VQ_ERR_SHAPE = -2,        /* negative sizes, M out of range */
+  VQ_ERR_BITS = -3,         /* v not in 1..16, bits1 not in 1..16, bits2 not in 0..16 */
+  VQ_ERR_UNSUPPORTED = -4,  /* valid but not built for the GPU (v, bits, dtype combination), unknown layout */
+  VQ_ERR_ALIGN = -5,        /* a device pointer is not aligned as the call requires */
+  VQ_ERR_INDEX_RANGE = -6,  /* vq_pack: an index is >= 2^bits */
+  VQ_ERR_BUFFER_SIZE = -7,  /* vq_pack: nbytes < vq_packed_bytes */
+  VQ_ERR_HIP = -8           /* the HIP runtime reported an error at launch */
+} vq_status;
+
+typedef enum vq_dtype { VQ_F16 = 0, VQ_BF16 = 1, VQ_F32 = 2 } vq_dtype;
+
+/* W is [out_features][in_features]; vectors of v weights run along in_features.
+ * bits1 in 1..16 (K1 = 2^bits1), bits2 in 0..16 (0: no residual book), layout = 1. */
+typedef struct vq_desc {
+  int32_t out_features;
+  int32_t in_features;
+  int32_t v;
+  int32_t bits1;
+  int32_t bits2;
+  int32_t layout;
+} vq_desc;
+
+/* VQ_ABI_VERSION of the loaded library. */
+int32_t vq_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char* vq_status_string(vq_status status);
+
+/* Bytes of the packed index buffer for `desc` (bitrate log2(K)/v per book, VPTQ guide
+ * "3. Effective Bit-Width Calculation", plus row padding to 16 bytes). */
+vq_status vq_packed_bytes(const vq_desc* desc, size_t* nbytes);
+
+/* Pack idx1 [N][nv] (and idx2 [N][nv] when bits2 > 0; must be NULL-free then, ignored
+ * otherwise) into `packed` (HOST memory, nbytes >= vq_packed_bytes).  Writes every byte
+ * of the packed size, pad bits zero.  VQ_ERR_INDEX_RANGE if any index >= 2^bits, with
+ * `packed` untouched. */
+vq_status vq_pack(const vq_desc* desc, const uint32_t* idx1, const uint32_t* idx2, void* packed, size_t nbytes);
+
+/* Rebuild W^ [N][IN] into `w` (device, row-major, w_dtype; fp16 / bf16 outputs are the
+ * nearest-even rounding of the exact fp32 value).  packed: device, 4-byte aligned;
+ * cb1: fp16 [2^bits1][v]; cb2: fp16 [2^bits2][v] (NULL iff bits2 == 0);
+ * scale: fp16 [N] or NULL (scale 1).  Codebook and scale pointers must be 2-byte
+ * aligned, w aligned to its element size. */
+vq_status vq_dequant(const vq_desc* desc, const void* packed, const void* cb1, const void* cb2, const void* scale,
+                     void* w, vq_dtype w_dtype, void* stream);
+
+/* Decode-batch product y [M][N] = x [M][IN] * W^T (+ bias), 1 <= M <= 16 (M = 0: no-op).
+ * The VALU path: each wavefront reduces whole rows; accumulation in fp32.
+ * x: device, x_dtype VQ_F16 or VQ_BF16, row-major [M][IN]; bias: fp16 [N] or NULL;
+ * y: device, y_dtype VQ_F16, VQ_BF16 or VQ_F32, row-major [M][N].  Other pointers as
+ * for vq_dequant.  IN == 0 gives y = bias (or 0). */
+vq_status vq_gemv(const vq_desc* desc, const void* packed, const void* cb1, const void* cb2, const void* scale,
+                  const void* bias, const void* x, vq_dtype x_dtype, int32_t M, void* y, vq_dtype y_dtype,
+                  void* stream);
+
+/* Same operation and arguments as vq_gemv for any M >= 1 (M = 0: no-op), on the matrix
+ * cores: rebuilt weight tiles are staged in LDS in the activation's 16-bit type and
+ * multiplied with MFMA, fp32 accumulation.  Meant for prefill batches (M >= 32). */
+vq_status vq_gemm(const vq_desc* desc, const void* packed, const void* cb1, const void* cb2, const void* scale,
+                  const void* bias, const void* x, vq_dtype x_dtype, int32_t M, void* y, vq_dtype y_dtype,
+                  void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* VQ_H */

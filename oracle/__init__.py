@@ -64,6 +64,10 @@ def _load():
         lib.oracle_f64_to_f16_rne.restype = ctypes.c_uint16
         lib.oracle_f64_to_bf16_rne.argtypes = [ctypes.c_double]
         lib.oracle_f64_to_bf16_rne.restype = ctypes.c_uint16
+        lib.oracle_f32_to_f16_rne_array.argtypes = [vp, vp, i64]
+        lib.oracle_f32_to_f16_rne_array.restype = None
+        lib.oracle_f32_to_bf16_rne_array.argtypes = [vp, vp, i64]
+        lib.oracle_f32_to_bf16_rne_array.restype = None
         lib.oracle_row_stride.argtypes = [i64, i32, i32]
         lib.oracle_row_stride.restype = i64
         lib.oracle_packed_bytes.argtypes = [i64, i64, i32, i32, i32]
@@ -131,6 +135,21 @@ def f64_to_bf16_rne(vals) -> np.ndarray:
     lib = _load()
     v = np.asarray(vals, dtype=np.float64).ravel()
     return np.array([lib.oracle_f64_to_bf16_rne(float(x)) for x in v], dtype=np.uint16)
+
+
+def f32_array_to_f16_rne(a) -> np.ndarray:
+    """RNE of an fp32 array to binary16 bits (same rounding as f64_to_f16_rne)."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    out = np.zeros(a.shape, dtype=np.uint16)
+    _load().oracle_f32_to_f16_rne_array(_ptr(a), _ptr(out), a.size)
+    return out
+
+
+def f32_array_to_bf16_rne(a) -> np.ndarray:
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    out = np.zeros(a.shape, dtype=np.uint16)
+    _load().oracle_f32_to_bf16_rne_array(_ptr(a), _ptr(out), a.size)
+    return out
 
 
 # ------------------------------------------------------------------ layout

@@ -110,6 +110,13 @@ static uint16_t encode_rne(double x, int mbits, int emin, int emax, int ebias, i
 uint16_t oracle_f64_to_f16_rne(double x) { return encode_rne(x, 10, -14, 15, 15, 5); }
 uint16_t oracle_f64_to_bf16_rne(double x) { return encode_rne(x, 7, -126, 127, 127, 8); }
 
+void oracle_f32_to_f16_rne_array(const float* in, uint16_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_f64_to_f16_rne((double)in[i]);
+}
+void oracle_f32_to_bf16_rne_array(const float* in, uint16_t* out, int64_t n) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_f64_to_bf16_rne((double)in[i]);
+}
+
 /* ---------------------------------------------------------------- layout */
 
 static int valid_desc(int64_t n, int64_t in_features, int v, int bits1, int bits2) {

@@ -39,6 +39,9 @@ double oracle_bf16_to_f64(uint16_t b);
 /* Round-to-nearest-even of a finite double holding an fp32 value to binary16 / bfloat16 bits. */
 uint16_t oracle_f64_to_f16_rne(double x);
 uint16_t oracle_f64_to_bf16_rne(double x);
+/* The same roundings applied to an fp32 array. */
+void oracle_f32_to_f16_rne_array(const float* in, uint16_t* out, int64_t n);
+void oracle_f32_to_bf16_rne_array(const float* in, uint16_t* out, int64_t n);
 
 /* Bytes of one row's bitstream for nv fields of `bits` bits (0 if bits == 0). */
 int64_t oracle_row_stride(int64_t in_features, int v, int bits);

@@ -1,0 +1,168 @@
+"""The C ABI on the host (no GPU): symbols, sizes, the packer, and every validation
+path that must return before anything is launched."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def vq():
+    import gemv_bit_unpack_amd as g
+
+    if not os.path.exists(g.LIB_PATH):
+        from gemv_bit_unpack_amd import build
+
+        build.build()
+    g.lib()
+    return g
+
+
+def _declared_symbols():
+    text = open(os.path.join(ROOT, "include", "vq.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(vq_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol(vq):
+    names = _declared_symbols()
+    assert set(names) == set(vq.EXPORTED)
+    for name in names:
+        assert hasattr(vq.lib(), name), name
+    assert vq.abi_version() == 1
+
+
+def test_status_strings(vq):
+    for code in range(-8, 1):
+        s = vq.lib().vq_status_string(code).decode()
+        assert s.startswith("VQ_")
+    assert vq.lib().vq_status_string(-99).decode() == "unknown vq_status"
+
+
+@pytest.mark.parametrize("n,i,v,b1,b2", [
+    (256, 256, 8, 8, 0), (4096, 4096, 8, 16, 0), (4096, 4096, 8, 16, 8), (14336, 4096, 6, 12, 12),
+    (4096, 14336, 6, 12, 12), (28672, 8192, 8, 16, 8), (8192, 28672, 8, 16, 8), (7, 13, 3, 5, 7),
+    (1, 1, 1, 1, 0), (0, 64, 8, 8, 0), (64, 0, 8, 8, 8), (3, 1000, 16, 16, 16),
+])
+def test_packed_bytes_matches_oracle(vq, n, i, v, b1, b2):
+    assert vq.packed_bytes(vq.make_desc(n, i, v, b1, b2)) == oracle.packed_bytes(n, i, v, b1, b2)
+
+
+@pytest.mark.parametrize("n,i,v,b1,b2", [
+    (3, 40, 8, 16, 8), (5, 37, 6, 12, 12), (2, 100, 3, 5, 0), (4, 64, 8, 8, 0), (1, 7, 1, 13, 3),
+    (7, 200, 16, 16, 16), (9, 13, 4, 1, 2), (33, 300, 6, 12, 0), (17, 512, 8, 3, 0),
+])
+def test_pack_byte_equal_to_oracle(vq, n, i, v, b1, b2):
+    lay = synth.make_layer(n, i, v, b1, b2, wid=60, copy=n)
+    d = vq.make_desc(n, i, v, b1, b2)
+    ours = vq.pack(d, lay["idx1"], lay["idx2"])
+    ref = oracle.pack(n, i, v, b1, b2, lay["idx1"], lay["idx2"])
+    assert np.array_equal(ours, ref)
+
+
+@pytest.mark.parametrize("key", ["dec4k_res", "mlp8b", "l70b"])
+def test_pack_workloads_row_sample_equal_to_oracle(vq, key):
+    w = synth.WORKLOADS[key]
+    for layer, (n, i) in enumerate(w.layers):
+        lay = synth.workload_layer(key, layer)
+        ours = vq.pack(vq.make_desc(n, i, w.v, w.bits1, w.bits2), lay["idx1"], lay["idx2"])
+        rows = np.unique(np.concatenate([[0, n - 1], np.random.default_rng(layer).integers(0, n, 30)]))
+        sub2 = lay["idx2"][rows] if w.bits2 else None
+        ref = oracle.pack(rows.size, i, w.v, w.bits1, w.bits2, lay["idx1"][rows], sub2)
+        s1 = oracle.row_stride(i, w.v, w.bits1)
+        s2 = oracle.row_stride(i, w.v, w.bits2)
+        mine1 = ours[: n * s1].reshape(n, s1)[rows].reshape(-1)
+        assert np.array_equal(mine1, ref[: rows.size * s1])
+        if w.bits2:
+            mine2 = ours[n * s1:].reshape(n, s2)[rows].reshape(-1)
+            assert np.array_equal(mine2, ref[rows.size * s1:])
+
+
+def _raw_pack(vq, desc, idx1, idx2, nbytes, out=None):
+    out = np.full(max(nbytes, 16) + 16, 0xAB, dtype=np.uint8) if out is None else out
+    st = vq.lib().vq_pack(ctypes.byref(desc) if desc is not None else None,
+                          None if idx1 is None else idx1.ctypes.data_as(ctypes.c_void_p),
+                          None if idx2 is None else idx2.ctypes.data_as(ctypes.c_void_p),
+                          out.ctypes.data_as(ctypes.c_void_p), nbytes)
+    return st, out
+
+
+def test_pack_errors_leave_output_untouched(vq):
+    d = vq.make_desc(2, 16, 8, 3, 0)
+    good = np.array([[1, 7], [0, 5]], dtype=np.uint32)
+    bad = np.array([[1, 8], [0, 5]], dtype=np.uint32)
+    nb = vq.packed_bytes(d)
+    st, out = _raw_pack(vq, d, bad, None, nb)
+    assert st == vq.VQ_ERR_INDEX_RANGE and (out == 0xAB).all()
+    st, out = _raw_pack(vq, d, good, None, nb - 1)
+    assert st == vq.VQ_ERR_BUFFER_SIZE and (out == 0xAB).all()
+    st, out = _raw_pack(vq, None, good, None, nb)
+    assert st == vq.VQ_ERR_NULL and (out == 0xAB).all()
+    st, out = _raw_pack(vq, vq.make_desc(2, 16, 8, 3, 2), good, None, 64)
+    assert st == vq.VQ_ERR_NULL and (out == 0xAB).all()
+    st, out = _raw_pack(vq, d, good, None, nb)
+    assert st == vq.VQ_OK and not out[:nb].tolist() == [0xAB] * nb
+
+
+@pytest.mark.parametrize("fields,code", [
+    (dict(v=0), -3), (dict(v=17), -3), (dict(bits1=0), -3), (dict(bits1=17), -3), (dict(bits2=-1), -3),
+    (dict(bits2=17), -3), (dict(out_features=-1), -2), (dict(in_features=-5), -2), (dict(layout=2), -4),
+])
+def test_descriptor_validation(vq, fields, code):
+    base = dict(out_features=8, in_features=64, v=8, bits1=8, bits2=0, layout=1)
+    base.update(fields)
+    d = vq.Desc(**base)
+    n = ctypes.c_size_t(0)
+    assert vq.lib().vq_packed_bytes(ctypes.byref(d), ctypes.byref(n)) == code
+    assert vq.lib().vq_packed_bytes(None, ctypes.byref(n)) == vq.VQ_ERR_NULL
+
+
+# Fake, never-dereferenced device addresses: every call below must be refused on the host.
+P = ctypes.c_void_p(0x10000)
+P_MIS = ctypes.c_void_p(0x10002)
+
+
+def _gemv(vq, fn, desc, packed=P, cb1=P, cb2=P, scale=None, bias=None, x=P, xt=0, m=1, y=P, yt=2):
+    return getattr(vq.lib(), fn)(ctypes.byref(desc) if desc is not None else None, packed, cb1, cb2, scale, bias, x,
+                                 xt, m, y, yt, None)
+
+
+@pytest.mark.parametrize("fn", ["vq_gemv", "vq_gemm"])
+def test_product_validation_paths(vq, fn):
+    d = vq.make_desc(64, 64, 8, 8, 8)
+    assert _gemv(vq, fn, None) == vq.VQ_ERR_NULL
+    assert _gemv(vq, fn, vq.make_desc(64, 64, 8, 0, 0)) == vq.VQ_ERR_BITS
+    assert _gemv(vq, fn, d, m=-1) == vq.VQ_ERR_SHAPE
+    assert _gemv(vq, fn, d, xt=2) == vq.VQ_ERR_UNSUPPORTED  # fp32 activations are not an input type
+    assert _gemv(vq, fn, d, yt=7) == vq.VQ_ERR_UNSUPPORTED
+    assert _gemv(vq, fn, d, y=None) == vq.VQ_ERR_NULL
+    assert _gemv(vq, fn, d, cb2=None) == vq.VQ_ERR_NULL
+    assert _gemv(vq, fn, d, packed=None) == vq.VQ_ERR_NULL
+    assert _gemv(vq, fn, d, x=None) == vq.VQ_ERR_NULL
+    assert _gemv(vq, fn, d, packed=P_MIS) == vq.VQ_ERR_ALIGN
+    assert _gemv(vq, fn, d, y=P_MIS, yt=2) == vq.VQ_ERR_ALIGN
+    assert _gemv(vq, fn, d, x=ctypes.c_void_p(0x10001)) == vq.VQ_ERR_ALIGN
+    assert _gemv(vq, fn, vq.Desc(64, 64, 8, 8, 8, 3)) == vq.VQ_ERR_UNSUPPORTED
+    # nothing to do: no launch, no pointer needed
+    assert _gemv(vq, fn, d, m=0, y=None, x=None, packed=None) == vq.VQ_OK
+    assert _gemv(vq, fn, vq.make_desc(0, 64, 8, 8, 8), y=None, x=None, packed=None) == vq.VQ_OK
+    if fn == "vq_gemv":
+        assert _gemv(vq, fn, d, m=17) == vq.VQ_ERR_SHAPE
+
+
+def test_dequant_validation_paths(vq):
+    f = vq.lib().vq_dequant
+    d = vq.make_desc(64, 64, 8, 8, 8)
+    assert f(None, P, P, P, None, P, 2, None) == vq.VQ_ERR_NULL
+    assert f(ctypes.byref(d), P, P, None, None, P, 2, None) == vq.VQ_ERR_NULL
+    assert f(ctypes.byref(d), P, P, P, None, P, 9, None) == vq.VQ_ERR_UNSUPPORTED
+    assert f(ctypes.byref(d), P_MIS, P, P, None, P, 2, None) == vq.VQ_ERR_ALIGN
+    assert f(ctypes.byref(d), P, P, P, None, P_MIS, 2, None) == vq.VQ_ERR_ALIGN
+    assert f(ctypes.byref(vq.make_desc(64, 0, 8, 8, 8)), None, None, None, None, None, 2, None) == vq.VQ_OK

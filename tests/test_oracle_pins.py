@@ -392,3 +392,11 @@ def test_bias_and_empty_shapes(oracle_mod):
     y0 = oracle_mod.forward(0, 64, 8, 8, 0, np.zeros(0, np.uint8), np.zeros((256, 8), np.uint16), None, None, None,
                             np.zeros((1, 64), np.uint16), False, 1)
     assert y0.shape == (1, 0)
+
+
+def test_array_rounding_matches_scalar_and_numpy(oracle_mod):
+    vals = _rounding_probe_values(3)
+    with np.errstate(over="ignore"):
+        assert np.array_equal(oracle_mod.f32_array_to_f16_rne(vals), vals.astype(np.float16).view(np.uint16))
+    ref = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle_mod.f32_array_to_bf16_rne(vals), ref)

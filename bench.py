@@ -1,0 +1,305 @@
+"""Benchmark of the VQ dequantize-and-multiply path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one vq_gemv call (M = 1) on a 4096 x 4096 layer with v = 8 and a
+65536-entry main codebook (2 index bits per weight), fp16 x, fp16 y: the decode GEMV
+the metric is quoted on.  Steps rotate through a ring of distinct layer copies (own
+indices, codebook and scale each) totalling more than 1 GiB, so the 256 MB
+Infinity Cache cannot hold the stream and every step reads its indices from HBM.
+
+Printed: ONE JSON line with the throughput on algorithmic bytes (packed indices +
+each codebook once + scales + x + y), the roofline of the kernel, the prefill GEMM
+(vq_gemm at M = 128 on the 28672 x 8192 / 8192 x 28672 layers), the GEMV at M = 1 on
+every workload, and the CPU oracle timed on the host on a bounded sample.
+
+Inputs are synthetic: uniform indices (a packed stream of uniform random bits),
+centroids 0.02*N(0,1) main and 0.005*N(0,1) residual in fp16, scales U(0.5, 1.5),
+x ~ N(0,1); all seeded.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+import zlib
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E
+MFMA_PEAK_TFLOPS = 2500.0    # MI355X dense fp16 / bf16
+RING_BYTES = 1 << 30         # > 4x the 256 MB Infinity Cache
+MAX_COPIES = 512             # tiny layers: the ring stays cache-resident, said in the output
+
+WORKLOADS = {
+    # key: (layers [(N, IN)], v, bits1, bits2, x dtype)
+    "tiny": ([(256, 256)], 8, 8, 0, "f16"),
+    "dec4k": ([(4096, 4096)], 8, 16, 0, "f16"),
+    "dec4k_res": ([(4096, 4096)], 8, 16, 8, "f16"),
+    "mlp8b": ([(14336, 4096), (4096, 14336)], 6, 12, 12, "f16"),
+    "l70b": ([(28672, 8192), (8192, 28672)], 8, 16, 8, "bf16"),
+}
+DESCRIBE = {
+    "tiny": "256x256 v8 K1=256 (1 bit/weight)",
+    "dec4k": "4096x4096 v8 K1=65536 (2 bits/weight)",
+    "dec4k_res": "4096x4096 v8 K1=65536+K2=256 (3 bits/weight)",
+    "mlp8b": "MLP pair 14336x4096 + 4096x14336 v6 K1=K2=4096 (4 bits/weight)",
+    "l70b": "70B-class pair 28672x8192 + 8192x28672 v8 K1=65536+K2=256 (3 bits/weight)",
+}
+GEMV_SOURCES = ["gemv_bit_unpack_amd/csrc/vq_gemv.hip", "gemv_bit_unpack_amd/csrc/vq_device.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_vq_gemv_dec4k_m1.json")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+# ------------------------------------------------------------------ byte and flop counts
+
+def layer_bytes(vq, desc, m, y_bytes=2):
+    """Algorithmic bytes of one call: packed indices + each codebook once + scale + x + y."""
+    n, i, v = desc.out_features, desc.in_features, desc.v
+    books = (1 << desc.bits1) * v * 2 + ((1 << desc.bits2) * v * 2 if desc.bits2 else 0)
+    return vq.packed_bytes(desc) + books + 2 * n + 2 * m * i + y_bytes * m * n
+
+
+def gathered_bytes(desc):
+    """Centroid bytes gathered from books that are not staged in LDS (K > 4096)."""
+    nv = (desc.in_features + desc.v - 1) // desc.v
+    g = 0
+    for bits in (desc.bits1, desc.bits2):
+        if bits > 12:
+            g += desc.out_features * nv * desc.v * 2
+    return g
+
+
+# ------------------------------------------------------------------ device rings
+
+class Ring:
+    """Distinct copies of one workload layer on the device, plus ctypes argument tuples."""
+
+    def __init__(self, vq, torch, key, layer, m, copies=None, fn="vq_gemv", y_dtype=None):
+        layers, v, b1, b2, xd = WORKLOADS[key]
+        n, i = layers[layer]
+        self.desc = vq.make_desc(n, i, v, b1, b2)
+        self.m = m
+        dev = torch.device("cuda")
+        per = layer_bytes(vq, self.desc, m)
+        self.copies = copies or min(MAX_COPIES, max(1, -(-RING_BYTES // per)))
+        g = torch.Generator(device=dev)
+        g.manual_seed(zlib.crc32(("%d/%s/%d" % (42, key, layer)).encode()))
+        nb = vq.packed_bytes(self.desc)
+        xdt = torch.bfloat16 if xd == "bf16" else torch.float16
+        self.x = torch.randn((m, i), generator=g, device=dev, dtype=torch.float32).to(xdt)
+        self.y_dtype = y_dtype or xdt
+        self.items = []
+        lib = vq.lib()
+        self.fn = getattr(lib, fn)
+        code = {torch.float16: vq.VQ_F16, torch.bfloat16: vq.VQ_BF16, torch.float32: vq.VQ_F32}
+        self.tensors = []
+        for c in range(self.copies):
+            packed = torch.randint(0, 256, (nb,), generator=g, device=dev, dtype=torch.uint8)
+            cb1 = (torch.randn((1 << b1, v), generator=g, device=dev) * 0.02).half()
+            cb2 = (torch.randn((1 << b2, v), generator=g, device=dev) * 0.005).half() if b2 else None
+            scale = (torch.rand((n,), generator=g, device=dev) + 0.5).half()
+            y = torch.empty((m, n), device=dev, dtype=self.y_dtype)
+            self.tensors.append((packed, cb1, cb2, scale, y))
+            p = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
+            self.items.append((ctypes.byref(self.desc), p(packed), p(cb1), p(cb2), p(scale), None, p(self.x),
+                               code[xdt], m, p(y), code[self.y_dtype]))
+        self.bytes_per_call = layer_bytes(vq, self.desc, m, 4 if self.y_dtype == torch.float32 else 2)
+        self.flops_per_call = 2.0 * m * n * i
+
+    def call(self, k, stream_ptr):
+        st = self.fn(*self.items[k % self.copies], stream_ptr)
+        if st != 0:
+            raise RuntimeError("%s failed with status %d" % (self.fn.__name__, st))
+
+
+def time_ring(torch, rings, steps, warmup, use_graph=True):
+    """Average seconds per call over `steps` calls rotating through the ring(s)."""
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    seq = [(r, k) for k in range(max(r.copies for r in rings)) for r in rings]
+    for s in range(max(warmup, 1)):
+        r, k = seq[s % len(seq)]
+        r.call(k, sp)
+    torch.cuda.synchronize()
+    graph = None
+    if use_graph:
+        try:
+            graph = torch.cuda.CUDAGraph()
+            side = torch.cuda.Stream()
+            side.wait_stream(stream)
+            with torch.cuda.graph(graph, stream=side):
+                gsp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+                for r, k in seq:
+                    r.call(k, gsp)
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+        except Exception as e:  # capture unsupported: time eager launches
+            log("graph capture failed (%s); timing eager launches" % e)
+            graph = None
+    reps = max(1, -(-steps // len(seq)))
+    n_calls = reps * len(seq) if graph is not None else steps
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    if graph is not None:
+        for _ in range(reps):
+            graph.replay()
+    else:
+        for s in range(steps):
+            r, k = seq[s % len(seq)]
+            r.call(k, sp)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_s = start.elapsed_time(end) * 1e-3
+    return gpu_s / n_calls, n_calls, wall, ("hipgraph" if graph is not None else "eager")
+
+
+# ------------------------------------------------------------------ CPU baseline
+
+def cpu_baseline(budget_s=12.0):
+    """The oracle (unpack + fp32 dequant + fp64 product) on the host, 4096x4096 K=65536 M=1."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    try:
+        threads = min(len(os.sched_getaffinity(0)), 16)
+    except AttributeError:
+        threads = min(os.cpu_count() or 1, 16)
+    lay = synth.workload_layer("dec4k", 0)
+    n, i = lay["n"], lay["in_features"]
+    packed = oracle.pack(n, i, 8, 16, 0, lay["idx1"])
+    xb = synth.workload_x("dec4k", 0, 1)
+    per = packed.size + (1 << 16) * 8 * 2 + 2 * n + 2 * i + 2 * n
+    calls, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward(n, i, 8, 16, 0, packed, lay["cb1"], None, lay["scale"], None, xb, False, 1, nthreads=threads)
+        calls += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    return {"value": round(per * calls / el / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "%d calls of the 4096x4096 K1=65536 M=1 layer (bit-by-bit unpack, fp32 dequant, fp64 "
+                      "product) in %.1f s; same algorithmic bytes per call as the GPU step" % (calls, el),
+            "ms_per_call": round(el / calls * 1e3, 3)}
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a HIP graph")
+    ap.add_argument("--only-headline", action="store_true", help="skip the GEMM, per-workload and CPU legs")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gemv_bit_unpack_amd as vq
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    vq.lib()
+    use_graph = not args.no_graph
+
+    # Headline: vq_gemv, 4096x4096, K1 = 65536, M = 1.
+    ring = Ring(vq, torch, "dec4k", 0, 1)
+    log("headline ring: %d copies of %s, %.2f MB per call" % (ring.copies, DESCRIBE["dec4k"],
+                                                              ring.bytes_per_call / 1e6))
+    sec, n_calls, wall, launch = time_ring(torch, [ring], args.steps, args.warmup, use_graph)
+    gbps = ring.bytes_per_call / sec / 1e9
+    g_cb = (ring.bytes_per_call + gathered_bytes(ring.desc)) / sec / 1e9
+    nv = (ring.desc.in_features + 7) // 8
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        if tr.get("source_hash") == source_hash(GEMV_SOURCES):
+            traffic = tr.get("hbm_bytes_per_launch")
+    out = {
+        "metric": "vq_gemv effective GB/s & % HBM peak at M=1; vq_gemm TFLOP/s at M=128",
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": n_calls,
+        "warmup": args.warmup,
+        "ms_per_step": round(sec * 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "decode GEMV, " + DESCRIBE["dec4k"] + ", M=1, fp16 x and y", "global_batch": 1,
+                   "layer_copies_in_ring": ring.copies, "launch": launch,
+                   "bytes_per_step": ring.bytes_per_call},
+        "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "kernel": "gemv_kernel<8,1,0,false>"},
+        "gather": {"gathers_per_s": round(ring.desc.out_features * nv / sec, 1),
+                   "effective_incl_gathered_centroids_GBps": round(g_cb, 2),
+                   "note": "16-byte centroid gathers from the 1 MiB book through L2; the pages warn that "
+                           "L2-served lookups eat the bandwidth savings"},
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.only_headline:
+        # Prefill GEMM at M = 128 on the 70B-class pair.
+        up = Ring(vq, torch, "l70b", 0, 128, copies=6, fn="vq_gemm")
+        down = Ring(vq, torch, "l70b", 1, 128, copies=6, fn="vq_gemm")
+        gsec, gcalls, _, glaunch = time_ring(torch, [up, down], 48, 12, use_graph)
+        flops = (up.flops_per_call + down.flops_per_call) / 2
+        tflops = flops / gsec / 1e12
+        out["gemm"] = {"workload": "prefill GEMM, " + DESCRIBE["l70b"] + ", M=128, bf16 x and y",
+                       "tflops": round(tflops, 2), "frac_mfma_peak": round(tflops / MFMA_PEAK_TFLOPS, 4),
+                       "ms_per_call": round(gsec * 1e3, 4), "calls": gcalls, "launch": glaunch}
+        del up, down
+        torch.cuda.empty_cache()
+        per = {}
+        for key in WORKLOADS:
+            layers = WORKLOADS[key][0]
+            rings = [Ring(vq, torch, key, li, 1) for li in range(len(layers))]
+            s, c, _, _ = time_ring(torch, rings, max(200, 2 * sum(r.copies for r in rings)), 20, use_graph)
+            b = sum(r.bytes_per_call for r in rings) / len(rings)
+            bcb = sum(r.bytes_per_call + gathered_bytes(r.desc) for r in rings) / len(rings)
+            per[key] = {"us_per_call": round(s * 1e6, 3), "GBps": round(b / s / 1e9, 1),
+                        "pct_hbm": round(100 * b / s / 1e9 / HBM_PEAK_GBPS, 2),
+                        "GBps_incl_gathered": round(bcb / s / 1e9, 1)}
+            del rings
+            torch.cuda.empty_cache()
+        out["gemv_m1_per_workload"] = per
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

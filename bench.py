@@ -92,7 +92,7 @@ def gathered_bytes(desc):
 class Ring:
     """Distinct copies of one workload layer on the device, plus ctypes argument tuples."""
 
-    def __init__(self, vq, torch, key, layer, m, copies=None, fn="vq_gemv", y_dtype=None):
+    def __init__(self, vq, torch, key, layer, m, copies=None, fn="vq_gemv", y_dtype=None, shared_book=False):
         layers, v, b1, b2, xd = WORKLOADS[key]
         n, i = layers[layer]
         self.desc = vq.make_desc(n, i, v, b1, b2)
@@ -113,8 +113,11 @@ class Ring:
         self.tensors = []
         for c in range(self.copies):
             packed = torch.randint(0, 256, (nb,), generator=g, device=dev, dtype=torch.uint8)
-            cb1 = (torch.randn((1 << b1, v), generator=g, device=dev) * 0.02).half()
-            cb2 = (torch.randn((1 << b2, v), generator=g, device=dev) * 0.005).half() if b2 else None
+            if shared_book and c > 0:
+                cb1, cb2 = self.tensors[0][1], self.tensors[0][2]
+            else:
+                cb1 = (torch.randn((1 << b1, v), generator=g, device=dev) * 0.02).half()
+                cb2 = (torch.randn((1 << b2, v), generator=g, device=dev) * 0.005).half() if b2 else None
             scale = (torch.rand((n,), generator=g, device=dev) + 0.5).half()
             y = torch.empty((m, n), device=dev, dtype=self.y_dtype)
             self.tensors.append((packed, cb1, cb2, scale, y))
@@ -217,6 +220,10 @@ def main():
     ap.add_argument("--only-headline", action="store_true", help="skip the GEMM, per-workload and CPU legs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 512 MiB device copy (known bytes) to scale rocprofv3 counters")
+    ap.add_argument("--shared-book", action="store_true",
+                    help="diagnostic: every ring copy shares one codebook (warm in L2), headline only")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
@@ -230,9 +237,17 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     vq.lib()
     use_graph = not args.no_graph
+    if args.copy_calibration:
+        src = torch.ones(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": src.numel(), "bytes_written": dst.numel(), "copies": 5}))
+        return
 
     # Headline: vq_gemv, 4096x4096, K1 = 65536, M = 1.
-    ring = Ring(vq, torch, "dec4k", 0, 1)
+    ring = Ring(vq, torch, "dec4k", 0, 1, shared_book=args.shared_book)
     log("headline ring: %d copies of %s, %.2f MB per call" % (ring.copies, DESCRIBE["dec4k"],
                                                               ring.bytes_per_call / 1e6))
     sec, n_calls, wall, launch = time_ring(torch, [ring], args.steps, args.warmup, use_graph)
@@ -271,7 +286,9 @@ def main():
                            "L2-served lookups eat the bandwidth savings"},
         "wall_s_timed": round(wall, 4),
     }
-    if not args.only_headline:
+    if args.shared_book:
+        out["config"]["diagnostic"] = "shared codebook across the ring (not the headline protocol)"
+    if not args.only_headline and not args.shared_book:
         # Prefill GEMM at M = 128 on the 70B-class pair.
         up = Ring(vq, torch, "l70b", 0, 128, copies=6, fn="vq_gemm")
         down = Ring(vq, torch, "l70b", 1, 128, copies=6, fn="vq_gemm")

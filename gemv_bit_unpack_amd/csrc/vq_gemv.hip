@@ -6,16 +6,20 @@
 // production-VQ post's "Dequantization Kernels and Inference Dynamics": small books in
 // on-chip memory, K >= 65536 books served from L2).
 //
-// gfx950 mapping.  One wavefront owns one output row at a time and walks its index
-// stream 64 vectors per step, lane l taking vector j0 + l, so the index words, the x
-// slices and the output of a step are contiguous across the wavefront.  Per vector a
-// lane unpacks its indices (one funnel shift), gathers the main centroid (LDS when
-// K1 <= 4096, else global memory through L2/MALL: a 1 MiB book stays cache-resident),
-// gathers the residual centroid from LDS, adds them in fp32 and multiply-accumulates
-// with x in fp32.  At the end of the row the 64 partial sums are reduced across the
-// wavefront and lane 0 applies the channel scale and bias.  Small codebooks are staged
-// once per workgroup (16 B per centroid, v <= 8); workgroups are persistent and
-// grid-stride over rows so the staging is amortised.
+// gfx950 mapping.  A wavefront walks its rows in groups of 64*U vectors; lane l takes
+// vectors g*64*U + u*64 + l (u < U), so the index words, the x slices and the gathers
+// of one instruction are spread over a contiguous run of the row: index and x loads are
+// coalesced, only the centroid gathers are random.  Per vector a lane unpacks its
+// indices, gathers the main centroid (LDS when K1 <= 4096, else global memory: a 1 MiB
+// book stays resident in each XCD's L2), gathers the residual centroid from LDS, adds
+// them in fp32 and multiply-accumulates with x in fp32.  The loop is software-pipelined:
+// the index loads of the next group are in flight while the current group's gathers
+// return, so every lane keeps U gathers outstanding.  At the end of a row the 64 partial
+// sums are reduced across the wavefront and lane 0 applies the channel scale and bias.
+// Small codebooks are staged once per workgroup (16 bytes per centroid, v <= 8) and
+// workgroups are persistent (grid-stride over rows) so the staging is amortised.  A
+// global main book is first streamed through L2 with coalesced loads (each workgroup its
+// share), so the random gathers that follow do not each pay an HBM miss.
 #include <mutex>
 
 #include "vq_device.h"
@@ -24,61 +28,65 @@ namespace {
 
 using vqi::ProductArgs;
 
-constexpr int kUnroll = 4;  // vectors in flight per lane
-
-// v halves of a centroid (fp16 bits) -> fp32.  Fast path for v = 6 and v = 8.
-template <int V>
-__device__ __forceinline__ void load_centroid_global(const uint16_t* __restrict__ cb, uint32_t k, float (&c)[V]) {
-  if constexpr (V == 8) {
-    const uint4 q = *(const uint4*)(cb + (size_t)k * 8);
-    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      c[2 * i] = vqd::f16_to_f32(w[i]);
-      c[2 * i + 1] = vqd::f16_to_f32(w[i] >> 16);
-    }
+// Index j of a row: IB = 16 reads a 16-bit field directly, IB = 0 funnels two words
+// (any width up to 16 bits).  Branch-free: the second word's index is clamped into the
+// row, so the last field of the last row never reads past the buffer.
+template <int IB>
+__device__ __forceinline__ uint32_t load_index(const uint32_t* __restrict__ row, int32_t row_words, uint32_t j,
+                                               uint32_t bits) {
+  if constexpr (IB == 16) {
+    return ((const uint16_t*)row)[j];
   } else {
-    static_assert(V == 6, "fast path covers v = 6 and v = 8");
-    const uint32_t* p = (const uint32_t*)(cb + (size_t)k * 6);
-    const uint32_t w[3] = {p[0], p[1], p[2]};
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      c[2 * i] = vqd::f16_to_f32(w[i]);
-      c[2 * i + 1] = vqd::f16_to_f32(w[i] >> 16);
-    }
+    const uint32_t bitpos = j * bits;
+    const uint32_t w = bitpos >> 5;
+    const uint32_t lo = row[w];
+    const uint32_t hi = row[min(w + 1u, (uint32_t)row_words - 1u)];
+    return __builtin_amdgcn_alignbit(hi, lo, bitpos & 31u) & ((1u << bits) - 1u);
   }
 }
 
+// Raw centroid (fp16 bits, zero padded to 8 halves).  v = 6 and v = 8.
 template <int V>
-__device__ __forceinline__ void load_centroid_lds(const uint4* lds, uint32_t k, float (&c)[V]) {
-  const uint4 q = lds[k];
-  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-  for (int t = 0; t < V; ++t) c[t] = vqd::f16_to_f32(w[t >> 1] >> (16 * (t & 1)));
+__device__ __forceinline__ uint4 gather_global(const uint16_t* __restrict__ cb, uint32_t k) {
+  if constexpr (V == 8) {
+    return *(const uint4*)(cb + (size_t)k * 8);
+  } else {
+    static_assert(V == 6, "fast path covers v = 6 and v = 8");
+    const uint32_t* p = (const uint32_t*)(cb + (size_t)k * 6);
+    return make_uint4(p[0], p[1], p[2], 0u);
+  }
 }
 
-// x[m][col0 .. col0 + V) as fp32; lanes past IN read as 0 without touching memory.
+__device__ __forceinline__ float half_at(const uint4& q, int t) {
+  const uint32_t w = t < 2 ? q.x : t < 4 ? q.y : t < 6 ? q.z : q.w;
+  return vqd::f16_to_f32((t & 1) ? (w >> 16) : w);
+}
+
+// x[m][col0 .. col0 + V) as fp32, branch-free.  The fast path guarantees IN % 8 == 0 for
+// v = 8 (so a vector is either whole or past the row: such lanes read a clamped vector
+// and are zeroed by the caller) and IN even for v = 6 (each x pair is either inside the
+// row or dropped, so the last, partial vector keeps exactly its valid lanes).
 template <int V, int XT>
 __device__ __forceinline__ void load_x(const uint16_t* __restrict__ xrow, int32_t col0, int32_t in_features,
                                        float (&xv)[V]) {
-  if (col0 + V <= in_features) {
-    uint32_t w[V / 2];
-    if constexpr (V == 8) {
-      const uint4 q = *(const uint4*)(xrow + col0);
-      w[0] = q.x; w[1] = q.y; w[2] = q.z; w[3] = q.w;
-    } else {
-      const uint32_t* p = (const uint32_t*)(xrow + col0);
-#pragma unroll
-      for (int i = 0; i < V / 2; ++i) w[i] = p[i];
-    }
-#pragma unroll
-    for (int i = 0; i < V / 2; ++i) {
-      xv[2 * i] = vqd::x_to_f32<XT>(w[i] & 0xFFFFu);
-      xv[2 * i + 1] = vqd::x_to_f32<XT>(w[i] >> 16);
-    }
+  uint32_t w[4];
+  if constexpr (V == 8) {
+    const uint4 q = *(const uint4*)(xrow + min(col0, in_features - 8));
+    w[0] = q.x; w[1] = q.y; w[2] = q.z; w[3] = q.w;
   } else {
+    const uint32_t* p = (const uint32_t*)xrow;
+    const int32_t last_pair = in_features / 2 - 1;
 #pragma unroll
-    for (int t = 0; t < V; ++t) xv[t] = (col0 + t < in_features) ? vqd::x_to_f32<XT>(xrow[col0 + t]) : 0.0f;
+    for (int d = 0; d < V / 2; ++d) {
+      const int32_t pair = col0 / 2 + d;
+      const uint32_t raw = p[min(pair, last_pair)];
+      w[d] = pair <= last_pair ? raw : 0u;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < V / 2; ++i) {
+    xv[2 * i] = vqd::x_to_f32<XT>(w[i] & 0xFFFFu);
+    xv[2 * i + 1] = vqd::x_to_f32<XT>(w[i] >> 16);
   }
 }
 
@@ -88,94 +96,160 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Fast path: v in {6, 8}, books staged as 16-byte LDS entries when small.
-template <int V, int MT, int XT, bool RES>
-__global__ __launch_bounds__(1024) void gemv_kernel(ProductArgs a, int lds1, int lds2) {
-  extern __shared__ uint4 lds_books[];
-  const uint4* book1 = lds_books;
-  const uint4* book2 = lds_books + (lds1 ? (1 << a.bits1) : 0);
-  // Stage small codebooks: entry k = v halves padded to 16 bytes.
-  {
-    const int k1 = lds1 ? (1 << a.bits1) : 0;
-    const int k2 = (RES && lds2) ? (1 << a.bits2) : 0;
-    for (int e = threadIdx.x; e < k1 + k2; e += blockDim.x) {
-      const uint16_t* src = e < k1 ? a.cb1 + (size_t)e * V : a.cb2 + (size_t)(e - k1) * V;
-      uint32_t w[4] = {0u, 0u, 0u, 0u};
+// Stage books into LDS as 16-byte entries.  Each thread first loads all of its entries
+// (up to kStageBatch per pass), then writes them, so the loads overlap.
+constexpr int kStageBatch = 8;
+template <int V>
+__device__ __forceinline__ void stage_books(uint4* lds, const uint16_t* cb1, int k1, const uint16_t* cb2, int k2,
+                                            int block) {
+  const int total = k1 + k2;
+  for (int base = 0; base < total; base += kStageBatch * block) {
+    uint4 q[kStageBatch];
 #pragma unroll
-      for (int i = 0; i < V / 2; ++i) w[i] = ((const uint32_t*)src)[i];
-      lds_books[e] = make_uint4(w[0], w[1], w[2], w[3]);
+    for (int b = 0; b < kStageBatch; ++b) {
+      const int e = min(base + b * block + (int)threadIdx.x, total - 1);
+      q[b] = e < k1 ? gather_global<V>(cb1, (uint32_t)e) : gather_global<V>(cb2, (uint32_t)(e - k1));
     }
+#pragma unroll
+    for (int b = 0; b < kStageBatch; ++b) {
+      const int e = base + b * block + (int)threadIdx.x;
+      if (e < total) lds[e] = q[b];
+    }
+  }
+}
+
+// Stream this workgroup's share of a global book through L2 (one 4-byte load per
+// 128-byte line, at most two per thread).  Workgroups are dealt to the XCDs round-robin,
+// so the groups on one XCD together cover the book.  The loaded words are only consumed
+// at the end of the kernel, so nothing waits for them.
+__device__ __forceinline__ void warm_book(const uint16_t* __restrict__ cb, uint32_t book_bytes, uint32_t block,
+                                          uint32_t grid, uint32_t (&w)[2]) {
+  const uint32_t lines = (book_bytes + 127u) / 128u;
+  const uint32_t per_xcd = (grid + 7u) / 8u;
+  const uint32_t share = (lines + per_xcd - 1u) / per_xcd;
+  const uint32_t first = (blockIdx.x / 8u) * share;
+  const uint32_t end = min(first + share, lines);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const uint32_t l = first + threadIdx.x + k * block;
+    w[k] = 0u;
+    if (l < end) w[k] = *(const uint32_t*)((const uint8_t*)cb + (size_t)l * 128u);
+  }
+}
+
+// IB1 = 16: 16-bit main indices into a global book (K1 = 65536); IB1 = 0: main book in
+// LDS (K1 <= 4096), any index width.  RES: residual book in LDS (K2 <= 4096).
+template <int V, int MT, int XT, int IB1, bool RES, int U>
+__global__ __launch_bounds__(1024) void gemv_kernel(ProductArgs a, int block, int grid) {
+  constexpr bool kLds1 = IB1 != 16;
+  extern __shared__ uint4 lds_books[];
+  const int k1 = kLds1 ? (1 << a.bits1) : 0;
+  const int k2 = RES ? (1 << a.bits2) : 0;
+  const uint4* book1 = lds_books;
+  const uint4* book2 = lds_books + k1;
+  uint32_t warm[2] = {0u, 0u};
+  if constexpr (!kLds1) warm_book(a.cb1, (uint32_t)(V * 2) << a.bits1, (uint32_t)block, (uint32_t)grid, warm);
+  if (k1 + k2 > 0) {
+    stage_books<V>(lds_books, a.cb1, k1, a.cb2, k2, block);
     __syncthreads();
   }
   const int lane = threadIdx.x & (vqd::kWave - 1);
-  const int waves_per_block = blockDim.x / vqd::kWave;
-  const int wave = blockIdx.x * waves_per_block + (threadIdx.x / vqd::kWave);
-  const int total_waves = gridDim.x * waves_per_block;
+  const int waves_per_block = block / vqd::kWave;
+  const int total_waves = grid * waves_per_block;
   const int m_count = a.m;
-  for (int row = wave; row < a.n; row += total_waves) {
-    const uint32_t* r1 = a.packed1 + (size_t)row * a.s1_words;
-    const uint32_t* r2 = RES ? a.packed2 + (size_t)row * a.s2_words : nullptr;
+  constexpr int kGroup = vqd::kWave * U;
+  const int groups = (a.nv + kGroup - 1) / kGroup;
+  const uint32_t last_j = (uint32_t)a.nv - 1u;
+
+  int row = blockIdx.x * waves_per_block + (threadIdx.x / vqd::kWave);
+  int g = 0;
+  if (row < a.n) {
+    uint32_t i1[U], i2[U];
+    auto fetch_idx = [&](int r, int gg, uint32_t(&o1)[U], uint32_t(&o2)[U]) {
+      const uint32_t* r1 = a.packed1 + (size_t)r * a.s1_words;
+      const uint32_t* r2 = RES ? a.packed2 + (size_t)r * a.s2_words : nullptr;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t j = min((uint32_t)(gg * kGroup + u * vqd::kWave + lane), last_j);
+        o1[u] = load_index<IB1>(r1, a.s1_words, j, a.bits1);
+        if constexpr (RES) o2[u] = load_index<0>(r2, a.s2_words, j, a.bits2);
+      }
+    };
+    fetch_idx(row, g, i1, i2);
     float acc[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
-    for (int j0 = 0; j0 < a.nv; j0 += vqd::kWave * kUnroll) {
-      uint32_t i1[kUnroll], i2[kUnroll];
-      bool live[kUnroll];
+    while (true) {
+      // gathers of the current group
+      uint4 c1[U], c2[U];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const uint32_t j = (uint32_t)(j0 + u * vqd::kWave + lane);
-        live[u] = (int)j < a.nv;
-        i1[u] = live[u] ? vqd::extract_index(r1, a.s1_words, j, a.bits1) : 0u;
-        if constexpr (RES) i2[u] = live[u] ? vqd::extract_index(r2, a.s2_words, j, a.bits2) : 0u;
-      }
-      float w[kUnroll][V];
-#pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        if (lds1) {
-          load_centroid_lds<V>(book1, i1[u], w[u]);
+      for (int u = 0; u < U; ++u) {
+        if constexpr (kLds1) {
+          c1[u] = book1[i1[u]];
         } else {
-          load_centroid_global<V>(a.cb1, i1[u], w[u]);
+          c1[u] = gather_global<V>(a.cb1, i1[u]);
         }
-        if constexpr (RES) {
-          float c2[V];
-          if (lds2) {
-            load_centroid_lds<V>(book2, i2[u], c2);
-          } else {
-            load_centroid_global<V>(a.cb2, i2[u], c2);
-          }
-#pragma unroll
-          for (int t = 0; t < V; ++t) w[u][t] = w[u][t] + c2[t];
-        }
+        if constexpr (RES) c2[u] = book2[i2[u]];
       }
+      // index loads of the next group (or a harmless repeat of this row's last group),
+      // in flight while the gathers return
+      int nrow = row, ng = g + 1;
+      if (ng == groups) {
+        ng = 0;
+        nrow = row + total_waves;
+      }
+      const bool has_next = nrow < a.n;
+      uint32_t n1[U], n2[U];
+      fetch_idx(has_next ? nrow : row, has_next ? ng : g, n1, n2);
+      // multiply-accumulate; lanes past the row contribute exactly zero
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        if (!live[u]) continue;
-        const int32_t col0 = (j0 + u * vqd::kWave + lane) * V;
+      for (int u = 0; u < U; ++u) {
+        const int j = g * kGroup + u * vqd::kWave + lane;
+        float w[V];
+#pragma unroll
+        for (int t = 0; t < V; ++t) {
+          w[t] = half_at(c1[u], t);
+          if constexpr (RES) w[t] = w[t] + half_at(c2[u], t);
+          if constexpr (V == 8) w[t] = j < a.nv ? w[t] : 0.0f;
+        }
+        const int32_t col0 = j * V;
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           if (m < m_count) {
             float xv[V];
             load_x<V, XT>(a.x + (size_t)m * a.in_features, col0, a.in_features, xv);
 #pragma unroll
-            for (int t = 0; t < V; ++t) acc[m] = __builtin_fmaf(xv[t], w[u][t], acc[m]);
+            for (int t = 0; t < V; ++t) acc[m] = __builtin_fmaf(xv[t], w[t], acc[m]);
           }
         }
       }
-    }
-    const float s = a.scale ? vqd::f16_to_f32(a.scale[row]) : 1.0f;
-    const float b = a.bias ? vqd::f16_to_f32(a.bias[row]) : 0.0f;
+      if (ng == 0 || !has_next) {  // row finished
+        const float s = a.scale ? vqd::f16_to_f32(a.scale[row]) : 1.0f;
+        const float b = a.bias ? vqd::f16_to_f32(a.bias[row]) : 0.0f;
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      if (m < m_count) {
-        float r = wave_sum(acc[m]);
-        if (lane == 0) {
-          if (a.scale) r = r * s;
-          if (a.bias) r = r + b;
-          vqd::store_out(a.y, (size_t)m * a.n + row, r, a.y_dtype);
+        for (int m = 0; m < MT; ++m) {
+          if (m < m_count) {
+            float r = wave_sum(acc[m]);
+            if (lane == 0) {
+              if (a.scale) r = r * s;
+              if (a.bias) r = r + b;
+              vqd::store_out(a.y, (size_t)m * a.n + row, r, a.y_dtype);
+            }
+          }
+          acc[m] = 0.0f;
         }
+      }
+      if (!has_next) break;
+      row = nrow;
+      g = ng;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        i1[u] = n1[u];
+        if constexpr (RES) i2[u] = n2[u];
       }
     }
   }
+  if (a.n < 0 && (warm[0] ^ warm[1]) == 0x9E3779B9u) ((uint32_t*)a.y)[0] = warm[0];  // never true: keeps the loads
 }
 
 // Generic path: any v in 1..16, centroids and x read element by element from global
@@ -223,47 +297,61 @@ __global__ __launch_bounds__(256) void gemv_generic_kernel(ProductArgs a) {
 }
 
 constexpr int kNumCU = 256;
+#ifndef VQ_GEMV_SMALL_BLOCK
+#define VQ_GEMV_SMALL_BLOCK 256  // threads per workgroup when the books need little LDS
+#endif
+#ifndef VQ_GEMV_SMALL_PER_CU
+#define VQ_GEMV_SMALL_PER_CU 8  // resident workgroups per CU assumed for the persistent grid
+#endif
+#ifndef VQ_GEMV_U1
+#define VQ_GEMV_U1 8  // vectors in flight per lane for M <= 2
+#endif
 
-template <int V, int MT, int XT, bool RES>
+template <int V, int MT, int XT, int IB1, bool RES>
 vq_status launch_fast(const ProductArgs& a, hipStream_t s) {
-  const int lds1 = a.bits1 <= 12 ? 1 : 0;
-  const int lds2 = (RES && a.bits2 <= 12) ? 1 : 0;
-  const size_t lds_bytes = 16u * ((lds1 ? (1u << a.bits1) : 0u) + (lds2 ? (1u << a.bits2) : 0u));
-  auto kern = gemv_kernel<V, MT, XT, RES>;
+  constexpr int U = MT <= 2 ? VQ_GEMV_U1 : (MT <= 8 ? 4 : 2);
+  constexpr bool kLds1 = IB1 != 16;
+  const size_t lds_bytes = 16u * ((kLds1 ? (1u << a.bits1) : 0u) + (RES ? (1u << a.bits2) : 0u));
+  auto kern = gemv_kernel<V, MT, XT, IB1, RES, U>;
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [&] {
     attr_err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   });
   if (attr_err != hipSuccess) return VQ_ERR_HIP;
-  // Big LDS footprint: one 1024-thread workgroup per CU; otherwise 256-thread groups.
-  const int block = lds_bytes > 32 * 1024 ? 1024 : 256;
-  const int per_cu = lds_bytes > 32 * 1024 ? 1 : (lds_bytes > 0 ? 8 : 8);
+  // Big LDS footprint: one 1024-thread workgroup per CU; otherwise smaller groups.
+  const bool big = lds_bytes > 32 * 1024;
+  const int block = big ? 1024 : VQ_GEMV_SMALL_BLOCK;
+  const int per_cu = big ? 1 : VQ_GEMV_SMALL_PER_CU;
   const int waves_per_block = block / vqd::kWave;
   const long want = (a.n + waves_per_block - 1) / waves_per_block;
   const long cap = (long)kNumCU * per_cu;
   const unsigned grid = (unsigned)(want < cap ? want : cap);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(block), lds_bytes, s, a, lds1, lds2);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(block), lds_bytes, s, a, block, (int)grid);
   return hipGetLastError() == hipSuccess ? VQ_OK : VQ_ERR_HIP;
 }
 
-template <int V, int XT, bool RES>
+template <int V, int XT, int IB1, bool RES>
 vq_status dispatch_m(const ProductArgs& a, hipStream_t s) {
-  if (a.m <= 1) return launch_fast<V, 1, XT, RES>(a, s);
-  if (a.m <= 2) return launch_fast<V, 2, XT, RES>(a, s);
-  if (a.m <= 4) return launch_fast<V, 4, XT, RES>(a, s);
-  if (a.m <= 8) return launch_fast<V, 8, XT, RES>(a, s);
-  return launch_fast<V, 16, XT, RES>(a, s);
+  if (a.m <= 1) return launch_fast<V, 1, XT, IB1, RES>(a, s);
+  if (a.m <= 2) return launch_fast<V, 2, XT, IB1, RES>(a, s);
+  if (a.m <= 4) return launch_fast<V, 4, XT, IB1, RES>(a, s);
+  if (a.m <= 8) return launch_fast<V, 8, XT, IB1, RES>(a, s);
+  return launch_fast<V, 16, XT, IB1, RES>(a, s);
 }
 
 template <int V, int XT>
-vq_status dispatch_res(const ProductArgs& a, hipStream_t s) {
-  return a.bits2 ? dispatch_m<V, XT, true>(a, s) : dispatch_m<V, XT, false>(a, s);
+vq_status dispatch_books(const ProductArgs& a, hipStream_t s) {
+  const bool main16 = a.bits1 == 16;
+  if (a.bits2) {
+    return main16 ? dispatch_m<V, XT, 16, true>(a, s) : dispatch_m<V, XT, 0, true>(a, s);
+  }
+  return main16 ? dispatch_m<V, XT, 16, false>(a, s) : dispatch_m<V, XT, 0, false>(a, s);
 }
 
 template <int V>
 vq_status dispatch_x(const ProductArgs& a, hipStream_t s) {
-  return a.x_dtype == VQ_BF16 ? dispatch_res<V, 1>(a, s) : dispatch_res<V, 0>(a, s);
+  return a.x_dtype == VQ_BF16 ? dispatch_books<V, 1>(a, s) : dispatch_books<V, 0>(a, s);
 }
 
 }  // namespace
@@ -272,14 +360,15 @@ namespace vqi {
 
 vq_status launch_gemv(const ProductArgs& a, void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  // The fast path needs vector-aligned codebooks and x rows.
-  const size_t vb = (size_t)a.v * 2;
+  // The fast path: v in {6, 8}; the main book either has 16-bit indices (global) or at
+  // most 4096 entries (LDS); the residual book, if any, at most 4096 entries (LDS);
+  // vector-aligned codebooks and x rows, IN a multiple of 8 (v = 8) or even (v = 6).
   const size_t align = (a.v == 8) ? 16 : 4;
-  const bool fast_shape = (a.v == 8 || a.v == 6);
+  const bool fast_shape = (a.v == 8 || a.v == 6) && (a.bits1 == 16 || a.bits1 <= 12) && a.bits2 <= 12 &&
+                          a.in_features >= 8;
   const bool fast_align = aligned(a.cb1, align) && (!a.cb2 || aligned(a.cb2, align)) && aligned(a.x, align) &&
                           (((size_t)a.in_features * 2) % align == 0);
-  (void)vb;
-  if (a.in_features > 0 && fast_shape && fast_align) {
+  if (fast_shape && fast_align) {
     return a.v == 8 ? dispatch_x<8>(a, s) : dispatch_x<6>(a, s);
   }
   const int block = 256;

@@ -219,6 +219,7 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a HIP graph")
     ap.add_argument("--only-headline", action="store_true", help="skip the GEMM, per-workload and CPU legs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-gemm", action="store_true", help="run only the M=128 prefill GEMM leg (for profiling)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 512 MiB device copy (known bytes) to scale rocprofv3 counters")
@@ -246,6 +247,14 @@ def main():
         print(json.dumps({"copy_calibration_bytes_read": src.numel(), "bytes_written": dst.numel(), "copies": 5}))
         return
 
+    if args.only_gemm:
+        up = Ring(vq, torch, "l70b", 0, 128, copies=6, fn="vq_gemm")
+        down = Ring(vq, torch, "l70b", 1, 128, copies=6, fn="vq_gemm")
+        gsec, gcalls, _, glaunch = time_ring(torch, [up, down], args.steps, args.warmup, use_graph)
+        flops = (up.flops_per_call + down.flops_per_call) / 2
+        print(json.dumps({"gemm_tflops": round(flops / gsec / 1e12, 2), "ms_per_call": round(gsec * 1e3, 4),
+                          "calls": gcalls, "launch": glaunch}))
+        return
     # Headline: vq_gemv, 4096x4096, K1 = 65536, M = 1.
     ring = Ring(vq, torch, "dec4k", 0, 1, shared_book=args.shared_book)
     log("headline ring: %d copies of %s, %.2f MB per call" % (ring.copies, DESCRIBE["dec4k"],

@@ -221,6 +221,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-gemm", action="store_true", help="run only the M=128 prefill GEMM leg (for profiling)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--ceilings", action="store_true",
+                    help="run only the hardware-ceiling microbenchmark (stream read, global and LDS gathers)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 512 MiB device copy (known bytes) to scale rocprofv3 counters")
     ap.add_argument("--shared-book", action="store_true",
@@ -230,6 +232,15 @@ def main():
         print("bench.py runs on one GPU: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
+
+    if args.ceilings:
+        import subprocess
+
+        exe = os.path.join(ROOT, "gemv_bit_unpack_amd", "micro", "vq_ceilings")
+        r = subprocess.run([exe], capture_output=True, text=True, timeout=300)
+        sys.stderr.write(r.stderr)
+        print(r.stdout.strip(), flush=True)
+        sys.exit(r.returncode)
 
     import torch
 
@@ -288,7 +299,7 @@ def main():
         "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": "gemv_kernel<8,1,0,false>"},
+                     "kernel": "gemv_kernel<8,1,0,16,false,8>"},
         "gather": {"gathers_per_s": round(ring.desc.out_features * nv / sec, 1),
                    "effective_incl_gathered_centroids_GBps": round(g_cb, 2),
                    "note": "16-byte centroid gathers from the 1 MiB book through L2; the pages warn that "

@@ -17,6 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libvq.so")
+CEILINGS_SRC = os.path.join(PKG, "micro", "ceilings.hip")
+CEILINGS_BIN = os.path.join(PKG, "micro", "vq_ceilings")
 SOURCES = ["vq_host.cpp", "vq_dequant.hip", "vq_gemv.hip", "vq_gemm.hip"]
 ARCH = "gfx950"
 
@@ -60,9 +62,21 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError("link failed: %s\n%s\n%s" % (" ".join(cmd), r.stdout, r.stderr))
     os.replace(tmp, LIB)
+    build_ceilings()
     if verbose:
         print("built", LIB)
     return LIB
+
+
+def build_ceilings() -> str:
+    """The hardware-ceiling microbenchmark (stream read, global and LDS gathers)."""
+    tmp = CEILINGS_BIN + ".tmp%d" % os.getpid()
+    cmd = [_hipcc(), "-O3", "-std=c++17", *HIP_ONLY, "-o", tmp, CEILINGS_SRC]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("compile failed: %s\n%s\n%s" % (" ".join(cmd), r.stdout, r.stderr))
+    os.replace(tmp, CEILINGS_BIN)
+    return CEILINGS_BIN
 
 
 if __name__ == "__main__":

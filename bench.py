@@ -2,9 +2,9 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
-A step is one vq_gemv call (M = 1) on a 4096 x 4096 layer with v = 8 and a
-65536-entry main codebook (2 index bits per weight), fp16 x, fp16 y: the decode GEMV
-the metric is quoted on.  Steps rotate through a ring of distinct layer copies (own
+A step is one vq_gemv_ws call (vq_gemv with a caller-owned workspace, M = 1) on a
+4096 x 4096 layer with v = 8 and a 65536-entry main codebook (2 index bits per weight),
+fp16 x, fp16 y: the decode GEMV the metric is quoted on.  Steps rotate through a ring of distinct layer copies (own
 indices, codebook and scale each) totalling more than 1 GiB, so the 256 MB
 Infinity Cache cannot hold the stream and every step reads its indices from HBM.
 
@@ -92,7 +92,7 @@ def gathered_bytes(desc):
 class Ring:
     """Distinct copies of one workload layer on the device, plus ctypes argument tuples."""
 
-    def __init__(self, vq, torch, key, layer, m, copies=None, fn="vq_gemv", y_dtype=None, shared_book=False):
+    def __init__(self, vq, torch, key, layer, m, copies=None, fn="vq_gemv_ws", y_dtype=None, shared_book=False):
         layers, v, b1, b2, xd = WORKLOADS[key]
         n, i = layers[layer]
         self.desc = vq.make_desc(n, i, v, b1, b2)
@@ -109,6 +109,12 @@ class Ring:
         self.items = []
         lib = vq.lib()
         self.fn = getattr(lib, fn)
+        # one workspace for the whole ring: its calls run in order on one stream
+        self.ws = vq.workspace(self.desc, m, xdt, dev) if fn == "vq_gemv_ws" else None
+        self.sliced = self.ws is not None
+        extra = ()
+        if fn == "vq_gemv_ws":
+            extra = (None, 0) if self.ws is None else (ctypes.c_void_p(self.ws.data_ptr()), self.ws.numel())
         code = {torch.float16: vq.VQ_F16, torch.bfloat16: vq.VQ_BF16, torch.float32: vq.VQ_F32}
         self.tensors = []
         for c in range(self.copies):
@@ -123,7 +129,7 @@ class Ring:
             self.tensors.append((packed, cb1, cb2, scale, y))
             p = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
             self.items.append((ctypes.byref(self.desc), p(packed), p(cb1), p(cb2), p(scale), None, p(self.x),
-                               code[xdt], m, p(y), code[self.y_dtype]))
+                               code[xdt], m, p(y), code[self.y_dtype]) + extra)
         self.bytes_per_call = layer_bytes(vq, self.desc, m, 4 if self.y_dtype == torch.float32 else 2)
         self.flops_per_call = 2.0 * m * n * i
 
@@ -148,6 +154,11 @@ def time_ring(torch, rings, steps, warmup, use_graph=True):
             graph = torch.cuda.CUDAGraph()
             side = torch.cuda.Stream()
             side.wait_stream(stream)
+            # warm up on the capture stream too
+            ssp = ctypes.c_void_p(side.cuda_stream)
+            for r, k in seq[:2]:
+                r.call(k, ssp)
+            side.synchronize()
             with torch.cuda.graph(graph, stream=side):
                 gsp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
                 for r, k in seq:
@@ -278,7 +289,7 @@ def main():
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        if tr.get("source_hash") == source_hash(GEMV_SOURCES):
+        if not ring.sliced and tr.get("source_hash") == source_hash(GEMV_SOURCES):
             traffic = tr.get("hbm_bytes_per_launch")
     out = {
         "metric": "vq_gemv effective GB/s & % HBM peak at M=1; vq_gemm TFLOP/s at M=128",
@@ -299,11 +310,11 @@ def main():
         "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": "gemv_kernel<8,1,0,16,false,8>"},
+                     "kernel": "gemv_sliced_kernel<false>" if ring.sliced else "gemv_kernel<8,1,0,16,false,8>"},
         "gather": {"gathers_per_s": round(ring.desc.out_features * nv / sec, 1),
                    "effective_incl_gathered_centroids_GBps": round(g_cb, 2),
-                   "note": "16-byte centroid gathers from the 1 MiB book through L2; the pages warn that "
-                           "L2-served lookups eat the bandwidth savings"},
+                   "note": "every 16-byte centroid lookup counted once: through L2 for the gather kernel, "
+                           "from the 128 KiB LDS slices for the codebook-sliced one"},
         "wall_s_timed": round(wall, 4),
     }
     if args.shared_book:
@@ -321,18 +332,45 @@ def main():
         del up, down
         torch.cuda.empty_cache()
         per = {}
-        for key in WORKLOADS:
-            layers = WORKLOADS[key][0]
-            rings = [Ring(vq, torch, key, li, 1) for li in range(len(layers))]
-            s, c, _, _ = time_ring(torch, rings, max(200, 2 * sum(r.copies for r in rings)), 20, use_graph)
+
+        def measure(rings):
+            s, _, _, _ = time_ring(torch, rings, max(200, 2 * sum(r.copies for r in rings)), 20, use_graph)
             b = sum(r.bytes_per_call for r in rings) / len(rings)
             bcb = sum(r.bytes_per_call + gathered_bytes(r.desc) for r in rings) / len(rings)
-            per[key] = {"us_per_call": round(s * 1e6, 3), "GBps": round(b / s / 1e9, 1),
-                        "pct_hbm": round(100 * b / s / 1e9 / HBM_PEAK_GBPS, 2),
-                        "GBps_incl_gathered": round(bcb / s / 1e9, 1)}
+            return {"us_per_call": round(s * 1e6, 3), "GBps": round(b / s / 1e9, 1),
+                    "pct_hbm": round(100 * b / s / 1e9 / HBM_PEAK_GBPS, 2),
+                    "GBps_incl_gathered": round(bcb / s / 1e9, 1)}
+
+        for key in WORKLOADS:
+            n_layers = len(WORKLOADS[key][0])
+            rings = [Ring(vq, torch, key, li, 1) for li in range(n_layers)]
+            sliced = any(r.sliced for r in rings)
+            entry = measure(rings)
+            entry["kernel"] = "codebook-sliced" if sliced else "gather"
             del rings
             torch.cuda.empty_cache()
+            if sliced:  # the same layers through vq_gemv (no workspace): the L2-gather kernel
+                rings = [Ring(vq, torch, key, li, 1, fn="vq_gemv") for li in range(n_layers)]
+                entry["gather_kernel_us_per_call"] = measure(rings)["us_per_call"]
+                del rings
+                torch.cuda.empty_cache()
+            per[key] = entry
         out["gemv_m1_per_workload"] = per
+        # Decode batches with the 65536-entry book: vq_gemv_ws against vq_gemv.
+        batch = {}
+        for key, m in (("dec4k_res", 4), ("dec4k_res", 16), ("l70b", 8)):
+            n_layers = len(WORKLOADS[key][0])
+            entry = {}
+            for fn in ("vq_gemv_ws", "vq_gemv"):
+                rings = [Ring(vq, torch, key, li, m, fn=fn, copies=8) for li in range(n_layers)]
+                s, _, _, _ = time_ring(torch, rings, 64, 8, use_graph)
+                entry[fn + "_us_per_call"] = round(s * 1e6, 3)
+                if fn == "vq_gemv_ws":
+                    entry["kernel"] = "codebook-sliced" if any(r.sliced for r in rings) else "gather"
+                del rings
+                torch.cuda.empty_cache()
+            batch["%s_m%d" % (key, m)] = entry
+        out["gemv_batched"] = batch
         if not args.no_cpu_baseline:
             out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)

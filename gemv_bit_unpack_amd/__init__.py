@@ -10,9 +10,12 @@ Calls (same names as the C ABI):
     pack(desc, idx1, idx2=None) -> numpy uint8 (host packing, layout of vq.h)
     dequant(desc, packed, cb1, cb2, scale, w_dtype=torch.float32, out=None) -> W^ [N, IN]
     gemv(desc, packed, cb1, cb2, scale, bias, x, y_dtype=None, out=None)  # 1 <= M <= 16
+    gemv_workspace_bytes(desc, m, x_dtype) -> int
+    gemv_ws(desc, packed, cb1, cb2, scale, bias, x, workspace, y_dtype=None, out=None)
     gemm(desc, packed, cb1, cb2, scale, bias, x, y_dtype=None, out=None)  # any M, MFMA
-and ``VQLinear``, a layer object holding the packed weights that picks gemv or gemm
-by batch size, the analogue of the VPTQ guide's ``VPTQLinear`` module.
+plus ``workspace(desc, m, x_dtype, device)``, a zero-filled device buffer for gemv_ws,
+and ``VQLinear``, a layer object holding the packed weights that picks gemv(_ws) or
+gemm by batch size, the analogue of the VPTQ guide's ``VPTQLinear`` module.
 """
 from __future__ import annotations
 
@@ -37,7 +40,8 @@ VQ_ERR_HIP = -8
 VQ_F16, VQ_BF16, VQ_F32 = 0, 1, 2
 LAYOUT_ROWSTREAM = 1
 
-EXPORTED = ("vq_abi_version", "vq_status_string", "vq_packed_bytes", "vq_pack", "vq_dequant", "vq_gemv", "vq_gemm")
+EXPORTED = ("vq_abi_version", "vq_status_string", "vq_packed_bytes", "vq_pack", "vq_dequant", "vq_gemv",
+            "vq_gemv_workspace_bytes", "vq_gemv_ws", "vq_gemm")
 
 
 class Desc(ctypes.Structure):
@@ -79,6 +83,10 @@ def _load():
         f = getattr(lib, name)
         f.argtypes = [dp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i32, vp, ctypes.c_int, vp]
         f.restype = ctypes.c_int
+    lib.vq_gemv_workspace_bytes.argtypes = [dp, i32, ctypes.c_int, ctypes.POINTER(sz)]
+    lib.vq_gemv_workspace_bytes.restype = ctypes.c_int
+    lib.vq_gemv_ws.argtypes = [dp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i32, vp, ctypes.c_int, vp, sz, vp]
+    lib.vq_gemv_ws.restype = ctypes.c_int
     return lib
 
 
@@ -177,7 +185,7 @@ def dequant(desc: Desc, packed, cb1, cb2, scale, w_dtype=None, out=None):
     return out
 
 
-def _product(fn, name, desc, packed, cb1, cb2, scale, bias, x, y_dtype, out):
+def _product(fn, name, desc, packed, cb1, cb2, scale, bias, x, y_dtype, out, extra=()):
     torch = _torch()
     if x.dim() != 2 or x.shape[1] != desc.in_features:
         raise ValueError("x must be [M, %d], got %s" % (desc.in_features, tuple(x.shape)))
@@ -189,7 +197,7 @@ def _product(fn, name, desc, packed, cb1, cb2, scale, bias, x, y_dtype, out):
     st = fn(ctypes.byref(desc), _dev_ptr(packed, "packed"), _dev_ptr(cb1, "cb1", f16),
             _dev_ptr(cb2, "cb2", f16) if desc.bits2 else None, _dev_ptr(scale, "scale", f16),
             _dev_ptr(bias, "bias", f16), _dev_ptr(x, "x", (torch.float16, torch.bfloat16)), _dtype_code(x.dtype),
-            m, _dev_ptr(out, "out"), _dtype_code(out.dtype), _stream_ptr(x.device))
+            m, _dev_ptr(out, "out"), _dtype_code(out.dtype), *extra, _stream_ptr(x.device))
     _check(st, name)
     return out
 
@@ -198,15 +206,60 @@ def gemv(desc, packed, cb1, cb2, scale, bias, x, y_dtype=None, out=None):
     return _product(lib().vq_gemv, "vq_gemv", desc, packed, cb1, cb2, scale, bias, x, y_dtype, out)
 
 
+def gemv_workspace_bytes(desc: Desc, m: int, x_dtype) -> int:
+    """Workspace bytes for gemv_ws at batch m with activations of torch dtype x_dtype (0: none used)."""
+    n = ctypes.c_size_t(0)
+    _check(lib().vq_gemv_workspace_bytes(ctypes.byref(desc), int(m), _dtype_code(x_dtype), ctypes.byref(n)),
+           "vq_gemv_workspace_bytes")
+    return int(n.value)
+
+
+def workspace(desc: Desc, m: int, x_dtype, device="cuda"):
+    """A zero-filled device workspace for gemv_ws (None when the shape needs none)."""
+    nbytes = gemv_workspace_bytes(desc, m, x_dtype)
+    if nbytes == 0:
+        return None
+    return _torch().zeros(nbytes, dtype=_torch().uint8, device=device)
+
+
+def gemv_ws(desc, packed, cb1, cb2, scale, bias, x, ws, y_dtype=None, out=None):
+    """gemv with a caller-owned workspace (from ``workspace``; None: plain gemv).
+
+    Calls that share a workspace must be ordered (one stream)."""
+    extra = (None, 0) if ws is None else (_dev_ptr(ws, "workspace"), ws.numel() * ws.element_size())
+    return _product(lib().vq_gemv_ws, "vq_gemv_ws", desc, packed, cb1, cb2, scale, bias, x, y_dtype, out, extra)
+
+
 def gemm(desc, packed, cb1, cb2, scale, bias, x, y_dtype=None, out=None):
     return _product(lib().vq_gemm, "vq_gemm", desc, packed, cb1, cb2, scale, bias, x, y_dtype, out)
+
+
+_stream_ws = {}
+
+
+def stream_workspace(desc: Desc, m: int, x_dtype, device):
+    """A workspace kept per (device, current stream), grown on demand, for layers that run
+    their calls in stream order.  None when the shape needs none."""
+    torch = _torch()
+    nbytes = gemv_workspace_bytes(desc, m, x_dtype)
+    if nbytes == 0:
+        return None
+    dev = torch.device(device)
+    key = (dev.index if dev.index is not None else torch.cuda.current_device(),
+           torch.cuda.current_stream(dev).cuda_stream)
+    ws = _stream_ws.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
+        _stream_ws[key] = ws
+    return ws
 
 
 class VQLinear:
     """A quantized linear layer: packed indices, fp16 codebooks, per-channel scale, bias.
 
     ``forward(x)`` computes x W^T (+ bias) for x of shape [..., in_features]; batches of
-    up to ``gemv_max_m`` rows take the VALU decode kernel, larger ones the MFMA kernel.
+    up to ``gemv_max_m`` rows take gemv_ws (the codebook-sliced kernel where the shape has
+    it, with a workspace kept per device and stream), larger ones the MFMA GEMM.
     """
 
     def __init__(self, desc: Desc, packed, cb1, cb2=None, scale=None, bias=None, gemv_max_m: int = 16):
@@ -223,8 +276,12 @@ class VQLinear:
     def forward(self, x, y_dtype=None):
         lead = x.shape[:-1]
         x2 = x.reshape(-1, x.shape[-1]).contiguous()
-        fn = gemv if x2.shape[0] <= self.gemv_max_m else gemm
-        y = fn(self.desc, self.packed, self.cb1, self.cb2, self.scale, self.bias, x2, y_dtype)
+        args = (self.desc, self.packed, self.cb1, self.cb2, self.scale, self.bias, x2)
+        if x2.shape[0] <= self.gemv_max_m:
+            ws = stream_workspace(self.desc, x2.shape[0], x2.dtype, x2.device)
+            y = gemv_ws(*args, ws, y_dtype)
+        else:
+            y = gemm(*args, y_dtype)
         return y.reshape(*lead, self.desc.out_features)
 
     __call__ = forward

@@ -183,6 +183,32 @@ vq_status vq_gemv(const vq_desc* desc, const void* packed, const void* cb1, cons
   return launch_gemv(a, stream);
 }
 
+vq_status vq_gemv_workspace_bytes(const vq_desc* desc, int32_t M, vq_dtype x_dtype, size_t* nbytes) {
+  if (!nbytes) return VQ_ERR_NULL;
+  vq_status st = check_desc(desc);
+  if (st != VQ_OK) return st;
+  if (M < 0 || M > 16) return VQ_ERR_SHAPE;
+  if (x_dtype != VQ_F16 && x_dtype != VQ_BF16) return VQ_ERR_UNSUPPORTED;
+  *nbytes = sliced_gemv_workspace(*desc, M, x_dtype);
+  return VQ_OK;
+}
+
+vq_status vq_gemv_ws(const vq_desc* desc, const void* packed, const void* cb1, const void* cb2, const void* scale,
+                     const void* bias, const void* x, vq_dtype x_dtype, int32_t M, void* y, vq_dtype y_dtype,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  ProductArgs a;
+  vq_status st = prepare_product(desc, packed, cb1, cb2, scale, bias, x, x_dtype, M, y, y_dtype, 16, &a);
+  if (st != VQ_OK) return st;
+  if (a.n == 0 || a.m == 0) return VQ_OK;
+  const size_t need = sliced_gemv_workspace(*desc, a.m, a.x_dtype);
+  if (workspace && need > 0) {
+    if (workspace_bytes < need) return VQ_ERR_BUFFER_SIZE;
+    if (!aligned(workspace, 256)) return VQ_ERR_ALIGN;
+    if (sliced_gemv_pointers_ok(a)) return launch_gemv_sliced(a, workspace, stream);
+  }
+  return launch_gemv(a, stream);
+}
+
 vq_status vq_gemm(const vq_desc* desc, const void* packed, const void* cb1, const void* cb2, const void* scale,
                   const void* bias, const void* x, vq_dtype x_dtype, int32_t M, void* y, vq_dtype y_dtype,
                   void* stream) {

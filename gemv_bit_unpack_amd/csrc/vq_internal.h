@@ -4,6 +4,8 @@
 #include <cstddef>
 #include <cstdint>
 
+#include <hip/hip_runtime_api.h>
+
 #include "vq.h"
 
 namespace vqi {
@@ -54,6 +56,13 @@ vq_status prepare_product(const vq_desc* desc, const void* packed, const void* c
 vq_status launch_dequant(const vq_desc& d, const void* packed, const void* cb1, const void* cb2, const void* scale,
                          void* w, vq_dtype w_dtype, void* stream);
 vq_status launch_gemv(const ProductArgs& a, void* stream);
+// The codebook-sliced GEMV (65536-entry main book, v = 8, 1 <= M <= 16) that runs with a
+// caller-owned workspace: whether the shape has that path and the workspace it needs (0:
+// none), whether the pointers allow it, and the launch.
+bool sliced_gemv_shape_ok(const vq_desc& d, int32_t m, vq_dtype x_dtype);
+size_t sliced_gemv_workspace(const vq_desc& d, int32_t m, vq_dtype x_dtype);
+bool sliced_gemv_pointers_ok(const ProductArgs& a);
+vq_status launch_gemv_sliced(const ProductArgs& a, void* workspace, void* stream);
 vq_status launch_gemm(const ProductArgs& a, void* stream);
 
 }  // namespace vqi

@@ -35,7 +35,8 @@
  * (NULL = the default stream).  These three calls validate on the host, enqueue kernels
  * on `stream` and return without synchronising: inputs must stay unchanged until the
  * stream has run them, and y / w must not alias any input.  The library allocates no
- * memory, keeps no pointer after returning and is safe to call from several threads.
+ * memory (vq_gemv_ws takes its scratch space from the caller), keeps no pointer after
+ * returning and is safe to call from several threads.
  * vq_packed_bytes and vq_pack work on HOST memory and are synchronous.
  *
  * Errors.  Every argument is checked before anything is enqueued; on error nothing is
@@ -63,7 +64,7 @@ typedef enum vq_status {
   VQ_ERR_UNSUPPORTED = -4,  /* valid but not built for the GPU (v, bits, dtype combination), unknown layout */
   VQ_ERR_ALIGN = -5,        /* a device pointer is not aligned as the call requires */
   VQ_ERR_INDEX_RANGE = -6,  /* vq_pack: an index is >= 2^bits */
-  VQ_ERR_BUFFER_SIZE = -7,  /* vq_pack: nbytes < vq_packed_bytes */
+  VQ_ERR_BUFFER_SIZE = -7,  /* vq_pack: nbytes < vq_packed_bytes; vq_gemv_ws: workspace too small */
   VQ_ERR_HIP = -8           /* the HIP runtime reported an error at launch */
 } vq_status;
 
@@ -112,6 +113,34 @@ vq_status vq_dequant(const vq_desc* desc, const void* packed, const void* cb1, c
 vq_status vq_gemv(const vq_desc* desc, const void* packed, const void* cb1, const void* cb2, const void* scale,
                   const void* bias, const void* x, vq_dtype x_dtype, int32_t M, void* y, vq_dtype y_dtype,
                   void* stream);
+
+/* Bytes of device workspace with which vq_gemv_ws runs `desc` at batch M (1..16) with
+ * activations of x_dtype on its codebook-sliced path; 0 when the shape does not take
+ * that path.  It needs v = 8, bits1 = 16, bits2 = 0 or 8, IN a multiple of 8, and at
+ * least 2^22 weight vectors (N * IN / 8) for M < 8 or 2^19 for M >= 8: below that the
+ * vq_gemv kernels are as fast.  M = 0 gives 0. */
+vq_status vq_gemv_workspace_bytes(const vq_desc* desc, int32_t M, vq_dtype x_dtype, size_t* nbytes);
+
+/* vq_gemv with a caller-owned device workspace, for the 65536-entry main book (VPTQ
+ * guide, "Step 3: Fused Low-Bit VPTQ Linear Layer"; the production-VQ post, "Lookup
+ * Table (LUT) Overhead vs. Bit-Shifting", on lookups that spill out of fast memory).
+ * The book is split into eight 8192-centroid slices, each held in the LDS of the CUs
+ * that serve it; the matrix cores form the dot products; per-slice fp32 partial sums
+ * go to the workspace and a second kernel adds them in a fixed order, so results are
+ * deterministic.  bf16 activations are rewritten as fp16 times a power of two per
+ * batch row, which is exact for every value whose magnitude lies within
+ * 2^-16 .. 65504 times that power; smaller values round with an absolute error below
+ * 2^-25 times it.
+ * Same arguments, results (to the vq_gemv tolerance) and errors as vq_gemv, plus:
+ *   workspace: NULL (then this is vq_gemv), or device memory, 256-byte aligned, of at
+ *     least vq_gemv_workspace_bytes(desc, M, x_dtype) bytes (VQ_ERR_BUFFER_SIZE /
+ *     VQ_ERR_ALIGN otherwise).  Its contents need no initialisation and are scratch
+ *     after the call; calls that may run at the same time need different workspaces.
+ * Shapes without the sliced path, or packed / cb1 / cb2 / x pointers that are not
+ * 16-byte aligned, run the vq_gemv kernels and leave the workspace untouched. */
+vq_status vq_gemv_ws(const vq_desc* desc, const void* packed, const void* cb1, const void* cb2, const void* scale,
+                     const void* bias, const void* x, vq_dtype x_dtype, int32_t M, void* y, vq_dtype y_dtype,
+                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Same operation and arguments as vq_gemv for any M >= 1 (M = 0: no-op), on the matrix
  * cores: rebuilt weight tiles are staged in LDS in the activation's 16-bit type and

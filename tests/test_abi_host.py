@@ -166,3 +166,56 @@ def test_dequant_validation_paths(vq):
     assert f(ctypes.byref(d), P_MIS, P, P, None, P, 2, None) == vq.VQ_ERR_ALIGN
     assert f(ctypes.byref(d), P, P, P, None, P_MIS, 2, None) == vq.VQ_ERR_ALIGN
     assert f(ctypes.byref(vq.make_desc(64, 0, 8, 8, 8)), None, None, None, None, None, 2, None) == vq.VQ_OK
+
+
+def _gemv_ws(vq, desc, ws=None, ws_bytes=0, packed=P, cb1=P, cb2=P, x=P, xt=0, m=1, y=P, yt=2):
+    return vq.lib().vq_gemv_ws(ctypes.byref(desc) if desc is not None else None, packed, cb1, cb2, None, None, x, xt,
+                               m, y, yt, ws, ws_bytes, None)
+
+
+def _ws_bytes(vq, desc, m, xt):
+    n = ctypes.c_size_t(12345)
+    st = vq.lib().vq_gemv_workspace_bytes(ctypes.byref(desc) if desc is not None else None, m, xt, ctypes.byref(n))
+    return st, int(n.value)
+
+
+def test_gemv_workspace_bytes(vq):
+    big = vq.make_desc(8192, 4096, 8, 16, 0)  # 2^22 vectors: sliced from M = 1
+    st, f16 = _ws_bytes(vq, big, 1, vq.VQ_F16)
+    assert st == vq.VQ_OK and f16 > 0 and f16 % 256 == 0
+    assert _ws_bytes(vq, big, 1, vq.VQ_BF16)[1] > f16          # + the fp16 copy of x
+    assert _ws_bytes(vq, big, 16, vq.VQ_F16)[1] > f16          # partials per batch row
+    assert _ws_bytes(vq, vq.make_desc(16384, 4096, 8, 16, 8), 1, vq.VQ_F16)[1] > f16
+    dec = vq.make_desc(4096, 4096, 8, 16, 0)  # 2^21 vectors: sliced from M = 8 only
+    assert _ws_bytes(vq, dec, 1, vq.VQ_F16) == (vq.VQ_OK, 0)
+    assert _ws_bytes(vq, dec, 7, vq.VQ_F16) == (vq.VQ_OK, 0)
+    assert _ws_bytes(vq, dec, 8, vq.VQ_F16)[1] > 0
+    # shapes without the sliced path need none
+    for d in (vq.make_desc(14336, 4096, 6, 12, 12), vq.make_desc(4096, 4096, 8, 12, 0),
+              vq.make_desc(4096, 4096, 8, 16, 4), vq.make_desc(4096, 4100, 8, 16, 0),
+              vq.make_desc(256, 256, 8, 16, 0), vq.make_desc(0, 4096, 8, 16, 0)):
+        assert _ws_bytes(vq, d, 8, vq.VQ_F16) == (vq.VQ_OK, 0), d
+    assert _ws_bytes(vq, big, 0, vq.VQ_F16) == (vq.VQ_OK, 0)
+    # errors leave the output alone
+    assert _ws_bytes(vq, big, 17, vq.VQ_F16) == (vq.VQ_ERR_SHAPE, 12345)
+    assert _ws_bytes(vq, big, -1, vq.VQ_F16) == (vq.VQ_ERR_SHAPE, 12345)
+    assert _ws_bytes(vq, big, 1, vq.VQ_F32) == (vq.VQ_ERR_UNSUPPORTED, 12345)
+    assert _ws_bytes(vq, None, 1, vq.VQ_F16) == (vq.VQ_ERR_NULL, 12345)
+    assert _ws_bytes(vq, vq.make_desc(64, 64, 8, 0, 0), 1, vq.VQ_F16) == (vq.VQ_ERR_BITS, 12345)
+    assert vq.lib().vq_gemv_workspace_bytes(ctypes.byref(big), 1, 0, None) == vq.VQ_ERR_NULL
+
+
+def test_gemv_ws_validation_paths(vq):
+    d = vq.make_desc(8192, 4096, 8, 16, 0)  # a shape with the sliced path
+    need = _ws_bytes(vq, d, 1, vq.VQ_F16)[1]
+    # the vq_gemv argument checks come first
+    assert _gemv_ws(vq, None, ws=P, ws_bytes=need) == vq.VQ_ERR_NULL
+    assert _gemv_ws(vq, d, ws=P, ws_bytes=need, m=17) == vq.VQ_ERR_SHAPE
+    assert _gemv_ws(vq, d, ws=P, ws_bytes=need, xt=2) == vq.VQ_ERR_UNSUPPORTED
+    assert _gemv_ws(vq, d, ws=P, ws_bytes=need, x=ctypes.c_void_p(0x10001)) == vq.VQ_ERR_ALIGN
+    # then the workspace: size, 256-byte alignment
+    assert _gemv_ws(vq, d, ws=P, ws_bytes=need - 1) == vq.VQ_ERR_BUFFER_SIZE
+    assert _gemv_ws(vq, d, ws=P, ws_bytes=0) == vq.VQ_ERR_BUFFER_SIZE
+    assert _gemv_ws(vq, d, ws=ctypes.c_void_p(0x10010), ws_bytes=need) == vq.VQ_ERR_ALIGN
+    # nothing to do
+    assert _gemv_ws(vq, d, ws=P, ws_bytes=0, m=0, y=None, x=None, packed=None) == vq.VQ_OK

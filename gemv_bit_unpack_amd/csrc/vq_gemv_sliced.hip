@@ -18,7 +18,7 @@
 //     slice s and a zero centroid otherwise (a select, no branch), and the matrix core
 //     forms the 16 rows' dot products with x, batch row m in output column m.  The 8
 //     row groups of the tile keep their accumulators in registers across the chunks;
-//   - the residual centroid of vector j is added by slice workgroup s = j mod 8;
+//   - the residual centroids of the tile's row group s are added by slice workgroup s;
 //   - a chunk's activations are loaded one chunk ahead, and each row group's index words
 //     for the next chunk are loaded right after the row group is used;
 //   - at the end of a tile the 8 column blocks are added in LDS and the workgroup stores
@@ -135,24 +135,24 @@ __global__ __launch_bounds__(kThreads) void gemv_sliced_kernel(ProductArgs a, Sl
     const uint32_t c16 = j0 < (uint32_t)nv ? (j0 >> 3) : 0u;
     return (uint32_t)row * s1b + c16 * 16u;
   };
-  auto res_off = [&](int rb, int cc, int q) __attribute__((always_inline)) -> uint32_t {
-    const int row = min(rb * kRT + q * 16 + r16, N - 1);
-    const uint32_t jr = min((uint32_t)cc * kChunk + lane_col + (uint32_t)s, (uint32_t)nv - 1u);
-    return (uint32_t)row * s2b + jr;
+  // byte offset of the lane's 8 residual indices (row group s of row block rb, chunk cc)
+  auto res_off = [&](int rb, int cc) __attribute__((always_inline)) -> uint32_t {
+    const int row = min(rb * kRT + s * 16 + r16, N - 1);
+    const uint32_t j0 = (uint32_t)cc * kChunk + lane_col;
+    return (uint32_t)row * s2b + (j0 < (uint32_t)nv ? j0 : 0u);
   };
-  // activations of the lane's 8 vectors and of the vector whose residual this slice adds;
-  // lanes of batch rows >= M load row M - 1 (they feed output columns that are dropped)
-  auto load_x = [&](int cc, uint4 (&xr)[8], uint4& xres) __attribute__((always_inline)) {
+  // activations of the lane's 8 vectors; lanes of batch rows >= M load row M - 1 (they
+  // feed output columns that are dropped)
+  auto load_x = [&](int cc, uint4 (&xr)[8]) __attribute__((always_inline)) {
     const uint32_t j0 = (uint32_t)cc * kChunk + lane_col;
     const char* row = xbase + (size_t)min(r16, M - 1) * a.in_features * 2;
 #pragma unroll
     for (int k = 0; k < 8; ++k) xr[k] = *(const uint4*)(row + (size_t)min(j0 + k, (uint32_t)nv - 1u) * 16u);
-    if constexpr (RES) xres = *(const uint4*)(row + (size_t)min(j0 + (uint32_t)s, (uint32_t)nv - 1u) * 16u);
   };
 
-  uint4 iw[kRG];     // index words of the current chunk, one per row group
-  uint32_t ir[kRG];  // residual indices
-  uint4 xa[8], xb[8], xra = make_uint4(0u, 0u, 0u, 0u), xrb = make_uint4(0u, 0u, 0u, 0u);
+  uint4 iw[kRG];  // index words of the current chunk, one per row group
+  uint2 ir = make_uint2(0u, 0u);  // residual indices of row group s, one byte per vector
+  uint4 xa[8], xb[8];
 
   // stage the slice (and the residual book): the 16 loads per thread first, then the
   // first chunk's indices and activations, then the LDS writes
@@ -167,11 +167,9 @@ __global__ __launch_bounds__(kThreads) void gemv_sliced_kernel(ProductArgs a, Sl
     u32x4 qr = {0u, 0u, 0u, 0u};
     if (RES && tid < kRes) qr = ((const u32x4*)a.cb2)[tid];
 #pragma unroll
-    for (int q = 0; q < kRG; ++q) {
-      iw[q] = *(const uint4*)(p1 + idx_off(rbk, c, q));
-      if constexpr (RES) ir[q] = *(const uint8_t*)(p2 + res_off(rbk, c, q));
-    }
-    load_x(c, xa, xra);
+    for (int q = 0; q < kRG; ++q) iw[q] = *(const uint4*)(p1 + idx_off(rbk, c, q));
+    if constexpr (RES) ir = *(const uint2*)(p2 + res_off(rbk, c));
+    load_x(c, xa);
     dst[0 * kThreads] = q0;
     dst[1 * kThreads] = q1;
     dst[2 * kThreads] = q2;
@@ -200,38 +198,60 @@ __global__ __launch_bounds__(kThreads) void gemv_sliced_kernel(ProductArgs a, Sl
 
   // One chunk: the next chunk's activations first, then per row group the centroid
   // reads (those of row group q + 1 are issued before the products of row group q), the
-  // refill of the row group's index slot with the next chunk, and the 8 (9) products.
-  // Vectors past the row end (the ragged last chunk) take the zero centroid and zero x.
-  auto chunk = [&](const uint4 (&xr)[8], const uint4& xres, uint4 (&xn)[8], uint4& xresn)
-                   __attribute__((always_inline)) {
-    load_x(pc, xn, xresn);
-    const bool full = (c + 1) * kChunk <= nv;
+  // refill of the row group's index slot with the next chunk, and the 8 products; row
+  // group s also takes the 8 residual centroids.  In the ragged last chunk of a row the
+  // vectors past its end get zero x and an index outside every slice (bit 13 set after
+  // the slice XOR), so they read the zero centroid; this fix-up is a uniform branch.
+  auto chunk = [&](uint4 (&xr)[8], uint4 (&xn)[8]) __attribute__((always_inline)) {
+    load_x(pc, xn);
     const int nvalid = nv - (c * kChunk + (int)lane_col);
-    const bool res_ok = full || s < nvalid;
-    uint4 cv[2][8];
-    uint4 crv[2] = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
-    auto reads = [&](int q, uint4 (&c8)[8], uint4& cr) __attribute__((always_inline)) {
-      uint32_t ad[8];
-      slice_addrs(iw[q], tag, ad);
-      if (!full) {
+    uint32_t rmask = 0u;  // residual slots past the row end
+    if ((c + 1) * kChunk > nv) {
+      // a 16-bit index (s ^ 7) << 13 gives 0xE000 after the slice XOR: the zero centroid
+      const uint32_t fill = ((uint32_t)(s ^ 7) << 13) * 0x10001u;
+      uint32_t keep[4];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) ad[k] = k < nvalid ? ad[k] : (uint32_t)kSlice * 16u;
+      for (int h = 0; h < 4; ++h) keep[h] = (2 * h < nvalid ? 0xFFFFu : 0u) | (2 * h + 1 < nvalid ? 0xFFFF0000u : 0u);
+#pragma unroll
+      for (int q = 0; q < kRG; ++q) {
+        iw[q].x = (iw[q].x & keep[0]) | (fill & ~keep[0]);
+        iw[q].y = (iw[q].y & keep[1]) | (fill & ~keep[1]);
+        iw[q].z = (iw[q].z & keep[2]) | (fill & ~keep[2]);
+        iw[q].w = (iw[q].w & keep[3]) | (fill & ~keep[3]);
       }
 #pragma unroll
+      for (int k = 0; k < 8; ++k) xr[k] = k < nvalid ? xr[k] : make_uint4(0u, 0u, 0u, 0u);
+      rmask = nvalid >= 8 ? 0u : (nvalid > 0 ? 0xFFu & ~((1u << nvalid) - 1u) : 0xFFu);
+    }
+    uint4 cv[2][8];
+    auto reads = [&](int q, uint4 (&c8)[8]) __attribute__((always_inline)) {
+      uint32_t ad[8];
+      slice_addrs(iw[q], tag, ad);
+#pragma unroll
       for (int k = 0; k < 8; ++k) c8[k] = *(const uint4*)((const char*)slice + ad[k]);
-      if constexpr (RES) cr = resb[res_ok ? ir[q] : (uint32_t)kRes];
     };
-    reads(0, cv[0], crv[0]);
+    reads(0, cv[0]);
 #pragma unroll
     for (int q = 0; q < kRG; ++q) {
-      if (q + 1 < kRG) reads(q + 1, cv[(q + 1) & 1], crv[(q + 1) & 1]);
+      if (q + 1 < kRG) reads(q + 1, cv[(q + 1) & 1]);
       iw[q] = *(const uint4*)(p1 + idx_off(prb, pc, q));
-      if constexpr (RES) ir[q] = *(const uint8_t*)(p2 + res_off(prb, pc, q));
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
-        d[q] = mfma16(cv[q & 1][k], full || k < nvalid ? xr[k] : make_uint4(0u, 0u, 0u, 0u), d[q]);
-      if constexpr (RES) d[q] = mfma16(crv[q & 1], res_ok ? xres : make_uint4(0u, 0u, 0u, 0u), d[q]);
+      for (int k = 0; k < 8; ++k) d[q] = mfma16(cv[q & 1][k], xr[k], d[q]);
+      if constexpr (RES) {
+        if (q == s) {  // uniform: this slice's residual row group
+          const uint32_t rw[2] = {ir.x, ir.y};
+          uint4 cr[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const uint32_t e = (rw[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+            cr[k] = resb[(rmask >> k) & 1u ? (uint32_t)kRes : e];
+          }
+          ir = *(const uint2*)(p2 + res_off(prb, pc));
+#pragma unroll
+          for (int k = 0; k < 8; ++k) d[q] = mfma16(cr[k], xr[k], d[q]);
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     adv_pre();
@@ -276,9 +296,9 @@ __global__ __launch_bounds__(kThreads) void gemv_sliced_kernel(ProductArgs a, Sl
   };
 
   for (;;) {  // activations alternate between two register sets
-    chunk(xa, xra, xb, xrb);
+    chunk(xa, xb);
     if (!next()) break;
-    chunk(xb, xrb, xa, xra);
+    chunk(xb, xa);
     if (!next()) break;
   }
 }

@@ -238,6 +238,8 @@ def main():
                     help="run only a plain 512 MiB device copy (known bytes) to scale rocprofv3 counters")
     ap.add_argument("--shared-book", action="store_true",
                     help="diagnostic: every ring copy shares one codebook (warm in L2), headline only")
+    ap.add_argument("--only-workload", default=None, choices=sorted(WORKLOADS),
+                    help="run only one workload's M=1 leg through vq_gemv_ws (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
@@ -277,7 +279,16 @@ def main():
         print(json.dumps({"gemm_tflops": round(flops / gsec / 1e12, 2), "ms_per_call": round(gsec * 1e3, 4),
                           "calls": gcalls, "launch": glaunch}))
         return
-    # Headline: vq_gemv, 4096x4096, K1 = 65536, M = 1.
+    if args.only_workload:
+        key = args.only_workload
+        rings = [Ring(vq, torch, key, li, 1) for li in range(len(WORKLOADS[key][0]))]
+        sec, calls, _, launch = time_ring(torch, rings, args.steps, args.warmup, use_graph)
+        b = sum(r.bytes_per_call for r in rings) / len(rings)
+        print(json.dumps({"workload": key, "us_per_call": round(sec * 1e6, 3), "GBps": round(b / sec / 1e9, 1),
+                          "kernel": "codebook-sliced" if any(r.sliced for r in rings) else "gather",
+                          "calls": calls, "launch": launch}))
+        return
+    # Headline: vq_gemv_ws, 4096x4096, K1 = 65536, M = 1.
     ring = Ring(vq, torch, "dec4k", 0, 1, shared_book=args.shared_book)
     log("headline ring: %d copies of %s, %.2f MB per call" % (ring.copies, DESCRIBE["dec4k"],
                                                               ring.bytes_per_call / 1e6))

@@ -439,6 +439,8 @@ bool sliced_gemv_pointers_ok(const ProductArgs& a) {
 }
 
 vq_status launch_gemv_sliced(const ProductArgs& a, void* workspace, void* stream) {
+  // the kernels store partial sums into the workspace: never launch without one
+  if (!workspace) return VQ_ERR_NULL;
   const bool bf16 = a.x_dtype == VQ_BF16;
   Plan p = make_plan(a.n, a.in_features, a.m, bf16);
   char* ws = (char*)workspace;

@@ -66,26 +66,30 @@ __device__ __forceinline__ float4_t mfma16(const uint4& a, const uint4& b, const
                                                 0, 0);
 }
 
-// LDS byte addresses of the centroids of 8 consecutive 16-bit indices: index XOR
+// LDS byte offsets of the centroids of 8 consecutive 16-bit indices: index XOR
 // (s << 13) is below 8192 exactly when the centroid lives in slice s; anything else
-// clamps to entry 8192, the zero centroid.  One XOR and one packed min per two indices.
+// clamps to entry 8192, the zero centroid.  Per two indices: one XOR, one packed min and
+// two shifts that read one 16-bit half each (SDWA word select), four VALU in all.
 __device__ __forceinline__ void slice_addrs(const uint4& w, uint32_t tag, uint32_t (&ad)[8]) {
   const uint32_t wd[4] = {w.x ^ tag, w.y ^ tag, w.z ^ tag, w.w ^ tag};
   const u16x2 lim = {(unsigned short)kSlice, (unsigned short)kSlice};
 #pragma unroll
   for (int h = 0; h < 4; ++h) {
-    const u16x2 v = __builtin_elementwise_min(__builtin_bit_cast(u16x2, wd[h]), lim);
-    ad[2 * h] = (uint32_t)v.x << 4;
-    ad[2 * h + 1] = (uint32_t)v.y << 4;
+    const uint32_t v = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, wd[h]), lim));
+    asm("v_lshlrev_b32_sdwa %0, 4, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:WORD_0"
+        : "=v"(ad[2 * h]) : "v"(v));
+    asm("v_lshlrev_b32_sdwa %0, 4, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:WORD_1"
+        : "=v"(ad[2 * h + 1]) : "v"(v));
   }
 }
 
 template <bool RES>
 __global__ __launch_bounds__(kThreads) void gemv_sliced_kernel(ProductArgs a, SlicedCfg g) {
-  extern __shared__ uint4 lds[];
-  uint4* slice = lds;                                                // [kSlice + 1]
-  uint4* resb = lds + (kSlice + 1);                                  // [kRes + 1]
-  float* red = (float*)(lds + (kSlice + 1) + (RES ? kRes + 1 : 0));  // [8][16][M]
+  // static LDS: the slice's base address is fixed when compiling, so a centroid read needs
+  // no base add on top of index * 16
+  __shared__ uint4 slice[kSlice + 1];
+  __shared__ uint4 resb[RES ? kRes + 1 : 1];
+  __shared__ float red[kRedFloats];
 
   const int tid = threadIdx.x;
   const int xcd = blockIdx.x & 7;
@@ -396,17 +400,12 @@ Plan make_plan(int32_t n, int32_t in_features, int32_t m, bool bf16) {
   return p;
 }
 
-constexpr size_t kLdsMax = 16 * ((size_t)(kSlice + 1) + (kRes + 1)) + 4 * (size_t)kRedFloats;
 
 template <bool RES>
 vq_status launch_res(const ProductArgs& a, const SlicedCfg& g, hipStream_t s) {
   auto kern = gemv_sliced_kernel<RES>;
-  const size_t lds = 16 * ((size_t)(kSlice + 1) + (RES ? kRes + 1 : 0)) + 4 * (size_t)kRedFloats;
-  static const hipError_t attr =
-      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax);
-  if (attr != hipSuccess) return VQ_ERR_HIP;
   const unsigned grid = 64u * (unsigned)((g.groups + 7) / 8);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, s, a, g);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, s, a, g);
   if (hipGetLastError() != hipSuccess) return VQ_ERR_HIP;
   const int total = a.n * a.m;
   hipLaunchKernelGGL(gemv_sliced_finalize, dim3((total + 255) / 256), dim3(256), 0, s, a, (const float*)g.part, g.xexp,

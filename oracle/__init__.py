@@ -81,6 +81,10 @@ def _load():
         lib.oracle_forward_rows.argtypes = [i64, i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, i32, i64, vp, i64,
                                             vp, i32]
         lib.oracle_forward_rows.restype = i32
+        lib.oracle_svq_dequant_rows.argtypes = [i64, i64, vp, vp, vp, vp, vp, i64, vp, i32]
+        lib.oracle_svq_dequant_rows.restype = i32
+        lib.oracle_svq_forward_rows.argtypes = [i64, i64, vp, vp, vp, vp, vp, vp, i32, i64, vp, i64, vp, i32]
+        lib.oracle_svq_forward_rows.restype = i32
         _lib = lib
         return lib
 
@@ -217,4 +221,33 @@ def forward(n, in_features, v, bits1, bits2, packed, cb1, cb2, scale, bias, x_bi
                                        _ptr(_u16(cb2) if bits2 else None), _ptr(_u16(scale)), _ptr(_u16(bias)),
                                        _ptr(xb), int(bool(x_is_bf16)), M, _ptr(r), nrows, _ptr(y), nthreads),
            "oracle_forward_rows")
+    return y
+
+
+# ------------------------------------------------------------------ affine lattice (UniSVQ)
+
+def svq_dequant(n, in_features, packed, a, b, scale=None, rows=None, nthreads=0):
+    """fp32 W rows of an affine-lattice layer: coordinate t of a vector is
+    fl32(B[t] + sum_u A[t][u] q_u) (times the channel scale in fp32)."""
+    p = np.ascontiguousarray(packed, dtype=np.uint8)
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    nrows = n if r is None else r.size
+    w = np.zeros((nrows, in_features), dtype=np.float32)
+    _check(_load().oracle_svq_dequant_rows(n, in_features, _ptr(p), _ptr(_u16(np.ravel(a))), _ptr(_u16(np.ravel(b))),
+                                           _ptr(_u16(scale)), _ptr(r), nrows, _ptr(w), nthreads),
+           "oracle_svq_dequant_rows")
+    return w
+
+
+def svq_forward(n, in_features, packed, a, b, scale, bias, x_bits, x_is_bf16, M, rows=None, nthreads=0):
+    """y64 [M, len(rows) or n] of an affine-lattice layer: fp64 sum of x times fp32 W (+ bias)."""
+    p = np.ascontiguousarray(packed, dtype=np.uint8)
+    xb = _u16(x_bits) if M * in_features > 0 else None
+    r = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    nrows = n if r is None else r.size
+    y = np.zeros((M, nrows), dtype=np.float64)
+    _check(_load().oracle_svq_forward_rows(n, in_features, _ptr(p), _ptr(_u16(np.ravel(a))), _ptr(_u16(np.ravel(b))),
+                                           _ptr(_u16(scale)), _ptr(_u16(bias)), _ptr(xb), int(bool(x_is_bf16)), M,
+                                           _ptr(r), nrows, _ptr(y), nthreads),
+           "oracle_svq_forward_rows")
     return y

@@ -222,6 +222,8 @@ typedef struct {
   int64_t M;
   const int64_t* rows;
   int64_t nrows;
+  const uint16_t* lat_a; /* affine-lattice decode: A [4][4] fp16 bits, NULL for codebooks */
+  const uint16_t* lat_b; /* affine-lattice decode: B [4] fp16 bits */
   float* w_out;  /* dequant-only: [nrows][in] */
   double* y_out; /* forward: [M][nrows] */
   int64_t begin, end;
@@ -256,6 +258,35 @@ static void dequant_row(const job_t* jb, int64_t o, float* wrow) {
   }
 }
 
+/* One row of W for the affine lattice (UniSVQ summary, "Mathematical Formulation":
+ * Phi(w) = A w + B over integer grid coordinates; "Efficiency": d = 4, 2 bits per
+ * coordinate).  The 8-bit field of vector j holds its four 2-bit codes, code u in bits
+ * [2u, 2u + 2); the code value itself is the integer coordinate q_u (reading taken: the
+ * pages do not say how the integers are stored).  Coordinate t of the vector is
+ * B[t] + sum_u A[t][u] q_u, summed in double, where every term (an fp16 value times an
+ * integer below 4) and every partial sum is exact, then rounded once to fp32; the
+ * channel scale then multiplies it in fp32. */
+static void dequant_row_lattice(const job_t* jb, int64_t o, float* wrow) {
+  int64_t nv = num_vectors(jb->in_features, 4);
+  int64_t stride = oracle_row_stride(jb->in_features, 4, 8);
+  const uint8_t* row = jb->packed + o * stride;
+  float s = jb->scale ? (float)oracle_f16_to_f64(jb->scale[o]) : 1.0f;
+  for (int64_t j = 0; j < nv; ++j) {
+    uint32_t field = read_field(row, j, 8);
+    int q[4];
+    for (int u = 0; u < 4; ++u) q[u] = (int)((field >> (2 * u)) & 3u);
+    for (int t = 0; t < 4; ++t) {
+      int64_t col = j * 4 + t;
+      if (col >= jb->in_features) break; /* tail lanes of the last vector are dropped */
+      double acc = oracle_f16_to_f64(jb->lat_b[t]);
+      for (int u = 0; u < 4; ++u) acc += oracle_f16_to_f64(jb->lat_a[t * 4 + u]) * (double)q[u];
+      float w = (float)acc;
+      if (jb->scale) w = w * s;
+      wrow[col] = w;
+    }
+  }
+}
+
 static void* worker(void* arg) {
   job_t* jb = (job_t*)arg;
   float* wrow = NULL;
@@ -266,10 +297,16 @@ static void* worker(void* arg) {
   for (int64_t r = jb->begin; r < jb->end; ++r) {
     int64_t o = jb->rows ? jb->rows[r] : r;
     if (!jb->y_out) {
-      dequant_row(jb, o, jb->w_out + r * jb->in_features);
+      if (jb->lat_a)
+        dequant_row_lattice(jb, o, jb->w_out + r * jb->in_features);
+      else
+        dequant_row(jb, o, jb->w_out + r * jb->in_features);
       continue;
     }
-    dequant_row(jb, o, wrow);
+    if (jb->lat_a)
+      dequant_row_lattice(jb, o, wrow);
+    else
+      dequant_row(jb, o, wrow);
     double b = jb->bias ? oracle_f16_to_f64(jb->bias[o]) : 0.0;
     for (int64_t m = 0; m < jb->M; ++m) {
       const double* xm = jb->xd + m * jb->in_features;
@@ -373,6 +410,66 @@ int oracle_forward_rows(int64_t n, int64_t in_features, int v, int bits1, int bi
   proto.packed = packed;
   proto.cb1 = cb1;
   proto.cb2 = cb2;
+  proto.scale = scale;
+  proto.bias = bias;
+  proto.xd = xd;
+  proto.M = M;
+  proto.rows = rows;
+  proto.nrows = nrows;
+  proto.y_out = y;
+  int rc = run_jobs(&proto, nthreads);
+  free(xd);
+  return rc;
+}
+
+/* ---------------------------------------------------------------- affine lattice entry points */
+
+int oracle_svq_dequant_rows(int64_t n, int64_t in_features, const uint8_t* packed, const uint16_t* a,
+                            const uint16_t* b, const uint16_t* scale, const int64_t* rows, int64_t nrows, float* w,
+                            int nthreads) {
+  if (n < 0 || in_features < 0) return ORACLE_BAD_ARGS;
+  if (!rows) nrows = n;
+  if (!check_rows(n, rows, nrows)) return ORACLE_BAD_ARGS;
+  if (nrows == 0 || in_features == 0) return ORACLE_OK;
+  if (!packed || !a || !b || !w) return ORACLE_BAD_ARGS;
+  job_t proto;
+  memset(&proto, 0, sizeof proto);
+  proto.n = n;
+  proto.in_features = in_features;
+  proto.v = 4;
+  proto.bits1 = 8;
+  proto.packed = packed;
+  proto.lat_a = a;
+  proto.lat_b = b;
+  proto.scale = scale;
+  proto.rows = rows;
+  proto.nrows = nrows;
+  proto.w_out = w;
+  return run_jobs(&proto, nthreads);
+}
+
+int oracle_svq_forward_rows(int64_t n, int64_t in_features, const uint8_t* packed, const uint16_t* a,
+                            const uint16_t* b, const uint16_t* scale, const uint16_t* bias, const uint16_t* x,
+                            int x_is_bf16, int64_t M, const int64_t* rows, int64_t nrows, double* y, int nthreads) {
+  if (n < 0 || in_features < 0 || M < 0) return ORACLE_BAD_ARGS;
+  if (!rows) nrows = n;
+  if (!check_rows(n, rows, nrows)) return ORACLE_BAD_ARGS;
+  if (nrows == 0 || M == 0) return ORACLE_OK;
+  if (!y) return ORACLE_BAD_ARGS;
+  if (in_features > 0 && (!packed || !a || !b || !x)) return ORACLE_BAD_ARGS;
+  double* xd = (double*)malloc(sizeof(double) * (size_t)(M * in_features > 0 ? M * in_features : 1));
+  if (!xd) return ORACLE_BAD_ARGS;
+  for (int64_t i = 0; i < M * in_features; ++i)
+    xd[i] = x_is_bf16 ? oracle_bf16_to_f64(x[i]) : oracle_f16_to_f64(x[i]);
+  job_t proto;
+  memset(&proto, 0, sizeof proto);
+  proto.n = n;
+  proto.in_features = in_features;
+  proto.v = 4;
+  proto.bits1 = 8;
+  proto.packed = packed;
+  proto.lat_a = a;
+  proto.lat_b = b;
   proto.scale = scale;
   proto.bias = bias;
   proto.xd = xd;

@@ -16,6 +16,8 @@
  *     fp32, then times the per-output-channel scale in fp32.
  *   - product (VPTQ guide, "Step 3: Fused Low-Bit VPTQ Linear Layer"): y = x W^T (+ bias),
  *     accumulated in fp64 in ascending column order.
+ *   - affine-lattice decode (UniSVQ summary): W's vectors are A q + B over 2-bit integer
+ *     codes instead of codebook entries; the same product follows.
  */
 #ifndef VQ_ORACLE_H
 #define VQ_ORACLE_H
@@ -73,6 +75,20 @@ int oracle_forward_rows(int64_t n, int64_t in_features, int v, int bits1, int bi
                         const uint16_t* cb1, const uint16_t* cb2, const uint16_t* scale, const uint16_t* bias,
                         const uint16_t* x, int x_is_bf16, int64_t M, const int64_t* rows, int64_t nrows,
                         double* y, int nthreads);
+
+/*
+ * Affine-lattice layers (UniSVQ summary, "Mathematical Formulation" and "Efficiency"):
+ * d = 4, each vector stored as one 8-bit field of four 2-bit codes (code u in bits
+ * [2u, 2u+2)), packed like a v = 4, bits1 = 8 index stream with no residual.  Coordinate
+ * t of a vector is fl32(B[t] + sum_u A[t][u] * q_u) with q_u the code value, then times
+ * the channel scale in fp32.  a: fp16 bits [4][4] (row t, column u); b: fp16 bits [4].
+ */
+int oracle_svq_dequant_rows(int64_t n, int64_t in_features, const uint8_t* packed, const uint16_t* a,
+                            const uint16_t* b, const uint16_t* scale, const int64_t* rows, int64_t nrows, float* w,
+                            int nthreads);
+int oracle_svq_forward_rows(int64_t n, int64_t in_features, const uint8_t* packed, const uint16_t* a,
+                            const uint16_t* b, const uint16_t* scale, const uint16_t* bias, const uint16_t* x,
+                            int x_is_bf16, int64_t M, const int64_t* rows, int64_t nrows, double* y, int nthreads);
 
 #ifdef __cplusplus
 }

@@ -27,7 +27,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 SEED = 42
-T_C1, T_C2, T_IDX1, T_IDX2, T_SCALE, T_X, T_BIAS = range(7)
+T_C1, T_C2, T_IDX1, T_IDX2, T_SCALE, T_X, T_BIAS, T_LATTICE = range(8)
 
 
 @dataclass(frozen=True)
@@ -54,6 +54,17 @@ WORKLOADS = {
     "l70b": Workload("l70b", 4, ((28672, 8192), (8192, 28672)), 8, 16, 8, (1, 8, 32, 128, 256), "bf16",
                      labels=("up", "down")),
 }
+
+
+# Affine-lattice layers (UniSVQ summary: d = 4, 2 bits per coordinate): one 8-bit field per
+# 4-vector (four 2-bit codes), packed like a v = 4, bits1 = 8 index stream.  Sizes follow the
+# decode layers above: a 4096 x 4096 layer and the 70B-class MLP pair.
+SVQ_WORKLOADS = {
+    "svq4k": Workload("svq4k", 5, ((4096, 4096),), 4, 8, 0, (1, 4, 16), "f16"),
+    "svq70b": Workload("svq70b", 6, ((28672, 8192), (8192, 28672)), 4, 8, 0, (1, 8), "bf16",
+                       labels=("up", "down")),
+}
+SVQ_STEP = 0.018  # grid step: codes 0..3 around 1.5 give a weight spread near 0.02
 
 
 def rng(workload: int, layer: int, copy: int, tensor: int) -> np.random.Generator:
@@ -124,5 +135,47 @@ def workload_layer(key: str, layer: int = 0, copy: int = 0) -> dict:
 
 def workload_x(key: str, layer: int, m: int) -> np.ndarray:
     w = WORKLOADS[key]
+    _, in_features = w.layers[layer]
+    return activations(rng(w.wid, layer, 0, T_X), m, in_features, w.x_dtype)
+
+
+def lattice(g: np.random.Generator, step: float = SVQ_STEP):
+    """Affine-grid parameters as fp16 bits: A [4, 4] = step * a Haar-random orthogonal
+    matrix (QR of a Gaussian matrix, signs fixed by R's diagonal), and B [4] = -1.5 * (row
+    sums of the rounded A), which centres the 256 grid points A q + B (q in {0..3}^4) on 0."""
+    z = g.standard_normal((4, 4))
+    qm, r = np.linalg.qr(z)
+    qm = qm * np.sign(np.diag(r))
+    a = f16_bits((qm * step).astype(np.float32))
+    b = -1.5 * a.view(np.float16).astype(np.float64).sum(axis=1)
+    return a, f16_bits(b.astype(np.float32))
+
+
+def make_svq_layer(n: int, in_features: int, *, wid: int = 98, layer: int = 0, copy: int = 0,
+                   step: float = SVQ_STEP, with_scale: bool = False, with_bias: bool = False) -> dict:
+    """One synthetic affine-lattice layer: codes (uint32 [n, ceil(in/4)], values 0..255, four
+    2-bit codes each), A / B fp16 bits, optional scale and bias."""
+    nv = num_vectors(in_features, 4)
+    a, b = lattice(rng(wid, layer, copy, T_LATTICE), step)
+    out = {
+        "n": n, "in_features": in_features, "v": 4, "bits1": 8, "bits2": 0,
+        "codes": indices(rng(wid, layer, copy, T_IDX1), n, nv, 8),
+        "a": a, "b": b, "scale": None, "bias": None,
+    }
+    if with_scale:
+        out["scale"] = scales(rng(wid, layer, copy, T_SCALE), n)
+    if with_bias:
+        out["bias"] = f16_bits(rng(wid, layer, copy, T_BIAS).standard_normal(n).astype(np.float32) * 0.1)
+    return out
+
+
+def svq_workload_layer(key: str, layer: int = 0, copy: int = 0) -> dict:
+    w = SVQ_WORKLOADS[key]
+    n, in_features = w.layers[layer]
+    return make_svq_layer(n, in_features, wid=w.wid, layer=layer, copy=copy)
+
+
+def svq_workload_x(key: str, layer: int, m: int) -> np.ndarray:
+    w = SVQ_WORKLOADS[key]
     _, in_features = w.layers[layer]
     return activations(rng(w.wid, layer, 0, T_X), m, in_features, w.x_dtype)

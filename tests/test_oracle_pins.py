@@ -400,3 +400,153 @@ def test_array_rounding_matches_scalar_and_numpy(oracle_mod):
         assert np.array_equal(oracle_mod.f32_array_to_f16_rne(vals), vals.astype(np.float16).view(np.uint16))
     ref = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(oracle_mod.f32_array_to_bf16_rne(vals), ref)
+
+
+# ------------------------------------------------------------------ affine lattice (UniSVQ)
+#
+# The UniSVQ summary ("Mathematical Formulation") decodes a d = 4 vector as A q + B over
+# integer grid coordinates q; "Efficiency" fixes d = 4, 2 bits per coordinate and 20 fp
+# parameters per matrix.  The readings tested here: the code value itself is the
+# integer coordinate, code u of a vector sits in bits [2u, 2u+2) of the vector's 8-bit
+# field, and the 8-bit fields are packed like a v = 4, bits1 = 8 index stream.
+
+
+def _svq_q(g, n, in_features):
+    """Random integer coordinates q [n, nv, 4] in 0..3 and their 8-bit fields [n, nv]."""
+    nv = (in_features + 3) // 4
+    q = g.integers(0, 4, size=(n, nv, 4), dtype=np.uint32)
+    fields = q[:, :, 0] | (q[:, :, 1] << 2) | (q[:, :, 2] << 4) | (q[:, :, 3] << 6)
+    return q, fields
+
+
+def _f16(vals):
+    return np.asarray(vals, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def _svq_packed(oracle_mod, n, in_features, fields):
+    return oracle_mod.pack(n, in_features, 4, 8, 0, fields)
+
+
+@pytest.mark.parametrize("in_features", [16, 13, 64, 70])
+def test_svq_identity_grid_returns_the_codes(oracle_mod, in_features):
+    g = np.random.default_rng(101)
+    n = 7
+    q, fields = _svq_q(g, n, in_features)
+    packed = _svq_packed(oracle_mod, n, in_features, fields)
+    w = oracle_mod.svq_dequant(n, in_features, packed, _f16(np.eye(4)), _f16(np.zeros(4)))
+    want = q.reshape(n, -1)[:, :in_features].astype(np.float32)
+    assert np.array_equal(w, want)
+
+
+def test_svq_scalar_grid_closed_form(oracle_mod):
+    g = np.random.default_rng(102)
+    n, in_features = 5, 40
+    q, fields = _svq_q(g, n, in_features)
+    packed = _svq_packed(oracle_mod, n, in_features, fields)
+    a, b = 0.25, -0.375  # both exact in fp16
+    w = oracle_mod.svq_dequant(n, in_features, packed, _f16(a * np.eye(4)), _f16(np.full(4, b)))
+    want = (a * q.reshape(n, -1)[:, :in_features] + b).astype(np.float32)
+    assert np.array_equal(w, want)
+    # the channel scale multiplies the decoded value once, in fp32
+    scale = _f16(g.uniform(0.5, 1.5, size=n))
+    ws = oracle_mod.svq_dequant(n, in_features, packed, _f16(a * np.eye(4)), _f16(np.full(4, b)), scale=scale)
+    s32 = scale.view(np.float16).astype(np.float32)[:, None]
+    assert np.array_equal(ws, want * s32)
+
+
+def test_svq_matrix_orientation(oracle_mod):
+    """A[t][u] feeds code u into coordinate t: a 3-cycle permutation tells A from its
+    transpose (the transpose would apply the inverse cycle)."""
+    g = np.random.default_rng(103)
+    n, in_features = 4, 32
+    q, fields = _svq_q(g, n, in_features)
+    packed = _svq_packed(oracle_mod, n, in_features, fields)
+    perm = [1, 2, 0, 3]  # coordinate t takes code perm[t]
+    a = np.zeros((4, 4))
+    for t, u in enumerate(perm):
+        a[t, u] = 1.0
+    w = oracle_mod.svq_dequant(n, in_features, packed, _f16(a), _f16(np.zeros(4)))
+    want = q[:, :, perm].reshape(n, -1).astype(np.float32)
+    assert np.array_equal(w, want)
+
+
+def test_svq_exact_value_rounded_once(oracle_mod):
+    """Brute force with exact rationals: every coordinate is the exact B[t] + sum A[t][u] q_u
+    rounded once to fp32."""
+    from fractions import Fraction
+
+    g = np.random.default_rng(104)
+    n, in_features = 6, 22
+    q, fields = _svq_q(g, n, in_features)
+    packed = _svq_packed(oracle_mod, n, in_features, fields)
+    a_bits, b_bits = synth.lattice(np.random.default_rng(7))
+    af = [Fraction(float(v)) for v in a_bits.view(np.float16).astype(np.float64).ravel()]
+    bf = [Fraction(float(v)) for v in b_bits.view(np.float16).astype(np.float64)]
+    w = oracle_mod.svq_dequant(n, in_features, packed, a_bits, b_bits)
+    for o in range(n):
+        for col in range(in_features):
+            j, t = divmod(col, 4)
+            exact = bf[t] + sum(af[t * 4 + u] * int(q[o, j, u]) for u in range(4))
+            assert w[o, col] == np.float32(float(exact)), (o, col)
+
+
+def test_svq_equals_the_256_entry_codebook(oracle_mod):
+    """The grid is a 256-entry codebook of 4-vectors: with dyadic A and B every grid point
+    is exact in fp16, and the codebook decode (pinned above) must give the same matrix."""
+    g = np.random.default_rng(105)
+    n, in_features = 9, 52
+    q, fields = _svq_q(g, n, in_features)
+    packed = _svq_packed(oracle_mod, n, in_features, fields)
+    a = g.choice([-0.5, -0.25, 0.0, 0.25, 0.5], size=(4, 4))
+    b = g.choice([-1.0, -0.5, 0.5], size=4)
+    book = np.zeros((256, 4))
+    for k in range(256):
+        qq = np.array([(k >> (2 * u)) & 3 for u in range(4)], dtype=np.float64)
+        book[k] = a @ qq + b
+    scale = _f16(g.uniform(0.5, 1.5, size=n))
+    w_grid = oracle_mod.svq_dequant(n, in_features, packed, _f16(a), _f16(b), scale=scale)
+    w_book = oracle_mod.dequant(n, in_features, 4, 8, 0, packed, _f16(book), scale=scale)
+    assert np.array_equal(w_grid, w_book)
+
+
+@pytest.mark.parametrize("x_dtype", ["f16", "bf16"])
+def test_svq_forward_matches_preapplied_activations(oracle_mod, x_dtype):
+    """UniSVQ summary, "Efficiency": the affine map can be moved onto the activations,
+    y = sum_j q_j . (A^T x_j) + B . sum_j x_j.  Evaluated here in fp64 from the exact
+    parameters; the oracle rounds each weight to fp32 first, so the two differ by at most
+    sum |x| |w| 2^-24 (plus fp64 noise)."""
+    g = np.random.default_rng(106)
+    n, in_features, M = 11, 45, 3
+    q, fields = _svq_q(g, n, in_features)
+    packed = _svq_packed(oracle_mod, n, in_features, fields)
+    a_bits, b_bits = synth.lattice(np.random.default_rng(8))
+    bias = _f16(g.standard_normal(n) * 0.1)
+    x_bits = synth.activations(g, M, in_features, x_dtype)
+    y = oracle_mod.svq_forward(n, in_features, packed, a_bits, b_bits, None, bias, x_bits, x_dtype == "bf16", M)
+    dec = oracle_mod.bf16_to_f64 if x_dtype == "bf16" else oracle_mod.f16_to_f64
+    x = dec(x_bits).reshape(M, in_features)
+    nv = (in_features + 3) // 4
+    xp = np.zeros((M, nv * 4))
+    xp[:, :in_features] = x
+    xg = xp.reshape(M, nv, 4)                      # [M, j, t]
+    A = a_bits.view(np.float16).astype(np.float64)
+    B = b_bits.view(np.float16).astype(np.float64)
+    xhat = np.einsum("mjt,tu->mju", xg, A)         # A^T x_j
+    c = xg.sum(axis=1) @ B                         # B . sum_j x_j
+    y_pre = np.einsum("oju,mju->mo", q.astype(np.float64), xhat) + c[:, None]
+    y_pre += bias.view(np.float16).astype(np.float64)[None, :]
+    w_exact = (q.astype(np.float64) @ A.T + B).reshape(n, -1)[:, :in_features]
+    bound = np.abs(x) @ np.abs(w_exact).T * 2.0 ** -24 + 1e-12
+    assert np.all(np.abs(y - y_pre) <= bound)
+
+
+def test_svq_sizes_from_the_pages(oracle_mod):
+    """UniSVQ summary, "Efficiency": 2 bits per weight for d = 4 and 20 parameters
+    (~40 bytes in fp16) per matrix, against ~2048 bytes for a standard d = 4, 2-bit VQ book."""
+    gold = {e["name"]: e for e in _golden("bitrate_examples.json")["codebook_bytes"]}
+    std = gold["unisvq-standard-vq-d4-2bit"]
+    assert std["k"] * std["v"] * 2 == std["bytes"] == 2048
+    a_bits, b_bits = synth.lattice(np.random.default_rng(9))
+    assert a_bits.nbytes + b_bits.nbytes == 40
+    for n, in_features in [(4096, 4096), (28672, 8192), (8192, 28672)]:
+        assert oracle_mod.packed_bytes(n, in_features, 4, 8, 0) * 8 == 2 * n * in_features

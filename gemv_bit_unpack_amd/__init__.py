@@ -41,7 +41,7 @@ VQ_F16, VQ_BF16, VQ_F32 = 0, 1, 2
 LAYOUT_ROWSTREAM = 1
 
 EXPORTED = ("vq_abi_version", "vq_status_string", "vq_packed_bytes", "vq_pack", "vq_dequant", "vq_gemv",
-            "vq_gemv_workspace_bytes", "vq_gemv_ws", "vq_gemm")
+            "vq_gemv_workspace_bytes", "vq_gemv_ws", "vq_gemm", "vq_svq_dequant", "vq_svq_gemv")
 
 
 class Desc(ctypes.Structure):
@@ -87,6 +87,10 @@ def _load():
     lib.vq_gemv_workspace_bytes.restype = ctypes.c_int
     lib.vq_gemv_ws.argtypes = [dp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i32, vp, ctypes.c_int, vp, sz, vp]
     lib.vq_gemv_ws.restype = ctypes.c_int
+    lib.vq_svq_dequant.argtypes = [dp, vp, vp, vp, vp, vp, ctypes.c_int, vp]
+    lib.vq_svq_dequant.restype = ctypes.c_int
+    lib.vq_svq_gemv.argtypes = [dp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i32, vp, ctypes.c_int, vp]
+    lib.vq_svq_gemv.restype = ctypes.c_int
     return lib
 
 
@@ -232,6 +236,49 @@ def gemv_ws(desc, packed, cb1, cb2, scale, bias, x, ws, y_dtype=None, out=None):
 
 def gemm(desc, packed, cb1, cb2, scale, bias, x, y_dtype=None, out=None):
     return _product(lib().vq_gemm, "vq_gemm", desc, packed, cb1, cb2, scale, bias, x, y_dtype, out)
+
+
+def svq_desc(out_features, in_features) -> Desc:
+    """Descriptor of an affine-lattice layer: one 8-bit field of four 2-bit codes per 4-vector."""
+    return make_desc(out_features, in_features, 4, 8, 0)
+
+
+def svq_fields(q):
+    """Integer grid coordinates q [..., 4] (values 0..3) -> the 8-bit fields vq_pack takes."""
+    q = np.asarray(q, dtype=np.uint32)
+    return q[..., 0] | (q[..., 1] << 2) | (q[..., 2] << 4) | (q[..., 3] << 6)
+
+
+def svq_dequant(desc: Desc, packed, a, b, scale, w_dtype=None, out=None):
+    """W^ of an affine-lattice layer (a: fp16 [4, 4], b: fp16 [4] device tensors)."""
+    torch = _torch()
+    w_dtype = w_dtype or torch.float32
+    if out is None:
+        out = torch.empty((desc.out_features, desc.in_features), dtype=w_dtype, device=packed.device)
+    f16 = (torch.float16,)
+    st = lib().vq_svq_dequant(ctypes.byref(desc), _dev_ptr(packed, "packed"), _dev_ptr(a, "a", f16),
+                             _dev_ptr(b, "b", f16), _dev_ptr(scale, "scale", f16), _dev_ptr(out, "out"),
+                             _dtype_code(out.dtype), _stream_ptr(packed.device))
+    _check(st, "vq_svq_dequant")
+    return out
+
+
+def svq_gemv(desc: Desc, packed, a, b, scale, bias, x, y_dtype=None, out=None):
+    """y [M, N] = x W^T (+ bias) of an affine-lattice layer, 1 <= M <= 16."""
+    torch = _torch()
+    if x.dim() != 2 or x.shape[1] != desc.in_features:
+        raise ValueError("x must be [M, %d], got %s" % (desc.in_features, tuple(x.shape)))
+    m = x.shape[0]
+    y_dtype = y_dtype or x.dtype
+    if out is None:
+        out = torch.empty((m, desc.out_features), dtype=y_dtype, device=x.device)
+    f16 = (torch.float16,)
+    st = lib().vq_svq_gemv(ctypes.byref(desc), _dev_ptr(packed, "packed"), _dev_ptr(a, "a", f16),
+                          _dev_ptr(b, "b", f16), _dev_ptr(scale, "scale", f16), _dev_ptr(bias, "bias", f16),
+                          _dev_ptr(x, "x", (torch.float16, torch.bfloat16)), _dtype_code(x.dtype), m,
+                          _dev_ptr(out, "out"), _dtype_code(out.dtype), _stream_ptr(x.device))
+    _check(st, "vq_svq_gemv")
+    return out
 
 
 _stream_ws = {}

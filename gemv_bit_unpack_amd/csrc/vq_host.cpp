@@ -66,6 +66,47 @@ vq_status prepare_product(const vq_desc* desc, const void* packed, const void* c
   return VQ_OK;
 }
 
+// Affine-lattice calls: the descriptor must be the lattice stream (v = 4, bits1 = 8, no
+// residual).  m < 0 marks the dequant (no x, y checked by the caller).
+static vq_status prepare_svq(const vq_desc* desc, const void* packed, const void* a, const void* b,
+                             const void* scale, const void* bias, const void* x, vq_dtype x_dtype, int32_t m,
+                             void* y, vq_dtype y_dtype, SvqArgs* p) {
+  vq_status st = check_desc(desc);
+  if (st != VQ_OK) return st;
+  const vq_desc& d = *desc;
+  if (d.v != 4 || d.bits1 != 8 || d.bits2 != 0) return VQ_ERR_UNSUPPORTED;
+  if (m > 16) return VQ_ERR_SHAPE;
+  if (m >= 0 && !valid_x_dtype(x_dtype)) return VQ_ERR_UNSUPPORTED;
+  if (!valid_out_dtype(y_dtype)) return VQ_ERR_UNSUPPORTED;
+  std::memset(p, 0, sizeof *p);
+  p->n = d.out_features;
+  p->in_features = d.in_features;
+  p->nv = (int32_t)num_vectors(d.in_features, 4);
+  p->stride = (int32_t)row_stride(d.in_features, 4, 8);
+  p->m = m < 0 ? 0 : m;
+  p->x_dtype = x_dtype;
+  p->y_dtype = y_dtype;
+  if (d.out_features == 0 || m == 0) return VQ_OK;
+  if (m < 0 && d.in_features == 0) return VQ_OK;
+  if (!y) return VQ_ERR_NULL;
+  if (!aligned(y, dtype_size(y_dtype))) return VQ_ERR_ALIGN;
+  if ((scale && !aligned(scale, 2)) || (bias && !aligned(bias, 2))) return VQ_ERR_ALIGN;
+  if (d.in_features > 0) {
+    if (!packed || !a || !b || (m > 0 && !x)) return VQ_ERR_NULL;
+    // the product reads up to 16 code bytes per load
+    if ((m > 0 && !aligned(packed, 16)) || !aligned(a, 2) || !aligned(b, 2) || (m > 0 && !aligned(x, 2)))
+      return VQ_ERR_ALIGN;
+  }
+  p->packed = (const uint8_t*)packed;
+  p->a = (const uint16_t*)a;
+  p->b = (const uint16_t*)b;
+  p->scale = (const uint16_t*)scale;
+  p->bias = (const uint16_t*)bias;
+  p->x = (const uint16_t*)x;
+  p->y = y;
+  return VQ_OK;
+}
+
 // Appends `bits`-bit fields LSB-first into a row of 32-bit little-endian words.
 struct BitWriter {
   uint8_t* row;
@@ -207,6 +248,26 @@ vq_status vq_gemv_ws(const vq_desc* desc, const void* packed, const void* cb1, c
     if (sliced_gemv_pointers_ok(a)) return launch_gemv_sliced(a, workspace, stream);
   }
   return launch_gemv(a, stream);
+}
+
+vq_status vq_svq_dequant(const vq_desc* desc, const void* packed, const void* a, const void* b, const void* scale,
+                         void* w, vq_dtype w_dtype, void* stream) {
+  SvqArgs p;
+  vq_status st = prepare_svq(desc, packed, a, b, scale, nullptr, nullptr, VQ_F16, -1, w, w_dtype, &p);
+  if (st != VQ_OK) return st;
+  if (p.n == 0 || p.in_features == 0) return VQ_OK;
+  return launch_svq_dequant(p, w, w_dtype, stream);
+}
+
+vq_status vq_svq_gemv(const vq_desc* desc, const void* packed, const void* a, const void* b, const void* scale,
+                      const void* bias, const void* x, vq_dtype x_dtype, int32_t M, void* y, vq_dtype y_dtype,
+                      void* stream) {
+  if (M < 0) return VQ_ERR_SHAPE;
+  SvqArgs p;
+  vq_status st = prepare_svq(desc, packed, a, b, scale, bias, x, x_dtype, M, y, y_dtype, &p);
+  if (st != VQ_OK) return st;
+  if (p.n == 0 || p.m == 0) return VQ_OK;
+  return launch_svq_gemv(p, stream);
 }
 
 vq_status vq_gemm(const vq_desc* desc, const void* packed, const void* cb1, const void* cb2, const void* scale,

@@ -65,4 +65,21 @@ bool sliced_gemv_pointers_ok(const ProductArgs& a);
 vq_status launch_gemv_sliced(const ProductArgs& a, void* workspace, void* stream);
 vq_status launch_gemm(const ProductArgs& a, void* stream);
 
+// Affine-lattice layers (v = 4, one 8-bit field of four 2-bit codes per vector), after
+// validation.
+struct SvqArgs {
+  int32_t n, in_features, nv, stride;  // stride: bytes per row of the code stream
+  const uint8_t* packed;
+  const uint16_t* a;      // fp16 bits [4][4], A[t][u]
+  const uint16_t* b;      // fp16 bits [4]
+  const uint16_t* scale;  // fp16 bits [n] or nullptr
+  const uint16_t* bias;   // fp16 bits [n] or nullptr
+  const uint16_t* x;      // [M][in] fp16 / bf16 bits
+  void* y;                // [M][n]
+  int32_t m;
+  vq_dtype x_dtype, y_dtype;
+};
+vq_status launch_svq_gemv(const SvqArgs& p, void* stream);
+vq_status launch_svq_dequant(const SvqArgs& p, void* w, vq_dtype w_dtype, void* stream);
+
 }  // namespace vqi

@@ -149,6 +149,43 @@ vq_status vq_gemm(const vq_desc* desc, const void* packed, const void* cb1, cons
                   const void* bias, const void* x, vq_dtype x_dtype, int32_t M, void* y, vq_dtype y_dtype,
                   void* stream);
 
+/*
+ * Affine-lattice layers (UniSVQ summary, gist.science, "Mathematical Formulation" and
+ * "Efficiency"): instead of codebook entries, each 4-vector of W^ is a point of an affine
+ * integer grid,
+ *
+ *   W^[o, 4j + t] = scale[o] * fp32( B[t] + sum_u A[t][u] * q_u(o, j) ),   t, u < 4,
+ *
+ * with q_u in 0..3 the 2-bit code of coordinate u (the integer grid coordinate itself),
+ * A an fp16 [4][4] matrix (row t, column u, row-major) and B an fp16 [4] vector: 20
+ * parameters per layer.  The sum is exact before its single rounding to fp32; the scale
+ * multiply is one more fp32 rounding (skipped when scale is NULL).  The codes are stored
+ * as the row stream of a descriptor with v = 4, bits1 = 8, bits2 = 0: vector j's 8-bit
+ * field holds code u in bits [2u, 2u + 2), so vq_pack packs them from idx1[o][j] =
+ * q_0 | q_1 << 2 | q_2 << 4 | q_3 << 6, and a row takes 16 * ceil(nv / 16) bytes
+ * (2 bits per weight).  Any other descriptor gives VQ_ERR_UNSUPPORTED.  As for the
+ * codebook calls, lanes of the last vector past IN are dropped.
+ */
+
+/* Write W^ [N][IN] of an affine-lattice layer into `w` (device, w_dtype; fp16 / bf16 are
+ * the nearest-even rounding of the exact fp32 value, which this call reproduces bit for
+ * bit).  packed, a, b, scale: device; a, b, scale 2-byte aligned. */
+vq_status vq_svq_dequant(const vq_desc* desc, const void* packed, const void* a, const void* b, const void* scale,
+                         void* w, vq_dtype w_dtype, void* stream);
+
+/* Decode-batch product y [M][N] = x [M][IN] * W^T (+ bias) of an affine-lattice layer,
+ * 0 <= M <= 16, without rebuilding W^: the affine map is applied to the activations
+ * (UniSVQ summary, "Efficiency"),
+ *   y[m, o] = scale[o] * ( sum_j q(o, j) . (A^T x_mj) + B . sum_j x_mj ) + bias[o],
+ * where x_mj are the 4 activations of vector j (zero past IN); the rest is a 2-bit
+ * scalar product accumulated in fp32, so results match W^ to the vq_gemv tolerance.
+ * packed: device, 16-byte aligned; x: device [M][IN], VQ_F16 or VQ_BF16; y: device
+ * [M][N], VQ_F16, VQ_BF16 or VQ_F32; bias: fp16 [N] or NULL.  IN == 0 gives y = bias
+ * (or 0).  Errors as for vq_gemv. */
+vq_status vq_svq_gemv(const vq_desc* desc, const void* packed, const void* a, const void* b, const void* scale,
+                      const void* bias, const void* x, vq_dtype x_dtype, int32_t M, void* y, vq_dtype y_dtype,
+                      void* stream);
+
 #ifdef __cplusplus
 }
 #endif

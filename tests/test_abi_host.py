@@ -219,3 +219,56 @@ def test_gemv_ws_validation_paths(vq):
     assert _gemv_ws(vq, d, ws=ctypes.c_void_p(0x10010), ws_bytes=need) == vq.VQ_ERR_ALIGN
     # nothing to do
     assert _gemv_ws(vq, d, ws=P, ws_bytes=0, m=0, y=None, x=None, packed=None) == vq.VQ_OK
+
+
+def _svq(vq, desc, packed=P, a=P, b=P, scale=None, bias=None, x=P, xt=0, m=1, y=P, yt=2):
+    return vq.lib().vq_svq_gemv(ctypes.byref(desc) if desc is not None else None, packed, a, b, scale, bias, x, xt,
+                                m, y, yt, None)
+
+
+def test_svq_gemv_validation_paths(vq):
+    d = vq.svq_desc(64, 64)
+    assert _svq(vq, None) == vq.VQ_ERR_NULL
+    assert _svq(vq, vq.make_desc(64, 64, 4, 0, 0)) == vq.VQ_ERR_BITS
+    # only the lattice stream: v = 4, one 8-bit field per vector, no residual
+    for other in (vq.make_desc(64, 64, 8, 8, 0), vq.make_desc(64, 64, 4, 8, 8), vq.make_desc(64, 64, 4, 16, 0)):
+        assert _svq(vq, other) == vq.VQ_ERR_UNSUPPORTED, other
+    assert _svq(vq, d, m=-1) == vq.VQ_ERR_SHAPE
+    assert _svq(vq, d, m=17) == vq.VQ_ERR_SHAPE
+    assert _svq(vq, d, xt=2) == vq.VQ_ERR_UNSUPPORTED
+    assert _svq(vq, d, yt=7) == vq.VQ_ERR_UNSUPPORTED
+    assert _svq(vq, d, y=None) == vq.VQ_ERR_NULL
+    assert _svq(vq, d, packed=None) == vq.VQ_ERR_NULL
+    assert _svq(vq, d, a=None) == vq.VQ_ERR_NULL
+    assert _svq(vq, d, b=None) == vq.VQ_ERR_NULL
+    assert _svq(vq, d, x=None) == vq.VQ_ERR_NULL
+    assert _svq(vq, d, packed=ctypes.c_void_p(0x10008)) == vq.VQ_ERR_ALIGN  # 16-byte code loads
+    assert _svq(vq, d, a=ctypes.c_void_p(0x10001)) == vq.VQ_ERR_ALIGN
+    assert _svq(vq, d, x=ctypes.c_void_p(0x10001)) == vq.VQ_ERR_ALIGN
+    assert _svq(vq, d, y=P_MIS, yt=2) == vq.VQ_ERR_ALIGN
+    # nothing to do
+    assert _svq(vq, d, m=0, y=None, x=None, packed=None, a=None, b=None) == vq.VQ_OK
+    assert _svq(vq, vq.svq_desc(0, 64), y=None, x=None, packed=None) == vq.VQ_OK
+
+
+def test_svq_dequant_validation_paths(vq):
+    f = vq.lib().vq_svq_dequant
+    d = vq.svq_desc(64, 64)
+    assert f(None, P, P, P, None, P, 2, None) == vq.VQ_ERR_NULL
+    assert f(ctypes.byref(vq.make_desc(64, 64, 8, 16, 0)), P, P, P, None, P, 2, None) == vq.VQ_ERR_UNSUPPORTED
+    assert f(ctypes.byref(d), None, P, P, None, P, 2, None) == vq.VQ_ERR_NULL
+    assert f(ctypes.byref(d), P, None, P, None, P, 2, None) == vq.VQ_ERR_NULL
+    assert f(ctypes.byref(d), P, P, None, None, P, 2, None) == vq.VQ_ERR_NULL
+    assert f(ctypes.byref(d), P, P, P, None, P, 9, None) == vq.VQ_ERR_UNSUPPORTED
+    assert f(ctypes.byref(d), P, P, P, None, P_MIS, 2, None) == vq.VQ_ERR_ALIGN
+    assert f(ctypes.byref(vq.svq_desc(64, 0)), None, None, None, None, None, 2, None) == vq.VQ_OK
+
+
+def test_svq_pack_fields_match_oracle(vq):
+    """The binding's svq_fields + vq_pack give the oracle's lattice stream."""
+    lay = synth.make_svq_layer(5, 37)
+    q = np.stack([(lay["codes"] >> (2 * u)) & 3 for u in range(4)], axis=-1)
+    fields = vq.svq_fields(q)
+    assert np.array_equal(fields, lay["codes"])
+    ours = vq.pack(vq.svq_desc(5, 37), fields)
+    assert np.array_equal(ours, oracle.pack(5, 37, 4, 8, 0, lay["codes"]))

@@ -52,6 +52,15 @@ DESCRIBE = {
     "mlp8b": "MLP pair 14336x4096 + 4096x14336 v6 K1=K2=4096 (4 bits/weight)",
     "l70b": "70B-class pair 28672x8192 + 8192x28672 v8 K1=65536+K2=256 (3 bits/weight)",
 }
+SVQ_WORKLOADS = {
+    # affine-lattice layers: one 8-bit field of four 2-bit codes per 4-vector (2 bits/weight)
+    "svq4k": ([(4096, 4096)], "f16"),
+    "svq70b": ([(28672, 8192), (8192, 28672)], "bf16"),
+}
+SVQ_DESCRIBE = {
+    "svq4k": "4096x4096 affine lattice d=4 (2 bits/weight)",
+    "svq70b": "70B-class pair 28672x8192 + 8192x28672 affine lattice d=4 (2 bits/weight)",
+}
 GEMV_SOURCES = ["gemv_bit_unpack_amd/csrc/vq_gemv.hip", "gemv_bit_unpack_amd/csrc/vq_device.h"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_vq_gemv_dec4k_m1.json")
 
@@ -137,6 +146,59 @@ class Ring:
         st = self.fn(*self.items[k % self.copies], stream_ptr)
         if st != 0:
             raise RuntimeError("%s failed with status %d" % (self.fn.__name__, st))
+
+
+class SvqRing:
+    """Distinct copies of an affine-lattice layer (own codes and A, B; shared x) for vq_svq_gemv."""
+
+    def __init__(self, vq, torch, key, layer, m, copies=None):
+        layers, xd = SVQ_WORKLOADS[key]
+        n, i = layers[layer]
+        self.desc = vq.svq_desc(n, i)
+        self.m = m
+        dev = torch.device("cuda")
+        nb = vq.packed_bytes(self.desc)
+        xdt = torch.bfloat16 if xd == "bf16" else torch.float16
+        self.bytes_per_call = nb + 40 + 2 * m * i + 2 * m * n   # codes + A, B + x + y
+        self.copies = copies or min(MAX_COPIES, max(1, -(-RING_BYTES // self.bytes_per_call)))
+        g = torch.Generator(device=dev)
+        g.manual_seed(zlib.crc32(("%d/%s/%d/svq" % (42, key, layer)).encode()))
+        self.x = torch.randn((m, i), generator=g, device=dev, dtype=torch.float32).to(xdt)
+        code = {torch.float16: vq.VQ_F16, torch.bfloat16: vq.VQ_BF16}
+        self.fn = vq.lib().vq_svq_gemv
+        self.items, self.tensors = [], []
+        p = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
+        for _ in range(self.copies):
+            packed = torch.randint(0, 256, (nb,), generator=g, device=dev, dtype=torch.uint8)
+            a = (torch.randn((4, 4), generator=g, device=dev) * 0.018).half()
+            b = (torch.randn((4,), generator=g, device=dev) * 0.03).half()
+            y = torch.empty((m, n), device=dev, dtype=xdt)
+            self.tensors.append((packed, a, b, y))
+            self.items.append((ctypes.byref(self.desc), p(packed), p(a), p(b), None, None, p(self.x), code[xdt], m,
+                               p(y), code[xdt]))
+        self.sliced = False
+
+    def call(self, k, stream_ptr):
+        st = self.fn(*self.items[k % self.copies], stream_ptr)
+        if st != 0:
+            raise RuntimeError("vq_svq_gemv failed with status %d" % st)
+
+
+def svq_leg(vq, torch, use_graph, steps=None):
+    """vq_svq_gemv on the affine-lattice workloads: M = 1 on both, M = 16 on the 4096^2 layer."""
+    out = {}
+    for key, m in (("svq4k", 1), ("svq70b", 1), ("svq4k", 16), ("svq70b", 8)):
+        rings = [SvqRing(vq, torch, key, li, m) for li in range(len(SVQ_WORKLOADS[key][0]))]
+        n_steps = steps or max(400, 2 * sum(r.copies for r in rings))
+        sec, calls, _, launch = time_ring(torch, rings, n_steps, 20, use_graph)
+        b = sum(r.bytes_per_call for r in rings) / len(rings)
+        out["%s_m%d" % (key, m)] = {
+            "workload": SVQ_DESCRIBE[key] + ", M=%d" % m, "us_per_call": round(sec * 1e6, 3),
+            "GBps": round(b / sec / 1e9, 1), "pct_hbm": round(100 * b / sec / 1e9 / HBM_PEAK_GBPS, 2),
+            "bytes_per_call": int(b), "copies": rings[0].copies, "calls": calls, "launch": launch}
+        del rings
+        torch.cuda.empty_cache()
+    return out
 
 
 def time_ring(torch, rings, steps, warmup, use_graph=True):
@@ -238,6 +300,8 @@ def main():
                     help="run only a plain 512 MiB device copy (known bytes) to scale rocprofv3 counters")
     ap.add_argument("--shared-book", action="store_true",
                     help="diagnostic: every ring copy shares one codebook (warm in L2), headline only")
+    ap.add_argument("--only-svq", action="store_true",
+                    help="run only the affine-lattice (vq_svq_gemv) leg (for profiling)")
     ap.add_argument("--only-workload", default=None, choices=sorted(WORKLOADS),
                     help="run only one workload's M=1 leg through vq_gemv_ws (for profiling)")
     args = ap.parse_args()
@@ -278,6 +342,9 @@ def main():
         flops = (up.flops_per_call + down.flops_per_call) / 2
         print(json.dumps({"gemm_tflops": round(flops / gsec / 1e12, 2), "ms_per_call": round(gsec * 1e3, 4),
                           "calls": gcalls, "launch": glaunch}))
+        return
+    if args.only_svq:
+        print(json.dumps({"affine_lattice": svq_leg(vq, torch, use_graph, steps=args.steps)}))
         return
     if args.only_workload:
         key = args.only_workload
@@ -382,6 +449,7 @@ def main():
                 torch.cuda.empty_cache()
             batch["%s_m%d" % (key, m)] = entry
         out["gemv_batched"] = batch
+        out["affine_lattice"] = svq_leg(vq, torch, use_graph)
         if not args.no_cpu_baseline:
             out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)

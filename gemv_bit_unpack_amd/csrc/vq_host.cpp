@@ -104,6 +104,7 @@ static vq_status prepare_svq(const vq_desc* desc, const void* packed, const void
   p->bias = (const uint16_t*)bias;
   p->x = (const uint16_t*)x;
   p->y = y;
+  p->x_vec4 = (m > 0 && d.in_features % 4 == 0 && aligned(x, 8)) ? 1 : 0;
   return VQ_OK;
 }
 

@@ -78,6 +78,7 @@ struct SvqArgs {
   void* y;                // [M][n]
   int32_t m;
   vq_dtype x_dtype, y_dtype;
+  int32_t x_vec4;  // IN % 4 == 0 and x 8-byte aligned: x read one 4-vector per load
 };
 vq_status launch_svq_gemv(const SvqArgs& p, void* stream);
 vq_status launch_svq_dequant(const SvqArgs& p, void* w, vq_dtype w_dtype, void* stream);

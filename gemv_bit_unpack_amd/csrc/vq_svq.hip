@@ -92,9 +92,31 @@ __device__ __forceinline__ void bytes_to_f32(uint32_t w, float (&q)[4]) {
   if constexpr (NB > 3) q[3] = ubyte_to_f32<3>(w);
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_shuffle(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 64 lanes, the same value in every lane, in a fixed order: within each row
+// of 16 lanes by DPP (quad_perm [1,0,3,2], [2,3,0,1], row_ror 4, row_ror 8), then the four
+// row sums read from lanes 0, 16, 32, 48.
 __device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_shuffle<0xB1>(v);
+  v += dpp_shuffle<0x4E>(v);
+  v += dpp_shuffle<0x124>(v);
+  v += dpp_shuffle<0x128>(v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
+// Sum over the lanes that agree with this one modulo S (S a power of two up to 64).
+template <int S>
+__device__ __forceinline__ float wave_sum_stride(float v) {
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, vqd::kWave);
+  for (int off = 32; off >= S; off >>= 1) v += __shfl_xor(v, off, vqd::kWave);
   return v;
 }
 
@@ -102,11 +124,16 @@ template <int MT, int XT, int L, int R>
 __global__ __launch_bounds__(kSvqThreads) void svq_gemv_kernel(SvqArgs p) {
   constexpr int SW = 256 * L;               // columns per slice
   constexpr int SG = SW / 4;                // 4-vectors (code bytes) per slice
+  constexpr int XS = SW + 4;                // xh row pitch: batch rows start in different banks
   constexpr int NB = L < 4 ? L : 4;         // code bytes per 32-bit word
   constexpr int ND = L < 4 ? 1 : L / 4;     // 32-bit words per lane and row
+  constexpr int PSTEP = kSvqThreads / MT;   // pre-pass: threads per batch row
+  constexpr int PI = SG / PSTEP;            // pre-pass: 4-vectors per thread and slice
+  static_assert(PI * PSTEP == SG && PI >= 1, "the pre-pass covers the slice exactly");
   using CT = typename CodeWord<L>::T;
-  __shared__ float xh[MT * SW];
-  __shared__ float cred[kSvqWaves * MT];
+  __shared__ float xh[MT * XS];
+  __shared__ float cbuf[kSvqWaves * MT];
+  __shared__ float cfin[MT];
 
   const int tid = threadIdx.x;
   const int lane = tid & (vqd::kWave - 1);
@@ -127,56 +154,78 @@ __global__ __launch_bounds__(kSvqThreads) void svq_gemv_kernel(SvqArgs p) {
   for (int r = 0; r < R; ++r) prow[r] = p.packed + (size_t)min(row0 + r, N - 1) * (size_t)p.stride;
   const int nsl = (p.nv + SG - 1) / SG;
 
-  float acc[R][MT];
-  float cpart[MT];
-#pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    cpart[m] = 0.0f;
-#pragma unroll
-    for (int r = 0; r < R; ++r) acc[r][m] = 0.0f;
-  }
-
-  for (int s = 0; s < nsl; ++s) {
-    // code bytes of the lane's 4L columns in each of its rows; a lane past the row end
-    // reads the row start instead (its activations below are zero)
+  // code bytes of the lane's 4L columns of slice s in each of its rows; a lane past the
+  // row end reads the row start instead (its activations are zero)
+  auto load_codes = [&](int s, CT (&cw)[R]) __attribute__((always_inline)) {
     const uint32_t boff = (uint32_t)s * SG + (uint32_t)lane * L;
     const uint32_t off = boff < (uint32_t)p.stride ? boff : 0u;
-    CT cw[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) cw[r] = *(const CT*)(prow[r] + off);
+  };
 
+  // pre-pass: thread tid serves batch row pm (rows >= M write zeros) for 4-vectors
+  // pi0, pi0 + PSTEP, ...; its loads are clamped into the row and zeroed afterwards, so
+  // they issue back to back
+  const int pm = tid % MT;
+  const int pi0 = tid / MT;
+  const bool pm_live = pm < M;
+  const uint16_t* xrow = p.x + (size_t)min(pm, M - 1) * (size_t)IN;
+  float cpart = 0.0f;
+
+  float acc[R][MT];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
+  }
+
+  CT cw[R], cn[R];
+  for (int s = 0; s < nsl; ++s) {
     // pre-applied activations of the slice (zero past the row end).  Vector g of the slice
-    // belongs to lane g / L as its (g % L)-th vector; xh keeps [g % L][lane][4] so that the
-    // lanes' float4 reads below, and these writes (lane fastest), do not share banks.
-    for (int idx = tid; idx < SG; idx += kSvqThreads) {
-      const int g = (idx % vqd::kWave) * L + idx / vqd::kWave;
-      const int j = s * SG + g;
+    // belongs to lane g / L as its (g % L)-th vector; xh keeps [g % L][lane][4] per batch
+    // row so that the lanes' float4 reads below do not share banks.  The thread's PI
+    // activation loads are issued together (and, for the first slice, ahead of the first
+    // code loads), so the pre-pass waits on L2 only.
+    uint2 xw[PI];  // the 4 activations of each 4-vector, two 16-bit values per word
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        float xv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (m < M) {
-          const uint16_t* xrow = p.x + (size_t)m * IN;
+    for (int e = 0; e < PI; ++e) {
+      const int pi = pi0 + e * PSTEP;
+      const int g = (pi % vqd::kWave) * L + pi / vqd::kWave;
+      const int c0 = 4 * (s * SG + g);
+      if (p.x_vec4) {  // IN % 4 == 0 and x 8-byte aligned: one load per vector
+        xw[e] = *(const uint2*)(xrow + min(c0, IN - 4));
+      } else {
+        uint32_t raw[4];
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int col = 4 * j + t;
-            if (col < IN) xv[t] = vqd::x_to_f32<XT>(xrow[col]);
-          }
-        }
-        float h[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          h[u] = 0.0f;
-#pragma unroll
-          for (int t = 0; t < 4; ++t) h[u] = __builtin_fmaf(A[t][u], xv[t], h[u]);
-          h[u] = h[u] * quarter_pow[u];
-        }
-        *(float4*)&xh[m * SW + 4 * idx] = make_float4(h[0], h[1], h[2], h[3]);
-        float cb = 0.0f;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) cb = __builtin_fmaf(B[t], xv[t], cb);
-        cpart[m] += cb;
+        for (int t = 0; t < 4; ++t) raw[t] = xrow[min(c0 + t, IN - 1)];
+        xw[e] = make_uint2(raw[0] | (raw[1] << 16), raw[2] | (raw[3] << 16));
       }
     }
+    if (s == 0) load_codes(0, cw);
+#pragma unroll
+    for (int e = 0; e < PI; ++e) {
+      const int pi = pi0 + e * PSTEP;
+      const int g = (pi % vqd::kWave) * L + pi / vqd::kWave;
+      const int c0 = 4 * (s * SG + g);
+      float xv[4];
+      const uint32_t raw[4] = {xw[e].x & 0xFFFFu, xw[e].x >> 16, xw[e].y & 0xFFFFu, xw[e].y >> 16};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) xv[t] = (pm_live && c0 + t < IN) ? vqd::x_to_f32<XT>(raw[t]) : 0.0f;
+      float h[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        h[u] = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) h[u] = __builtin_fmaf(A[t][u], xv[t], h[u]);
+        h[u] = h[u] * quarter_pow[u];
+      }
+      *(float4*)&xh[pm * XS + 4 * pi] = make_float4(h[0], h[1], h[2], h[3]);
+      float cb = 0.0f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) cb = __builtin_fmaf(B[t], xv[t], cb);
+      cpart += cb;
+    }
+    if (s + 1 < nsl) load_codes(s + 1, cn);  // next slice's codes in flight during this one
     __syncthreads();
 
     float xr[MT][4 * L];
@@ -184,7 +233,7 @@ __global__ __launch_bounds__(kSvqThreads) void svq_gemv_kernel(SvqArgs p) {
     for (int m = 0; m < MT; ++m) {
 #pragma unroll
       for (int i = 0; i < L; ++i) {
-        const float4 v = *(const float4*)&xh[m * SW + 4 * (i * vqd::kWave + lane)];
+        const float4 v = *(const float4*)&xh[m * XS + 4 * (i * vqd::kWave + lane)];
         xr[m][4 * i] = v.x;
         xr[m][4 * i + 1] = v.y;
         xr[m][4 * i + 2] = v.z;
@@ -209,23 +258,23 @@ __global__ __launch_bounds__(kSvqThreads) void svq_gemv_kernel(SvqArgs p) {
         }
       }
     }
+#pragma unroll
+    for (int r = 0; r < R; ++r) cw[r] = cn[r];
     __syncthreads();  // xh is rewritten by the next slice
   }
 
-  // constant term B . sum_j x_mj, over the whole workgroup in a fixed order
+  // constant term B . sum_j x_mj, over the workgroup in a fixed order: lanes that serve
+  // the same batch row (lane % MT) are added across the wavefront, then the wavefronts
+  cpart = wave_sum_stride<MT>(cpart);
+  if (lane < MT) cbuf[wave * MT + lane] = cpart;
+  __syncthreads();
+  if (tid < MT) {
+    float c = 0.0f;
 #pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    const float v = wave_sum(cpart[m]);
-    if (lane == 0) cred[wave * MT + m] = v;
+    for (int w = 0; w < kSvqWaves; ++w) c += cbuf[w * MT + tid];
+    cfin[tid] = c;
   }
   __syncthreads();
-  float c[MT];
-#pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    c[m] = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kSvqWaves; ++w) c[m] += cred[w * MT + m];
-  }
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int row = row0 + r;
@@ -235,13 +284,175 @@ __global__ __launch_bounds__(kSvqThreads) void svq_gemv_kernel(SvqArgs p) {
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       if (m < M) {
-        float v = wave_sum(acc[r][m]) + c[m];
+        float v = wave_sum(acc[r][m]) + cfin[m];
         if (lane == 0 && row < N) {
           if (p.scale) v = v * sc;
           if (p.bias) v = v + bi;
           vqd::store_out(p.y, (size_t)m * N + row, v, p.y_dtype);
         }
       }
+    }
+  }
+}
+
+// M = 1 with the whole row's pre-applied activations resident in LDS (IN4 floats): a
+// persistent workgroup of 16 wavefronts computes them once, then each wavefront streams
+// work items (a block of R of its rows, one 4096-column slice) with the code loads of the
+// next two items in flight, and no barrier until the end.
+constexpr int kStreamThreads = 1024;
+constexpr int kStreamWaves = kStreamThreads / vqd::kWave;
+constexpr int kStreamSW = 4096;              // columns per slice: 16 code bytes per lane
+constexpr int kStreamSG = kStreamSW / 4;
+constexpr int kStreamMaxSlices = 7;          // 28672 columns
+constexpr size_t kStreamLdsMax = (size_t)kStreamMaxSlices * kStreamSW * sizeof(float);
+
+template <int XT, int R>
+__global__ __launch_bounds__(kStreamThreads) void svq_gemv_stream_kernel(SvqArgs p, int nsl, int nblocks) {
+  extern __shared__ float xs[];  // [nsl][16][64][4]: slice s, vector i of lane l
+  __shared__ float cbuf[kStreamWaves];
+  const int tid = threadIdx.x;
+  const int lane = tid & (vqd::kWave - 1);
+  const int wave = tid / vqd::kWave;
+  const int IN = p.in_features, N = p.n;
+  float A[4][4], B[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    B[t] = vqd::f16_to_f32(p.b[t]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) A[t][u] = vqd::f16_to_f32(p.a[t * 4 + u]);
+  }
+  const float quarter_pow[4] = {1.0f, 0.25f, 0.0625f, 0.015625f};
+
+  // work items of this wavefront: it = k * nsl + s for its row blocks k (block index
+  // blockIdx.x + k * gridDim.x) and slices s; rows of block b: b * 16R + wave * R + r
+  const int my_blocks = (nblocks - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int items = my_blocks * nsl;
+  auto item_addr = [&](int it, int r) __attribute__((always_inline)) -> const uint4* {
+    const int itc = min(it, items - 1);  // past the end: repeat the last item (not used)
+    const int k = itc / nsl;
+    const int sl = itc - k * nsl;
+    const int blk = (int)blockIdx.x + k * (int)gridDim.x;
+    const int row = min(blk * (kStreamWaves * R) + wave * R + r, N - 1);
+    const uint32_t boff = (uint32_t)sl * kStreamSG + (uint32_t)lane * 16u;
+    const uint32_t off = boff < (uint32_t)p.stride ? boff : 0u;
+    return (const uint4*)(p.packed + (size_t)row * (size_t)p.stride + off);
+  };
+  // pre-applied activations of the whole row (zero past IN), and the constant term.
+  // Thread tid serves the 4-vectors idx = tid + e * 1024, e < nsl (at most 7): their
+  // activations are loaded first, all at once, ahead of the code prefetch, so that the
+  // pre-pass waits on L2 only.
+  const int total = nsl * kStreamSG;
+  uint32_t xraw[kStreamMaxSlices][4];
+#pragma unroll
+  for (int e = 0; e < kStreamMaxSlices; ++e) {
+    const int idx = min(tid + e * kStreamThreads, total - 1);
+    const int sl = idx / kStreamSG;
+    const int pi = idx - sl * kStreamSG;
+    const int g = (pi % vqd::kWave) * 16 + pi / vqd::kWave;
+    const int c0c = 4 * (sl * kStreamSG + g);
+    if (p.x_vec4) {
+      const uint2 w = *(const uint2*)(p.x + min(c0c, IN - 4));
+      xraw[e][0] = w.x & 0xFFFFu;
+      xraw[e][1] = w.x >> 16;
+      xraw[e][2] = w.y & 0xFFFFu;
+      xraw[e][3] = w.y >> 16;
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) xraw[e][t] = p.x[min(c0c + t, IN - 1)];
+    }
+  }
+  uint4 c0[R], c1[R], c2[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    c0[r] = *item_addr(0, r);
+    c1[r] = *item_addr(1, r);
+  }
+  float cpart = 0.0f;
+#pragma unroll
+  for (int e = 0; e < kStreamMaxSlices; ++e) {
+    const int idx = tid + e * kStreamThreads;
+    if (idx >= total) break;  // uniform across the wavefront: total is a multiple of 1024
+    const int sl = idx / kStreamSG;
+    const int pi = idx - sl * kStreamSG;
+    const int g = (pi % vqd::kWave) * 16 + pi / vqd::kWave;
+    const int c0c = 4 * (sl * kStreamSG + g);
+    float xv[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) xv[t] = c0c + t < IN ? vqd::x_to_f32<XT>(xraw[e][t]) : 0.0f;
+    float h[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      h[u] = 0.0f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) h[u] = __builtin_fmaf(A[t][u], xv[t], h[u]);
+      h[u] = h[u] * quarter_pow[u];
+    }
+    *(float4*)&xs[4 * idx] = make_float4(h[0], h[1], h[2], h[3]);
+    float cb = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) cb = __builtin_fmaf(B[t], xv[t], cb);
+    cpart += cb;
+  }
+  cpart = wave_sum(cpart);
+  if (lane == 0) cbuf[wave] = cpart;
+  __syncthreads();  // the activations and the wavefront partials of the constant term
+  float c = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kStreamWaves; ++w) c += cbuf[w];
+
+  float xr[64];
+  auto load_xr = [&](int sl) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float4 v = *(const float4*)&xs[sl * kStreamSW + 4 * (i * vqd::kWave + lane)];
+      xr[4 * i] = v.x;
+      xr[4 * i + 1] = v.y;
+      xr[4 * i + 2] = v.z;
+      xr[4 * i + 3] = v.w;
+    }
+  };
+  if (nsl == 1) load_xr(0);
+  float acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+  for (int it = 0; it < items; ++it) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) c2[r] = *item_addr(it + 2, r);
+    const int k = it / nsl;
+    const int sl = it - k * nsl;
+    if (nsl > 1) load_xr(sl);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t wd[4] = {c0[r].x, c0[r].y, c0[r].z, c0[r].w};
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          float q[4];
+          bytes_to_f32<4>(wd[d] & (0x03030303u << (2 * kk)), q);
+#pragma unroll
+          for (int b = 0; b < 4; ++b) acc[r] = __builtin_fmaf(q[b], xr[16 * d + 4 * b + kk], acc[r]);
+        }
+      }
+    }
+    if (sl == nsl - 1) {  // row block done
+      const int blk = (int)blockIdx.x + k * (int)gridDim.x;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int row = blk * (kStreamWaves * R) + wave * R + r;
+        float v = wave_sum(acc[r]) + c;
+        if (lane == 0 && row < N) {
+          if (p.scale) v = v * vqd::f16_to_f32(p.scale[row]);
+          if (p.bias) v = v + vqd::f16_to_f32(p.bias[row]);
+          vqd::store_out(p.y, row, v, p.y_dtype);
+        }
+        acc[r] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      c0[r] = c1[r];
+      c1[r] = c2[r];
     }
   }
 }
@@ -277,15 +488,36 @@ vq_status launch_rows(const SvqArgs& p, hipStream_t s) {
 template <int MT, int XT>
 vq_status launch_m(const SvqArgs& p, hipStream_t s) {
   constexpr int L = MT == 1 ? 16 : MT == 2 ? 8 : MT <= 8 ? 4 : 2;
-  // four rows per wavefront once there are enough rows to fill the chip with 512-row
-  // steps of 32 rows; one row per wavefront below that
-  if (p.n >= 16384) return launch_rows<MT, XT, L, 4>(p, s);
+  // four rows per wavefront once there are enough rows to fill the chip in steps of 32
+  // rows, or when the batch makes the per-slice activation copy worth sharing across
+  // more rows; one row per wavefront otherwise
+  if (MT >= 8 || p.n >= 16384) return launch_rows<MT, XT, L, 4>(p, s);
   return launch_rows<MT, XT, L, 1>(p, s);
+}
+
+template <int XT, int R>
+vq_status launch_stream(const SvqArgs& p, int nsl, hipStream_t s) {
+  auto kern = svq_gemv_stream_kernel<XT, R>;
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kStreamLdsMax);
+  if (attr != hipSuccess) return VQ_ERR_HIP;
+  const int nblocks = (p.n + kStreamWaves * R - 1) / (kStreamWaves * R);
+  const int grid = nblocks < 256 ? nblocks : 256;  // one persistent workgroup per CU
+  const size_t lds = (size_t)nsl * kStreamSW * sizeof(float);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kStreamThreads), lds, s, p, nsl, nblocks);
+  return hipGetLastError() == hipSuccess ? VQ_OK : VQ_ERR_HIP;
 }
 
 template <int XT>
 vq_status launch_x(const SvqArgs& p, hipStream_t s) {
-  if (p.m <= 1) return launch_m<1, XT>(p, s);
+  if (p.m <= 1) {
+    // the streaming kernel when one row's pre-applied activations fit in LDS
+    const int nsl = (p.nv + kStreamSG - 1) / kStreamSG;
+    // when one row's pre-applied activations fit in LDS and there are enough rows for
+    // every persistent workgroup to stream several items
+    if (nsl > 0 && nsl <= kStreamMaxSlices && p.n >= 2 * 256 * kStreamWaves) return launch_stream<XT, 2>(p, nsl, s);
+    return launch_m<1, XT>(p, s);
+  }
   if (p.m <= 2) return launch_m<2, XT>(p, s);
   if (p.m <= 4) return launch_m<4, XT>(p, s);
   if (p.m <= 8) return launch_m<8, XT>(p, s);

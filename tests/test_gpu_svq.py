@@ -7,7 +7,8 @@ C ABI.
   oracle's fp32;
 - gemv: shapes with ragged rows and columns (vector tails of 1..3 lanes, rows ending
   inside a column slice, several slices), M from 1 to 16, bias and scale, every output
-  dtype, fp16 and bf16 activations, both row mappings (one and four rows per wavefront);
+  dtype, fp16 and bf16 activations, every kernel shape (for M = 1: the whole row's
+  activations resident in LDS with one or two rows per wavefront, or walked in slices);
   the workloads (4096^2 at M = 1, 4, 16; the 70B-class pair at M = 1, 8) on sampled rows
   at full size;
 - dyadic grids with one-hot activations reproduce columns of W^ bit-exactly;
@@ -117,6 +118,9 @@ SHAPES = [
     (16500, 64, 1, "f16", "f32", True, True),      # four rows per wavefront
     (16390, 36, 16, "bf16", "f16", False, True),   # four rows per wavefront, M = 16
     (16385, 520, 7, "f16", "f32", True, False),
+    (300, 28670, 1, "bf16", "f32", True, True),    # M = 1, seven slices resident in LDS
+    (9000, 28673, 1, "f16", "f32", False, True),   # M = 1, eight slices: the sliced pass
+    (8200, 4098, 1, "f16", "bf16", True, False),   # M = 1, two rows per wavefront, ragged
 ]
 
 

@@ -131,7 +131,7 @@ __global__ __launch_bounds__(kSvqThreads) void svq_gemv_kernel(SvqArgs p) {
   constexpr int PI = SG / PSTEP;            // pre-pass: 4-vectors per thread and slice
   static_assert(PI * PSTEP == SG && PI >= 1, "the pre-pass covers the slice exactly");
   using CT = typename CodeWord<L>::T;
-  __shared__ float xh[MT * XS];
+  __shared__ float4 xh[MT * XS / 4];
   __shared__ float cbuf[kSvqWaves * MT];
   __shared__ float cfin[MT];
 
@@ -219,7 +219,7 @@ __global__ __launch_bounds__(kSvqThreads) void svq_gemv_kernel(SvqArgs p) {
         for (int t = 0; t < 4; ++t) h[u] = __builtin_fmaf(A[t][u], xv[t], h[u]);
         h[u] = h[u] * quarter_pow[u];
       }
-      *(float4*)&xh[pm * XS + 4 * pi] = make_float4(h[0], h[1], h[2], h[3]);
+      xh[(pm * XS) / 4 + pi] = make_float4(h[0], h[1], h[2], h[3]);
       float cb = 0.0f;
 #pragma unroll
       for (int t = 0; t < 4; ++t) cb = __builtin_fmaf(B[t], xv[t], cb);
@@ -233,7 +233,7 @@ __global__ __launch_bounds__(kSvqThreads) void svq_gemv_kernel(SvqArgs p) {
     for (int m = 0; m < MT; ++m) {
 #pragma unroll
       for (int i = 0; i < L; ++i) {
-        const float4 v = *(const float4*)&xh[m * XS + 4 * (i * vqd::kWave + lane)];
+        const float4 v = xh[(m * XS) / 4 + i * vqd::kWave + lane];
         xr[m][4 * i] = v.x;
         xr[m][4 * i + 1] = v.y;
         xr[m][4 * i + 2] = v.z;
@@ -308,7 +308,7 @@ constexpr size_t kStreamLdsMax = (size_t)kStreamMaxSlices * kStreamSW * sizeof(f
 
 template <int XT, int R>
 __global__ __launch_bounds__(kStreamThreads) void svq_gemv_stream_kernel(SvqArgs p, int nsl, int nblocks) {
-  extern __shared__ float xs[];  // [nsl][16][64][4]: slice s, vector i of lane l
+  extern __shared__ float4 xs[];  // [nsl][16][64]: slice s, vector i of lane l
   __shared__ float cbuf[kStreamWaves];
   const int tid = threadIdx.x;
   const int lane = tid & (vqd::kWave - 1);
@@ -323,26 +323,34 @@ __global__ __launch_bounds__(kStreamThreads) void svq_gemv_stream_kernel(SvqArgs
   }
   const float quarter_pow[4] = {1.0f, 0.25f, 0.0625f, 0.015625f};
 
-  // work items of this wavefront: it = k * nsl + s for its row blocks k (block index
-  // blockIdx.x + k * gridDim.x) and slices s; rows of block b: b * 16R + wave * R + r
+  // Work items of this wavefront, in order: (k, sl) for its row blocks k (block index
+  // blockIdx.x + k * gridDim.x, rows block * 16R + wave * R + r) and slices sl.
   const int my_blocks = (nblocks - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
   const int items = my_blocks * nsl;
-  auto item_addr = [&](int it, int r) __attribute__((always_inline)) -> const uint4* {
-    const int itc = min(it, items - 1);  // past the end: repeat the last item (not used)
-    const int k = itc / nsl;
-    const int sl = itc - k * nsl;
-    const int blk = (int)blockIdx.x + k * (int)gridDim.x;
-    const int row = min(blk * (kStreamWaves * R) + wave * R + r, N - 1);
+  auto load_item = [&](int k, int sl, uint4 (&cw)[R]) __attribute__((always_inline)) {
+    const int row0 = ((int)blockIdx.x + k * (int)gridDim.x) * (kStreamWaves * R) + wave * R;
     const uint32_t boff = (uint32_t)sl * kStreamSG + (uint32_t)lane * 16u;
-    const uint32_t off = boff < (uint32_t)p.stride ? boff : 0u;
-    return (const uint4*)(p.packed + (size_t)row * (size_t)p.stride + off);
+    const uint32_t off = boff < (uint32_t)p.stride ? boff : 0u;  // past the row: its start
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      cw[r] = *(const uint4*)(p.packed + (size_t)min(row0 + r, N - 1) * (size_t)p.stride + off);
   };
+  // next item; past the last one the cursor stays there (its loads repeat, unused)
+  auto advance = [&](int& k, int& sl) __attribute__((always_inline)) {
+    if (sl + 1 < nsl) {
+      ++sl;
+    } else if (k + 1 < my_blocks) {
+      ++k;
+      sl = 0;
+    }
+  };
+
   // pre-applied activations of the whole row (zero past IN), and the constant term.
   // Thread tid serves the 4-vectors idx = tid + e * 1024, e < nsl (at most 7): their
   // activations are loaded first, all at once, ahead of the code prefetch, so that the
   // pre-pass waits on L2 only.
   const int total = nsl * kStreamSG;
-  uint32_t xraw[kStreamMaxSlices][4];
+  uint2 xw[kStreamMaxSlices];
 #pragma unroll
   for (int e = 0; e < kStreamMaxSlices; ++e) {
     const int idx = min(tid + e * kStreamThreads, total - 1);
@@ -351,34 +359,34 @@ __global__ __launch_bounds__(kStreamThreads) void svq_gemv_stream_kernel(SvqArgs
     const int g = (pi % vqd::kWave) * 16 + pi / vqd::kWave;
     const int c0c = 4 * (sl * kStreamSG + g);
     if (p.x_vec4) {
-      const uint2 w = *(const uint2*)(p.x + min(c0c, IN - 4));
-      xraw[e][0] = w.x & 0xFFFFu;
-      xraw[e][1] = w.x >> 16;
-      xraw[e][2] = w.y & 0xFFFFu;
-      xraw[e][3] = w.y >> 16;
+      xw[e] = *(const uint2*)(p.x + min(c0c, IN - 4));
     } else {
+      uint32_t raw[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) xraw[e][t] = p.x[min(c0c + t, IN - 1)];
+      for (int t = 0; t < 4; ++t) raw[t] = p.x[min(c0c + t, IN - 1)];
+      xw[e] = make_uint2(raw[0] | (raw[1] << 16), raw[2] | (raw[3] << 16));
     }
   }
   uint4 c0[R], c1[R], c2[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    c0[r] = *item_addr(0, r);
-    c1[r] = *item_addr(1, r);
-  }
+  int pk = 0, ps = 0;  // prefetch cursor: two items ahead of the one in use
+  load_item(pk, ps, c0);
+  advance(pk, ps);
+  load_item(pk, ps, c1);
+  advance(pk, ps);
+
   float cpart = 0.0f;
 #pragma unroll
   for (int e = 0; e < kStreamMaxSlices; ++e) {
     const int idx = tid + e * kStreamThreads;
-    if (idx >= total) break;  // uniform across the wavefront: total is a multiple of 1024
+    if (idx >= total) break;  // uniform across the workgroup: total is a multiple of 1024
     const int sl = idx / kStreamSG;
     const int pi = idx - sl * kStreamSG;
     const int g = (pi % vqd::kWave) * 16 + pi / vqd::kWave;
     const int c0c = 4 * (sl * kStreamSG + g);
+    const uint32_t raw[4] = {xw[e].x & 0xFFFFu, xw[e].x >> 16, xw[e].y & 0xFFFFu, xw[e].y >> 16};
     float xv[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) xv[t] = c0c + t < IN ? vqd::x_to_f32<XT>(xraw[e][t]) : 0.0f;
+    for (int t = 0; t < 4; ++t) xv[t] = c0c + t < IN ? vqd::x_to_f32<XT>(raw[t]) : 0.0f;
     float h[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -387,7 +395,7 @@ __global__ __launch_bounds__(kStreamThreads) void svq_gemv_stream_kernel(SvqArgs
       for (int t = 0; t < 4; ++t) h[u] = __builtin_fmaf(A[t][u], xv[t], h[u]);
       h[u] = h[u] * quarter_pow[u];
     }
-    *(float4*)&xs[4 * idx] = make_float4(h[0], h[1], h[2], h[3]);
+    xs[idx] = make_float4(h[0], h[1], h[2], h[3]);
     float cb = 0.0f;
 #pragma unroll
     for (int t = 0; t < 4; ++t) cb = __builtin_fmaf(B[t], xv[t], cb);
@@ -404,7 +412,7 @@ __global__ __launch_bounds__(kStreamThreads) void svq_gemv_stream_kernel(SvqArgs
   auto load_xr = [&](int sl) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      const float4 v = *(const float4*)&xs[sl * kStreamSW + 4 * (i * vqd::kWave + lane)];
+      const float4 v = xs[sl * kStreamSG + i * vqd::kWave + lane];
       xr[4 * i] = v.x;
       xr[4 * i + 1] = v.y;
       xr[4 * i + 2] = v.z;
@@ -412,15 +420,19 @@ __global__ __launch_bounds__(kStreamThreads) void svq_gemv_stream_kernel(SvqArgs
     }
   };
   if (nsl == 1) load_xr(0);
-  float acc[R];
+  // four partial sums per row (code position k of each byte), so the FMAs of a row form
+  // four independent chains
+  float acc[R][4];
 #pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = 0.0f;
+  for (int r = 0; r < R; ++r) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) acc[r][kk] = 0.0f;
+  }
+  int ck = 0, cs = 0;  // item in use
   for (int it = 0; it < items; ++it) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) c2[r] = *item_addr(it + 2, r);
-    const int k = it / nsl;
-    const int sl = it - k * nsl;
-    if (nsl > 1) load_xr(sl);
+    load_item(pk, ps, c2);
+    advance(pk, ps);
+    if (nsl > 1) load_xr(cs);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const uint32_t wd[4] = {c0[r].x, c0[r].y, c0[r].z, c0[r].w};
@@ -431,24 +443,26 @@ __global__ __launch_bounds__(kStreamThreads) void svq_gemv_stream_kernel(SvqArgs
           float q[4];
           bytes_to_f32<4>(wd[d] & (0x03030303u << (2 * kk)), q);
 #pragma unroll
-          for (int b = 0; b < 4; ++b) acc[r] = __builtin_fmaf(q[b], xr[16 * d + 4 * b + kk], acc[r]);
+          for (int b = 0; b < 4; ++b) acc[r][kk] = __builtin_fmaf(q[b], xr[16 * d + 4 * b + kk], acc[r][kk]);
         }
       }
     }
-    if (sl == nsl - 1) {  // row block done
-      const int blk = (int)blockIdx.x + k * (int)gridDim.x;
+    if (cs == nsl - 1) {  // row block done
+      const int row0 = ((int)blockIdx.x + ck * (int)gridDim.x) * (kStreamWaves * R) + wave * R;
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        const int row = blk * (kStreamWaves * R) + wave * R + r;
-        float v = wave_sum(acc[r]) + c;
+        const int row = row0 + r;
+        float v = wave_sum((acc[r][0] + acc[r][1]) + (acc[r][2] + acc[r][3])) + c;
         if (lane == 0 && row < N) {
           if (p.scale) v = v * vqd::f16_to_f32(p.scale[row]);
           if (p.bias) v = v + vqd::f16_to_f32(p.bias[row]);
           vqd::store_out(p.y, row, v, p.y_dtype);
         }
-        acc[r] = 0.0f;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) acc[r][kk] = 0.0f;
       }
     }
+    advance(ck, cs);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       c0[r] = c1[r];
@@ -489,10 +503,14 @@ template <int MT, int XT>
 vq_status launch_m(const SvqArgs& p, hipStream_t s) {
   constexpr int L = MT == 1 ? 16 : MT == 2 ? 8 : MT <= 8 ? 4 : 2;
   // four rows per wavefront once there are enough rows to fill the chip in steps of 32
-  // rows, or when the batch makes the per-slice activation copy worth sharing across
-  // more rows; one row per wavefront otherwise
-  if (MT >= 8 || p.n >= 16384) return launch_rows<MT, XT, L, 4>(p, s);
-  return launch_rows<MT, XT, L, 1>(p, s);
+  // rows, one below that; two from M = 8, where the per-slice activation copy is worth
+  // sharing and four rows would not fit in registers
+  if constexpr (MT >= 8) {
+    return launch_rows<MT, XT, L, 2>(p, s);
+  } else {
+    if (p.n >= 16384) return launch_rows<MT, XT, L, 4>(p, s);
+    return launch_rows<MT, XT, L, 1>(p, s);
+  }
 }
 
 template <int XT, int R>

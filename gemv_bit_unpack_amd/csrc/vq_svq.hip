@@ -130,6 +130,7 @@ __global__ __launch_bounds__(kSvqThreads) void svq_gemv_kernel(SvqArgs p) {
   constexpr int PSTEP = kSvqThreads / MT;   // pre-pass: threads per batch row
   constexpr int PI = SG / PSTEP;            // pre-pass: 4-vectors per thread and slice
   static_assert(PI * PSTEP == SG && PI >= 1, "the pre-pass covers the slice exactly");
+  constexpr int PB = PI < 2 ? PI : 2;       // pre-pass: activation loads in flight per batch
   using CT = typename CodeWord<L>::T;
   __shared__ float4 xh[MT * XS / 4];
   __shared__ float cbuf[kSvqWaves * MT];
@@ -184,46 +185,49 @@ __global__ __launch_bounds__(kSvqThreads) void svq_gemv_kernel(SvqArgs p) {
     // pre-applied activations of the slice (zero past the row end).  Vector g of the slice
     // belongs to lane g / L as its (g % L)-th vector; xh keeps [g % L][lane][4] per batch
     // row so that the lanes' float4 reads below do not share banks.  The thread's PI
-    // activation loads are issued together (and, for the first slice, ahead of the first
-    // code loads), so the pre-pass waits on L2 only.
-    uint2 xw[PI];  // the 4 activations of each 4-vector, two 16-bit values per word
+    // activation loads go out PB at a time, without branches (and for the first slice
+    // ahead of the first code loads), so the pre-pass waits on L2 only.
 #pragma unroll
-    for (int e = 0; e < PI; ++e) {
-      const int pi = pi0 + e * PSTEP;
-      const int g = (pi % vqd::kWave) * L + pi / vqd::kWave;
-      const int c0 = 4 * (s * SG + g);
-      if (p.x_vec4) {  // IN % 4 == 0 and x 8-byte aligned: one load per vector
-        xw[e] = *(const uint2*)(xrow + min(c0, IN - 4));
-      } else {
-        uint32_t raw[4];
+    for (int e0 = 0; e0 < PI; e0 += PB) {
+      uint2 xw[PB];  // the 4 activations of each 4-vector, two 16-bit values per word
 #pragma unroll
-        for (int t = 0; t < 4; ++t) raw[t] = xrow[min(c0 + t, IN - 1)];
-        xw[e] = make_uint2(raw[0] | (raw[1] << 16), raw[2] | (raw[3] << 16));
+      for (int e = 0; e < PB; ++e) {
+        const int pi = pi0 + (e0 + e) * PSTEP;
+        const int g = (pi % vqd::kWave) * L + pi / vqd::kWave;
+        const int c0 = 4 * (s * SG + g);
+        if (p.x_vec4) {  // IN % 4 == 0 and x 8-byte aligned: one load per vector
+          xw[e] = *(const uint2*)(xrow + min(c0, IN - 4));
+        } else {
+          uint32_t raw[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) raw[t] = xrow[min(c0 + t, IN - 1)];
+          xw[e] = make_uint2(raw[0] | (raw[1] << 16), raw[2] | (raw[3] << 16));
+        }
       }
-    }
-    if (s == 0) load_codes(0, cw);
+      if (s == 0 && e0 == 0) load_codes(0, cw);
 #pragma unroll
-    for (int e = 0; e < PI; ++e) {
-      const int pi = pi0 + e * PSTEP;
-      const int g = (pi % vqd::kWave) * L + pi / vqd::kWave;
-      const int c0 = 4 * (s * SG + g);
-      float xv[4];
-      const uint32_t raw[4] = {xw[e].x & 0xFFFFu, xw[e].x >> 16, xw[e].y & 0xFFFFu, xw[e].y >> 16};
+      for (int e = 0; e < PB; ++e) {
+        const int pi = pi0 + (e0 + e) * PSTEP;
+        const int g = (pi % vqd::kWave) * L + pi / vqd::kWave;
+        const int c0 = 4 * (s * SG + g);
+        float xv[4];
+        const uint32_t raw[4] = {xw[e].x & 0xFFFFu, xw[e].x >> 16, xw[e].y & 0xFFFFu, xw[e].y >> 16};
 #pragma unroll
-      for (int t = 0; t < 4; ++t) xv[t] = (pm_live && c0 + t < IN) ? vqd::x_to_f32<XT>(raw[t]) : 0.0f;
-      float h[4];
+        for (int t = 0; t < 4; ++t) xv[t] = (pm_live && c0 + t < IN) ? vqd::x_to_f32<XT>(raw[t]) : 0.0f;
+        float h[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        h[u] = 0.0f;
+        for (int u = 0; u < 4; ++u) {
+          h[u] = 0.0f;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) h[u] = __builtin_fmaf(A[t][u], xv[t], h[u]);
-        h[u] = h[u] * quarter_pow[u];
+          for (int t = 0; t < 4; ++t) h[u] = __builtin_fmaf(A[t][u], xv[t], h[u]);
+          h[u] = h[u] * quarter_pow[u];
+        }
+        xh[(pm * XS) / 4 + pi] = make_float4(h[0], h[1], h[2], h[3]);
+        float cb = 0.0f;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) cb = __builtin_fmaf(B[t], xv[t], cb);
+        cpart += cb;
       }
-      xh[(pm * XS) / 4 + pi] = make_float4(h[0], h[1], h[2], h[3]);
-      float cb = 0.0f;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) cb = __builtin_fmaf(B[t], xv[t], cb);
-      cpart += cb;
     }
     if (s + 1 < nsl) load_codes(s + 1, cn);  // next slice's codes in flight during this one
     __syncthreads();
@@ -503,10 +507,12 @@ template <int MT, int XT>
 vq_status launch_m(const SvqArgs& p, hipStream_t s) {
   constexpr int L = MT == 1 ? 16 : MT == 2 ? 8 : MT <= 8 ? 4 : 2;
   // four rows per wavefront once there are enough rows to fill the chip in steps of 32
-  // rows, one below that; two from M = 8, where the per-slice activation copy is worth
-  // sharing and four rows would not fit in registers
-  if constexpr (MT >= 8) {
+  // rows, one below that; from M = 8 the per-slice activation copy is worth sharing
+  // over four rows (two at M = 16, where four would not fit in registers)
+  if constexpr (MT >= 16) {
     return launch_rows<MT, XT, L, 2>(p, s);
+  } else if constexpr (MT >= 8) {
+    return launch_rows<MT, XT, L, 4>(p, s);
   } else {
     if (p.n >= 16384) return launch_rows<MT, XT, L, 4>(p, s);
     return launch_rows<MT, XT, L, 1>(p, s);

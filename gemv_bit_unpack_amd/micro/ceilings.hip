@@ -43,7 +43,7 @@ __global__ void gather_global(const uint4* __restrict__ tab, unsigned mask, int 
       v[k] = tab[(s >> 7) & mask];
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) acc ^= v[k].x ^ v[k].w;
+    for (int k = 0; k < 8; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;  // all four words: full 16-byte loads
   }
   if (acc == 0x12345678u) out[0] = acc;
 }
@@ -63,7 +63,7 @@ __global__ void gather_lds(const uint4* __restrict__ tab, unsigned entries, int 
       v[k] = lds_tab[(s >> 7) & mask];
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) acc ^= v[k].x ^ v[k].w;
+    for (int k = 0; k < 8; ++k) acc ^= v[k].x ^ v[k].y ^ v[k].z ^ v[k].w;  // all four words: full 16-byte loads
   }
   if (acc == 0x12345678u) out[0] = acc;
 }

@@ -44,6 +44,8 @@ WORKLOADS = {
     "dec4k_res": ([(4096, 4096)], 8, 16, 8, "f16"),
     "mlp8b": ([(14336, 4096), (4096, 14336)], 6, 12, 12, "f16"),
     "l70b": ([(28672, 8192), (8192, 28672)], 8, 16, 8, "bf16"),
+    "aqlm4k": ([(4096, 4096)], 8, 16, 16, "f16"),
+    "v16_4k": ([(4096, 4096)], 16, 16, 8, "f16"),
 }
 DESCRIBE = {
     "tiny": "256x256 v8 K1=256 (1 bit/weight)",
@@ -51,6 +53,8 @@ DESCRIBE = {
     "dec4k_res": "4096x4096 v8 K1=65536+K2=256 (3 bits/weight)",
     "mlp8b": "MLP pair 14336x4096 + 4096x14336 v6 K1=K2=4096 (4 bits/weight)",
     "l70b": "70B-class pair 28672x8192 + 8192x28672 v8 K1=65536+K2=256 (3 bits/weight)",
+    "aqlm4k": "4096x4096 v8 two additive books K1=K2=65536 (4 bits/weight)",
+    "v16_4k": "4096x4096 v16 K1=65536+K2=256 (1.5 bits/weight)",
 }
 SVQ_WORKLOADS = {
     # affine-lattice layers: one 8-bit field of four 2-bit codes per 4-vector (2 bits/weight)

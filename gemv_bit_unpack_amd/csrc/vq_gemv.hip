@@ -45,34 +45,54 @@ __device__ __forceinline__ uint32_t load_index(const uint32_t* __restrict__ row,
   }
 }
 
-// Raw centroid (fp16 bits, zero padded to 8 halves).  v = 6 and v = 8.
+// A raw centroid: fp16 bits in 16-byte words, zero padded (v = 6 and 8: one word; v = 16:
+// two, read with two 16-byte loads of the same cache line, which the memory pipeline
+// serves as one request).
 template <int V>
-__device__ __forceinline__ uint4 gather_global(const uint16_t* __restrict__ cb, uint32_t k) {
-  if constexpr (V == 8) {
-    return *(const uint4*)(cb + (size_t)k * 8);
+struct Cent {
+  static constexpr int kWords = V > 8 ? 2 : 1;
+  uint4 q[kWords];
+};
+
+template <int V>
+__device__ __forceinline__ Cent<V> gather_global(const uint16_t* __restrict__ cb, uint32_t k) {
+  Cent<V> c;
+  if constexpr (V == 16) {
+    c.q[0] = *(const uint4*)(cb + (size_t)k * 16);
+    c.q[1] = *(const uint4*)(cb + (size_t)k * 16 + 8);
+  } else if constexpr (V == 8) {
+    c.q[0] = *(const uint4*)(cb + (size_t)k * 8);
   } else {
-    static_assert(V == 6, "fast path covers v = 6 and v = 8");
+    static_assert(V == 6, "fast path covers v = 6, 8 and 16");
     const uint32_t* p = (const uint32_t*)(cb + (size_t)k * 6);
-    return make_uint4(p[0], p[1], p[2], 0u);
+    c.q[0] = make_uint4(p[0], p[1], p[2], 0u);
   }
+  return c;
 }
 
-__device__ __forceinline__ float half_at(const uint4& q, int t) {
-  const uint32_t w = t < 2 ? q.x : t < 4 ? q.y : t < 6 ? q.z : q.w;
-  return vqd::f16_to_f32((t & 1) ? (w >> 16) : w);
+template <int V>
+__device__ __forceinline__ float half_at(const Cent<V>& c, int t) {
+  const uint4& q = c.q[t / 8];
+  const int tt = t % 8;
+  const uint32_t w = tt < 2 ? q.x : tt < 4 ? q.y : tt < 6 ? q.z : q.w;
+  return vqd::f16_to_f32((tt & 1) ? (w >> 16) : w);
 }
 
 // x[m][col0 .. col0 + V) as fp32, branch-free.  The fast path guarantees IN % 8 == 0 for
-// v = 8 (so a vector is either whole or past the row: such lanes read a clamped vector
-// and are zeroed by the caller) and IN even for v = 6 (each x pair is either inside the
-// row or dropped, so the last, partial vector keeps exactly its valid lanes).
+// v = 8 and 16 (so each group of 8 columns is either whole or past the row: such groups
+// read a clamped group and the caller zeroes their weights) and IN even for v = 6 (each x
+// pair is either inside the row or dropped, so the last, partial vector keeps exactly its
+// valid lanes).
 template <int V, int XT>
 __device__ __forceinline__ void load_x(const uint16_t* __restrict__ xrow, int32_t col0, int32_t in_features,
                                        float (&xv)[V]) {
-  uint32_t w[4];
-  if constexpr (V == 8) {
-    const uint4 q = *(const uint4*)(xrow + min(col0, in_features - 8));
-    w[0] = q.x; w[1] = q.y; w[2] = q.z; w[3] = q.w;
+  uint32_t w[V / 2];
+  if constexpr (V == 8 || V == 16) {
+#pragma unroll
+    for (int h = 0; h < V / 8; ++h) {
+      const uint4 q = *(const uint4*)(xrow + min(col0 + 8 * h, in_features - 8));
+      w[4 * h] = q.x; w[4 * h + 1] = q.y; w[4 * h + 2] = q.z; w[4 * h + 3] = q.w;
+    }
   } else {
     const uint32_t* p = (const uint32_t*)xrow;
     const int32_t last_pair = in_features / 2 - 1;
@@ -96,15 +116,16 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Stage books into LDS as 16-byte entries.  Each thread first loads all of its entries
-// (up to kStageBatch per pass), then writes them, so the loads overlap.
+// Stage books into LDS as entries of Cent<V>::kWords 16-byte words.  Each thread first
+// loads all of its entries (up to kStageBatch per pass), then writes them, so the loads
+// overlap.
 constexpr int kStageBatch = 8;
 template <int V>
-__device__ __forceinline__ void stage_books(uint4* lds, const uint16_t* cb1, int k1, const uint16_t* cb2, int k2,
+__device__ __forceinline__ void stage_books(Cent<V>* lds, const uint16_t* cb1, int k1, const uint16_t* cb2, int k2,
                                             int block) {
   const int total = k1 + k2;
   for (int base = 0; base < total; base += kStageBatch * block) {
-    uint4 q[kStageBatch];
+    Cent<V> q[kStageBatch];
 #pragma unroll
     for (int b = 0; b < kStageBatch; ++b) {
       const int e = min(base + b * block + (int)threadIdx.x, total - 1);
@@ -138,17 +159,21 @@ __device__ __forceinline__ void warm_book(const uint16_t* __restrict__ cb, uint3
 }
 
 // IB1 = 16: 16-bit main indices into a global book (K1 = 65536); IB1 = 0: main book in
-// LDS (K1 <= 4096), any index width.  RES: residual book in LDS (K2 <= 4096).
-template <int V, int MT, int XT, int IB1, bool RES, int U>
+// LDS (K1 <= 4096), any index width.  RK: the second book -- 0 none, 1 in LDS
+// (K2 <= 4096), 2 a global book with 16-bit indices (K2 = 65536: two large additive
+// books, as in the production-VQ post's AQLM 2 x 2^16 configuration).
+template <int V, int MT, int XT, int IB1, int RK, int U>
 __global__ __launch_bounds__(1024) void gemv_kernel(ProductArgs a, int block, int grid) {
   constexpr bool kLds1 = IB1 != 16;
-  extern __shared__ uint4 lds_books[];
+  extern __shared__ uint4 lds_words[];
+  Cent<V>* lds_books = (Cent<V>*)lds_words;
   const int k1 = kLds1 ? (1 << a.bits1) : 0;
-  const int k2 = RES ? (1 << a.bits2) : 0;
-  const uint4* book1 = lds_books;
-  const uint4* book2 = lds_books + k1;
-  uint32_t warm[2] = {0u, 0u};
+  const int k2 = RK == 1 ? (1 << a.bits2) : 0;
+  const Cent<V>* book1 = lds_books;
+  const Cent<V>* book2 = lds_books + k1;
+  uint32_t warm[2] = {0u, 0u}, warm2[2] = {0u, 0u};
   if constexpr (!kLds1) warm_book(a.cb1, (uint32_t)(V * 2) << a.bits1, (uint32_t)block, (uint32_t)grid, warm);
+  if constexpr (RK == 2) warm_book(a.cb2, (uint32_t)(V * 2) << a.bits2, (uint32_t)block, (uint32_t)grid, warm2);
   if (k1 + k2 > 0) {
     stage_books<V>(lds_books, a.cb1, k1, a.cb2, k2, block);
     __syncthreads();
@@ -167,12 +192,13 @@ __global__ __launch_bounds__(1024) void gemv_kernel(ProductArgs a, int block, in
     uint32_t i1[U], i2[U];
     auto fetch_idx = [&](int r, int gg, uint32_t(&o1)[U], uint32_t(&o2)[U]) {
       const uint32_t* r1 = a.packed1 + (size_t)r * a.s1_words;
-      const uint32_t* r2 = RES ? a.packed2 + (size_t)r * a.s2_words : nullptr;
+      const uint32_t* r2 = RK ? a.packed2 + (size_t)r * a.s2_words : nullptr;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const uint32_t j = min((uint32_t)(gg * kGroup + u * vqd::kWave + lane), last_j);
         o1[u] = load_index<IB1>(r1, a.s1_words, j, a.bits1);
-        if constexpr (RES) o2[u] = load_index<0>(r2, a.s2_words, j, a.bits2);
+        if constexpr (RK == 1) o2[u] = load_index<0>(r2, a.s2_words, j, a.bits2);
+        if constexpr (RK == 2) o2[u] = load_index<16>(r2, a.s2_words, j, a.bits2);
       }
     };
     fetch_idx(row, g, i1, i2);
@@ -181,7 +207,7 @@ __global__ __launch_bounds__(1024) void gemv_kernel(ProductArgs a, int block, in
     for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
     while (true) {
       // gathers of the current group
-      uint4 c1[U], c2[U];
+      Cent<V> c1[U], c2[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         if constexpr (kLds1) {
@@ -189,7 +215,8 @@ __global__ __launch_bounds__(1024) void gemv_kernel(ProductArgs a, int block, in
         } else {
           c1[u] = gather_global<V>(a.cb1, i1[u]);
         }
-        if constexpr (RES) c2[u] = book2[i2[u]];
+        if constexpr (RK == 1) c2[u] = book2[i2[u]];
+        if constexpr (RK == 2) c2[u] = gather_global<V>(a.cb2, i2[u]);
       }
       // index loads of the next group (or a harmless repeat of this row's last group),
       // in flight while the gathers return
@@ -205,14 +232,16 @@ __global__ __launch_bounds__(1024) void gemv_kernel(ProductArgs a, int block, in
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int j = g * kGroup + u * vqd::kWave + lane;
+        const int32_t col0 = j * V;
         float w[V];
 #pragma unroll
         for (int t = 0; t < V; ++t) {
-          w[t] = half_at(c1[u], t);
-          if constexpr (RES) w[t] = w[t] + half_at(c2[u], t);
-          if constexpr (V == 8) w[t] = j < a.nv ? w[t] : 0.0f;
+          w[t] = half_at<V>(c1[u], t);
+          if constexpr (RK != 0) w[t] = w[t] + half_at<V>(c2[u], t);
+          // v = 8, 16: columns past the row (whole groups of 8, IN % 8 == 0) weigh zero;
+          // v = 6 zeroes them through x instead
+          if constexpr (V != 6) w[t] = col0 + t < a.in_features ? w[t] : 0.0f;
         }
-        const int32_t col0 = j * V;
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           if (m < m_count) {
@@ -245,11 +274,12 @@ __global__ __launch_bounds__(1024) void gemv_kernel(ProductArgs a, int block, in
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         i1[u] = n1[u];
-        if constexpr (RES) i2[u] = n2[u];
+        if constexpr (RK != 0) i2[u] = n2[u];
       }
     }
   }
-  if (a.n < 0 && (warm[0] ^ warm[1]) == 0x9E3779B9u) ((uint32_t*)a.y)[0] = warm[0];  // never true: keeps the loads
+  if (a.n < 0 && (warm[0] ^ warm[1] ^ warm2[0] ^ warm2[1]) == 0x9E3779B9u)  // never true: keeps the loads
+    ((uint32_t*)a.y)[0] = warm[0];
 }
 
 // Generic path: any v in 1..16, centroids and x read element by element from global
@@ -307,19 +337,24 @@ constexpr int kNumCU = 256;
 #define VQ_GEMV_U1 8  // vectors in flight per lane for M <= 2
 #endif
 
-template <int V, int MT, int XT, int IB1, bool RES>
+template <int V, int MT, int XT, int IB1, int RK>
 vq_status launch_fast(const ProductArgs& a, hipStream_t s) {
-  constexpr int U = MT <= 2 ? VQ_GEMV_U1 : (MT <= 8 ? 4 : 2);
+  // vectors in flight per lane: fewer for wide centroids and large batches (registers)
+  constexpr int U0 = MT <= 2 ? VQ_GEMV_U1 : (MT <= 8 ? 4 : 2);
+  constexpr int U = V > 8 ? (U0 > 4 ? 4 : (U0 > 1 ? U0 / 2 : 1)) : U0;
   constexpr bool kLds1 = IB1 != 16;
-  const size_t lds_bytes = 16u * ((kLds1 ? (1u << a.bits1) : 0u) + (RES ? (1u << a.bits2) : 0u));
-  auto kern = gemv_kernel<V, MT, XT, IB1, RES, U>;
+  const size_t lds_bytes =
+      16u * Cent<V>::kWords * ((kLds1 ? (1u << a.bits1) : 0u) + (RK == 1 ? (1u << a.bits2) : 0u));
+  auto kern = gemv_kernel<V, MT, XT, IB1, RK, U>;
   static std::once_flag once;
   static hipError_t attr_err = hipSuccess;
   std::call_once(once, [&] {
     attr_err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   });
   if (attr_err != hipSuccess) return VQ_ERR_HIP;
-  // Big LDS footprint: one 1024-thread workgroup per CU; otherwise smaller groups.
+  // Big LDS footprint: one 1024-thread workgroup per CU; otherwise smaller groups.  (The
+  // 128-register budget of the 1024-thread bound costs a few bytes of spill in the
+  // residual-book instances for M <= 2; measured, the occupancy it keeps is worth more.)
   const bool big = lds_bytes > 32 * 1024;
   const int block = big ? 1024 : VQ_GEMV_SMALL_BLOCK;
   const int per_cu = big ? 1 : VQ_GEMV_SMALL_PER_CU;
@@ -331,22 +366,32 @@ vq_status launch_fast(const ProductArgs& a, hipStream_t s) {
   return hipGetLastError() == hipSuccess ? VQ_OK : VQ_ERR_HIP;
 }
 
-template <int V, int XT, int IB1, bool RES>
+template <int V, int XT, int IB1, int RK>
 vq_status dispatch_m(const ProductArgs& a, hipStream_t s) {
-  if (a.m <= 1) return launch_fast<V, 1, XT, IB1, RES>(a, s);
-  if (a.m <= 2) return launch_fast<V, 2, XT, IB1, RES>(a, s);
-  if (a.m <= 4) return launch_fast<V, 4, XT, IB1, RES>(a, s);
-  if (a.m <= 8) return launch_fast<V, 8, XT, IB1, RES>(a, s);
-  return launch_fast<V, 16, XT, IB1, RES>(a, s);
+  if (a.m <= 1) return launch_fast<V, 1, XT, IB1, RK>(a, s);
+  if (a.m <= 2) return launch_fast<V, 2, XT, IB1, RK>(a, s);
+  if (a.m <= 4) return launch_fast<V, 4, XT, IB1, RK>(a, s);
+  if (a.m <= 8) return launch_fast<V, 8, XT, IB1, RK>(a, s);
+  return launch_fast<V, 16, XT, IB1, RK>(a, s);
 }
 
+// Book placements with a fast kernel (checked by launch_gemv): main book global (16-bit)
+// or in LDS; second book none, in LDS, or global with 16-bit indices when the main book is
+// global too.  v = 16 only with the global 65536-entry main book.
 template <int V, int XT>
 vq_status dispatch_books(const ProductArgs& a, hipStream_t s) {
   const bool main16 = a.bits1 == 16;
-  if (a.bits2) {
-    return main16 ? dispatch_m<V, XT, 16, true>(a, s) : dispatch_m<V, XT, 0, true>(a, s);
+  if constexpr (V == 6) {
+    if (a.bits2) return main16 ? dispatch_m<V, XT, 16, 1>(a, s) : dispatch_m<V, XT, 0, 1>(a, s);
+    return main16 ? dispatch_m<V, XT, 16, 0>(a, s) : dispatch_m<V, XT, 0, 0>(a, s);
+  } else if constexpr (V == 16) {
+    if (a.bits2 == 16) return dispatch_m<V, XT, 16, 2>(a, s);
+    return a.bits2 ? dispatch_m<V, XT, 16, 1>(a, s) : dispatch_m<V, XT, 16, 0>(a, s);
+  } else {
+    if (a.bits2 == 16) return dispatch_m<V, XT, 16, 2>(a, s);
+    if (a.bits2) return main16 ? dispatch_m<V, XT, 16, 1>(a, s) : dispatch_m<V, XT, 0, 1>(a, s);
+    return main16 ? dispatch_m<V, XT, 16, 0>(a, s) : dispatch_m<V, XT, 0, 0>(a, s);
   }
-  return main16 ? dispatch_m<V, XT, 16, false>(a, s) : dispatch_m<V, XT, 0, false>(a, s);
 }
 
 template <int V>
@@ -360,15 +405,23 @@ namespace vqi {
 
 vq_status launch_gemv(const ProductArgs& a, void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  // The fast path: v in {6, 8}; the main book either has 16-bit indices (global) or at
-  // most 4096 entries (LDS); the residual book, if any, at most 4096 entries (LDS);
-  // vector-aligned codebooks and x rows, IN a multiple of 8 (v = 8) or even (v = 6).
-  const size_t align = (a.v == 8) ? 16 : 4;
-  const bool fast_shape = (a.v == 8 || a.v == 6) && (a.bits1 == 16 || a.bits1 <= 12) && a.bits2 <= 12 &&
-                          a.in_features >= 8;
+  // The fast path: v in {6, 8, 16}; the main book either has 16-bit indices (global) or
+  // at most 4096 entries (LDS, not for v = 16); the second book none, at most 4096 entries
+  // (LDS), or 65536 entries (global) beside a global main book (v = 8, 16); both LDS
+  // books within 160 KiB; vector-aligned codebooks and x rows, IN a multiple of 8
+  // (v = 8, 16) or even (v = 6).
+  const size_t align = (a.v == 6) ? 4 : 16;
+  const bool v_ok = a.v == 6 || a.v == 8 || a.v == 16;
+  const bool b1_ok = a.bits1 == 16 || (a.bits1 <= 12 && a.v != 16);
+  const bool b2_ok = a.bits2 <= 12 || (a.bits2 == 16 && a.bits1 == 16 && a.v != 6);
+  const size_t words = a.v > 8 ? 2 : 1;  // 16-byte LDS words per centroid
+  const size_t lds_need = 16u * words * ((a.bits1 <= 12 ? (1u << a.bits1) : 0u) +
+                                         (a.bits2 >= 1 && a.bits2 <= 12 ? (1u << a.bits2) : 0u));
+  const bool fast_shape = v_ok && b1_ok && b2_ok && lds_need <= 160u * 1024u && a.in_features >= 8;
   const bool fast_align = aligned(a.cb1, align) && (!a.cb2 || aligned(a.cb2, align)) && aligned(a.x, align) &&
                           (((size_t)a.in_features * 2) % align == 0);
   if (fast_shape && fast_align) {
+    if (a.v == 16) return dispatch_x<16>(a, s);
     return a.v == 8 ? dispatch_x<8>(a, s) : dispatch_x<6>(a, s);
   }
   const int block = 256;

@@ -12,6 +12,8 @@ dimensions, so the sizes are the usual LLaMA-3 ones):
   dec4k_res  4096 x 4096,          v=8, K1=65536 + K2=256      (3 bits),       M in {1,4,16}, fp16
   mlp8b      up 14336x4096 / down 4096x14336, v=6, K1=K2=4096  (4 bits),       M in {1,4,16}, fp16
   l70b       up 28672x8192 / down 8192x28672, v=8, K1=65536 + K2=256 (3 bits), M in {1,8,32,128,256}, bf16
+  aqlm4k     4096 x 4096,          v=8, K1=K2=65536 (two additive books, 4 bits), M in {1,4,16}, x fp16
+  v16_4k     4096 x 4096,          v=16, K1=65536 + K2=256     (1.5 bits),     M in {1,4},    x fp16
 
 Distributions: main centroids 0.02*N(0,1) (the weight scale of the VPTQ guide's
 verification harness), residual centroids 0.005*N(0,1), both rounded to fp16;
@@ -53,6 +55,11 @@ WORKLOADS = {
                       labels=("up", "down")),
     "l70b": Workload("l70b", 4, ((28672, 8192), (8192, 28672)), 8, 16, 8, (1, 8, 32, 128, 256), "bf16",
                      labels=("up", "down")),
+    # two large additive books (the production-VQ post's AQLM 2 x 2^16, d = 8: 4 bits/weight)
+    "aqlm4k": Workload("aqlm4k", 7, ((4096, 4096),), 8, 16, 16, (1, 4, 16), "f16", sigma1=0.014, sigma2=0.014),
+    # v = 16 with a 65536-entry main book and a 256-entry residual (the VPTQ guide's
+    # 1.0-1.5 bits range: 1.5 bits/weight)
+    "v16_4k": Workload("v16_4k", 8, ((4096, 4096),), 16, 16, 8, (1, 4), "f16"),
 }
 
 

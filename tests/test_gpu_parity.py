@@ -132,7 +132,13 @@ def test_gemv_parity_workloads(vq, key, layer, m):
     (129, 1024, 8, 16, 8, 2, "bf16", True, False),
     (1, 8, 8, 16, 0, 1, "f16", True, True),
     (300, 4096, 8, 12, 4, 7, "f16", False, True),   # 12-bit main book staged in LDS
-    (17, 256, 16, 16, 16, 4, "bf16", True, True),
+    (17, 256, 16, 16, 16, 4, "bf16", True, True),   # v = 16, two 65536-entry books
+    (100, 4104, 16, 16, 0, 1, "f16", True, True),   # v = 16: last vector keeps 8 lanes
+    (70, 1032, 16, 16, 8, 3, "bf16", True, False),  # v = 16 with a residual in LDS
+    (9, 200, 16, 16, 16, 16, "f16", False, True),   # v = 16, two global books, M = 16
+    (65, 512, 8, 16, 16, 2, "f16", False, True),    # two global books (AQLM 2 x 2^16)
+    (33, 1000, 8, 16, 16, 16, "bf16", True, True),
+    (5, 104, 16, 12, 0, 2, "f16", True, False),     # v = 16 with an LDS main book: generic path
 ])
 def test_gemv_parity_shapes(vq, n, i, v, b1, b2, m, xd, bias, scale):
     lay = synth.make_layer(n, i, v, b1, b2, wid=71, copy=n, with_scale=scale, with_bias=bias)
@@ -145,7 +151,8 @@ def test_gemv_parity_shapes(vq, n, i, v, b1, b2, m, xd, bias, scale):
 
 
 @pytest.mark.parametrize("n,i,v,b1,b2", [(64, 512, 8, 16, 8), (48, 96, 6, 12, 12), (32, 256, 8, 8, 0),
-                                         (40, 4096, 8, 16, 8)])
+                                         (40, 4096, 8, 16, 8), (40, 1032, 16, 16, 8), (32, 512, 8, 16, 16),
+                                         (24, 264, 16, 16, 16)])
 def test_gemv_one_hot_columns_bit_exact(vq, n, i, v, b1, b2):
     """x = e_col gives y[o] = s_o * (c1 + c2)[col], the exact fp32 W^ entry."""
     lay = synth.make_layer(n, i, v, b1, b2, wid=72, copy=i)

@@ -85,6 +85,10 @@ def _load():
         lib.oracle_svq_dequant_rows.restype = i32
         lib.oracle_svq_forward_rows.argtypes = [i64, i64, vp, vp, vp, vp, vp, vp, i32, i64, vp, i64, vp, i32]
         lib.oracle_svq_forward_rows.restype = i32
+        lib.oracle_rht_block.argtypes = [i64]
+        lib.oracle_rht_block.restype = i64
+        lib.oracle_rht.argtypes = [i64, i64, vp, vp, i32, vp]
+        lib.oracle_rht.restype = i32
         _lib = lib
         return lib
 
@@ -250,4 +254,24 @@ def svq_forward(n, in_features, packed, a, b, scale, bias, x_bits, x_is_bf16, M,
                                            _ptr(_u16(scale)), _ptr(_u16(bias)), _ptr(xb), int(bool(x_is_bf16)), M,
                                            _ptr(r), nrows, _ptr(y), nthreads),
            "oracle_svq_forward_rows")
+    return y
+
+
+# ------------------------------------------------------------------ randomized Hadamard transform
+
+def rht_block(n: int) -> int:
+    """Block size of the transform: the largest power of two dividing n, at most 16384."""
+    return int(_load().oracle_rht_block(n))
+
+
+def rht(x, signs, transpose=False):
+    """Randomized Walsh-Hadamard transform of the rows of x (any float array [M, n]),
+    computed in fp64 as the matrix product.  signs: uint8 bit array (bit j set: s_j = -1)."""
+    xd = np.ascontiguousarray(np.atleast_2d(np.asarray(x, dtype=np.float64)))
+    m, n = xd.shape
+    sg = np.ascontiguousarray(signs, dtype=np.uint8)
+    if sg.size * 8 < n:
+        raise OracleError("sign bits too short")
+    y = np.zeros_like(xd)
+    _check(_load().oracle_rht(m, n, _ptr(xd), _ptr(sg), int(bool(transpose)), _ptr(y)), "oracle_rht")
     return y

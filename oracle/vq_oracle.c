@@ -481,3 +481,54 @@ int oracle_svq_forward_rows(int64_t n, int64_t in_features, const uint8_t* packe
   free(xd);
   return rc;
 }
+
+/* ---------------------------------------------------------------- randomized Hadamard transform */
+
+/* Block of the transform: the largest power of two that divides n, at most 16384. */
+int64_t oracle_rht_block(int64_t n) {
+  if (n <= 0) return 0;
+  int64_t b = 1;
+  while (b < 16384 && n % (2 * b) == 0) b *= 2;
+  return b;
+}
+
+static int popcount64(uint64_t v) {
+  int c = 0;
+  while (v) {
+    v &= v - 1;
+    ++c;
+  }
+  return c;
+}
+
+/* Randomized Walsh-Hadamard transform of each row of x (production-VQ post, QuIP#: random
+ * orthogonal Hadamard transforms with random signs on the layer's inputs; sub-4-bit
+ * lecture, "QuIP#: Incoherence Processing": Hadamard + random signs; UniSVQ summary,
+ * "Preprocessing (Randomized Hadamard Transform - RHT)").  With b = oracle_rht_block(n),
+ * each block of b columns is transformed on its own (the transform is I kron H_b / sqrt(b)
+ * with random signs): forward y = H_b (s . x) / sqrt(b), transpose y = s . (H_b x) / sqrt(b),
+ * where H_b[i][j] = (-1)^popcount(i & j) and s_j = -1 when bit j (LSB-first within byte j/8)
+ * of signs is set.  Written out as the matrix product, O(b) per output. */
+int oracle_rht(int64_t M, int64_t n, const double* x, const uint8_t* signs, int transpose, double* y) {
+  if (M < 0 || n < 0 || (M * n > 0 && (!x || !signs || !y))) return ORACLE_BAD_ARGS;
+  const int64_t b = oracle_rht_block(n);
+  const double inv = b > 0 ? 1.0 / sqrt((double)b) : 0.0;
+  for (int64_t m = 0; m < M; ++m) {
+    const double* xr = x + m * n;
+    double* yr = y + m * n;
+    for (int64_t base = 0; base < n; base += b) {
+      for (int64_t i = 0; i < b; ++i) {
+        double acc = 0.0;
+        for (int64_t j = 0; j < b; ++j) {
+          double v = xr[base + j];
+          if (!transpose && ((signs[(base + j) >> 3] >> ((base + j) & 7)) & 1)) v = -v;
+          acc += (popcount64((uint64_t)(i & j)) & 1) ? -v : v;
+        }
+        acc *= inv;
+        if (transpose && ((signs[(base + i) >> 3] >> ((base + i) & 7)) & 1)) acc = -acc;
+        yr[base + i] = acc;
+      }
+    }
+  }
+  return ORACLE_OK;
+}

@@ -18,6 +18,8 @@
  *     accumulated in fp64 in ascending column order.
  *   - affine-lattice decode (UniSVQ summary): W's vectors are A q + B over 2-bit integer
  *     codes instead of codebook entries; the same product follows.
+ *   - the randomized Hadamard transform of the activations (QuIP# incoherence processing):
+ *     the definition as a matrix product.
  */
 #ifndef VQ_ORACLE_H
 #define VQ_ORACLE_H
@@ -89,6 +91,15 @@ int oracle_svq_dequant_rows(int64_t n, int64_t in_features, const uint8_t* packe
 int oracle_svq_forward_rows(int64_t n, int64_t in_features, const uint8_t* packed, const uint16_t* a,
                             const uint16_t* b, const uint16_t* scale, const uint16_t* bias, const uint16_t* x,
                             int x_is_bf16, int64_t M, const int64_t* rows, int64_t nrows, double* y, int nthreads);
+
+/*
+ * Randomized Walsh-Hadamard transform of the rows of x [M][n] (fp64 in and out): blocks of
+ * b = oracle_rht_block(n) columns (the largest power of two dividing n, at most 16384);
+ * forward y = H_b (s . x) / sqrt(b), transpose (its inverse) y = s . (H_b x) / sqrt(b), with
+ * H_b[i][j] = (-1)^popcount(i & j) and s_j = -1 where bit j of signs (LSB-first) is set.
+ */
+int64_t oracle_rht_block(int64_t n);
+int oracle_rht(int64_t M, int64_t n, const double* x, const uint8_t* signs, int transpose, double* y);
 
 #ifdef __cplusplus
 }

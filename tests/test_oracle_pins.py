@@ -550,3 +550,64 @@ def test_svq_sizes_from_the_pages(oracle_mod):
     assert a_bits.nbytes + b_bits.nbytes == 40
     for n, in_features in [(4096, 4096), (28672, 8192), (8192, 28672)]:
         assert oracle_mod.packed_bytes(n, in_features, 4, 8, 0) * 8 == 2 * n * in_features
+
+
+# ------------------------------------------------------------------ randomized Hadamard transform
+#
+# QuIP# incoherence processing (production-VQ post; sub-4-bit lecture, "QuIP#: Incoherence
+# Processing"; UniSVQ summary, "Preprocessing"): random signs, then a Walsh-Hadamard
+# matrix, orthonormal, O(n log n).  Readings: blocks of the largest power of two dividing
+# n (at most 16384), s applied before H (forward) or after it (transpose, the inverse).
+
+
+@pytest.mark.parametrize("n,b", [(4096, 4096), (14336, 2048), (28672, 4096), (8192, 8192), (16384, 16384),
+                                 (32768, 16384), (4100, 4), (7, 1), (1, 1), (96, 32)])
+def test_rht_block_rule(oracle_mod, n, b):
+    assert oracle_mod.rht_block(n) == b
+
+
+def test_rht_two_point_closed_form(oracle_mod):
+    a, c = 3.0, 1.0
+    r2 = math.sqrt(2.0)
+    no_sign, sign1 = np.array([0], np.uint8), np.array([2], np.uint8)
+    assert np.allclose(oracle_mod.rht([[a, c]], no_sign), [[(a + c) / r2, (a - c) / r2]], rtol=0, atol=1e-15)
+    assert np.allclose(oracle_mod.rht([[a, c]], sign1), [[(a - c) / r2, (a + c) / r2]], rtol=0, atol=1e-15)
+    assert np.allclose(oracle_mod.rht([[a, c]], sign1, transpose=True), [[(a + c) / r2, -(a - c) / r2]], rtol=0,
+                       atol=1e-15)
+
+
+@pytest.mark.parametrize("n", [16, 256, 1024, 96])
+def test_rht_matches_sylvester_matrix(oracle_mod, n):
+    """Against scipy's Sylvester-construction Hadamard matrix, block by block."""
+    import scipy.linalg
+
+    g = np.random.default_rng(n)
+    m = 3
+    x = g.standard_normal((m, n))
+    signs = g.integers(0, 256, size=(n + 7) // 8, dtype=np.uint8)
+    s = np.where(np.unpackbits(signs, bitorder="little")[:n] == 1, -1.0, 1.0)
+    b = oracle_mod.rht_block(n)
+    h = scipy.linalg.hadamard(b).astype(np.float64) / math.sqrt(b)
+    want = np.concatenate([(x[:, k:k + b] * s[k:k + b]) @ h.T for k in range(0, n, b)], axis=1)
+    assert np.allclose(oracle_mod.rht(x, signs), want, rtol=0, atol=1e-12)
+    want_t = np.concatenate([(x[:, k:k + b] @ h.T) * s[k:k + b] for k in range(0, n, b)], axis=1)
+    assert np.allclose(oracle_mod.rht(x, signs, transpose=True), want_t, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("n", [64, 1000, 4096])
+def test_rht_orthonormal_and_inverse(oracle_mod, n):
+    g = np.random.default_rng(n + 1)
+    x = g.standard_normal((2, n))
+    signs = g.integers(0, 256, size=(n + 7) // 8, dtype=np.uint8)
+    y = oracle_mod.rht(x, signs)
+    assert np.allclose((y * y).sum(axis=1), (x * x).sum(axis=1), rtol=1e-12, atol=0)  # Parseval
+    assert np.allclose(oracle_mod.rht(y, signs, transpose=True), x, rtol=0, atol=1e-12)  # inverse
+
+
+def test_rht_blocks_are_independent(oracle_mod):
+    n = 12  # b = 4: three blocks
+    x = np.zeros((1, n))
+    x[0, 5] = 1.0  # one-hot in block 1
+    y = oracle_mod.rht(x, np.zeros(2, np.uint8))
+    assert np.all(y[0, :4] == 0) and np.all(y[0, 8:] == 0)
+    assert np.allclose(np.abs(y[0, 4:8]), 0.5, rtol=0, atol=1e-15)  # a column of H_4 / 2

@@ -41,7 +41,7 @@ VQ_F16, VQ_BF16, VQ_F32 = 0, 1, 2
 LAYOUT_ROWSTREAM = 1
 
 EXPORTED = ("vq_abi_version", "vq_status_string", "vq_packed_bytes", "vq_pack", "vq_dequant", "vq_gemv",
-            "vq_gemv_workspace_bytes", "vq_gemv_ws", "vq_gemm", "vq_svq_dequant", "vq_svq_gemv")
+            "vq_gemv_workspace_bytes", "vq_gemv_ws", "vq_gemm", "vq_svq_dequant", "vq_svq_gemv", "vq_rht", "vq_rht_block")
 
 
 class Desc(ctypes.Structure):
@@ -91,6 +91,10 @@ def _load():
     lib.vq_svq_dequant.restype = ctypes.c_int
     lib.vq_svq_gemv.argtypes = [dp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i32, vp, ctypes.c_int, vp]
     lib.vq_svq_gemv.restype = ctypes.c_int
+    lib.vq_rht.argtypes = [i32, i32, vp, ctypes.c_int, vp, i32, vp, ctypes.c_int, vp]
+    lib.vq_rht.restype = ctypes.c_int
+    lib.vq_rht_block.argtypes = [i32]
+    lib.vq_rht_block.restype = i32
     return lib
 
 
@@ -278,6 +282,30 @@ def svq_gemv(desc: Desc, packed, a, b, scale, bias, x, y_dtype=None, out=None):
                           _dev_ptr(x, "x", (torch.float16, torch.bfloat16)), _dtype_code(x.dtype), m,
                           _dev_ptr(out, "out"), _dtype_code(out.dtype), _stream_ptr(x.device))
     _check(st, "vq_svq_gemv")
+    return out
+
+
+def rht_block(n: int) -> int:
+    """Block size of vq_rht for rows of n columns."""
+    return int(lib().vq_rht_block(int(n)))
+
+
+def rht(x, signs, transpose=False, y_dtype=None, out=None):
+    """Randomized Hadamard transform of the rows of x [M, n] (device tensor); signs: uint8
+    device tensor of ceil(n / 8) bytes.  ``transpose=True`` applies the inverse."""
+    torch = _torch()
+    if x.dim() != 2:
+        raise ValueError("x must be [M, n]")
+    m, n = x.shape
+    if signs.dtype != torch.uint8 or signs.numel() * 8 < n:
+        raise ValueError("signs must be a uint8 tensor of at least ceil(n / 8) bytes")
+    y_dtype = y_dtype or x.dtype
+    if out is None:
+        out = torch.empty((m, n), dtype=y_dtype, device=x.device)
+    st = lib().vq_rht(m, n, _dev_ptr(x, "x", (torch.float16, torch.bfloat16, torch.float32)), _dtype_code(x.dtype),
+                      _dev_ptr(signs, "signs"), int(bool(transpose)), _dev_ptr(out, "out"), _dtype_code(out.dtype),
+                      _stream_ptr(x.device))
+    _check(st, "vq_rht")
     return out
 
 

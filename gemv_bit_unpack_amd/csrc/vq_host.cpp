@@ -271,6 +271,20 @@ vq_status vq_svq_gemv(const vq_desc* desc, const void* packed, const void* a, co
   return launch_svq_gemv(p, stream);
 }
 
+int32_t vq_rht_block(int32_t n) { return rht_block(n); }
+
+vq_status vq_rht(int32_t M, int32_t n, const void* x, vq_dtype x_dtype, const void* signs, int32_t transpose, void* y,
+                 vq_dtype y_dtype, void* stream) {
+  if (M < 0 || n < 0) return VQ_ERR_SHAPE;
+  if (!valid_out_dtype(x_dtype) || !valid_out_dtype(y_dtype)) return VQ_ERR_UNSUPPORTED;
+  if (transpose != 0 && transpose != 1) return VQ_ERR_UNSUPPORTED;
+  if (M == 0 || n == 0) return VQ_OK;
+  if (rht_block(n) < 16) return VQ_ERR_UNSUPPORTED;  // n must be a multiple of 16
+  if (!x || !signs || !y) return VQ_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(y, dtype_size(y_dtype))) return VQ_ERR_ALIGN;
+  return launch_rht(M, n, x, x_dtype, (const uint8_t*)signs, transpose, y, y_dtype, stream);
+}
+
 vq_status vq_gemm(const vq_desc* desc, const void* packed, const void* cb1, const void* cb2, const void* scale,
                   const void* bias, const void* x, vq_dtype x_dtype, int32_t M, void* y, vq_dtype y_dtype,
                   void* stream) {

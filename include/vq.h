@@ -186,6 +186,31 @@ vq_status vq_svq_gemv(const vq_desc* desc, const void* packed, const void* a, co
                       const void* bias, const void* x, vq_dtype x_dtype, int32_t M, void* y, vq_dtype y_dtype,
                       void* stream);
 
+/*
+ * Randomized Walsh-Hadamard transform of activations, the incoherence step that runs
+ * ahead of (and, transposed, after) a product with incoherence-processed weights
+ * (production-VQ post, llms.blog, QuIP#: randomized orthogonal Hadamard transforms on a
+ * layer's inputs and outputs; sub-4-bit lecture, "QuIP#: Incoherence Processing": Hadamard
+ * plus random signs at O(d log d); UniSVQ summary, "Preprocessing (Randomized Hadamard
+ * Transform - RHT)").  For each row of x [M][n] and each block of b = vq_rht_block(n)
+ * columns (the largest power of two dividing n, at most 16384):
+ *
+ *   transpose = 0:  y = H_b (s . x) / sqrt(b)
+ *   transpose = 1:  y = s . (H_b x) / sqrt(b)      (the inverse of transpose = 0)
+ *
+ * with H_b[i][j] = (-1)^popcount(i & j) (Sylvester order) and s_j = -1 where bit j of
+ * `signs` is set (bit j is bit j % 8 of byte j / 8).  Computed in fp32.
+ * x: device [M][n], VQ_F16, VQ_BF16 or VQ_F32, 16-byte aligned; signs: device, ceil(n / 8)
+ * bytes; y: device [M][n], VQ_F16, VQ_BF16 or VQ_F32, aligned to its element; y may be x
+ * itself when both have the same type.  n must be a multiple of 16 (VQ_ERR_UNSUPPORTED
+ * otherwise); M = 0 or n = 0: no-op.  Errors as for the other calls.
+ */
+vq_status vq_rht(int32_t M, int32_t n, const void* x, vq_dtype x_dtype, const void* signs, int32_t transpose, void* y,
+                 vq_dtype y_dtype, void* stream);
+
+/* The transform's block size for row length n (0 for n <= 0). */
+int32_t vq_rht_block(int32_t n);
+
 #ifdef __cplusplus
 }
 #endif

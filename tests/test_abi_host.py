@@ -272,3 +272,22 @@ def test_svq_pack_fields_match_oracle(vq):
     assert np.array_equal(fields, lay["codes"])
     ours = vq.pack(vq.svq_desc(5, 37), fields)
     assert np.array_equal(ours, oracle.pack(5, 37, 4, 8, 0, lay["codes"]))
+
+
+def test_rht_block_and_validation(vq):
+    for n in (16, 48, 96, 1000, 4096, 4100, 14336, 28672, 32768, 65536, 7, 0, -3):
+        assert vq.rht_block(n) == (oracle.rht_block(n) if n > 0 else 0), n
+    f = vq.lib().vq_rht
+    assert f(-1, 64, P, 0, P, 0, P, 2, None) == vq.VQ_ERR_SHAPE
+    assert f(1, -64, P, 0, P, 0, P, 2, None) == vq.VQ_ERR_SHAPE
+    assert f(1, 64, P, 7, P, 0, P, 2, None) == vq.VQ_ERR_UNSUPPORTED
+    assert f(1, 64, P, 0, P, 0, P, 9, None) == vq.VQ_ERR_UNSUPPORTED
+    assert f(1, 64, P, 0, P, 2, P, 2, None) == vq.VQ_ERR_UNSUPPORTED   # transpose is 0 or 1
+    assert f(1, 1000, P, 0, P, 0, P, 2, None) == vq.VQ_ERR_UNSUPPORTED  # block 8: n must be a multiple of 16
+    assert f(1, 64, None, 0, P, 0, P, 2, None) == vq.VQ_ERR_NULL
+    assert f(1, 64, P, 0, None, 0, P, 2, None) == vq.VQ_ERR_NULL
+    assert f(1, 64, P, 0, P, 0, None, 2, None) == vq.VQ_ERR_NULL
+    assert f(1, 64, ctypes.c_void_p(0x10008), 0, P, 0, P, 2, None) == vq.VQ_ERR_ALIGN
+    assert f(1, 64, P, 0, P, 0, P_MIS, 2, None) == vq.VQ_ERR_ALIGN
+    assert f(0, 64, None, 0, None, 0, None, 2, None) == vq.VQ_OK
+    assert f(3, 0, None, 0, None, 0, None, 2, None) == vq.VQ_OK

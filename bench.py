@@ -205,6 +205,45 @@ def svq_leg(vq, torch, use_graph, steps=None):
     return out
 
 
+class RhtRing:
+    """Distinct activation rows for vq_rht (fresh inputs per call, outputs in place of new buffers)."""
+
+    def __init__(self, vq, torch, m, n, dtype, copies=64):
+        dev = torch.device("cuda")
+        g = torch.Generator(device=dev)
+        g.manual_seed(zlib.crc32(("%d/rht/%d/%d" % (42, m, n)).encode()))
+        self.copies = copies
+        self.bytes_per_call = 2 * 2 * m * n + (n + 7) // 8
+        self.fn = vq.lib().vq_rht
+        code = vq.VQ_BF16 if dtype == torch.bfloat16 else vq.VQ_F16
+        self.signs = torch.randint(0, 256, ((n + 7) // 8,), generator=g, device=dev, dtype=torch.uint8)
+        self.tensors, self.items = [], []
+        for _ in range(copies):
+            x = torch.randn((m, n), generator=g, device=dev).to(dtype)
+            y = torch.empty_like(x)
+            self.tensors.append((x, y))
+            self.items.append((m, n, ctypes.c_void_p(x.data_ptr()), code, ctypes.c_void_p(self.signs.data_ptr()), 0,
+                               ctypes.c_void_p(y.data_ptr()), code))
+
+    def call(self, k, stream_ptr):
+        st = self.fn(*self.items[k % self.copies], stream_ptr)
+        if st != 0:
+            raise RuntimeError("vq_rht failed with status %d" % st)
+
+
+def rht_leg(vq, torch, use_graph):
+    """vq_rht at decode batches on the row lengths of the workloads."""
+    out = {}
+    for m, n in ((1, 4096), (1, 8192), (1, 14336), (1, 28672), (16, 4096)):
+        ring = RhtRing(vq, torch, m, n, torch.bfloat16 if n in (8192, 28672) else torch.float16)
+        sec, _, _, launch = time_ring(torch, [ring], 640, 20, use_graph)
+        out["m%d_n%d" % (m, n)] = {"us_per_call": round(sec * 1e6, 3), "block": vq.rht_block(n),
+                                   "GBps": round(ring.bytes_per_call / sec / 1e9, 1), "launch": launch}
+        del ring
+        torch.cuda.empty_cache()
+    return out
+
+
 def time_ring(torch, rings, steps, warmup, use_graph=True):
     """Average seconds per call over `steps` calls rotating through the ring(s)."""
     stream = torch.cuda.current_stream()
@@ -304,6 +343,7 @@ def main():
                     help="run only a plain 512 MiB device copy (known bytes) to scale rocprofv3 counters")
     ap.add_argument("--shared-book", action="store_true",
                     help="diagnostic: every ring copy shares one codebook (warm in L2), headline only")
+    ap.add_argument("--only-rht", action="store_true", help="run only the Hadamard-transform leg (for profiling)")
     ap.add_argument("--only-svq", action="store_true",
                     help="run only the affine-lattice (vq_svq_gemv) leg (for profiling)")
     ap.add_argument("--only-workload", default=None, choices=sorted(WORKLOADS),
@@ -346,6 +386,9 @@ def main():
         flops = (up.flops_per_call + down.flops_per_call) / 2
         print(json.dumps({"gemm_tflops": round(flops / gsec / 1e12, 2), "ms_per_call": round(gsec * 1e3, 4),
                           "calls": gcalls, "launch": glaunch}))
+        return
+    if args.only_rht:
+        print(json.dumps({"rht": rht_leg(vq, torch, use_graph)}))
         return
     if args.only_svq:
         print(json.dumps({"affine_lattice": svq_leg(vq, torch, use_graph, steps=args.steps)}))
@@ -454,6 +497,7 @@ def main():
             batch["%s_m%d" % (key, m)] = entry
         out["gemv_batched"] = batch
         out["affine_lattice"] = svq_leg(vq, torch, use_graph)
+        out["rht"] = rht_leg(vq, torch, use_graph)
         if not args.no_cpu_baseline:
             out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -89,6 +89,8 @@ def _load():
         lib.oracle_rht_block.restype = i64
         lib.oracle_rht.argtypes = [i64, i64, vp, vp, i32, vp]
         lib.oracle_rht.restype = i32
+        lib.oracle_rvq_assign.argtypes = [i64, i64, i32, i64, i64, vp, vp, vp, vp, vp]
+        lib.oracle_rvq_assign.restype = i32
         _lib = lib
         return lib
 
@@ -275,3 +277,23 @@ def rht(x, signs, transpose=False):
     y = np.zeros_like(xd)
     _check(_load().oracle_rht(m, n, _ptr(xd), _ptr(sg), int(bool(transpose)), _ptr(y)), "oracle_rht")
     return y
+
+
+# ------------------------------------------------------------------ residual VQ encode
+
+def rvq_assign(w, v, cb1, cb2=None):
+    """(idx1, idx2 or None) [n, in / v]: nearest main centroid, then nearest residual centroid of
+    the fp32 residual; ranking |c|^2 - 2 w.c in fp64, ties to the lowest index.  w: any float
+    array [n, in] whose values are fp32-representable (fp16 / bf16 / fp32 weights)."""
+    wd = np.ascontiguousarray(np.atleast_2d(np.asarray(w, dtype=np.float64)))
+    n, i = wd.shape
+    c1 = np.ascontiguousarray(_u16(cb1)).reshape(-1)
+    k1 = c1.size // v
+    c2 = None if cb2 is None else np.ascontiguousarray(_u16(cb2)).reshape(-1)
+    k2 = 0 if c2 is None else c2.size // v
+    nv = i // v if v > 0 else 0
+    idx1 = np.zeros((n, nv), dtype=np.uint32)
+    idx2 = np.zeros((n, nv), dtype=np.uint32) if k2 else None
+    _check(_load().oracle_rvq_assign(n, i, v, k1, k2, _ptr(wd), _ptr(c1), _ptr(c2), _ptr(idx1), _ptr(idx2)),
+           "oracle_rvq_assign")
+    return idx1, idx2

@@ -532,3 +532,59 @@ int oracle_rht(int64_t M, int64_t n, const double* x, const uint8_t* signs, int 
   }
   return ORACLE_OK;
 }
+
+/* ---------------------------------------------------------------- residual VQ encode */
+
+/* Squared-distance ranking of centroid c (v fp16 values) against vector w (v doubles), the
+ * quantity the assignment minimises: |c|^2 - 2 w.c (the constant |w|^2 dropped), in fp64,
+ * each sum an ascending chain of fused multiply-adds, then fma(-2, w.c, |c|^2). */
+static double rank_distance(const double* w, const uint16_t* c, int v) {
+  double nc = 0.0, dot = 0.0;
+  for (int t = 0; t < v; ++t) {
+    const double ct = oracle_f16_to_f64(c[t]);
+    nc = fma(ct, ct, nc);
+    dot = fma(w[t], ct, dot);
+  }
+  return fma(-2.0, dot, nc);
+}
+
+/* Nearest centroid: the lowest index among those with the smallest ranking distance. */
+static uint32_t nearest(const double* w, const uint16_t* cb, int64_t k, int v) {
+  uint32_t best = 0;
+  double bd = INFINITY;
+  for (int64_t i = 0; i < k; ++i) {
+    const double d = rank_distance(w, cb + i * v, v);
+    if (d < bd) {
+      bd = d;
+      best = (uint32_t)i;
+    }
+  }
+  return best;
+}
+
+/* Two-stage residual VQ encode (VPTQ guide, "Step 2: Multi-Stage Residual Vector Quantizer
+ * (RVQ)": each v-vector of W takes the nearest main centroid, the residual
+ * r = w - C1[idx1] (computed in fp32) takes the nearest residual centroid; the guide uses
+ * Euclidean distances and argmin, which keeps the first of equal distances).  Codebooks
+ * are given (the guide's random-sample initialisation and any k-means are outside this).
+ * w: [n][in] as doubles holding fp32 values; in % v == 0; cb1 fp16 [k1][v]; cb2 fp16
+ * [k2][v] or NULL when k2 == 0 (idx2 untouched). */
+int oracle_rvq_assign(int64_t n, int64_t in_features, int v, int64_t k1, int64_t k2, const double* w,
+                      const uint16_t* cb1, const uint16_t* cb2, uint32_t* idx1, uint32_t* idx2) {
+  if (n < 0 || in_features < 0 || v < 1 || v > 16 || k1 < 1 || k2 < 0 || in_features % v != 0) return ORACLE_BAD_ARGS;
+  if (n * in_features > 0 && (!w || !cb1 || !idx1 || (k2 > 0 && (!cb2 || !idx2)))) return ORACLE_BAD_ARGS;
+  const int64_t nv = in_features / v;
+  for (int64_t o = 0; o < n; ++o) {
+    for (int64_t j = 0; j < nv; ++j) {
+      const double* wv = w + o * in_features + j * v;
+      const uint32_t i1 = nearest(wv, cb1, k1, v);
+      idx1[o * nv + j] = i1;
+      if (k2 > 0) {
+        double r[16];
+        for (int t = 0; t < v; ++t) r[t] = (double)((float)wv[t] - (float)oracle_f16_to_f64(cb1[(int64_t)i1 * v + t]));
+        idx2[o * nv + j] = nearest(r, cb2, k2, v);
+      }
+    }
+  }
+  return ORACLE_OK;
+}

@@ -20,6 +20,8 @@
  *     codes instead of codebook entries; the same product follows.
  *   - the randomized Hadamard transform of the activations (QuIP# incoherence processing):
  *     the definition as a matrix product.
+ *   - the residual VQ encode (VPTQ guide, "Step 2"): nearest main centroid, then nearest
+ *     residual centroid of the fp32 residual, ties to the lowest index.
  */
 #ifndef VQ_ORACLE_H
 #define VQ_ORACLE_H
@@ -100,6 +102,15 @@ int oracle_svq_forward_rows(int64_t n, int64_t in_features, const uint8_t* packe
  */
 int64_t oracle_rht_block(int64_t n);
 int oracle_rht(int64_t M, int64_t n, const double* x, const uint8_t* signs, int transpose, double* y);
+
+/*
+ * Two-stage residual VQ encode with given codebooks: idx1 = nearest main centroid of each
+ * v-vector of w, idx2 = nearest residual centroid of r = fl32(w - C1[idx1]); "nearest" is the
+ * lowest index minimising |c|^2 - 2 w.c in fp64 (fma chains).  w: [n][in] doubles holding
+ * fp32 values, in % v == 0.
+ */
+int oracle_rvq_assign(int64_t n, int64_t in_features, int v, int64_t k1, int64_t k2, const double* w,
+                      const uint16_t* cb1, const uint16_t* cb2, uint32_t* idx1, uint32_t* idx2);
 
 #ifdef __cplusplus
 }

@@ -20,7 +20,13 @@ verification harness), residual centroids 0.005*N(0,1), both rounded to fp16;
 indices uniform on [0, 2^B); per-channel scale U(0.5, 1.5) in fp16; x ~ N(0,1) in
 fp16 or bf16 (round-to-nearest-even).  Seeds: numpy PCG64 seeded with
 [42, workload, layer, copy, tensor], tensor ids 0 c1, 1 c2, 2 idx1, 3 idx2, 4 scale,
-5 x, 6 bias.
+5 x, 6 bias, 7 lattice, 8 dense weights, 9 codebook sample positions.
+
+Encode inputs (make_encode_problem): dense W ~ 0.02*N(0,1) in fp16 (or bf16 / fp32); the
+main book holds fp16 copies of W's own v-vectors taken at distinct random positions, the
+way the VPTQ guide seeds its codebook for simulation (rows past the number of vectors are
+0.02*N(0,1)); the residual book is 0.005*N(0,1) in fp16 (the guide samples residuals,
+which would need the encoder's output here).
 """
 from __future__ import annotations
 
@@ -29,7 +35,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 SEED = 42
-T_C1, T_C2, T_IDX1, T_IDX2, T_SCALE, T_X, T_BIAS, T_LATTICE = range(8)
+T_C1, T_C2, T_IDX1, T_IDX2, T_SCALE, T_X, T_BIAS, T_LATTICE, T_W, T_PICK = range(10)
 
 
 @dataclass(frozen=True)
@@ -186,3 +192,31 @@ def svq_workload_x(key: str, layer: int, m: int) -> np.ndarray:
     w = SVQ_WORKLOADS[key]
     _, in_features = w.layers[layer]
     return activations(rng(w.wid, layer, 0, T_X), m, in_features, w.x_dtype)
+
+
+def make_encode_problem(n: int, in_features: int, v: int, bits1: int, bits2: int, *, wid: int = 96, layer: int = 0,
+                        w_dtype: str = "f16", sigma: float = 0.02, sigma2: float = 0.005) -> dict:
+    """Inputs of the residual VQ encode.  w: [n, in] fp16 / bf16 bits (uint16) or float32
+    values; w_f32: the same weights as float32; cb1 fp16 bits [2^bits1, v]; cb2 fp16 bits
+    [2^bits2, v] or None."""
+    a = rng(wid, layer, 0, T_W).standard_normal((n, in_features), dtype=np.float32) * np.float32(sigma)
+    if w_dtype == "f16":
+        w = f16_bits(a)
+        w32 = w.view(np.float16).astype(np.float32)
+    elif w_dtype == "bf16":
+        w = f32_to_bf16_bits(a)
+        w32 = (w.astype(np.uint32) << 16).view(np.float32)
+    else:
+        w = np.ascontiguousarray(a)
+        w32 = w
+    k1 = 1 << bits1
+    vecs = w32.reshape(-1, v) if in_features % v == 0 else np.zeros((0, v), np.float32)
+    take = min(k1, vecs.shape[0])
+    pos = rng(wid, layer, 0, T_PICK).choice(vecs.shape[0], size=take, replace=False) if take else np.zeros(0, int)
+    cb1 = np.empty((k1, v), dtype=np.uint16)
+    cb1[:take] = f16_bits(vecs[pos])
+    if take < k1:
+        cb1[take:] = codebook(rng(wid, layer, 0, T_C1), k1 - take, v, sigma)
+    cb2 = codebook(rng(wid, layer, 0, T_C2), 1 << bits2, v, sigma2) if bits2 else None
+    return {"n": n, "in_features": in_features, "v": v, "bits1": bits1, "bits2": bits2, "w_dtype": w_dtype,
+            "w": w, "w_f32": w32, "cb1": cb1, "cb2": cb2}

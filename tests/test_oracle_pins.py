@@ -611,3 +611,148 @@ def test_rht_blocks_are_independent(oracle_mod):
     y = oracle_mod.rht(x, np.zeros(2, np.uint8))
     assert np.all(y[0, :4] == 0) and np.all(y[0, 8:] == 0)
     assert np.allclose(np.abs(y[0, 4:8]), 0.5, rtol=0, atol=1e-15)  # a column of H_4 / 2
+
+
+# ------------------------------------------------------------------ residual VQ encode
+# VPTQ guide, "Step 2: Multi-Stage Residual Vector Quantizer (RVQ)": nearest main centroid
+# by Euclidean distance (argmin keeps the first of equal distances), then the nearest
+# residual centroid of w - C1[idx1].
+
+
+def _f16v(vals):
+    return np.asarray(vals, dtype=np.float16).view(np.uint16)
+
+
+def _exact_nearest(vec, book_bits):
+    """Lowest index minimising the exact squared distance (rational arithmetic)."""
+    from fractions import Fraction
+
+    c = book_bits.view(np.float16).astype(np.float64)
+    d = [sum((Fraction(float(a)) - Fraction(float(b))) ** 2 for a, b in zip(vec, row)) for row in c]
+    best = min(d)
+    order = sorted(d)
+    gap = order[1] - order[0] if len(order) > 1 else Fraction(1)
+    return d.index(best), gap
+
+
+@pytest.mark.parametrize("seed,v,k1,k2", [(1, 4, 16, 8), (2, 8, 32, 16), (3, 1, 8, 4), (4, 16, 12, 5)])
+def test_rvq_matches_exact_rational_distances(oracle_mod, seed, v, k1, k2):
+    g = np.random.default_rng(seed)
+    n, nv = 3, 3
+    w = (g.standard_normal((n, nv * v)) * 0.02).astype(np.float16).astype(np.float32)
+    cb1 = _f16v(g.standard_normal((k1, v)) * 0.02)
+    cb2 = _f16v(g.standard_normal((k2, v)) * 0.005)
+    i1, i2 = oracle_mod.rvq_assign(w, v, cb1, cb2)
+    for o in range(n):
+        for j in range(nv):
+            vec = w[o, j * v:(j + 1) * v]
+            e1, gap1 = _exact_nearest(vec, cb1)
+            assert gap1 > 1e-12 and i1[o, j] == e1
+            r = (vec - cb1[e1].view(np.float16).astype(np.float32)).astype(np.float32)
+            e2, gap2 = _exact_nearest(r, cb2)
+            assert gap2 > 1e-12 and i2[o, j] == e2
+
+
+def test_rvq_agrees_with_scipy_cdist(oracle_mod):
+    from scipy.spatial.distance import cdist
+
+    p = synth.make_encode_problem(64, 128, 8, 8, 6, wid=90)
+    i1, i2 = oracle_mod.rvq_assign(p["w_f32"], 8, p["cb1"], p["cb2"])
+    vecs = p["w_f32"].reshape(-1, 8).astype(np.float64)
+    c1 = p["cb1"].view(np.float16).astype(np.float64)
+    c2 = p["cb2"].view(np.float16).astype(np.float64)
+    d1 = cdist(vecs, c1)
+    ref1 = np.argmin(d1, axis=1)
+    srt = np.sort(d1, axis=1)
+    clear = srt[:, 1] - srt[:, 0] > 1e-9
+    assert clear.mean() > 0.5  # main book holds copies of some vectors: exact-zero distances
+    assert np.array_equal(i1.reshape(-1)[clear], ref1[clear])
+    res = (vecs.astype(np.float32) - c1[i1.reshape(-1)].astype(np.float32)).astype(np.float64)
+    d2 = cdist(res, c2)
+    srt2 = np.sort(d2, axis=1)
+    clear2 = srt2[:, 1] - srt2[:, 0] > 1e-9
+    assert clear2.all()
+    assert np.array_equal(i2.reshape(-1), np.argmin(d2, axis=1))
+
+
+def test_rvq_codebook_holding_the_vectors(oracle_mod):
+    """A main book made of the vectors themselves returns each vector's own row (the
+    lowest one among duplicates); the residual is then zero, whose nearest residual
+    centroid is the shortest one."""
+    g = np.random.default_rng(7)
+    v, nvec = 8, 40
+    vecs = _f16v(g.standard_normal((nvec, v)) * 0.02)
+    perm = g.permutation(nvec)
+    book = np.concatenate([vecs[perm], vecs[perm[:5]]])  # rows 40..44 duplicate rows 0..4
+    book = np.concatenate([book[40:], book[:40]])        # the duplicates come first now
+    cb2 = _f16v(g.standard_normal((16, v)) * 0.005)
+    w = vecs.view(np.float16).astype(np.float32).reshape(4, 10 * v)
+    i1, i2 = oracle_mod.rvq_assign(w, v, book, cb2)
+    pos = {int(p): i for i, p in enumerate(perm)}
+    want = np.array([(pos[k] + 5) if pos[k] >= 5 else pos[k] for k in range(nvec)])
+    assert np.array_equal(i1.reshape(-1), want)
+    norms = (cb2.view(np.float16).astype(np.float64) ** 2).sum(axis=1)
+    assert np.all(i2 == int(np.argmin(norms)))
+
+
+def test_rvq_ties_go_to_the_lowest_index(oracle_mod):
+    v = 4
+    book = _f16v([[0, 0, 0, 0], [1, 0, 0, 0], [0, -1, 0, 0], [-1, 0, 0, 0], [0.5, 0, 0, 0], [0, 1, 0, 0]])
+    w = np.array([[0.5, 0, 0, 0,      # |w - c| = 0.5 for rows 0 and 1, 0 for row 4: row 4
+                   0.25, 0, 0, 0,     # rows 0 and 4 at 0.25: row 0
+                   0, 0, 0, 0,        # row 0 exact
+                   -0.5, 0, 0, 0,     # rows 0 and 3 at 0.5: row 0
+                   -0.75, 0.5, 0, 0,  # row 3 (0.25^2 + 0.5^2) vs rows 0, 2: row 3
+                   0, 0.5, 0, 0]],    # rows 0 and 5 at 0.5: row 0
+                 dtype=np.float32)
+    i1, _ = oracle_mod.rvq_assign(w, v, book)
+    assert i1.tolist() == [[4, 0, 0, 0, 3, 0]]
+    book2 = _f16v([[1, 1, 0, 0], [2, 0, 0, 0], [1, 1, 0, 0], [0, 2, 0, 0]])  # rows 0 and 2 equal
+    w2 = np.array([[1, 1, 0, 0, 1.5, 0.5, 0, 0]], dtype=np.float32)     # second: rows 0, 1, 2 tie
+    i1, _ = oracle_mod.rvq_assign(w2, v, book2)
+    assert i1.tolist() == [[0, 0]]
+
+
+def test_rvq_residual_stage_recovers_grid_sums(oracle_mod):
+    """With the main book on an integer grid and small residual centroids (no u with -u
+    also present), w = C1[j] + C2[m] is exact in fp16 and both indices come back; a
+    residual taken the wrong way round (C1[j] - w) would pick other rows."""
+    g = np.random.default_rng(11)
+    v, k1, k2 = 4, 64, 32
+    c1 = g.integers(-3, 4, size=(k1, v)).astype(np.float64)
+    c1 = np.unique(c1, axis=0)
+    k1 = c1.shape[0]
+    c2 = (g.integers(1, 16, size=(k2, v)) / 64.0) * np.array([1, -1, 1, -1])  # |u| < 0.25, fixed sign pattern
+    c2 = np.unique(c2, axis=0)
+    k2 = c2.shape[0]
+    j = g.integers(0, k1, size=30)
+    m = g.integers(0, k2, size=30)
+    w = (c1[j] + c2[m]).reshape(3, 10 * v).astype(np.float32)
+    i1, i2 = oracle_mod.rvq_assign(w, v, _f16v(c1), _f16v(c2))
+    assert np.array_equal(i1.reshape(-1), j)
+    assert np.array_equal(i2.reshape(-1), m)
+
+
+def test_rvq_scalar_levels_closed_form(oracle_mod):
+    """v = 1 with sorted levels: the nearest level is the one whose midpoint cell holds w
+    (lower level on a midpoint)."""
+    levels = np.array([-1.0, -0.5, -0.125, 0.0, 0.25, 1.0])
+    g = np.random.default_rng(3)
+    w = np.concatenate([g.uniform(-1.5, 1.5, 200), (levels[1:] + levels[:-1]) / 2]).astype(np.float16)
+    w = w.astype(np.float32)[None, :]
+    i1, _ = oracle_mod.rvq_assign(w, 1, _f16v(levels))
+    mids = (levels[1:] + levels[:-1]) / 2
+    want = np.searchsorted(mids, w[0].astype(np.float64), side="left")
+    assert np.array_equal(i1[0], want)
+
+
+def test_rvq_permuting_the_book_permutes_the_indices(oracle_mod):
+    p = synth.make_encode_problem(8, 64, 8, 7, 5, wid=91)
+    i1, i2 = oracle_mod.rvq_assign(p["w_f32"], 8, p["cb1"], p["cb2"])
+    g = np.random.default_rng(5)
+    q1, q2 = g.permutation(128), g.permutation(32)
+    j1, j2 = oracle_mod.rvq_assign(p["w_f32"], 8, p["cb1"][q1], p["cb2"][q2])
+    assert np.array_equal(q1[j1], i1)
+    assert np.array_equal(q2[j2], i2)
+    k1, k2 = oracle_mod.rvq_assign(p["w_f32"], 8, p["cb1"])
+    assert k2 is None and np.array_equal(k1, i1)

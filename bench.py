@@ -244,6 +244,43 @@ def rht_leg(vq, torch, use_graph):
     return out
 
 
+FP64_PEAK_TFLOPS = 78.6  # MI355X vector fp64 (FMA = 2 flops)
+
+
+def encode_leg(vq, torch, calls=3):
+    """vq_assign on a 4096 x 4096 fp16 layer, v = 8, K1 = 65536 + K2 = 256 (the books of
+    the 3-bit layer): main book = fp16 copies of W's vectors at random positions, residual
+    book 0.005 N(0,1), as the seeded generators draw them."""
+    dev = torch.device("cuda")
+    g = torch.Generator(device=dev)
+    g.manual_seed(zlib.crc32(b"42/encode/4096/4096"))
+    n, inf, v, b1, b2 = 4096, 4096, 8, 16, 8
+    w = (torch.randn((n, inf), generator=g, device=dev) * 0.02).to(torch.float16)
+    pick = torch.randperm(n * inf // v, generator=g, device=dev)[: 1 << b1]
+    cb1 = w.view(-1, v)[pick].contiguous()
+    cb2 = (torch.randn((1 << b2, v), generator=g, device=dev) * 0.005).to(torch.float16)
+    d = vq.make_desc(n, inf, v, b1, b2)
+    ws = torch.empty(vq.assign_workspace_bytes(d), dtype=torch.uint8, device=dev)
+    i1 = torch.empty((n, inf // v), dtype=torch.int32, device=dev)
+    i2 = torch.empty_like(i1)
+    vq.assign(d, w, cb1, cb2, ws=ws, out1=i1, out2=i2)  # warm-up
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(calls):
+        vq.assign(d, w, cb1, cb2, ws=ws, out1=i1, out2=i2)
+    end.record(stream)
+    torch.cuda.synchronize()
+    sec = start.elapsed_time(end) * 1e-3 / calls
+    nvec = n * inf // v
+    flops = nvec * ((1 << b1) + (1 << b2)) * (2 * v + 2)
+    return {"workload": "4096x4096 fp16 W, v=8, K1=65536 + K2=256", "ms_per_call": round(sec * 1e3, 3),
+            "vectors_per_s": round(nvec / sec), "weights_per_s": round(n * inf / sec),
+            "fp64_tflops": round(flops / sec / 1e12, 2), "pct_fp64_peak": round(100 * flops / sec / 1e12 / FP64_PEAK_TFLOPS, 1),
+            "flops_per_call": flops, "calls": calls}
+
+
 def time_ring(torch, rings, steps, warmup, use_graph=True):
     """Average seconds per call over `steps` calls rotating through the ring(s)."""
     stream = torch.cuda.current_stream()
@@ -344,6 +381,7 @@ def main():
     ap.add_argument("--shared-book", action="store_true",
                     help="diagnostic: every ring copy shares one codebook (warm in L2), headline only")
     ap.add_argument("--only-rht", action="store_true", help="run only the Hadamard-transform leg (for profiling)")
+    ap.add_argument("--only-encode", action="store_true", help="run only the residual VQ encode leg (for profiling)")
     ap.add_argument("--only-svq", action="store_true",
                     help="run only the affine-lattice (vq_svq_gemv) leg (for profiling)")
     ap.add_argument("--only-workload", default=None, choices=sorted(WORKLOADS),
@@ -389,6 +427,9 @@ def main():
         return
     if args.only_rht:
         print(json.dumps({"rht": rht_leg(vq, torch, use_graph)}))
+        return
+    if args.only_encode:
+        print(json.dumps({"encode": encode_leg(vq, torch)}))
         return
     if args.only_svq:
         print(json.dumps({"affine_lattice": svq_leg(vq, torch, use_graph, steps=args.steps)}))
@@ -498,6 +539,7 @@ def main():
         out["gemv_batched"] = batch
         out["affine_lattice"] = svq_leg(vq, torch, use_graph)
         out["rht"] = rht_leg(vq, torch, use_graph)
+        out["encode"] = encode_leg(vq, torch)
         if not args.no_cpu_baseline:
             out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)

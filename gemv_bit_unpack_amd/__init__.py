@@ -41,7 +41,8 @@ VQ_F16, VQ_BF16, VQ_F32 = 0, 1, 2
 LAYOUT_ROWSTREAM = 1
 
 EXPORTED = ("vq_abi_version", "vq_status_string", "vq_packed_bytes", "vq_pack", "vq_dequant", "vq_gemv",
-            "vq_gemv_workspace_bytes", "vq_gemv_ws", "vq_gemm", "vq_svq_dequant", "vq_svq_gemv", "vq_rht", "vq_rht_block")
+            "vq_gemv_workspace_bytes", "vq_gemv_ws", "vq_gemm", "vq_svq_dequant", "vq_svq_gemv", "vq_rht", "vq_rht_block",
+            "vq_assign_workspace_bytes", "vq_assign")
 
 
 class Desc(ctypes.Structure):
@@ -95,6 +96,10 @@ def _load():
     lib.vq_rht.restype = ctypes.c_int
     lib.vq_rht_block.argtypes = [i32]
     lib.vq_rht_block.restype = i32
+    lib.vq_assign_workspace_bytes.argtypes = [dp, ctypes.POINTER(sz)]
+    lib.vq_assign_workspace_bytes.restype = ctypes.c_int
+    lib.vq_assign.argtypes = [dp, vp, ctypes.c_int, vp, vp, vp, vp, vp, sz, vp]
+    lib.vq_assign.restype = ctypes.c_int
     return lib
 
 
@@ -307,6 +312,38 @@ def rht(x, signs, transpose=False, y_dtype=None, out=None):
                       _stream_ptr(x.device))
     _check(st, "vq_rht")
     return out
+
+
+def assign_workspace_bytes(desc: Desc) -> int:
+    """Device workspace bytes that vq_assign needs for desc's codebooks."""
+    n = ctypes.c_size_t(0)
+    _check(lib().vq_assign_workspace_bytes(ctypes.byref(desc), ctypes.byref(n)), "vq_assign_workspace_bytes")
+    return int(n.value)
+
+
+def assign(desc: Desc, w, cb1, cb2=None, ws=None, out1=None, out2=None):
+    """Residual VQ encode of W [N, IN] (fp16 / bf16 / fp32 device tensor) against fp16
+    codebooks: (idx1, idx2) as int32 tensors [N, IN / v] holding the uint32 indices
+    (idx2 None when desc.bits2 == 0).  ws: a uint8 device tensor of at least
+    assign_workspace_bytes(desc) bytes (allocated here when None)."""
+    torch = _torch()
+    if w.dim() != 2 or tuple(w.shape) != (desc.out_features, desc.in_features):
+        raise ValueError("w must be [%d, %d], got %s" % (desc.out_features, desc.in_features, tuple(w.shape)))
+    nv = desc.in_features // desc.v if desc.v > 0 else 0
+    if out1 is None:
+        out1 = torch.empty((desc.out_features, nv), dtype=torch.int32, device=w.device)
+    if desc.bits2 and out2 is None:
+        out2 = torch.empty((desc.out_features, nv), dtype=torch.int32, device=w.device)
+    if ws is None:
+        ws = torch.empty(max(assign_workspace_bytes(desc), 256), dtype=torch.uint8, device=w.device)
+    f16 = (torch.float16,)
+    st = lib().vq_assign(ctypes.byref(desc), _dev_ptr(w, "w", (torch.float16, torch.bfloat16, torch.float32)),
+                         _dtype_code(w.dtype), _dev_ptr(cb1, "cb1", f16),
+                         _dev_ptr(cb2, "cb2", f16) if desc.bits2 else None, _dev_ptr(out1, "idx1", (torch.int32,)),
+                         _dev_ptr(out2, "idx2", (torch.int32,)) if desc.bits2 else None, _dev_ptr(ws, "workspace"),
+                         ws.numel() * ws.element_size(), _stream_ptr(w.device))
+    _check(st, "vq_assign")
+    return out1, (out2 if desc.bits2 else None)
 
 
 _stream_ws = {}

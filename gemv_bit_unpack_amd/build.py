@@ -19,7 +19,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libvq.so")
 CEILINGS_SRC = os.path.join(PKG, "micro", "ceilings.hip")
 CEILINGS_BIN = os.path.join(PKG, "micro", "vq_ceilings")
-SOURCES = ["vq_host.cpp", "vq_dequant.hip", "vq_gemv.hip", "vq_gemv_sliced.hip", "vq_gemm.hip", "vq_svq.hip", "vq_rht.hip"]
+SOURCES = ["vq_host.cpp", "vq_dequant.hip", "vq_gemv.hip", "vq_gemv_sliced.hip", "vq_gemm.hip", "vq_svq.hip", "vq_rht.hip",
+           "vq_assign.hip"]
 ARCH = "gfx950"
 
 COMMON = [

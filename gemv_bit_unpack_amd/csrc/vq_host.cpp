@@ -285,6 +285,31 @@ vq_status vq_rht(int32_t M, int32_t n, const void* x, vq_dtype x_dtype, const vo
   return launch_rht(M, n, x, x_dtype, (const uint8_t*)signs, transpose, y, y_dtype, stream);
 }
 
+vq_status vq_assign_workspace_bytes(const vq_desc* desc, size_t* nbytes) {
+  if (!nbytes) return VQ_ERR_NULL;
+  const vq_status st = check_desc(desc);
+  if (st != VQ_OK) return st;
+  *nbytes = assign_workspace(*desc);
+  return VQ_OK;
+}
+
+vq_status vq_assign(const vq_desc* desc, const void* w, vq_dtype w_dtype, const void* cb1, const void* cb2,
+                    uint32_t* idx1, uint32_t* idx2, void* workspace, size_t workspace_bytes, void* stream) {
+  const vq_status st = check_desc(desc);
+  if (st != VQ_OK) return st;
+  const vq_desc& d = *desc;
+  if (w_dtype != VQ_F16 && w_dtype != VQ_BF16 && w_dtype != VQ_F32) return VQ_ERR_UNSUPPORTED;
+  if (d.in_features % d.v != 0) return VQ_ERR_UNSUPPORTED;
+  if ((int64_t)d.out_features * d.in_features == 0) return VQ_OK;
+  if (!w || !cb1 || !idx1 || !workspace || (d.bits2 > 0 && (!cb2 || !idx2))) return VQ_ERR_NULL;
+  if (workspace_bytes < assign_workspace(d)) return VQ_ERR_BUFFER_SIZE;
+  if (!aligned(workspace, 256) || !aligned(w, dtype_size(w_dtype)) || !aligned(cb1, 2) || !aligned(idx1, 4) ||
+      (d.bits2 > 0 && (!aligned(cb2, 2) || !aligned(idx2, 4))))
+    return VQ_ERR_ALIGN;
+  return launch_assign(d, w, w_dtype, (const uint16_t*)cb1, d.bits2 > 0 ? (const uint16_t*)cb2 : nullptr, idx1,
+                       d.bits2 > 0 ? idx2 : nullptr, workspace, stream);
+}
+
 vq_status vq_gemm(const vq_desc* desc, const void* packed, const void* cb1, const void* cb2, const void* scale,
                   const void* bias, const void* x, vq_dtype x_dtype, int32_t M, void* y, vq_dtype y_dtype,
                   void* stream) {

@@ -86,5 +86,10 @@ int32_t rht_block(int32_t n);
 vq_status launch_rht(int32_t m, int32_t n, const void* x, vq_dtype x_dtype, const uint8_t* signs, int32_t transpose,
                      void* y, vq_dtype y_dtype, void* stream);
 vq_status launch_svq_dequant(const SvqArgs& p, void* w, vq_dtype w_dtype, void* stream);
+// Residual VQ encode (validated arguments: IN % v == 0, N * IN / v >= 1, workspace of at
+// least assign_workspace(d) bytes, 256-byte aligned).
+size_t assign_workspace(const vq_desc& d);
+vq_status launch_assign(const vq_desc& d, const void* w, vq_dtype w_dtype, const uint16_t* cb1, const uint16_t* cb2,
+                        uint32_t* idx1, uint32_t* idx2, void* workspace, void* stream);
 
 }  // namespace vqi

@@ -211,6 +211,34 @@ vq_status vq_rht(int32_t M, int32_t n, const void* x, vq_dtype x_dtype, const vo
 /* The transform's block size for row length n (0 for n <= 0). */
 int32_t vq_rht_block(int32_t n);
 
+/*
+ * Two-stage residual VQ encode with given codebooks (VPTQ guide, "Step 2: Multi-Stage
+ * Residual Vector Quantizer (RVQ)": Euclidean distance and argmin, then the same on the
+ * residuals; "2. Multi-Stage Residual Vector Quantization" for the residual).  W [N][IN]
+ * is cut into nv = IN / v vectors per row; for each vector w
+ *
+ *   idx1 = the lowest k minimising |C1[k]|^2 - 2 w . C1[k]
+ *   idx2 = the lowest k minimising |C2[k]|^2 - 2 r . C2[k],    r = fp32(w - C1[idx1])
+ *
+ * (the squared Euclidean distance less |w|^2, which all centroids share), evaluated in
+ * fp64: |c|^2 as fma(c_t, c_t, .) over t = 0 .. v-1 from 0, w . c the same way, then
+ * fma(-2, w . c, |c|^2).  Every product is exact, so the result is the same on any
+ * machine that runs that sequence of IEEE operations.  Codebook initialisation (the
+ * guide's random samples) and refinement are the caller's.
+ * desc: N = out_features, IN = in_features (a multiple of v, else VQ_ERR_UNSUPPORTED),
+ *   v, K1 = 2^bits1, K2 = 2^bits2 (bits2 = 0: one stage; idx2 and cb2 ignored), layout
+ *   as for the other calls.
+ * w: device [N][IN], VQ_F16, VQ_BF16 or VQ_F32, aligned to its element.
+ * cb1: device fp16 [K1][v]; cb2: device fp16 [K2][v]; 2-byte aligned.
+ * idx1, idx2: device uint32 [N][nv] (the layout vq_pack takes), 4-byte aligned.
+ * workspace: device, 256-byte aligned, at least vq_assign_workspace_bytes(desc) bytes
+ *   (VQ_ERR_BUFFER_SIZE otherwise); scratch after the call, one per concurrent call.
+ * N * IN = 0: no-op.  Errors as for the other calls.
+ */
+vq_status vq_assign_workspace_bytes(const vq_desc* desc, size_t* nbytes);
+vq_status vq_assign(const vq_desc* desc, const void* w, vq_dtype w_dtype, const void* cb1, const void* cb2,
+                    uint32_t* idx1, uint32_t* idx2, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -291,3 +291,33 @@ def test_rht_block_and_validation(vq):
     assert f(1, 64, P, 0, P, 0, P_MIS, 2, None) == vq.VQ_ERR_ALIGN
     assert f(0, 64, None, 0, None, 0, None, 2, None) == vq.VQ_OK
     assert f(3, 0, None, 0, None, 0, None, 2, None) == vq.VQ_OK
+
+
+def test_assign_workspace_and_validation(vq):
+    d = vq.make_desc(4096, 4096, 8, 16, 8)
+    assert vq.assign_workspace_bytes(d) == ((65536 + 256) * 9 * 8 + 255) // 256 * 256
+    d1 = vq.make_desc(7, 12, 3, 5, 0)
+    assert vq.assign_workspace_bytes(d1) == (32 * 4 * 8 + 255) // 256 * 256
+    f = vq.lib().vq_assign
+    big = ctypes.c_size_t(1 << 30)
+    ok = vq.make_desc(8, 64, 8, 8, 4)
+    br = ctypes.byref
+    assert f(None, P, 0, P, P, P, P, P, big, None) == vq.VQ_ERR_NULL
+    assert f(br(vq.make_desc(8, 64, 17, 8, 4)), P, 0, P, P, P, P, P, big, None) == vq.VQ_ERR_BITS
+    assert f(br(vq.make_desc(8, 64, 8, 0, 4)), P, 0, P, P, P, P, P, big, None) == vq.VQ_ERR_BITS
+    assert f(br(vq.make_desc(-8, 64, 8, 8, 4)), P, 0, P, P, P, P, P, big, None) == vq.VQ_ERR_SHAPE
+    assert f(br(vq.make_desc(8, 60, 8, 8, 4)), P, 0, P, P, P, P, P, big, None) == vq.VQ_ERR_UNSUPPORTED  # IN % v
+    assert f(br(ok), P, 5, P, P, P, P, P, big, None) == vq.VQ_ERR_UNSUPPORTED                          # w dtype
+    assert f(br(ok), None, 0, P, P, P, P, P, big, None) == vq.VQ_ERR_NULL
+    assert f(br(ok), P, 0, None, P, P, P, P, big, None) == vq.VQ_ERR_NULL
+    assert f(br(ok), P, 0, P, None, P, P, P, big, None) == vq.VQ_ERR_NULL      # cb2 with bits2 > 0
+    assert f(br(ok), P, 0, P, P, None, P, P, big, None) == vq.VQ_ERR_NULL
+    assert f(br(ok), P, 0, P, P, P, None, P, big, None) == vq.VQ_ERR_NULL      # idx2 with bits2 > 0
+    assert f(br(ok), P, 0, P, P, P, P, None, big, None) == vq.VQ_ERR_NULL      # workspace
+    need = vq.assign_workspace_bytes(ok)
+    assert f(br(ok), P, 0, P, P, P, P, P, need - 1, None) == vq.VQ_ERR_BUFFER_SIZE
+    assert f(br(ok), P, 0, P, P, P, P, P_MIS, big, None) == vq.VQ_ERR_ALIGN     # workspace 256-byte aligned
+    assert f(br(ok), P_MIS, 2, P, P, P, P, P, big, None) == vq.VQ_ERR_ALIGN     # fp32 w
+    assert f(br(ok), P, 0, P, P, P_MIS, P, P, big, None) == vq.VQ_ERR_ALIGN     # idx1
+    assert f(br(vq.make_desc(0, 64, 8, 8, 4)), None, 0, None, None, None, None, None, 0, None) == vq.VQ_OK
+    assert f(br(vq.make_desc(8, 0, 8, 8, 4)), None, 0, None, None, None, None, None, 0, None) == vq.VQ_OK

@@ -39,11 +39,16 @@ def _hipcc() -> str:
     return cand if os.path.exists(cand) else "hipcc"
 
 
+# Per-unit additions.  vq_assign: matrix-core results go straight to VGPRs (the VALU reads
+# every one of them), instead of through the accumulation registers.
+EXTRA = {"vq_assign.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     cmd = [_hipcc(), *COMMON]
     if src.endswith(".hip"):
-        cmd += HIP_ONLY + ["-x", "hip"]
+        cmd += HIP_ONLY + EXTRA.get(src, []) + ["-x", "hip"]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

@@ -95,7 +95,9 @@ __device__ __forceinline__ void nearest(const double (&w)[R][V], const double* _
   }
 }
 
-template <int V, int R, int WT>
+// FIRST: both stages (stage 2 skipped when k2 == 0); otherwise stage 1 has run already and
+// only the residual stage runs, on the idx1 it wrote.
+template <int V, int R, int WT, bool FIRST>
 __global__ __launch_bounds__(kThreads) void assign_kernel(const void* __restrict__ w, int64_t nvec,
                                                           const double* __restrict__ tab1, int32_t k1,
                                                           const double* __restrict__ tab2, int32_t k2,
@@ -109,13 +111,18 @@ __global__ __launch_bounds__(kThreads) void assign_kernel(const void* __restrict
     for (int t = 0; t < V; ++t) wv[r][t] = weight_at<WT>(w, g * V + t);
   }
   uint32_t i1[R];
-  nearest<V, R>(wv, tab1, k1, i1);
+  if constexpr (FIRST) {
+    nearest<V, R>(wv, tab1, k1, i1);
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int64_t g = base + (int64_t)r * kThreads;
-    if (g < nvec) idx1[g] = i1[r];
+    for (int r = 0; r < R; ++r) {
+      const int64_t g = base + (int64_t)r * kThreads;
+      if (g < nvec) idx1[g] = i1[r];
+    }
+    if (k2 == 0) return;
+  } else {
+#pragma unroll
+    for (int r = 0; r < R; ++r) i1[r] = idx1[min(base + (int64_t)r * kThreads, nvec - 1)];
   }
-  if (k2 == 0) return;
   // residual in fp32, held exactly in fp64
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -132,38 +139,363 @@ __global__ __launch_bounds__(kThreads) void assign_kernel(const void* __restrict
   }
 }
 
+// ---------------------------------------------------------------------------------------
+// Matrix-core pass for stage 1 with fp16 weights.  The matrix cores form, for 32 centroids
+// x 32 vectors at a time, the fp32 half-distance h = |c|^2 / 2 - w . c
+// (v_mfma_f32_32x32x8_f16 with A = -c, B = w, C = fl32(|c|^2 / 2)).  Each product of two
+// fp16 values is exact in fp32, so h differs from the fp64 ranking above (halved) by at
+// most E = (v + 2) 2^-23 (S_w Cmax + NCmax / 2), with S_w = sum |w_t| and Cmax, NCmax
+// the largest |c_t| and |c|^2 of the book (the sum of v + 1 terms with at most 2^-23
+// relative error per addition, and the rounding of C).  If k* is the centroid the fp64
+// ranking picks and m the smallest h seen so far, then h(k*) <= m + 2E at every point
+// of the walk.  Each lane therefore keeps a threshold thr = min over seen tiles of
+// (tile minimum + delta), delta = 4 (v + 2) 2^-23 (S_w Cmax + NCmax / 2) (twice the bound,
+// which also covers the rounding of thr itself), and ranks in fp64, exactly as above,
+// every centroid with h <= thr; the lowest index of the smallest fp64 distance among them
+// is the answer.  A tile costs one or two MFMAs and eight three-way minima per 32x32
+// block; the fp64 ranking runs only where a tile holds a candidate, which after the first
+// few hundred centroids is rare.  NaN or infinite values make delta infinite: every
+// centroid is then ranked in fp64.
+//
+// Work split: 256 threads = 4 wavefronts; a wavefront owns kGroups groups of 32 vectors
+// (B operands in registers for the whole walk); lanes l and l + 32 share vector l % 32
+// (the two K halves of the B operand, and rows 4 .. 7 of every 8 in the output), and
+// combine their results at the end.  The book is staged through LDS in chunks of
+// kChunk centroids, double-buffered, one barrier per chunk.
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kChunk = 512;                                // centroids per LDS chunk
+constexpr int kTile = 32;                                  // centroids per MFMA tile
+constexpr int kGroups = 4;                                 // 32-vector groups per wavefront
+constexpr int kMfmaVectors = (kThreads / 64) * kGroups * 32;  // vectors per workgroup
+
+struct MfmaTable {
+  const uint16_t* a16;  // [kp][KB][8] fp16: -c, zero padded
+  const float* cf;      // [kp] fl32(|c|^2 / 2), +inf on padding rows
+  const float2* bmax;   // [nbmax] per-256-centroid {max |c_t|, max |c|^2}
+  int32_t nbmax, kp;
+};
+
+// Smallest of the 16 values of an MFMA result; NaN if any of them is NaN (IEEE minimum,
+// which propagates NaN and so needs no quieting of its inputs).
+__device__ __forceinline__ float min16(const f32x16_t& d) {
+  auto mn = [](float a, float b) { return __builtin_elementwise_minimum(a, b); };
+  const float m0 = mn(mn(d[0], d[1]), d[2]);
+  const float m1 = mn(mn(d[3], d[4]), d[5]);
+  const float m2 = mn(mn(d[6], d[7]), d[8]);
+  const float m3 = mn(mn(d[9], d[10]), d[11]);
+  const float m4 = mn(mn(d[12], d[13]), d[14]);
+  return mn(mn(mn(m0, m1), mn(m2, m3)), mn(m4, d[15]));
+}
+
+template <int KB>
+__global__ __launch_bounds__(kThreads) void assign_mfma_table_kernel(const uint16_t* __restrict__ cb, int32_t k,
+                                                                     int32_t kp, int32_t v,
+                                                                     uint16_t* __restrict__ a16,
+                                                                     float* __restrict__ cf,
+                                                                     float2* __restrict__ bmax) {
+  __shared__ float2 red[kThreads / 64];
+  const int32_t c = blockIdx.x * kThreads + threadIdx.x;  // grid covers kp exactly
+  float cm = 0.f, nm = 0.f;
+  uint16_t* row = a16 + (size_t)c * (KB * 8);
+  if (c < k) {
+    double nc = 0.0;
+    for (int t = 0; t < KB * 8; ++t) {
+      uint16_t hbits = 0;
+      if (t < v) {
+        hbits = cb[(size_t)c * v + t];
+        const double ct = (double)vqd::f16_to_f32(hbits);
+        nc = fma(ct, ct, nc);
+        cm = fmaxf(cm, fabsf((float)ct));
+        hbits ^= 0x8000u;  // -c
+      }
+      row[t] = hbits;
+    }
+    cf[c] = (float)(nc * 0.5);
+    nm = (float)nc;
+    if (!(cm <= __builtin_inff()) || !(nm <= __builtin_inff())) cm = nm = __builtin_inff();  // NaN: rank all
+  } else {
+    for (int t = 0; t < KB * 8; ++t) row[t] = 0;
+    cf[c] = __builtin_inff();
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    cm = fmaxf(cm, __shfl_xor(cm, o));
+    nm = fmaxf(nm, __shfl_xor(nm, o));
+  }
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = make_float2(cm, nm);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float2 m = red[0];
+    for (int i = 1; i < kThreads / 64; ++i) m = make_float2(fmaxf(m.x, red[i].x), fmaxf(m.y, red[i].y));
+    bmax[blockIdx.x] = m;
+  }
+}
+
+template <int V>
+__global__ __launch_bounds__(kThreads) void assign_mfma_kernel(const uint16_t* __restrict__ w, int64_t nvec,
+                                                               const uint16_t* __restrict__ a16,
+                                                               const float* __restrict__ cf,
+                                                               const float2* __restrict__ bmax, int32_t nbmax,
+                                                               int32_t kp, int32_t k1,
+                                                               uint32_t* __restrict__ idx1) {
+  constexpr int KB = (V + 7) / 8;     // 8-wide K blocks
+  constexpr int R = kGroups;
+  constexpr int kAWords = kChunk * KB;  // uint4 (8 fp16) per (centroid, K block)
+  __shared__ uint4 sa[2][kAWords];
+  __shared__ float4 sc[2][kChunk / 4];
+  __shared__ float2 sred[kThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, col = lane & 31;
+
+  // book maxima
+  float cmax = 0.f, ncmax = 0.f;
+  for (int i = tid; i < nbmax; i += kThreads) {
+    const float2 m = bmax[i];
+    cmax = fmaxf(cmax, m.x);
+    ncmax = fmaxf(ncmax, m.y);
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    cmax = fmaxf(cmax, __shfl_xor(cmax, o));
+    ncmax = fmaxf(ncmax, __shfl_xor(ncmax, o));
+  }
+  if (lane == 0) sred[wave] = make_float2(cmax, ncmax);
+
+  // B operands: lane (col, h) holds coordinates 8 h .. 8 h + 7 of vector col of each group
+  const int64_t vbase = (int64_t)blockIdx.x * kMfmaVectors + (int64_t)wave * (R * 32) + col;
+  half8_t b[R];
+  float swp[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const uint16_t* wp = w + min(vbase + r * 32, nvec - 1) * V;  // lanes past the end rank a copy
+    float sw = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int t = 8 * h + q;
+      const uint16_t hv = t < V ? wp[t] : (uint16_t)0;
+      b[r][q] = __builtin_bit_cast(_Float16, hv);
+      sw += fabsf(vqd::f16_to_f32(hv));
+    }
+    swp[r] = sw + __shfl_xor(sw, 32);
+  }
+  __syncthreads();
+  cmax = fmaxf(fmaxf(sred[0].x, sred[1].x), fmaxf(sred[2].x, sred[3].x));
+  ncmax = fmaxf(fmaxf(sred[0].y, sred[1].y), fmaxf(sred[2].y, sred[3].y));
+  float thr[R], dl[R];
+  double best[R];
+  uint32_t bi[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float d = (4.f * (V + 2) * 0x1p-23f) * (swp[r] * cmax + 0.5f * ncmax) + 0x1p-100f;
+    dl[r] = (d <= __builtin_inff()) ? d : __builtin_inff();  // NaN -> rank everything
+    thr[r] = __builtin_inff();
+    best[r] = __builtin_inf();
+    bi[r] = 0;
+  }
+
+  // chunk staging: thread tid copies A words tid, tid + 256, ... and C quad tid (< kChunk / 4)
+  constexpr int kAPer = kAWords / kThreads;
+  static_assert(kAPer == 2 || kAPer == 4, "chunk staging takes two or four words per thread");
+  uint4 ra0, ra1, ra2, ra3;  // staging registers (ra2, ra3 for two K blocks)
+  float4 rc;
+  const uint4* ga = (const uint4*)a16;
+  const float4* gc = (const float4*)cf;
+  const int nch = kp / kChunk;
+#pragma unroll
+  for (int i = 0; i < kAPer; ++i) sa[0][tid + i * kThreads] = ga[tid + i * kThreads];
+  if (tid < kChunk / 4) sc[0][tid] = gc[tid];
+  __syncthreads();
+  for (int ch = 0; ch < nch; ++ch) {
+    const int buf = ch & 1;
+    // next chunk (the last one again at the end) into registers while this one is walked
+    const size_t nx = (size_t)min(ch + 1, nch - 1);
+    ra0 = ga[nx * kAWords + tid];
+    ra1 = ga[nx * kAWords + tid + kThreads];
+    if constexpr (kAPer == 4) {
+      ra2 = ga[nx * kAWords + tid + 2 * kThreads];
+      ra3 = ga[nx * kAWords + tid + 3 * kThreads];
+    }
+    rc = gc[nx * (kChunk / 4) + (tid & (kChunk / 4 - 1))];
+    for (int tt = 0; tt < kChunk / kTile; ++tt) {
+      const int c0 = tt * kTile;
+      // A operand: row c0 + col, coordinates 8 h .. 8 h + 7 (zero past the book's K blocks)
+      half8_t a = __builtin_bit_cast(half8_t, sa[buf][(c0 + col) * KB + (KB == 2 ? h : 0)]);
+      if constexpr (KB == 1) a = h ? half8_t{} : a;
+      f32x16_t cv;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 f = sc[buf][(c0 + 8 * g + 4 * h) >> 2];
+        cv[4 * g] = f.x;
+        cv[4 * g + 1] = f.y;
+        cv[4 * g + 2] = f.z;
+        cv[4 * g + 3] = f.w;
+      }
+      float tmin[R];
+      bool any = false;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const f32x16_t d = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b[r], cv, 0, 0, 0);
+        tmin[r] = min16(d);
+        any |= !(tmin[r] > thr[r]);
+      }
+      if (__any(any)) {
+        // a tile holds candidates: tighten the thresholds, rank the candidates in fp64
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const bool trig = !(tmin[r] > thr[r]);
+          if (__any(trig)) {
+            const f32x16_t d = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b[r], cv, 0, 0, 0);
+            // the whole vector: coordinates 8 h .. 8 h + 7 here, the others in the partner lane
+            const uint4 own = __builtin_bit_cast(uint4, b[r]);
+            uint4 oth;
+            oth.x = (uint32_t)__shfl_xor((int)own.x, 32);
+            oth.y = (uint32_t)__shfl_xor((int)own.y, 32);
+            oth.z = (uint32_t)__shfl_xor((int)own.z, 32);
+            oth.w = (uint32_t)__shfl_xor((int)own.w, 32);
+            if (trig) {
+              thr[r] = fminf(thr[r], tmin[r] + dl[r]);
+              double wv[V];
+#pragma unroll
+              for (int t = 0; t < V; ++t) {
+                const uint4 u = ((t >> 3) == h) ? own : oth;
+                const int e = t & 7;
+                const uint32_t word = e < 2 ? u.x : e < 4 ? u.y : e < 6 ? u.z : u.w;
+                wv[t] = (double)vqd::f16_to_f32((e & 1) ? (word >> 16) : (word & 0xFFFFu));
+              }
+              uint32_t cand = 0;
+#pragma unroll
+              for (int q = 0; q < 16; ++q) cand |= (d[q] > thr[r] ? 0u : 1u) << q;
+              while (cand) {
+                const int q = __builtin_ctz(cand);
+                cand &= cand - 1;
+                const int ci = c0 + 8 * (q >> 2) + 4 * h + (q & 3);  // row of the chunk
+                const int32_t k = ch * kChunk + ci;
+                if (k < k1) {
+                  // the fp64 ranking, on the centroid's fp16 values from the chunk in LDS
+                  double nc = 0.0, dot = 0.0;
+#pragma unroll
+                  for (int kb = 0; kb < KB; ++kb) {
+                    const uint4 u = sa[buf][ci * KB + kb];
+                    const uint32_t words[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                      const int t = kb * 8 + e;
+                      if (t < V) {
+                        const uint32_t neg = (e & 1) ? (words[e >> 1] >> 16) : (words[e >> 1] & 0xFFFFu);
+                        const double ct = (double)vqd::f16_to_f32(neg ^ 0x8000u);
+                        nc = fma(ct, ct, nc);
+                        dot = fma(wv[t], ct, dot);
+                      }
+                    }
+                  }
+                  const double dd = fma(-2.0, dot, nc);
+                  if (dd < best[r]) {  // a lane meets its centroids in increasing index order
+                    best[r] = dd;
+                    bi[r] = (uint32_t)k;
+                  }
+                }
+              }
+            }
+          }
+        }
+      }
+    }
+    sa[buf ^ 1][tid] = ra0;
+    sa[buf ^ 1][tid + kThreads] = ra1;
+    if constexpr (kAPer == 4) {
+      sa[buf ^ 1][tid + 2 * kThreads] = ra2;
+      sa[buf ^ 1][tid + 3 * kThreads] = ra3;
+    }
+    if (tid < kChunk / 4) sc[buf ^ 1][tid] = rc;
+    __syncthreads();
+  }
+  // lanes l and l + 32 hold the same vector: smaller fp64 distance, then lower index
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const double ob = __shfl_xor(best[r], 32);
+    const uint32_t oi = (uint32_t)__shfl_xor((int)bi[r], 32);
+    if (ob < best[r] || (ob == best[r] && oi < bi[r])) bi[r] = oi;
+    const int64_t g = vbase + r * 32;
+    if (h == 0 && g < nvec) idx1[g] = bi[r];
+  }
+}
+
 template <int V>
 vq_status launch_v(const void* w, vq_dtype w_dtype, int64_t nvec, const double* tab1, int32_t k1, const double* tab2,
-                   int32_t k2, uint32_t* idx1, uint32_t* idx2, hipStream_t s) {
+                   int32_t k2, uint32_t* idx1, uint32_t* idx2, const MfmaTable* mt, hipStream_t s) {
   constexpr int R = V <= 4 ? 4 : 2;
   const int64_t blocks = (nvec + (int64_t)kThreads * R - 1) / ((int64_t)kThreads * R);
   if (blocks > 0x7FFFFFFF) return VQ_ERR_UNSUPPORTED;
   const dim3 grid((unsigned)blocks), block(kThreads);
-  if (w_dtype == VQ_F16) {
-    hipLaunchKernelGGL((assign_kernel<V, R, VQ_F16>), grid, block, 0, s, w, nvec, tab1, k1, tab2, k2, idx1, idx2);
+  if (mt) {
+    const int64_t mblocks = (nvec + kMfmaVectors - 1) / kMfmaVectors;
+    if (mblocks > 0x7FFFFFFF) return VQ_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL((assign_mfma_kernel<V>), dim3((unsigned)mblocks), dim3(kThreads), 0, s, (const uint16_t*)w,
+                       nvec, mt->a16, mt->cf, mt->bmax, mt->nbmax, mt->kp, k1, idx1);
+    if (k2) {
+      hipLaunchKernelGGL((assign_kernel<V, R, VQ_F16, false>), grid, block, 0, s, w, nvec, tab1, k1, tab2, k2, idx1,
+                         idx2);
+    }
+  } else if (w_dtype == VQ_F16) {
+    hipLaunchKernelGGL((assign_kernel<V, R, VQ_F16, true>), grid, block, 0, s, w, nvec, tab1, k1, tab2, k2, idx1,
+                       idx2);
   } else if (w_dtype == VQ_BF16) {
-    hipLaunchKernelGGL((assign_kernel<V, R, VQ_BF16>), grid, block, 0, s, w, nvec, tab1, k1, tab2, k2, idx1, idx2);
+    hipLaunchKernelGGL((assign_kernel<V, R, VQ_BF16, true>), grid, block, 0, s, w, nvec, tab1, k1, tab2, k2, idx1,
+                       idx2);
   } else {
-    hipLaunchKernelGGL((assign_kernel<V, R, VQ_F32>), grid, block, 0, s, w, nvec, tab1, k1, tab2, k2, idx1, idx2);
+    hipLaunchKernelGGL((assign_kernel<V, R, VQ_F32, true>), grid, block, 0, s, w, nvec, tab1, k1, tab2, k2, idx1,
+                       idx2);
   }
   return VQ_OK;
 }
 
 }  // namespace
 
+namespace {
+
+// Workspace layout: the fp64 records of both books, then (K1 >= 256) the matrix-core
+// tables of the main book, each part 256-byte aligned.
+struct WsLayout {
+  size_t tab, a16, cf, bmax, total;
+  int32_t kp;
+  bool mfma;
+};
+
+inline size_t up256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(const vq_desc& d) {
+  WsLayout l{};
+  const size_t k1 = (size_t)1 << d.bits1, k2 = d.bits2 ? (size_t)1 << d.bits2 : 0;
+  l.tab = 0;
+  size_t off = up256((k1 + k2) * (size_t)(d.v + 1) * sizeof(double));
+  l.mfma = d.bits1 >= 8;
+  if (l.mfma) {
+    const int kb = (d.v + 7) / 8;
+    l.kp = (int32_t)((k1 + kChunk - 1) / kChunk * kChunk);
+    l.a16 = off;
+    off += up256((size_t)l.kp * kb * 16);
+    l.cf = off;
+    off += up256((size_t)l.kp * sizeof(float));
+    l.bmax = off;
+    off += up256((size_t)(l.kp / kThreads) * sizeof(float2));
+  }
+  l.total = off;
+  return l;
+}
+
+}  // namespace
+
 namespace vqi {
 
-size_t assign_workspace(const vq_desc& d) {
-  const size_t k = ((size_t)1 << d.bits1) + (d.bits2 ? ((size_t)1 << d.bits2) : 0);
-  const size_t bytes = k * (size_t)(d.v + 1) * sizeof(double);
-  return (bytes + 255) & ~(size_t)255;
-}
+size_t assign_workspace(const vq_desc& d) { return ws_layout(d).total; }
 
 vq_status launch_assign(const vq_desc& d, const void* w, vq_dtype w_dtype, const uint16_t* cb1, const uint16_t* cb2,
                         uint32_t* idx1, uint32_t* idx2, void* workspace, void* stream) {
   hipStream_t s = (hipStream_t)stream;
+  const WsLayout l = ws_layout(d);
   const int32_t k1 = 1 << d.bits1, k2 = d.bits2 ? 1 << d.bits2 : 0;
-  double* tab1 = (double*)workspace;
+  char* ws = (char*)workspace;
+  double* tab1 = (double*)(ws + l.tab);
   double* tab2 = tab1 + (size_t)k1 * (d.v + 1);
   hipLaunchKernelGGL(assign_table_kernel, dim3((k1 + kThreads - 1) / kThreads), dim3(kThreads), 0, s, cb1, k1, d.v,
                      tab1);
@@ -171,12 +503,29 @@ vq_status launch_assign(const vq_desc& d, const void* w, vq_dtype w_dtype, const
     hipLaunchKernelGGL(assign_table_kernel, dim3((k2 + kThreads - 1) / kThreads), dim3(kThreads), 0, s, cb2, k2, d.v,
                        tab2);
   }
+  MfmaTable mt{};
+  const MfmaTable* mtp = nullptr;
+  if (l.mfma && w_dtype == VQ_F16) {
+    mt.a16 = (const uint16_t*)(ws + l.a16);
+    mt.cf = (const float*)(ws + l.cf);
+    mt.bmax = (const float2*)(ws + l.bmax);
+    mt.kp = l.kp;
+    mt.nbmax = l.kp / kThreads;
+    if (d.v > 8) {
+      hipLaunchKernelGGL(assign_mfma_table_kernel<2>, dim3(mt.nbmax), dim3(kThreads), 0, s, cb1, k1, l.kp, d.v,
+                         (uint16_t*)mt.a16, (float*)mt.cf, (float2*)mt.bmax);
+    } else {
+      hipLaunchKernelGGL(assign_mfma_table_kernel<1>, dim3(mt.nbmax), dim3(kThreads), 0, s, cb1, k1, l.kp, d.v,
+                         (uint16_t*)mt.a16, (float*)mt.cf, (float2*)mt.bmax);
+    }
+    mtp = &mt;
+  }
   const int64_t nvec = (int64_t)d.out_features * (d.in_features / d.v);
   vq_status st = VQ_OK;
   switch (d.v) {
-#define VQ_ASSIGN_CASE(V)                                                             \
-  case V:                                                                             \
-    st = launch_v<V>(w, w_dtype, nvec, tab1, k1, tab2, k2, idx1, idx2, s); \
+#define VQ_ASSIGN_CASE(V)                                                        \
+  case V:                                                                        \
+    st = launch_v<V>(w, w_dtype, nvec, tab1, k1, tab2, k2, idx1, idx2, mtp, s); \
     break;
     VQ_ASSIGN_CASE(1)
     VQ_ASSIGN_CASE(2)

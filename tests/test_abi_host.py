@@ -294,10 +294,16 @@ def test_rht_block_and_validation(vq):
 
 
 def test_assign_workspace_and_validation(vq):
+    up = lambda b: (b + 255) // 256 * 256
+    # fp64 records {|c|^2, c} of both books, then for K1 >= 256 the matrix-core tables of
+    # the main book (K1 rounded up to 512 rows: fp16 -c in 8-wide blocks, fp32 |c|^2 / 2,
+    # one {max |c_t|, max |c|^2} pair per 256 rows)
     d = vq.make_desc(4096, 4096, 8, 16, 8)
-    assert vq.assign_workspace_bytes(d) == ((65536 + 256) * 9 * 8 + 255) // 256 * 256
+    assert vq.assign_workspace_bytes(d) == up((65536 + 256) * 9 * 8) + 65536 * 16 + 65536 * 4 + 256 * 8
+    d16 = vq.make_desc(5, 64, 16, 9, 0)
+    assert vq.assign_workspace_bytes(d16) == up(512 * 17 * 8) + 512 * 32 + 512 * 4 + up(2 * 8)
     d1 = vq.make_desc(7, 12, 3, 5, 0)
-    assert vq.assign_workspace_bytes(d1) == (32 * 4 * 8 + 255) // 256 * 256
+    assert vq.assign_workspace_bytes(d1) == up(32 * 4 * 8)
     f = vq.lib().vq_assign
     big = ctypes.c_size_t(1 << 30)
     ok = vq.make_desc(8, 64, 8, 8, 4)

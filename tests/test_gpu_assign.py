@@ -3,7 +3,11 @@ ABI: indices are compared element by element and must be equal (the ranking is o
 sequence of fp64 operations on both sides, and ties go to the lowest index).
 
 - small shapes spanning several workgroups and a ragged tail of lanes, every v from 1 to
-  16 among them, one and two stages, fp16 / bf16 / fp32 weights;
+  16 among them, one and two stages, fp16 / bf16 / fp32 weights; with fp16 weights and
+  K1 >= 256 the main stage runs on the matrix cores (fp32 distances, fp64 re-ranking
+  within the proven error bound), every v from 1 to 16 there too;
+- books made of fp16 subnormals (the matrix cores must multiply them exactly) and
+  infinite / NaN weights and centroids (every centroid is then re-ranked in fp64);
 - exact ties: duplicated centroids and vectors that equal a centroid;
 - the 4096 x 4096 layer with a 65536-entry main book and a 256-entry residual book (the
   weights of the benchmark) on sampled rows at full size, plus the index range at any
@@ -88,6 +92,75 @@ def test_assign_parity_shapes(vq, n, in_features, v, bits1, bits2, wd):
         assert np.array_equal(g2, o2)
     else:
         assert g2 is None and o2 is None
+
+
+MFMA_SHAPES = [
+    # fp16 weights, K1 >= 256: n, in_features, v, bits1, bits2
+    (100, 50, 1, 8, 0),
+    (40, 60, 2, 9, 3),
+    (33, 63, 3, 9, 0),
+    (300, 80, 4, 10, 2),      # 6000 vectors: several workgroups of 1024, ragged tail
+    (70, 45, 5, 8, 8),
+    (61, 66, 6, 11, 0),
+    (50, 49, 7, 12, 4),
+    (300, 80, 8, 9, 0),       # 3000 vectors
+    (20, 72, 9, 8, 5),
+    (21, 70, 10, 10, 0),
+    (22, 66, 11, 9, 2),
+    (23, 72, 12, 8, 8),
+    (24, 65, 13, 9, 0),
+    (25, 70, 14, 11, 3),
+    (26, 75, 15, 8, 0),
+    (27, 80, 16, 10, 6),
+    (1, 8, 8, 14, 0),         # one vector, K1 = 16384
+    (1030, 8, 8, 8, 0),       # 1030 vectors: one workgroup plus a 6-vector tail
+]
+
+
+@pytest.mark.parametrize("n,in_features,v,bits1,bits2", MFMA_SHAPES)
+def test_assign_matrix_core_shapes(vq, n, in_features, v, bits1, bits2):
+    p = synth.make_encode_problem(n, in_features, v, bits1, bits2, wid=89)
+    g1, g2 = _gpu_assign(vq, p)
+    o1, o2 = _oracle_assign(p)
+    assert np.array_equal(g1, o1)
+    if bits2:
+        assert np.array_equal(g2, o2)
+
+
+@pytest.mark.parametrize("v", [4, 8, 12])
+def test_assign_subnormal_book(vq, v):
+    """Centroids and weights among the fp16 subnormals (|x| < 2^-14): a matrix core that
+    flushed them would rank by |c|^2 alone and miss the nearest centroids."""
+    g = np.random.default_rng(v)
+    k1 = 512
+    cb1 = g.integers(-1023, 1024, size=(k1, v)).astype(np.uint16)
+    cb1 = np.where(cb1.view(np.int16) < 0, 0x8000 | (-cb1.view(np.int16)).astype(np.uint16), cb1).astype(np.uint16)
+    w16 = cb1[g.integers(0, k1, size=200 * 4)] ^ (g.integers(0, 4, size=(800, v)).astype(np.uint16))
+    p = {"n": 200, "in_features": 4 * v, "v": v, "bits1": 9, "bits2": 0, "w_dtype": "f16",
+         "w": w16.reshape(200, 4 * v), "w_f32": w16.reshape(200, 4 * v).view(np.float16).astype(np.float32),
+         "cb1": cb1, "cb2": None}
+    assert np.all(np.abs(p["w_f32"]) < 2.0 ** -14)
+    g1, _ = _gpu_assign(vq, p)
+    o1, _ = _oracle_assign(p)
+    assert np.array_equal(g1, o1)
+    assert len(np.unique(o1)) > 100
+
+
+@pytest.mark.parametrize("wd", ["f16", "f32"])
+def test_assign_non_finite_values(vq, wd):
+    """Infinite and NaN weights, an infinite centroid: both sides rank the same fp64 values."""
+    p = synth.make_encode_problem(64, 64, 8, 9, 4, wid=88, w_dtype=wd)
+    specials = np.array([np.inf, -np.inf, np.nan], dtype=np.float32)
+    g = np.random.default_rng(2)
+    pos = g.choice(p["w_f32"].size, size=12, replace=False)
+    wf = p["w_f32"].copy().reshape(-1)
+    wf[pos] = specials[np.arange(12) % 3]
+    p["w_f32"] = wf.reshape(p["w_f32"].shape)
+    p["w"] = p["w_f32"].astype(np.float16).view(np.uint16) if wd == "f16" else p["w_f32"]
+    p["cb1"][17, 3] = np.float16(np.inf).view(np.uint16)
+    g1, g2 = _gpu_assign(vq, p)
+    o1, o2 = _oracle_assign(p)
+    assert np.array_equal(g1, o1) and np.array_equal(g2, o2)
 
 
 def test_assign_exact_ties_take_the_lowest_index(vq):

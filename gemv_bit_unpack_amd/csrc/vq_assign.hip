@@ -15,12 +15,15 @@
 // Kernels:
 //   assign_table_kernel  one thread per centroid: the fp64 record {|c|^2, c_0 .. c_{v-1}}
 //                        of each fp16 centroid into the workspace.
-//   assign_kernel<V, R>  one lane per R vectors (consecutive lanes on consecutive vectors),
-//                        the vectors held in fp64 registers; every wave walks the whole
-//                        record table in index order with uniform (scalar-unit) loads, so
-//                        each centroid costs V + 1 fp64 FMAs and one compare per vector,
-//                        and the rare improvements take a branch that the wave skips
-//                        when none of its lanes improves.
+//   assign_mfma_table_kernel, assign_mfma_kernel<V>  the main stage for fp16 weights and
+//                        books of 256 or more centroids on the matrix cores (below).
+//   assign_kernel<V, R, WT, FIRST>  both stages (the residual stage only, after the
+//                        matrix-core pass): one lane per R vectors (consecutive lanes on
+//                        consecutive vectors), the vectors held in fp64 registers; every
+//                        wave walks the whole record table in index order with uniform
+//                        (scalar-unit) loads, so each centroid costs V + 1 fp64 FMAs and
+//                        one compare per vector, and the rare improvements take a branch
+//                        that the wave skips when none of its lanes improves.
 #include "vq_device.h"
 
 namespace {
@@ -142,7 +145,8 @@ __global__ __launch_bounds__(kThreads) void assign_kernel(const void* __restrict
 // ---------------------------------------------------------------------------------------
 // Matrix-core pass for stage 1 with fp16 weights.  The matrix cores form, for 32 centroids
 // x 32 vectors at a time, the fp32 half-distance h = |c|^2 / 2 - w . c
-// (v_mfma_f32_32x32x8_f16 with A = -c, B = w, C = fl32(|c|^2 / 2)).  Each product of two
+// (v_mfma_f32_32x32x16_f16 with A = -c, B = w, C = fl32(|c|^2 / 2), K = 16 holding v <= 16
+// coordinates and zeros).  Each product of two
 // fp16 values is exact in fp32, so h differs from the fp64 ranking above (halved) by at
 // most E = (v + 2) 2^-23 (S_w Cmax + NCmax / 2), with S_w = sum |w_t| and Cmax, NCmax
 // the largest |c_t| and |c|^2 of the book (the sum of v + 1 terms with at most 2^-23
@@ -152,15 +156,16 @@ __global__ __launch_bounds__(kThreads) void assign_kernel(const void* __restrict
 // (tile minimum + delta), delta = 4 (v + 2) 2^-23 (S_w Cmax + NCmax / 2) (twice the bound,
 // which also covers the rounding of thr itself), and ranks in fp64, exactly as above,
 // every centroid with h <= thr; the lowest index of the smallest fp64 distance among them
-// is the answer.  A tile costs one or two MFMAs and eight three-way minima per 32x32
-// block; the fp64 ranking runs only where a tile holds a candidate, which after the first
-// few hundred centroids is rare.  NaN or infinite values make delta infinite: every
-// centroid is then ranked in fp64.
+// is the answer.  A 32x32 block costs one MFMA, eight three-way minima and a compare;
+// the fp64 ranking runs only where a block holds a candidate (a new running minimum or a
+// near tie), about one block in eight for 65536 centroids.  NaN or infinite values make
+// delta infinite: every centroid is then ranked in fp64.  The matrix cores must multiply
+// fp16 subnormals exactly (they do on gfx950; a book of subnormals is among the tests).
 //
 // Work split: 256 threads = 4 wavefronts; a wavefront owns kGroups groups of 32 vectors
 // (B operands in registers for the whole walk); lanes l and l + 32 share vector l % 32
-// (the two K halves of the B operand, and rows 4 .. 7 of every 8 in the output), and
-// combine their results at the end.  The book is staged through LDS in chunks of
+// (coordinates 0 .. 7 and 8 .. 15 of the B operand, and rows 4 .. 7 of every 8 in the
+// output), and combine their results at the end.  The book is staged through LDS in chunks of
 // kChunk centroids, double-buffered, one barrier per chunk.
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));

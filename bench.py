@@ -155,11 +155,12 @@ class Ring:
 class SvqRing:
     """Distinct copies of an affine-lattice layer (own codes and A, B; shared x) for vq_svq_gemv."""
 
-    def __init__(self, vq, torch, key, layer, m, copies=None):
+    def __init__(self, vq, torch, key, layer, m, copies=None, fn="vq_svq_gemv"):
         layers, xd = SVQ_WORKLOADS[key]
         n, i = layers[layer]
         self.desc = vq.svq_desc(n, i)
         self.m = m
+        self.flops_per_call = 2 * m * n * i
         dev = torch.device("cuda")
         nb = vq.packed_bytes(self.desc)
         xdt = torch.bfloat16 if xd == "bf16" else torch.float16
@@ -169,7 +170,8 @@ class SvqRing:
         g.manual_seed(zlib.crc32(("%d/%s/%d/svq" % (42, key, layer)).encode()))
         self.x = torch.randn((m, i), generator=g, device=dev, dtype=torch.float32).to(xdt)
         code = {torch.float16: vq.VQ_F16, torch.bfloat16: vq.VQ_BF16}
-        self.fn = vq.lib().vq_svq_gemv
+        self.name = fn
+        self.fn = getattr(vq.lib(), fn)
         self.items, self.tensors = [], []
         p = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
         for _ in range(self.copies):
@@ -185,7 +187,7 @@ class SvqRing:
     def call(self, k, stream_ptr):
         st = self.fn(*self.items[k % self.copies], stream_ptr)
         if st != 0:
-            raise RuntimeError("vq_svq_gemv failed with status %d" % st)
+            raise RuntimeError("%s failed with status %d" % (self.name, st))
 
 
 def svq_leg(vq, torch, use_graph, steps=None):
@@ -200,6 +202,19 @@ def svq_leg(vq, torch, use_graph, steps=None):
             "workload": SVQ_DESCRIBE[key] + ", M=%d" % m, "us_per_call": round(sec * 1e6, 3),
             "GBps": round(b / sec / 1e9, 1), "pct_hbm": round(100 * b / sec / 1e9 / HBM_PEAK_GBPS, 2),
             "bytes_per_call": int(b), "copies": rings[0].copies, "calls": calls, "launch": launch}
+        del rings
+        torch.cuda.empty_cache()
+    # the matrix-core product: prefill batches, and M = 16 against the VALU kernel above
+    for key, m in (("svq70b", 128), ("svq4k", 16), ("svq70b", 16)):
+        rings = [SvqRing(vq, torch, key, li, m, copies=4, fn="vq_svq_gemm")
+                 for li in range(len(SVQ_WORKLOADS[key][0]))]
+        sec, calls, _, launch = time_ring(torch, rings, 40, 4, use_graph)
+        fl = sum(r.flops_per_call for r in rings) / len(rings)
+        b = sum(r.bytes_per_call for r in rings) / len(rings)
+        out["%s_m%d_gemm" % (key, m)] = {
+            "workload": SVQ_DESCRIBE[key] + ", M=%d, vq_svq_gemm" % m, "us_per_call": round(sec * 1e6, 3),
+            "tflops": round(fl / sec / 1e12, 1), "pct_mfma_peak": round(100 * fl / sec / 1e12 / MFMA_F16_PEAK_TFLOPS, 2),
+            "GBps": round(b / sec / 1e9, 1), "calls": calls, "launch": launch}
         del rings
         torch.cuda.empty_cache()
     return out

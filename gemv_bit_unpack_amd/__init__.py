@@ -42,7 +42,7 @@ LAYOUT_ROWSTREAM = 1
 
 EXPORTED = ("vq_abi_version", "vq_status_string", "vq_packed_bytes", "vq_pack", "vq_dequant", "vq_gemv",
             "vq_gemv_workspace_bytes", "vq_gemv_ws", "vq_gemm", "vq_svq_dequant", "vq_svq_gemv", "vq_rht", "vq_rht_block",
-            "vq_assign_workspace_bytes", "vq_assign")
+            "vq_assign_workspace_bytes", "vq_assign", "vq_svq_gemm")
 
 
 class Desc(ctypes.Structure):
@@ -92,6 +92,8 @@ def _load():
     lib.vq_svq_dequant.restype = ctypes.c_int
     lib.vq_svq_gemv.argtypes = [dp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i32, vp, ctypes.c_int, vp]
     lib.vq_svq_gemv.restype = ctypes.c_int
+    lib.vq_svq_gemm.argtypes = [dp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i32, vp, ctypes.c_int, vp]
+    lib.vq_svq_gemm.restype = ctypes.c_int
     lib.vq_rht.argtypes = [i32, i32, vp, ctypes.c_int, vp, i32, vp, ctypes.c_int, vp]
     lib.vq_rht.restype = ctypes.c_int
     lib.vq_rht_block.argtypes = [i32]
@@ -274,6 +276,15 @@ def svq_dequant(desc: Desc, packed, a, b, scale, w_dtype=None, out=None):
 
 def svq_gemv(desc: Desc, packed, a, b, scale, bias, x, y_dtype=None, out=None):
     """y [M, N] = x W^T (+ bias) of an affine-lattice layer, 1 <= M <= 16."""
+    return _svq_product(lib().vq_svq_gemv, "vq_svq_gemv", desc, packed, a, b, scale, bias, x, y_dtype, out)
+
+
+def svq_gemm(desc: Desc, packed, a, b, scale, bias, x, y_dtype=None, out=None):
+    """y [M, N] = x W^T (+ bias) of an affine-lattice layer on the matrix cores, any M."""
+    return _svq_product(lib().vq_svq_gemm, "vq_svq_gemm", desc, packed, a, b, scale, bias, x, y_dtype, out)
+
+
+def _svq_product(fn, name, desc, packed, a, b, scale, bias, x, y_dtype, out):
     torch = _torch()
     if x.dim() != 2 or x.shape[1] != desc.in_features:
         raise ValueError("x must be [M, %d], got %s" % (desc.in_features, tuple(x.shape)))
@@ -282,11 +293,11 @@ def svq_gemv(desc: Desc, packed, a, b, scale, bias, x, y_dtype=None, out=None):
     if out is None:
         out = torch.empty((m, desc.out_features), dtype=y_dtype, device=x.device)
     f16 = (torch.float16,)
-    st = lib().vq_svq_gemv(ctypes.byref(desc), _dev_ptr(packed, "packed"), _dev_ptr(a, "a", f16),
-                          _dev_ptr(b, "b", f16), _dev_ptr(scale, "scale", f16), _dev_ptr(bias, "bias", f16),
-                          _dev_ptr(x, "x", (torch.float16, torch.bfloat16)), _dtype_code(x.dtype), m,
-                          _dev_ptr(out, "out"), _dtype_code(out.dtype), _stream_ptr(x.device))
-    _check(st, "vq_svq_gemv")
+    st = fn(ctypes.byref(desc), _dev_ptr(packed, "packed"), _dev_ptr(a, "a", f16), _dev_ptr(b, "b", f16),
+            _dev_ptr(scale, "scale", f16), _dev_ptr(bias, "bias", f16),
+            _dev_ptr(x, "x", (torch.float16, torch.bfloat16)), _dtype_code(x.dtype), m, _dev_ptr(out, "out"),
+            _dtype_code(out.dtype), _stream_ptr(x.device))
+    _check(st, name)
     return out
 
 

@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libvq.so")
 CEILINGS_SRC = os.path.join(PKG, "micro", "ceilings.hip")
 CEILINGS_BIN = os.path.join(PKG, "micro", "vq_ceilings")
 SOURCES = ["vq_host.cpp", "vq_dequant.hip", "vq_gemv.hip", "vq_gemv_sliced.hip", "vq_gemm.hip", "vq_svq.hip", "vq_rht.hip",
-           "vq_assign.hip"]
+           "vq_assign.hip", "vq_svq_gemm.hip"]
 ARCH = "gfx950"
 
 COMMON = [

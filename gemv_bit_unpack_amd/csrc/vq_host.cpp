@@ -67,15 +67,15 @@ vq_status prepare_product(const vq_desc* desc, const void* packed, const void* c
 }
 
 // Affine-lattice calls: the descriptor must be the lattice stream (v = 4, bits1 = 8, no
-// residual).  m < 0 marks the dequant (no x, y checked by the caller).
+// residual).  m < 0 marks the dequant (no x, y checked by the caller); max_m > 0 bounds M.
 static vq_status prepare_svq(const vq_desc* desc, const void* packed, const void* a, const void* b,
                              const void* scale, const void* bias, const void* x, vq_dtype x_dtype, int32_t m,
-                             void* y, vq_dtype y_dtype, SvqArgs* p) {
+                             void* y, vq_dtype y_dtype, int32_t max_m, SvqArgs* p) {
   vq_status st = check_desc(desc);
   if (st != VQ_OK) return st;
   const vq_desc& d = *desc;
   if (d.v != 4 || d.bits1 != 8 || d.bits2 != 0) return VQ_ERR_UNSUPPORTED;
-  if (m > 16) return VQ_ERR_SHAPE;
+  if (max_m > 0 && m > max_m) return VQ_ERR_SHAPE;
   if (m >= 0 && !valid_x_dtype(x_dtype)) return VQ_ERR_UNSUPPORTED;
   if (!valid_out_dtype(y_dtype)) return VQ_ERR_UNSUPPORTED;
   std::memset(p, 0, sizeof *p);
@@ -254,7 +254,7 @@ vq_status vq_gemv_ws(const vq_desc* desc, const void* packed, const void* cb1, c
 vq_status vq_svq_dequant(const vq_desc* desc, const void* packed, const void* a, const void* b, const void* scale,
                          void* w, vq_dtype w_dtype, void* stream) {
   SvqArgs p;
-  vq_status st = prepare_svq(desc, packed, a, b, scale, nullptr, nullptr, VQ_F16, -1, w, w_dtype, &p);
+  vq_status st = prepare_svq(desc, packed, a, b, scale, nullptr, nullptr, VQ_F16, -1, w, w_dtype, 0, &p);
   if (st != VQ_OK) return st;
   if (p.n == 0 || p.in_features == 0) return VQ_OK;
   return launch_svq_dequant(p, w, w_dtype, stream);
@@ -265,10 +265,22 @@ vq_status vq_svq_gemv(const vq_desc* desc, const void* packed, const void* a, co
                       void* stream) {
   if (M < 0) return VQ_ERR_SHAPE;
   SvqArgs p;
-  vq_status st = prepare_svq(desc, packed, a, b, scale, bias, x, x_dtype, M, y, y_dtype, &p);
+  vq_status st = prepare_svq(desc, packed, a, b, scale, bias, x, x_dtype, M, y, y_dtype, 16, &p);
   if (st != VQ_OK) return st;
   if (p.n == 0 || p.m == 0) return VQ_OK;
   return launch_svq_gemv(p, stream);
+}
+
+vq_status vq_svq_gemm(const vq_desc* desc, const void* packed, const void* a, const void* b, const void* scale,
+                      const void* bias, const void* x, vq_dtype x_dtype, int32_t M, void* y, vq_dtype y_dtype,
+                      void* stream) {
+  if (M < 0) return VQ_ERR_SHAPE;
+  if (M > 0 && (int64_t)(M + 255) / 256 > 65535) return VQ_ERR_SHAPE;  // grid rows of 256-row batch chunks
+  SvqArgs p;
+  vq_status st = prepare_svq(desc, packed, a, b, scale, bias, x, x_dtype, M, y, y_dtype, 0, &p);
+  if (st != VQ_OK) return st;
+  if (p.n == 0 || p.m == 0) return VQ_OK;
+  return launch_svq_gemm(p, stream);
 }
 
 int32_t vq_rht_block(int32_t n) { return rht_block(n); }

@@ -81,6 +81,7 @@ struct SvqArgs {
   int32_t x_vec4;  // IN % 4 == 0 and x 8-byte aligned: x read one 4-vector per load
 };
 vq_status launch_svq_gemv(const SvqArgs& p, void* stream);
+vq_status launch_svq_gemm(const SvqArgs& p, void* stream);
 // Randomized Hadamard transform (validated arguments; n a multiple of 16, m >= 1).
 int32_t rht_block(int32_t n);
 vq_status launch_rht(int32_t m, int32_t n, const void* x, vq_dtype x_dtype, const uint8_t* signs, int32_t transpose,

@@ -1,0 +1,203 @@
+// vq_svq_gemm: prefill-batch product of an affine-lattice layer (UniSVQ summary,
+// "Mathematical Formulation"; the prefill regime of the production-VQ post, "Prefill vs.
+// Decode Bottlenecks"), y[M][N] = x[M][IN] * W^T (+ bias) with
+//
+//   W^[o, 4j + t] = scale[o] * fp32(B[t] + sum_u A[t][u] * q_u(o, j)),
+//
+// on the matrix cores.  A lattice vector is one code byte, so the layer's weights take at
+// most 256 distinct 4-vectors: each workgroup first writes that table (byte -> the four
+// weights in the activation's 16-bit type; bf16 activations get a hi + lo pair,
+// hi = RNE(w), lo = RNE(w - hi), ~16 significant bits of w) into LDS, and the MFMA
+// A fragments are then read from it directly, two table entries per fragment, with no
+// weight tile at all.  Work split: a workgroup owns 128 output rows (wavefront w the 32
+// rows 32w .. 32w + 31) and a chunk of 32 * MB batch rows; per K-tile of 64 columns
+// (16 lattice vectors per row) each lane holds its row's 16 code bytes, the x tile
+// [32 * MB][64] sits in LDS (double-buffered), and each wavefront runs 4 x MB
+// v_mfma_f32_32x32x16 (twice for bf16) into fp32 accumulators.  The next tile's codes and
+// x are loaded into registers while the current tile is multiplied.  Columns past IN
+// meet zero activations, so the padding codes of the last tile contribute nothing.  The
+// channel scale and bias are applied once per output in the epilogue.
+#include "vq_device.h"
+
+namespace {
+
+using vqi::SvqArgs;
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kThreads = 256;    // 4 wavefronts
+constexpr int kBN = 128;         // output rows per workgroup (32 per wavefront)
+constexpr int kBK = 64;          // K-tile width in columns (16 lattice vectors)
+constexpr int kLd = kBK + 8;     // LDS row stride of the x tile in halves (16 bytes of padding)
+
+template <int XT>
+__device__ __forceinline__ void build_table(const SvqArgs& p, uint4* lut) {
+  // entry e: the four weights of code byte e (table of 16-byte entries: fp16 uses the
+  // first 8 bytes, bf16 holds hi in the first 8 and lo in the last 8)
+  const int e = threadIdx.x;  // kThreads == 256 entries
+  uint16_t hv[4], lv[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    float w = vqd::f16_to_f32(p.b[t]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) w = fmaf(vqd::f16_to_f32(p.a[t * 4 + u]), (float)((e >> (2 * u)) & 3), w);
+    if constexpr (XT == 0) {
+      hv[t] = vqd::f32_to_f16_rne(w);
+      lv[t] = 0;
+    } else {
+      hv[t] = vqd::f32_to_bf16_rne(w);
+      lv[t] = vqd::f32_to_bf16_rne(w - vqd::bf16_to_f32(hv[t]));
+    }
+  }
+  lut[e] = make_uint4(hv[0] | ((uint32_t)hv[1] << 16), hv[2] | ((uint32_t)hv[3] << 16),
+                      lv[0] | ((uint32_t)lv[1] << 16), lv[2] | ((uint32_t)lv[3] << 16));
+}
+
+template <int MB>
+__device__ __forceinline__ void load_x(const SvqArgs& p, int m0, int k0, bool x_vec, uint4 (&xr)[MB]) {
+  // 32 * MB rows x 8 chunks of 8 columns; thread t takes chunks t, t + 256, ...
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int ch = threadIdx.x + i * kThreads;
+    const int m = m0 + (ch >> 3);
+    const int k = k0 + (ch & 7) * 8;
+    uint4 q = make_uint4(0u, 0u, 0u, 0u);
+    if (m < p.m) {
+      const uint16_t* row = p.x + (size_t)m * p.in_features;
+      if (x_vec && k + 8 <= p.in_features) {
+        q = *(const uint4*)(row + k);
+      } else {
+        uint16_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) h[e] = (k + e < p.in_features) ? row[k + e] : (uint16_t)0;
+        q.x = h[0] | ((uint32_t)h[1] << 16);
+        q.y = h[2] | ((uint32_t)h[3] << 16);
+        q.z = h[4] | ((uint32_t)h[5] << 16);
+        q.w = h[6] | ((uint32_t)h[7] << 16);
+      }
+    }
+    xr[i] = q;
+  }
+}
+
+template <int MB>
+__device__ __forceinline__ void store_x(uint16_t* xt, const uint4 (&xr)[MB]) {
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int ch = threadIdx.x + i * kThreads;
+    *(uint4*)(xt + (ch >> 3) * kLd + (ch & 7) * 8) = xr[i];
+  }
+}
+
+template <int MB, int XT>  // XT: 0 fp16 activations, 1 bf16
+__global__ __launch_bounds__(kThreads) void svq_gemm_kernel(SvqArgs p) {
+  __shared__ uint4 lut[256];
+  __shared__ __attribute__((aligned(16))) uint16_t xt[2][32 * MB * kLd];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int ar = lane & 31;     // A row / B column of this lane
+  const int kh = lane >> 5;     // which 8 of the 16 k of a step
+  const int m0 = blockIdx.y * 32 * MB;
+  const int row = blockIdx.x * kBN + wave * 32 + ar;
+  const int nkt = (p.in_features + kBK - 1) / kBK;
+  const bool x_vec = p.in_features % 8 == 0 && ((uintptr_t)p.x & 15) == 0;
+
+  float16_t acc[MB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
+
+  if (nkt > 0) {
+    build_table<XT>(p, lut);
+    const uint8_t* crow = p.packed + (size_t)min(row, p.n - 1) * p.stride;  // rows past N read a copy
+    uint4 code = *(const uint4*)crow;  // 16 code bytes of K-tile 0
+    uint4 xr[MB];
+    load_x<MB>(p, m0, 0, x_vec, xr);
+    store_x<MB>(xt[0], xr);
+    __syncthreads();
+    for (int kt = 0; kt < nkt; ++kt) {
+      const int buf = kt & 1;
+      // next tile into registers while this one is multiplied
+      const int nt = min(kt + 1, nkt - 1);
+      const uint4 ncode = *(const uint4*)(crow + 16 * nt);
+      load_x<MB>(p, m0, nt * kBK, x_vec, xr);
+      const uint32_t cw[4] = {code.x, code.y, code.z, code.w};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        // this lane's 8 k of step ks: lattice vectors 4 ks + 2 kh and + 1 of its row
+        const uint32_t pair = cw[ks] >> (16 * kh);
+        const uint4 e0 = lut[pair & 0xFFu];
+        const uint4 e1 = lut[(pair >> 8) & 0xFFu];
+        const uint4 ahi = make_uint4(e0.x, e0.y, e1.x, e1.y);
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+          const uint4 bw = *(const uint4*)(xt[buf] + (i * 32 + ar) * kLd + ks * 16 + kh * 8);
+          if constexpr (XT == 0) {
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, ahi),
+                                                            __builtin_bit_cast(half8_t, bw), acc[i], 0, 0, 0);
+          } else {
+            const uint4 alo = make_uint4(e0.z, e0.w, e1.z, e1.w);
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ahi),
+                                                             __builtin_bit_cast(bf16x8_t, bw), acc[i], 0, 0, 0);
+            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, alo),
+                                                             __builtin_bit_cast(bf16x8_t, bw), acc[i], 0, 0, 0);
+          }
+        }
+      }
+      store_x<MB>(xt[buf ^ 1], xr);  // the other buffer: last read before the previous barrier
+      code = ncode;
+      __syncthreads();
+    }
+  }
+  // Epilogue: accumulator register r of lane l holds output row 8*(r/4) + 4*(l/32) + r%4
+  // of the wavefront's 32 and batch row l%32 of block i.
+  const int rbase = blockIdx.x * kBN + wave * 32;
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int m = m0 + i * 32 + ar;
+    if (m >= p.m) continue;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int n = rbase + 8 * (r >> 2) + 4 * kh + (r & 3);
+      if (n < p.n) {
+        float out = acc[i][r];
+        if (p.scale) out = out * vqd::f16_to_f32(p.scale[n]);
+        if (p.bias) out = out + vqd::f16_to_f32(p.bias[n]);
+        vqd::store_out(p.y, (size_t)m * p.n + n, out, p.y_dtype);
+      }
+    }
+  }
+}
+
+template <int MB>
+void launch_mb(const SvqArgs& p, hipStream_t s) {
+  const int chunk = 32 * MB;
+  const dim3 grid((unsigned)((p.n + kBN - 1) / kBN), (unsigned)((p.m + chunk - 1) / chunk));
+  if (p.x_dtype == VQ_BF16) {
+    hipLaunchKernelGGL((svq_gemm_kernel<MB, 1>), grid, dim3(kThreads), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((svq_gemm_kernel<MB, 0>), grid, dim3(kThreads), 0, s, p);
+  }
+}
+
+}  // namespace
+
+namespace vqi {
+
+vq_status launch_svq_gemm(const SvqArgs& p, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  // batch chunk: up to 128 rows per workgroup, fewer when the batch is small
+  if (p.m <= 32) {
+    launch_mb<1>(p, s);
+  } else if (p.m <= 64) {
+    launch_mb<2>(p, s);
+  } else {
+    launch_mb<4>(p, s);
+  }
+  return hipGetLastError() == hipSuccess ? VQ_OK : VQ_ERR_HIP;
+}
+
+}  // namespace vqi

@@ -186,6 +186,14 @@ vq_status vq_svq_gemv(const vq_desc* desc, const void* packed, const void* a, co
                       const void* bias, const void* x, vq_dtype x_dtype, int32_t M, void* y, vq_dtype y_dtype,
                       void* stream);
 
+/* Same operation, arguments and tolerance as vq_svq_gemv for any M >= 1 (M = 0: no-op;
+ * M up to 256 * 65535), on the matrix cores: the layer is rebuilt tile by tile into LDS
+ * in the activation's 16-bit type (bf16: a hi + lo pair) and multiplied with MFMA, fp32
+ * accumulation.  Meant for prefill batches (M >= 32). */
+vq_status vq_svq_gemm(const vq_desc* desc, const void* packed, const void* a, const void* b, const void* scale,
+                      const void* bias, const void* x, vq_dtype x_dtype, int32_t M, void* y, vq_dtype y_dtype,
+                      void* stream);
+
 /*
  * Randomized Walsh-Hadamard transform of activations, the incoherence step that runs
  * ahead of (and, transposed, after) a product with incoherence-processed weights

@@ -221,9 +221,9 @@ def test_gemv_ws_validation_paths(vq):
     assert _gemv_ws(vq, d, ws=P, ws_bytes=0, m=0, y=None, x=None, packed=None) == vq.VQ_OK
 
 
-def _svq(vq, desc, packed=P, a=P, b=P, scale=None, bias=None, x=P, xt=0, m=1, y=P, yt=2):
-    return vq.lib().vq_svq_gemv(ctypes.byref(desc) if desc is not None else None, packed, a, b, scale, bias, x, xt,
-                                m, y, yt, None)
+def _svq(vq, desc, packed=P, a=P, b=P, scale=None, bias=None, x=P, xt=0, m=1, y=P, yt=2, fn=None):
+    fn = fn or vq.lib().vq_svq_gemv
+    return fn(ctypes.byref(desc) if desc is not None else None, packed, a, b, scale, bias, x, xt, m, y, yt, None)
 
 
 def test_svq_gemv_validation_paths(vq):
@@ -249,6 +249,24 @@ def test_svq_gemv_validation_paths(vq):
     # nothing to do
     assert _svq(vq, d, m=0, y=None, x=None, packed=None, a=None, b=None) == vq.VQ_OK
     assert _svq(vq, vq.svq_desc(0, 64), y=None, x=None, packed=None) == vq.VQ_OK
+
+
+def test_svq_gemm_validation_paths(vq):
+    """vq_svq_gemm takes any M >= 0 and otherwise validates like vq_svq_gemv."""
+    g = lambda desc, **kw: _svq(vq, desc, **kw, fn=vq.lib().vq_svq_gemm)
+    d = vq.svq_desc(64, 64)
+    assert g(None) == vq.VQ_ERR_NULL
+    assert g(vq.make_desc(64, 64, 8, 8, 0)) == vq.VQ_ERR_UNSUPPORTED
+    assert g(d, m=-1) == vq.VQ_ERR_SHAPE
+    assert g(d, m=256 * 65535 + 1) == vq.VQ_ERR_SHAPE
+    assert g(d, xt=2) == vq.VQ_ERR_UNSUPPORTED
+    assert g(d, yt=7) == vq.VQ_ERR_UNSUPPORTED
+    assert g(d, m=17, y=None) == vq.VQ_ERR_NULL   # M > 16 passes the shape check
+    assert g(d, m=300, x=None) == vq.VQ_ERR_NULL
+    assert g(d, a=None) == vq.VQ_ERR_NULL
+    assert g(d, packed=ctypes.c_void_p(0x10008)) == vq.VQ_ERR_ALIGN
+    assert g(d, y=P_MIS, yt=2) == vq.VQ_ERR_ALIGN
+    assert g(d, m=0, y=None, x=None, packed=None, a=None, b=None) == vq.VQ_OK
 
 
 def test_svq_dequant_validation_paths(vq):

@@ -11,6 +11,9 @@ C ABI.
   activations resident in LDS with one or two rows per wavefront, or walked in slices);
   the workloads (4096^2 at M = 1, 4, 16; the 70B-class pair at M = 1, 8) on sampled rows
   at full size;
+- the matrix-core product (vq_svq_gemm) for any M: ragged shapes, M from 1 to 300 (more
+  than one batch chunk), every output dtype, fp16 and bf16 activations, IN = 0, the
+  workloads at prefill batches on sampled rows;
 - dyadic grids with one-hot activations reproduce columns of W^ bit-exactly;
 - determinism and replays of a captured graph.
 Tolerance: max |y - y64| <= 2e-3 * ||y64||_inf with fp32 outputs, plus half an output
@@ -55,6 +58,9 @@ class SvqLayer:
 
     def gemv(self, vq, x, y_dtype=None):
         return vq.svq_gemv(self.desc, self.packed, self.a, self.b, self.scale, self.bias, x, y_dtype=y_dtype)
+
+    def gemm(self, vq, x, y_dtype=None):
+        return vq.svq_gemm(self.desc, self.packed, self.a, self.b, self.scale, self.bias, x, y_dtype=y_dtype)
 
     def dequant(self, vq, w_dtype):
         return vq.svq_dequant(self.desc, self.packed, self.a, self.b, self.scale, w_dtype=w_dtype)
@@ -134,6 +140,42 @@ def test_svq_gemv_parity_shapes(vq, n, in_features, m, xd, yt, with_scale, with_
     check_y(y, _oracle_y(lay, x_bits, xd), yt)
 
 
+GEMM_SHAPES = [
+    # n, in_features, M, x dtype, y dtype, scale, bias
+    (1, 4, 1, "f16", "f32", False, False),
+    (7, 13, 3, "bf16", "f16", True, True),
+    (33, 100, 17, "f16", "f32", True, False),
+    (65, 4100, 40, "bf16", "bf16", False, True),
+    (130, 127, 64, "f16", "f32", True, True),
+    (300, 1000, 100, "bf16", "f32", True, False),
+    (97, 2000, 129, "f16", "f16", False, True),
+    (40, 64, 300, "bf16", "f32", True, True),      # two 256-row batch chunks
+    (1000, 4096, 16, "f16", "f32", True, False),
+]
+
+
+@pytest.mark.parametrize("n,in_features,m,xd,yt,with_scale,with_bias", GEMM_SHAPES)
+def test_svq_gemm_parity_shapes(vq, n, in_features, m, xd, yt, with_scale, with_bias):
+    lay = synth.make_svq_layer(n, in_features, with_scale=with_scale, with_bias=with_bias)
+    dl = SvqLayer(vq, lay)
+    x_bits = synth.activations(np.random.default_rng(n * 17 + m), m, in_features, xd)
+    y = dl.gemm(vq, x_tensor(x_bits, xd), y_dtype=_tdtype(yt))
+    torch.cuda.synchronize()
+    check_y(y, _oracle_y(lay, x_bits, xd), yt)
+
+
+def test_svq_gemm_empty_inner_dimension_gives_bias(vq):
+    lay = synth.make_svq_layer(50, 0, with_scale=True, with_bias=True)
+    desc = vq.svq_desc(50, 0)
+    x = torch.zeros((40, 0), dtype=torch.float16, device="cuda")
+    bias = f16_tensor(lay["bias"])
+    y = vq.svq_gemm(desc, torch.zeros(16, dtype=torch.uint8, device="cuda"), None, None, None, bias, x,
+                    y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    want = lay["bias"].view(np.float16).astype(np.float32)
+    assert np.array_equal(y.cpu().numpy(), np.broadcast_to(want, (40, 50)))
+
+
 @functools.lru_cache(maxsize=2)
 def _svq_workload(key, layer):
     import gemv_bit_unpack_amd as g
@@ -152,6 +194,17 @@ def test_svq_gemv_workloads_sampled(vq, key, layer, m):
     x_bits = synth.svq_workload_x(key, layer, m)
     y = dl.gemv(vq, x_tensor(x_bits, xd), y_dtype=torch.float32).cpu().numpy()
     rows = sample_rows(lay["n"], 48, seed=layer + 7 * m)
+    y64 = _oracle_y(lay, x_bits, xd, rows=rows)
+    check_y(y[:, rows], y64, "f32")
+
+
+@pytest.mark.parametrize("key,layer,m", [("svq4k", 0, 64), ("svq70b", 0, 128), ("svq70b", 1, 128)])
+def test_svq_gemm_workloads_sampled(vq, key, layer, m):
+    lay, dl = _svq_workload(key, layer)
+    xd = synth.SVQ_WORKLOADS[key].x_dtype
+    x_bits = synth.activations(np.random.default_rng(1000 + layer + m), m, lay["in_features"], xd)
+    y = dl.gemm(vq, x_tensor(x_bits, xd), y_dtype=torch.float32).cpu().numpy()
+    rows = sample_rows(lay["n"], 24, seed=layer + 3 * m)
     y64 = _oracle_y(lay, x_bits, xd, rows=rows)
     check_y(y[:, rows], y64, "f32")
 

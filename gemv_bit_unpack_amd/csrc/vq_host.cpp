@@ -275,7 +275,7 @@ vq_status vq_svq_gemm(const vq_desc* desc, const void* packed, const void* a, co
                       const void* bias, const void* x, vq_dtype x_dtype, int32_t M, void* y, vq_dtype y_dtype,
                       void* stream) {
   if (M < 0) return VQ_ERR_SHAPE;
-  if (M > 0 && (int64_t)(M + 255) / 256 > 65535) return VQ_ERR_SHAPE;  // grid rows of 256-row batch chunks
+  if (M > 0 && ((int64_t)M + 127) / 128 > 65535) return VQ_ERR_SHAPE;  // grid rows of 128-row batch chunks
   SvqArgs p;
   vq_status st = prepare_svq(desc, packed, a, b, scale, bias, x, x_dtype, M, y, y_dtype, 0, &p);
   if (st != VQ_OK) return st;

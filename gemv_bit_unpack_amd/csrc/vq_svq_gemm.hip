@@ -189,13 +189,20 @@ namespace vqi {
 
 vq_status launch_svq_gemm(const SvqArgs& p, void* stream) {
   hipStream_t s = (hipStream_t)stream;
-  // batch chunk: up to 128 rows per workgroup, fewer when the batch is small
-  if (p.m <= 32) {
-    launch_mb<1>(p, s);
-  } else if (p.m <= 64) {
+  // batch chunk: the largest of 128 / 64 / 32 rows that still gives at least 384 workgroups
+  // (1.5 per CU); layers with few rows take 32-row chunks and read their codes once per
+  // chunk.  (70B-class pair, M = 128: 64-row chunks for the 28672-row layer, 139 us
+  // against 174 us with 128-row chunks; 32-row chunks for the 8192-row layer, 240 us
+  // against 495 us.)
+  const int64_t row_blocks = (p.n + kBN - 1) / kBN;
+  auto wgs = [&](int mb) { return row_blocks * ((p.m + 32 * mb - 1) / (32 * mb)); };
+  const bool tall = (p.m + 31) / 32 > 65535;  // too many 32-row chunks for the grid: 128-row ones
+  if (tall || (p.m > 64 && wgs(4) >= 384)) {
+    launch_mb<4>(p, s);
+  } else if (p.m > 32 && (wgs(2) >= 384 || (p.m + 31) / 32 > 65535)) {
     launch_mb<2>(p, s);
   } else {
-    launch_mb<4>(p, s);
+    launch_mb<1>(p, s);
   }
   return hipGetLastError() == hipSuccess ? VQ_OK : VQ_ERR_HIP;
 }

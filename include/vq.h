@@ -187,7 +187,7 @@ vq_status vq_svq_gemv(const vq_desc* desc, const void* packed, const void* a, co
                       void* stream);
 
 /* Same operation, arguments and tolerance as vq_svq_gemv for any M >= 1 (M = 0: no-op;
- * M up to 256 * 65535), on the matrix cores: the layer is rebuilt tile by tile into LDS
+ * M up to 128 * 65535), on the matrix cores: the layer is rebuilt tile by tile into LDS
  * in the activation's 16-bit type (bf16: a hi + lo pair) and multiplied with MFMA, fp32
  * accumulation.  Meant for prefill batches (M >= 32). */
 vq_status vq_svq_gemm(const vq_desc* desc, const void* packed, const void* a, const void* b, const void* scale,

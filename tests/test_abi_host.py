@@ -258,7 +258,7 @@ def test_svq_gemm_validation_paths(vq):
     assert g(None) == vq.VQ_ERR_NULL
     assert g(vq.make_desc(64, 64, 8, 8, 0)) == vq.VQ_ERR_UNSUPPORTED
     assert g(d, m=-1) == vq.VQ_ERR_SHAPE
-    assert g(d, m=256 * 65535 + 1) == vq.VQ_ERR_SHAPE
+    assert g(d, m=128 * 65535 + 1) == vq.VQ_ERR_SHAPE
     assert g(d, xt=2) == vq.VQ_ERR_UNSUPPORTED
     assert g(d, yt=7) == vq.VQ_ERR_UNSUPPORTED
     assert g(d, m=17, y=None) == vq.VQ_ERR_NULL   # M > 16 passes the shape check

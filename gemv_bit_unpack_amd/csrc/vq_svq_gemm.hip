@@ -27,7 +27,8 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kThreads = 256;    // 4 wavefronts
+constexpr int kThreads = 256;    // 4 wavefronts per K-stream
+constexpr int kNumCUs = 256;
 constexpr int kBN = 128;         // output rows per workgroup (32 per wavefront)
 constexpr int kBK = 64;          // K-tile width in columns (16 lattice vectors)
 constexpr int kLd = kBK + 8;     // LDS row stride of the x tile in halves (16 bytes of padding)
@@ -36,7 +37,7 @@ template <int XT>
 __device__ __forceinline__ void build_table(const SvqArgs& p, uint4* lut) {
   // entry e: the four weights of code byte e (table of 16-byte entries: fp16 uses the
   // first 8 bytes, bf16 holds hi in the first 8 and lo in the last 8)
-  const int e = threadIdx.x;  // kThreads == 256 entries
+  const int e = threadIdx.x;  // the first 256 threads, one entry each
   uint16_t hv[4], lv[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -56,11 +57,11 @@ __device__ __forceinline__ void build_table(const SvqArgs& p, uint4* lut) {
 }
 
 template <int MB>
-__device__ __forceinline__ void load_x(const SvqArgs& p, int m0, int k0, bool x_vec, uint4 (&xr)[MB]) {
-  // 32 * MB rows x 8 chunks of 8 columns; thread t takes chunks t, t + 256, ...
+__device__ __forceinline__ void load_x(const SvqArgs& p, int m0, int k0, bool x_vec, int tg, uint4 (&xr)[MB]) {
+  // 32 * MB rows x 8 chunks of 8 columns; thread tg of the group takes chunks tg, tg + 256, ...
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
-    const int ch = threadIdx.x + i * kThreads;
+    const int ch = tg + i * kThreads;
     const int m = m0 + (ch >> 3);
     const int k = k0 + (ch & 7) * 8;
     uint4 q = make_uint4(0u, 0u, 0u, 0u);
@@ -83,25 +84,32 @@ __device__ __forceinline__ void load_x(const SvqArgs& p, int m0, int k0, bool x_
 }
 
 template <int MB>
-__device__ __forceinline__ void store_x(uint16_t* xt, const uint4 (&xr)[MB]) {
+__device__ __forceinline__ void store_x(uint16_t* xt, int tg, const uint4 (&xr)[MB]) {
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
-    const int ch = threadIdx.x + i * kThreads;
+    const int ch = tg + i * kThreads;
     *(uint4*)(xt + (ch >> 3) * kLd + (ch & 7) * 8) = xr[i];
   }
 }
 
-template <int MB, int XT>  // XT: 0 fp16 activations, 1 bf16
-__global__ __launch_bounds__(kThreads) void svq_gemm_kernel(SvqArgs p) {
+// KS K-streams per workgroup (1 or 2): stream g = threads 256 g .. 256 g + 255 takes the
+// K-tiles g, g + KS, ... with its own x buffers; stream 1 hands its sums to stream 0
+// through LDS at the end.  Two streams serve layers with fewer row blocks than CUs.
+template <int MB, int XT, int KS>  // XT: 0 fp16 activations, 1 bf16
+__global__ __launch_bounds__(kThreads * KS) void svq_gemm_kernel(SvqArgs p) {
   __shared__ uint4 lut[256];
-  __shared__ __attribute__((aligned(16))) uint16_t xt[2][32 * MB * kLd];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  __shared__ __attribute__((aligned(16))) uint16_t xt[KS][2][32 * MB * kLd];
+  static_assert(KS == 1 || sizeof(xt) >= 4 * MB * 16 * 64 * sizeof(float), "reduction area");
+  const int tg = threadIdx.x & (kThreads - 1);  // thread within its stream
+  const int grp = threadIdx.x / kThreads;       // K-stream
+  const int lane = tg & 63;
+  const int wave = tg >> 6;     // row block of the stream: rows 32 wave .. + 31
   const int ar = lane & 31;     // A row / B column of this lane
   const int kh = lane >> 5;     // which 8 of the 16 k of a step
   const int m0 = blockIdx.y * 32 * MB;
   const int row = blockIdx.x * kBN + wave * 32 + ar;
   const int nkt = (p.in_features + kBK - 1) / kBK;
+  const int nit = (nkt + KS - 1) / KS;  // iterations, the same for every stream
   const bool x_vec = p.in_features % 8 == 0 && ((uintptr_t)p.x & 15) == 0;
 
   float16_t acc[MB];
@@ -111,47 +119,69 @@ __global__ __launch_bounds__(kThreads) void svq_gemm_kernel(SvqArgs p) {
     for (int r = 0; r < 16; ++r) acc[i][r] = 0.0f;
 
   if (nkt > 0) {
-    build_table<XT>(p, lut);
+    if (threadIdx.x < 256) build_table<XT>(p, lut);
     const uint8_t* crow = p.packed + (size_t)min(row, p.n - 1) * p.stride;  // rows past N read a copy
-    uint4 code = *(const uint4*)crow;  // 16 code bytes of K-tile 0
+    const int kt0 = min(grp, nkt - 1);
+    uint4 code = *(const uint4*)(crow + 16 * kt0);  // 16 code bytes of the stream's first K-tile
     uint4 xr[MB];
-    load_x<MB>(p, m0, 0, x_vec, xr);
-    store_x<MB>(xt[0], xr);
+    load_x<MB>(p, m0, kt0 * kBK, x_vec, tg, xr);
+    store_x<MB>(xt[grp][0], tg, xr);
     __syncthreads();
-    for (int kt = 0; kt < nkt; ++kt) {
-      const int buf = kt & 1;
-      // next tile into registers while this one is multiplied
-      const int nt = min(kt + 1, nkt - 1);
+    for (int it = 0; it < nit; ++it) {
+      const int buf = it & 1;
+      const int kt = it * KS + grp;
+      // next tile of this stream into registers while this one is multiplied
+      const int nt = min(kt + KS, nkt - 1);
       const uint4 ncode = *(const uint4*)(crow + 16 * nt);
-      load_x<MB>(p, m0, nt * kBK, x_vec, xr);
-      const uint32_t cw[4] = {code.x, code.y, code.z, code.w};
+      load_x<MB>(p, m0, nt * kBK, x_vec, tg, xr);
+      if (KS == 1 || kt < nkt) {
+        const uint32_t cw[4] = {code.x, code.y, code.z, code.w};
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        // this lane's 8 k of step ks: lattice vectors 4 ks + 2 kh and + 1 of its row
-        const uint32_t pair = cw[ks] >> (16 * kh);
-        const uint4 e0 = lut[pair & 0xFFu];
-        const uint4 e1 = lut[(pair >> 8) & 0xFFu];
-        const uint4 ahi = make_uint4(e0.x, e0.y, e1.x, e1.y);
+        for (int ks = 0; ks < 4; ++ks) {
+          // this lane's 8 k of step ks: lattice vectors 4 ks + 2 kh and + 1 of its row
+          const uint32_t pair = cw[ks] >> (16 * kh);
+          const uint4 e0 = lut[pair & 0xFFu];
+          const uint4 e1 = lut[(pair >> 8) & 0xFFu];
+          const uint4 ahi = make_uint4(e0.x, e0.y, e1.x, e1.y);
 #pragma unroll
-        for (int i = 0; i < MB; ++i) {
-          const uint4 bw = *(const uint4*)(xt[buf] + (i * 32 + ar) * kLd + ks * 16 + kh * 8);
-          if constexpr (XT == 0) {
-            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, ahi),
-                                                            __builtin_bit_cast(half8_t, bw), acc[i], 0, 0, 0);
-          } else {
-            const uint4 alo = make_uint4(e0.z, e0.w, e1.z, e1.w);
-            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ahi),
-                                                             __builtin_bit_cast(bf16x8_t, bw), acc[i], 0, 0, 0);
-            acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, alo),
-                                                             __builtin_bit_cast(bf16x8_t, bw), acc[i], 0, 0, 0);
+          for (int i = 0; i < MB; ++i) {
+            const uint4 bw = *(const uint4*)(xt[grp][buf] + (i * 32 + ar) * kLd + ks * 16 + kh * 8);
+            if constexpr (XT == 0) {
+              acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, ahi),
+                                                              __builtin_bit_cast(half8_t, bw), acc[i], 0, 0, 0);
+            } else {
+              const uint4 alo = make_uint4(e0.z, e0.w, e1.z, e1.w);
+              acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ahi),
+                                                               __builtin_bit_cast(bf16x8_t, bw), acc[i], 0, 0, 0);
+              acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, alo),
+                                                               __builtin_bit_cast(bf16x8_t, bw), acc[i], 0, 0, 0);
+            }
           }
         }
       }
-      store_x<MB>(xt[buf ^ 1], xr);  // the other buffer: last read before the previous barrier
+      store_x<MB>(xt[grp][buf ^ 1], tg, xr);  // the other buffer: last read before the previous barrier
       code = ncode;
       __syncthreads();
     }
+    if constexpr (KS == 2) {
+      // stream 1 hands its sums to stream 0 (the x buffers are free after the last barrier)
+      float* red = (float*)&xt[0][0][0];
+      if (grp == 1) {
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) red[((wave * MB + i) * 16 + r) * 64 + lane] = acc[i][r];
+      }
+      __syncthreads();
+      if (grp == 0) {
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][r] += red[((wave * MB + i) * 16 + r) * 64 + lane];
+      }
+    }
   }
+  if (grp != 0) return;
   // Epilogue: accumulator register r of lane l holds output row 8*(r/4) + 4*(l/32) + r%4
   // of the wavefront's 32 and batch row l%32 of block i.
   const int rbase = blockIdx.x * kBN + wave * 32;
@@ -176,10 +206,21 @@ template <int MB>
 void launch_mb(const SvqArgs& p, hipStream_t s) {
   const int chunk = 32 * MB;
   const dim3 grid((unsigned)((p.n + kBN - 1) / kBN), (unsigned)((p.m + chunk - 1) / chunk));
+  // fewer than two workgroups per CU: two K-streams per workgroup (70B-class pair, M = 128:
+  // 128 / 184 us for the 28672- / 8192-row layers, against 143 / 236 us with one stream)
+  const bool ks2 = (int64_t)grid.x * grid.y < 2 * kNumCUs && p.in_features > kBK;
   if (p.x_dtype == VQ_BF16) {
-    hipLaunchKernelGGL((svq_gemm_kernel<MB, 1>), grid, dim3(kThreads), 0, s, p);
+    if (ks2) {
+      hipLaunchKernelGGL((svq_gemm_kernel<MB, 1, 2>), grid, dim3(2 * kThreads), 0, s, p);
+    } else {
+      hipLaunchKernelGGL((svq_gemm_kernel<MB, 1, 1>), grid, dim3(kThreads), 0, s, p);
+    }
   } else {
-    hipLaunchKernelGGL((svq_gemm_kernel<MB, 0>), grid, dim3(kThreads), 0, s, p);
+    if (ks2) {
+      hipLaunchKernelGGL((svq_gemm_kernel<MB, 0, 2>), grid, dim3(2 * kThreads), 0, s, p);
+    } else {
+      hipLaunchKernelGGL((svq_gemm_kernel<MB, 0, 1>), grid, dim3(kThreads), 0, s, p);
+    }
   }
 }
 

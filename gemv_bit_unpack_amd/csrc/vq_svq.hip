@@ -553,11 +553,11 @@ vq_status launch_x(const SvqArgs& p, hipStream_t s) {
 namespace vqi {
 
 vq_status launch_svq_gemv(const SvqArgs& p, void* stream) {
-  // From M = 12 (from M = 4 on layers of 12288 rows or more) the matrix-core kernel of
-  // vq_svq_gemm is faster: its cost hardly grows with M, the VALU kernels' grows linearly
-  // (4096^2 at M = 16: 19.7 against 29.4 us; 28672 x 8192 at M = 4: 45 against 73 us;
-  // 8192 x 28672 at M = 8: 135 against 98 us, so it stays here).
-  if (p.in_features > 0 && (p.m >= 12 || (p.m >= 4 && p.n >= 12288))) return launch_svq_gemm(p, stream);
+  // From M = 4 the matrix-core kernel of vq_svq_gemm is as fast or faster: its cost hardly
+  // grows with M, the VALU kernels' grows linearly (us, VALU / matrix cores: 4096^2 at M = 8
+  // 20.8 / 11.1; 8192 x 28672 at M = 4 85.0 / 51.6; 14336 x 4096 at M = 4 13.5 / 13.5; at
+  // M = 2 the VALU kernel is ahead on three of these four layers).
+  if (p.in_features > 0 && p.m >= 4) return launch_svq_gemm(p, stream);
   hipStream_t s = (hipStream_t)stream;
   return p.x_dtype == VQ_BF16 ? launch_x<1>(p, s) : launch_x<0>(p, s);
 }

@@ -181,8 +181,8 @@ vq_status vq_svq_dequant(const vq_desc* desc, const void* packed, const void* a,
  * scalar product accumulated in fp32, so results match W^ to the vq_gemv tolerance.
  * packed: device, 16-byte aligned; x: device [M][IN], VQ_F16 or VQ_BF16; y: device
  * [M][N], VQ_F16, VQ_BF16 or VQ_F32; bias: fp16 [N] or NULL.  IN == 0 gives y = bias
- * (or 0).  Errors as for vq_gemv.  From M = 12, and from M = 4 on layers of 12288 rows or
- * more, the call runs the vq_svq_gemm kernel (same results to the same tolerance). */
+ * (or 0).  Errors as for vq_gemv.  From M = 4 the call runs the vq_svq_gemm kernel (same
+ * results to the same tolerance). */
 vq_status vq_svq_gemv(const vq_desc* desc, const void* packed, const void* a, const void* b, const void* scale,
                       const void* bias, const void* x, vq_dtype x_dtype, int32_t M, void* y, vq_dtype y_dtype,
                       void* stream);

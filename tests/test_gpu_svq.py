@@ -127,12 +127,12 @@ SHAPES = [
     (300, 28670, 1, "bf16", "f32", True, True),    # M = 1, seven slices resident in LDS
     (9000, 28673, 1, "f16", "f32", False, True),   # M = 1, eight slices: the sliced pass
     (8200, 4098, 1, "f16", "bf16", True, False),   # M = 1, two rows per wavefront, ragged
-    # routing: M >= 12, or M >= 4 on 12288+ rows, runs the matrix-core kernel
-    (300, 777, 11, "bf16", "f32", True, True),     # VALU
-    (300, 777, 12, "bf16", "f32", True, True),     # matrix cores
-    (12287, 130, 4, "f16", "f16", False, True),    # VALU
-    (12288, 130, 4, "f16", "f16", False, True),    # matrix cores
-    (12300, 68, 3, "bf16", "bf16", True, False),   # VALU (M < 4)
+    # routing: from M = 4 the matrix-core kernel runs
+    (300, 777, 3, "bf16", "f32", True, True),      # VALU
+    (300, 777, 4, "bf16", "f32", True, True),      # matrix cores (one row block, eight K-streams)
+    (12288, 130, 4, "f16", "f16", False, True),    # matrix cores (96 row blocks: four K-streams)
+    (12300, 68, 3, "bf16", "bf16", True, False),   # VALU
+    (2000, 1030, 12, "f16", "f32", True, False),   # matrix cores (16 row blocks)
 ]
 
 

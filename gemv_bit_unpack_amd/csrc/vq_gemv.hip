@@ -337,6 +337,241 @@ constexpr int kNumCU = 256;
 #define VQ_GEMV_U1 8  // vectors in flight per lane for M <= 2
 #endif
 
+
+// ---------------------------------------------------------------------------------------
+// v = 6 decode kernel for fp16 activations with both books in LDS (the 8B-class MLP
+// layers: K1 = K2 = 4096, 12-bit indices).  The general kernel above spends ~97 VALU and
+// ~10 memory instructions per vector here (each lane extracts its own index fields from
+// global words and converts x and both centroids to fp32).  This one keeps the books'
+// fp16 values and x in fp16 and multiplies them on the packed dot unit
+// (v_dot2_f32_f16: exact products, fp32 sums; the main book is added first, so a one-hot
+// x still yields fp32(c1 + c2)), and moves the index streams through LDS: per chunk of
+// U groups of 64 vectors of a row (U = 4 for one batch row, 2 for two), the wavefront
+// loads the chunk's index dwords with coalesced loads (2 * U * bits dwords per stream,
+// 32-bit aligned), stores them in its own LDS
+// area, and each lane reads its two fields from there.  Two register sets take chunks in
+// turn: while one chunk is multiplied, the loads of the next one and of the one after it
+// are in flight (about two chunks of work cover each load; one chunk ahead left the
+// latency exposed).  Each lane loads its vector's three x pairs as one 12-byte load;
+// pairs past the row read as zero, which also drops the lanes of a partial last vector
+// (IN is even).
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kMaxDw6 = 2 * 4 * 16;  // dwords of one stream's chunk: 4 groups, bits <= 16
+
+__device__ __forceinline__ float dot6(const uint4& c, const uint32_t (&x)[3], float acc) {
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, c.x), __builtin_bit_cast(half2_t, x[0]), acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, c.y), __builtin_bit_cast(half2_t, x[1]), acc, false);
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, c.z), __builtin_bit_cast(half2_t, x[2]), acc, false);
+}
+
+// One chunk's loads, as loaded: U groups of 64 vectors.  q1/q2 hold this lane's share of
+// the index dwords, x the three dwords its vector's activation pairs sit in (per group and
+// batch row), sc/bi the raw fp16 scale and bias of the chunk's row.  What lies past the row
+// is masked off only when the chunk is used, so nothing waits on the loads before then.
+template <int MT, int U>
+struct Chunk6 {
+  uint32_t q1[U / 2], q2[U / 2], x[U][MT][3], sc, bi;
+};
+
+// Loads of chunk cc of row r, every address clamped into its buffer.  No branches: a
+// branch around a load makes the compiler wait for every load in flight where it rejoins.
+template <int MT, int RK, int U>
+__device__ __forceinline__ void fetch6(const ProductArgs& a, int r, int cc, int lane, int dw1, int dw2,
+                                       Chunk6<MT, U>& k) {
+  const uint32_t* r1 = a.packed1 + (size_t)r * a.s1_words;
+  // scale and bias first: the compiler may copy them between register sets where the loop
+  // turns, and that copy waits only for loads issued before them.  A missing scale or bias
+  // reads the row's first index halfword in its place (unused).
+  const uint16_t* sp = a.scale ? a.scale + r : (const uint16_t*)r1;
+  const uint16_t* bp = a.bias ? a.bias + r : (const uint16_t*)r1;
+  k.sc = *sp;
+  k.bi = *bp;
+#pragma unroll
+  for (int i = 0; i < U / 2; ++i) k.q1[i] = r1[min(cc * dw1 + lane + 64 * i, a.s1_words - 1)];
+  if constexpr (RK != 0) {
+    const uint32_t* r2 = a.packed2 + (size_t)r * a.s2_words;
+#pragma unroll
+    for (int i = 0; i < U / 2; ++i) k.q2[i] = r2[min(cc * dw2 + lane + 64 * i, a.s2_words - 1)];
+  }
+  // the three dwords from base = min(pair0, last_pair - 2) (IN >= 6)
+  const int32_t last_pair = a.in_features / 2 - 1;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int32_t base = min(3 * (cc * 64 * U + u * 64 + lane), last_pair - 2);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const uint32_t* xr = (const uint32_t*)(a.x + (size_t)min(m, a.m - 1) * a.in_features);
+#pragma unroll
+      for (int d = 0; d < 3; ++d) k.x[u][m][d] = xr[base + d];
+    }
+  }
+}
+
+// Per-wavefront walk state: the chunk being multiplied and the two behind it.
+struct Walk6 {
+  int row, c, row1, c1, row2, c2;
+};
+
+// Multiplies the chunk held in k (row w.row, chunk w.c), then refills k with the chunk two
+// ahead.  Past the wavefront's last chunk (w.row >= n) it runs on in-bounds repeat data
+// and stores nothing.
+template <int MT, int RK, int U>
+__device__ __forceinline__ void step6(const ProductArgs& a, Walk6& w, int chunks, int total_waves, int lane,
+                                      int dw1, int dw2, uint32_t mask1, uint32_t mask2, const uint4* book1,
+                                      const uint4* book2, uint32_t* my1, uint32_t* my2, Chunk6<MT, U>& k,
+                                      float (&acc)[MT]) {
+  // this chunk's index dwords into the wavefront's LDS area, zero past the chunk or row
+#pragma unroll
+  for (int i = 0; i < U / 2; ++i) {
+    const int d = lane + 64 * i;
+    my1[d] = k.q1[i] & (0u - (uint32_t)(d < dw1 && w.c * dw1 + d < a.s1_words));
+    if constexpr (RK != 0) my2[d] = k.q2[i] & (0u - (uint32_t)(d < dw2 && w.c * dw2 + d < a.s2_words));
+  }
+  // this lane's three pairs per group: inside the row the loaded dwords themselves; a lane
+  // at or past the end picks its pairs out of the row's last three, or zero
+  uint32_t xc[U][MT][3];
+  const int32_t last_pair = a.in_features / 2 - 1;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int32_t pair0 = 3 * (w.c * 64 * U + u * 64 + lane);
+    const int32_t off = pair0 - min(pair0, last_pair - 2);
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int d = 0; d < 3; ++d) {
+        const int32_t sel = off + d;
+        xc[u][m][d] = (k.x[u][m][0] & (0u - (uint32_t)(sel == 0))) | (k.x[u][m][1] & (0u - (uint32_t)(sel == 1))) |
+                      (k.x[u][m][2] & (0u - (uint32_t)(sel == 2)));  // masks: a select chain becomes branches
+      }
+  }
+  const uint32_t sc_raw = k.sc, bi_raw = k.bi;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // the chunk two ahead (past the end, an in-bounds row) in flight meanwhile
+  fetch6<MT, RK, U>(a, min(w.row2, a.n - 1), w.c2, lane, dw1, dw2, k);
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t jl = (uint32_t)(u * 64 + lane);
+    const uint32_t b1 = jl * (uint32_t)a.bits1;
+    const uint32_t i1 = __builtin_amdgcn_alignbit(my1[(b1 >> 5) + 1], my1[b1 >> 5], b1 & 31u) & mask1;
+    const uint4 c1 = book1[i1];
+    uint4 c2;
+    if constexpr (RK != 0) {
+      const uint32_t b2 = jl * (uint32_t)a.bits2;
+      const uint32_t i2 = __builtin_amdgcn_alignbit(my2[(b2 >> 5) + 1], my2[b2 >> 5], b2 & 31u) & mask2;
+      c2 = book2[i2];
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      float r = dot6(c1, xc[u][m], acc[m]);
+      if constexpr (RK != 0) r = dot6(c2, xc[u][m], r);
+      acc[m] = r;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();  // this chunk's index reads stay before the next chunk's writes
+  if (w.row < a.n && (w.row1 != w.row || w.row1 >= a.n)) {  // row finished
+    const float sc = a.scale ? vqd::f16_to_f32((uint16_t)sc_raw) : 1.0f;
+    const float bi = a.bias ? vqd::f16_to_f32((uint16_t)bi_raw) : 0.0f;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (m < a.m) {
+        float r = wave_sum(acc[m]);
+        if (lane == 0) {
+          if (a.scale) r = r * sc;
+          if (a.bias) r = r + bi;
+          vqd::store_out(a.y, (size_t)m * a.n + w.row, r, a.y_dtype);
+        }
+      }
+      acc[m] = 0.0f;
+    }
+  }
+  w.row = w.row1;
+  w.c = w.c1;
+  w.row1 = w.row2;
+  w.c1 = w.c2;
+  const bool wrap = w.c2 + 1 == chunks;
+  w.c2 = wrap ? 0 : w.c2 + 1;
+  w.row2 += wrap ? total_waves : 0;
+}
+
+template <int MT, int RK, int U>
+__global__ __launch_bounds__(1024) void gemv6_kernel(ProductArgs a, int grid) {
+  extern __shared__ uint4 lds_words[];
+  const int k1 = 1 << a.bits1;
+  const int k2 = RK != 0 ? 1 << a.bits2 : 0;
+  const uint4* book1 = lds_words;
+  const uint4* book2 = lds_words + k1;
+  stage_books<6>((Cent<6>*)lds_words, a.cb1, k1, a.cb2, k2, 1024);
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  // uniform to the compiler: the walk state and loop control stay in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint32_t* my1 = (uint32_t*)(lds_words + k1 + k2) + wave * 2 * kMaxDw6;  // this wavefront's index area
+  uint32_t* my2 = my1 + kMaxDw6;
+  const int dw1 = 2 * U * a.bits1;
+  const int dw2 = RK != 0 ? 2 * U * a.bits2 : 0;
+  const uint32_t mask1 = (1u << a.bits1) - 1u, mask2 = (1u << a.bits2) - 1u;
+  const int chunks = (a.nv + 64 * U - 1) / (64 * U);
+  const int total_waves = grid * 16;
+  Walk6 w;
+  w.row = blockIdx.x * 16 + wave;
+  if (w.row >= a.n) return;
+  w.c = 0;
+  w.row1 = w.row;
+  w.c1 = 1;
+  if (w.c1 == chunks) {
+    w.c1 = 0;
+    w.row1 += total_waves;
+  }
+  w.row2 = w.row1;
+  w.c2 = w.c1 + 1;
+  if (w.c2 == chunks) {
+    w.c2 = 0;
+    w.row2 += total_waves;
+  }
+  // two register sets in turn, so no register moves wait on loads in flight
+  Chunk6<MT, U> ka, kb;
+  fetch6<MT, RK, U>(a, w.row, w.c, lane, dw1, dw2, ka);
+  fetch6<MT, RK, U>(a, min(w.row1, a.n - 1), w.c1, lane, dw1, dw2, kb);
+  float acc[MT];
+#pragma unroll
+  for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
+  // both first chunks in before the loop, so that where the loop turns only the second
+  // set's loads are outstanding and the first step waits for none of them
+  __builtin_amdgcn_s_waitcnt(0);
+  // two steps per trip and one exit test: an exit between them leaves values undefined on
+  // that path, and the compiler then reads them out of registers whose loads are in flight
+  while (w.row < a.n) {
+    step6<MT, RK, U>(a, w, chunks, total_waves, lane, dw1, dw2, mask1, mask2, book1, book2, my1, my2, ka, acc);
+    step6<MT, RK, U>(a, w, chunks, total_waves, lane, dw1, dw2, mask1, mask2, book1, book2, my1, my2, kb, acc);
+  }
+}
+
+template <int MT, int RK, int U>
+vq_status launch_gemv6(const ProductArgs& a, hipStream_t s) {
+  auto kern = gemv6_kernel<MT, RK, U>;
+  static std::once_flag once;
+  static hipError_t attr_err = hipSuccess;
+  std::call_once(once, [&] {
+    attr_err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  });
+  if (attr_err != hipSuccess) return VQ_ERR_HIP;
+  const size_t lds = 16u * (((size_t)1 << a.bits1) + (RK != 0 ? ((size_t)1 << a.bits2) : 0u)) +
+                     16u * 2u * kMaxDw6 * 4u + 16u;  // books, 16 index areas, one dword of slack
+  const long want = (a.n + 15) / 16;
+  const unsigned grid = (unsigned)(want < kNumCU ? want : kNumCU);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(1024), lds, s, a, (int)grid);
+  return hipGetLastError() == hipSuccess ? VQ_OK : VQ_ERR_HIP;
+}
+
+template <int RK>
+vq_status dispatch_gemv6(const ProductArgs& a, hipStream_t s) {
+  // two batch rows halve the groups per chunk to stay within 128 registers
+  return a.m <= 1 ? launch_gemv6<1, RK, 4>(a, s) : launch_gemv6<2, RK, 2>(a, s);
+}
+
 template <int V, int MT, int XT, int IB1, int RK>
 vq_status launch_fast(const ProductArgs& a, hipStream_t s) {
   // vectors in flight per lane: fewer for wide centroids and large batches (registers)
@@ -382,6 +617,11 @@ template <int V, int XT>
 vq_status dispatch_books(const ProductArgs& a, hipStream_t s) {
   const bool main16 = a.bits1 == 16;
   if constexpr (V == 6) {
+    // fp16 activations, decode batches, both books in LDS (with room for the index areas)
+    if (XT == 0 && a.m <= 2 && !main16 && a.in_features >= 6 &&
+        16u * ((1u << a.bits1) + (a.bits2 ? (1u << a.bits2) : 0u)) + 16u * 2u * kMaxDw6 * 4u + 16u <= 160u * 1024u) {
+      return a.bits2 ? dispatch_gemv6<1>(a, s) : dispatch_gemv6<0>(a, s);
+    }
     if (a.bits2) return main16 ? dispatch_m<V, XT, 16, 1>(a, s) : dispatch_m<V, XT, 0, 1>(a, s);
     return main16 ? dispatch_m<V, XT, 16, 0>(a, s) : dispatch_m<V, XT, 0, 0>(a, s);
   } else if constexpr (V == 16) {

@@ -139,6 +139,13 @@ def test_gemv_parity_workloads(vq, key, layer, m):
     (65, 512, 8, 16, 16, 2, "f16", False, True),    # two global books (AQLM 2 x 2^16)
     (33, 1000, 8, 16, 16, 16, "bf16", True, True),
     (5, 104, 16, 12, 0, 2, "f16", True, False),     # v = 16 with an LDS main book: generic path
+    # v = 6, fp16 x, M <= 2, books in LDS: the packed-dot kernel with LDS-staged index chunks
+    (1000, 4100, 6, 12, 12, 1, "f16", True, True),  # last vector keeps 2 lanes
+    (333, 1538, 6, 11, 9, 2, "f16", False, True),   # odd index widths; 257 vectors: two chunks
+    (17, 14336, 6, 12, 0, 1, "f16", True, False),   # no residual, ten chunks per row
+    (4099, 96, 6, 12, 12, 2, "f16", True, True),    # more rows than wavefronts in the grid
+    (5, 6, 6, 4, 3, 1, "f16", False, False),        # one vector per row
+    (40, 2000, 6, 12, 12, 3, "f16", True, True),    # M = 3: the general v = 6 kernel
 ])
 def test_gemv_parity_shapes(vq, n, i, v, b1, b2, m, xd, bias, scale):
     lay = synth.make_layer(n, i, v, b1, b2, wid=71, copy=n, with_scale=scale, with_bias=bias)

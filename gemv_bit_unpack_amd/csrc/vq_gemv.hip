@@ -365,6 +365,16 @@ __device__ __forceinline__ float dot6(const uint4& c, const uint32_t (&x)[3], fl
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, c.z), __builtin_bit_cast(half2_t, x[2]), acc, false);
 }
 
+// A register copy the compiler cannot fold away: the early-clobber output takes a register
+// of its own.  The chunk loop multiplies copies of a chunk's activations while the same
+// registers already receive the chunk after next; folded, the copies would move the new
+// loads between registers where the loop turns, which waits for them.
+__device__ __forceinline__ uint32_t own_copy(uint32_t v) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=&v"(r) : "v"(v));
+  return r;
+}
+
 // One chunk's loads, as loaded: U groups of 64 vectors.  q1/q2 hold this lane's share of
 // the index dwords, x the three dwords its vector's activation pairs sit in (per group and
 // batch row), sc/bi the raw fp16 scale and bias of the chunk's row.  What lies past the row
@@ -421,29 +431,47 @@ __device__ __forceinline__ void step6(const ProductArgs& a, Walk6& w, int chunks
                                       int dw1, int dw2, uint32_t mask1, uint32_t mask2, const uint4* book1,
                                       const uint4* book2, uint32_t* my1, uint32_t* my2, Chunk6<MT, U>& k,
                                       float (&acc)[MT]) {
-  // this chunk's index dwords into the wavefront's LDS area, zero past the chunk or row
+  // this chunk's index dwords into the wavefront's LDS area, this lane's three x pairs per
+  // group into xc
 #pragma unroll
   for (int i = 0; i < U / 2; ++i) {
-    const int d = lane + 64 * i;
-    my1[d] = k.q1[i] & (0u - (uint32_t)(d < dw1 && w.c * dw1 + d < a.s1_words));
-    if constexpr (RK != 0) my2[d] = k.q2[i] & (0u - (uint32_t)(d < dw2 && w.c * dw2 + d < a.s2_words));
+    my1[lane + 64 * i] = k.q1[i];
+    if constexpr (RK != 0) my2[lane + 64 * i] = k.q2[i];
   }
-  // this lane's three pairs per group: inside the row the loaded dwords themselves; a lane
-  // at or past the end picks its pairs out of the row's last three, or zero
   uint32_t xc[U][MT][3];
-  const int32_t last_pair = a.in_features / 2 - 1;
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int32_t pair0 = 3 * (w.c * 64 * U + u * 64 + lane);
-    const int32_t off = pair0 - min(pair0, last_pair - 2);
+  for (int u = 0; u < U; ++u)
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int d = 0; d < 3; ++d) {
-        const int32_t sel = off + d;
-        xc[u][m][d] = (k.x[u][m][0] & (0u - (uint32_t)(sel == 0))) | (k.x[u][m][1] & (0u - (uint32_t)(sel == 1))) |
-                      (k.x[u][m][2] & (0u - (uint32_t)(sel == 2)));  // masks: a select chain becomes branches
+      for (int d = 0; d < 3; ++d) xc[u][m][d] = own_copy(k.x[u][m][d]);
+  // only a row's last chunk reaches past the row: there the index dwords past it are
+  // zeroed, and a lane at or past the row's end picks its pairs out of the row's last three,
+  // or zero.  A uniform branch that changes only copies: the loaded registers themselves
+  // keep one assignment around the loop, so no copy of them waits on loads in flight.
+  if (w.c == chunks - 1) {
+#pragma unroll
+    for (int i = 0; i < U / 2; ++i) {
+      const int d = lane + 64 * i;
+      if (w.c * dw1 + d >= a.s1_words) my1[d] = 0u;
+      if constexpr (RK != 0)
+        if (w.c * dw2 + d >= a.s2_words) my2[d] = 0u;
+    }
+    const int32_t last_pair = a.in_features / 2 - 1;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int32_t pair0 = 3 * (w.c * 64 * U + u * 64 + lane);
+      const int32_t off = pair0 - min(pair0, last_pair - 2);
+      const uint32_t e0 = 0u - (uint32_t)(off == 0), e1 = 0u - (uint32_t)(off == 1),
+                     e2 = 0u - (uint32_t)(off == 2);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {  // masks: a chain of selects becomes branches
+        const uint32_t x0 = xc[u][m][0], x1 = xc[u][m][1], x2 = xc[u][m][2];
+        xc[u][m][0] = (x0 & e0) | (x1 & e1) | (x2 & e2);
+        xc[u][m][1] = (x1 & e0) | (x2 & e1);
+        xc[u][m][2] = x2 & e0;
       }
+    }
   }
   const uint32_t sc_raw = k.sc, bi_raw = k.bi;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

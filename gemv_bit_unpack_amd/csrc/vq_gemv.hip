@@ -352,12 +352,25 @@ constexpr int kNumCU = 256;
 // area, and each lane reads its two fields from there.  Two register sets take chunks in
 // turn: while one chunk is multiplied, the loads of the next one and of the one after it
 // are in flight (about two chunks of work cover each load; one chunk ahead left the
-// latency exposed).  Each lane loads its vector's three x pairs as one 12-byte load;
-// pairs past the row read as zero, which also drops the lanes of a partial last vector
-// (IN is even).
+// latency exposed).  Each lane loads its vector's three x pairs as one 12-byte load.
+// All loads are buffer loads bounded by the row (IN is even): what lies past it reads as
+// zero, so the vectors past a row's end and the missing pairs of a partial last vector
+// add nothing.
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
 
-constexpr int kMaxDw6 = 2 * 4 * 16;  // dwords of one stream's chunk: 4 groups, bits <= 16
+// Dwords of one wavefront's LDS area per index stream: a chunk of U groups holds 2 * U * bits
+// dwords per stream; the area rounds the wider stream up to whole 64-lane stores.
+__host__ __device__ constexpr int area6(int u, int bits1, int bits2) {
+  return 64 * ((u * (bits1 > bits2 ? bits1 : bits2) + 31) / 32);
+}
+
+// LDS bytes of the v = 6 kernel: both books, 16 wavefronts' two index areas, one dword of
+// slack for the last field's read of the dword after it.
+inline size_t gemv6_lds(int u, int bits1, int bits2) {
+  return 16u * (((size_t)1 << bits1) + (bits2 ? ((size_t)1 << bits2) : 0u)) +
+         16u * 2u * 4u * (size_t)area6(u, bits1, bits2) + 16u;
+}
 
 __device__ __forceinline__ float dot6(const uint4& c, const uint32_t (&x)[3], float acc) {
   acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, c.x), __builtin_bit_cast(half2_t, x[0]), acc, false);
@@ -384,8 +397,16 @@ struct Chunk6 {
   uint32_t q1[U / 2], q2[U / 2], x[U][MT][3], sc, bi;
 };
 
-// Loads of chunk cc of row r, every address clamped into its buffer.  No branches: a
-// branch around a load makes the compiler wait for every load in flight where it rejoins.
+// Raw buffer resource over n bytes at p (stride 0, dword data).  A buffer load returns
+// zero for every dword that does not lie wholly inside the n bytes, offsets included, and
+// reads no memory for it.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc6(const void* p, uint32_t n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
+}
+
+// Loads of chunk cc of row r.  Buffer loads bounded by the row: index dwords and
+// activation pairs past the row's end read as zero, so a row's last chunk needs no masking
+// (its vectors past the end have zero indices and zero x) and the addresses stay scalar.
 template <int MT, int RK, int U>
 __device__ __forceinline__ void fetch6(const ProductArgs& a, int r, int cc, int lane, int dw1, int dw2,
                                        Chunk6<MT, U>& k) {
@@ -397,23 +418,26 @@ __device__ __forceinline__ void fetch6(const ProductArgs& a, int r, int cc, int 
   const uint16_t* bp = a.bias ? a.bias + r : (const uint16_t*)r1;
   k.sc = *sp;
   k.bi = *bp;
+  const __amdgpu_buffer_rsrc_t b1 = rsrc6(r1, 4u * (uint32_t)a.s1_words);
 #pragma unroll
-  for (int i = 0; i < U / 2; ++i) k.q1[i] = r1[min(cc * dw1 + lane + 64 * i, a.s1_words - 1)];
+  for (int i = 0; i < U / 2; ++i)
+    k.q1[i] = __builtin_amdgcn_raw_buffer_load_b32(b1, 4 * (lane + 64 * i), 4 * cc * dw1, 0);
   if constexpr (RK != 0) {
-    const uint32_t* r2 = a.packed2 + (size_t)r * a.s2_words;
+    const __amdgpu_buffer_rsrc_t b2 = rsrc6(a.packed2 + (size_t)r * a.s2_words, 4u * (uint32_t)a.s2_words);
 #pragma unroll
-    for (int i = 0; i < U / 2; ++i) k.q2[i] = r2[min(cc * dw2 + lane + 64 * i, a.s2_words - 1)];
+    for (int i = 0; i < U / 2; ++i)
+      k.q2[i] = __builtin_amdgcn_raw_buffer_load_b32(b2, 4 * (lane + 64 * i), 4 * cc * dw2, 0);
   }
-  // the three dwords from base = min(pair0, last_pair - 2) (IN >= 6)
-  const int32_t last_pair = a.in_features / 2 - 1;
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    const int32_t base = min(3 * (cc * 64 * U + u * 64 + lane), last_pair - 2);
+  for (int m = 0; m < MT; ++m) {
+    const __amdgpu_buffer_rsrc_t bx =
+        rsrc6(a.x + (size_t)min(m, a.m - 1) * a.in_features, 2u * (uint32_t)a.in_features);
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const uint32_t* xr = (const uint32_t*)(a.x + (size_t)min(m, a.m - 1) * a.in_features);
-#pragma unroll
-      for (int d = 0; d < 3; ++d) k.x[u][m][d] = xr[base + d];
+    for (int u = 0; u < U; ++u) {
+      const u32x3_t v = __builtin_amdgcn_raw_buffer_load_b96(bx, 12 * (u * 64 + lane), 12 * 64 * U * cc, 0);
+      k.x[u][m][0] = v.x;
+      k.x[u][m][1] = v.y;
+      k.x[u][m][2] = v.z;
     }
   }
 }
@@ -429,14 +453,16 @@ struct Walk6 {
 template <int MT, int RK, int U>
 __device__ __forceinline__ void step6(const ProductArgs& a, Walk6& w, int chunks, int total_waves, int lane,
                                       int dw1, int dw2, uint32_t mask1, uint32_t mask2, const uint4* book1,
-                                      const uint4* book2, uint32_t* my1, uint32_t* my2, Chunk6<MT, U>& k,
+                                      const uint4* book2, uint32_t* my1, uint32_t* my2, int area, Chunk6<MT, U>& k,
                                       float (&acc)[MT]) {
   // this chunk's index dwords into the wavefront's LDS area, this lane's three x pairs per
   // group into xc
 #pragma unroll
   for (int i = 0; i < U / 2; ++i) {
-    my1[lane + 64 * i] = k.q1[i];
-    if constexpr (RK != 0) my2[lane + 64 * i] = k.q2[i];
+    if (64 * i < area) {  // uniform: the area ends on a whole store
+      my1[lane + 64 * i] = k.q1[i];
+      if constexpr (RK != 0) my2[lane + 64 * i] = k.q2[i];
+    }
   }
   uint32_t xc[U][MT][3];
 #pragma unroll
@@ -445,34 +471,6 @@ __device__ __forceinline__ void step6(const ProductArgs& a, Walk6& w, int chunks
     for (int m = 0; m < MT; ++m)
 #pragma unroll
       for (int d = 0; d < 3; ++d) xc[u][m][d] = own_copy(k.x[u][m][d]);
-  // only a row's last chunk reaches past the row: there the index dwords past it are
-  // zeroed, and a lane at or past the row's end picks its pairs out of the row's last three,
-  // or zero.  A uniform branch that changes only copies: the loaded registers themselves
-  // keep one assignment around the loop, so no copy of them waits on loads in flight.
-  if (w.c == chunks - 1) {
-#pragma unroll
-    for (int i = 0; i < U / 2; ++i) {
-      const int d = lane + 64 * i;
-      if (w.c * dw1 + d >= a.s1_words) my1[d] = 0u;
-      if constexpr (RK != 0)
-        if (w.c * dw2 + d >= a.s2_words) my2[d] = 0u;
-    }
-    const int32_t last_pair = a.in_features / 2 - 1;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int32_t pair0 = 3 * (w.c * 64 * U + u * 64 + lane);
-      const int32_t off = pair0 - min(pair0, last_pair - 2);
-      const uint32_t e0 = 0u - (uint32_t)(off == 0), e1 = 0u - (uint32_t)(off == 1),
-                     e2 = 0u - (uint32_t)(off == 2);
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {  // masks: a chain of selects becomes branches
-        const uint32_t x0 = xc[u][m][0], x1 = xc[u][m][1], x2 = xc[u][m][2];
-        xc[u][m][0] = (x0 & e0) | (x1 & e1) | (x2 & e2);
-        xc[u][m][1] = (x1 & e0) | (x2 & e1);
-        xc[u][m][2] = x2 & e0;
-      }
-    }
-  }
   const uint32_t sc_raw = k.sc, bi_raw = k.bi;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -536,8 +534,9 @@ __global__ __launch_bounds__(1024) void gemv6_kernel(ProductArgs a, int grid) {
   const int lane = threadIdx.x & 63;
   // uniform to the compiler: the walk state and loop control stay in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  uint32_t* my1 = (uint32_t*)(lds_words + k1 + k2) + wave * 2 * kMaxDw6;  // this wavefront's index area
-  uint32_t* my2 = my1 + kMaxDw6;
+  const int area = area6(U, a.bits1, RK != 0 ? a.bits2 : 0);
+  uint32_t* my1 = (uint32_t*)(lds_words + k1 + k2) + wave * 2 * area;  // this wavefront's index areas
+  uint32_t* my2 = my1 + area;
   const int dw1 = 2 * U * a.bits1;
   const int dw2 = RK != 0 ? 2 * U * a.bits2 : 0;
   const uint32_t mask1 = (1u << a.bits1) - 1u, mask2 = (1u << a.bits2) - 1u;
@@ -572,8 +571,8 @@ __global__ __launch_bounds__(1024) void gemv6_kernel(ProductArgs a, int grid) {
   // two steps per trip and one exit test: an exit between them leaves values undefined on
   // that path, and the compiler then reads them out of registers whose loads are in flight
   while (w.row < a.n) {
-    step6<MT, RK, U>(a, w, chunks, total_waves, lane, dw1, dw2, mask1, mask2, book1, book2, my1, my2, ka, acc);
-    step6<MT, RK, U>(a, w, chunks, total_waves, lane, dw1, dw2, mask1, mask2, book1, book2, my1, my2, kb, acc);
+    step6<MT, RK, U>(a, w, chunks, total_waves, lane, dw1, dw2, mask1, mask2, book1, book2, my1, my2, area, ka, acc);
+    step6<MT, RK, U>(a, w, chunks, total_waves, lane, dw1, dw2, mask1, mask2, book1, book2, my1, my2, area, kb, acc);
   }
 }
 
@@ -586,8 +585,7 @@ vq_status launch_gemv6(const ProductArgs& a, hipStream_t s) {
     attr_err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
   });
   if (attr_err != hipSuccess) return VQ_ERR_HIP;
-  const size_t lds = 16u * (((size_t)1 << a.bits1) + (RK != 0 ? ((size_t)1 << a.bits2) : 0u)) +
-                     16u * 2u * kMaxDw6 * 4u + 16u;  // books, 16 index areas, one dword of slack
+  const size_t lds = gemv6_lds(U, a.bits1, RK != 0 ? a.bits2 : 0);
   const long want = (a.n + 15) / 16;
   const unsigned grid = (unsigned)(want < kNumCU ? want : kNumCU);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(1024), lds, s, a, (int)grid);
@@ -596,8 +594,11 @@ vq_status launch_gemv6(const ProductArgs& a, hipStream_t s) {
 
 template <int RK>
 vq_status dispatch_gemv6(const ProductArgs& a, hipStream_t s) {
-  // two batch rows halve the groups per chunk to stay within 128 registers
-  return a.m <= 1 ? launch_gemv6<1, RK, 4>(a, s) : launch_gemv6<2, RK, 2>(a, s);
+  // eight groups per chunk for one book where their index areas fit beside it (two books
+  // at eight would spill past 128 registers); two batch rows take two groups
+  if (a.m >= 2) return launch_gemv6<2, RK, 2>(a, s);
+  if (RK == 0 && gemv6_lds(8, a.bits1, a.bits2) <= 160u * 1024u) return launch_gemv6<1, RK, 8>(a, s);
+  return launch_gemv6<1, RK, 4>(a, s);
 }
 
 template <int V, int MT, int XT, int IB1, int RK>
@@ -646,8 +647,7 @@ vq_status dispatch_books(const ProductArgs& a, hipStream_t s) {
   const bool main16 = a.bits1 == 16;
   if constexpr (V == 6) {
     // fp16 activations, decode batches, both books in LDS (with room for the index areas)
-    if (XT == 0 && a.m <= 2 && !main16 && a.in_features >= 6 &&
-        16u * ((1u << a.bits1) + (a.bits2 ? (1u << a.bits2) : 0u)) + 16u * 2u * kMaxDw6 * 4u + 16u <= 160u * 1024u) {
+    if (XT == 0 && a.m <= 2 && !main16 && a.in_features >= 6 && gemv6_lds(4, a.bits1, a.bits2) <= 160u * 1024u) {
       return a.bits2 ? dispatch_gemv6<1>(a, s) : dispatch_gemv6<0>(a, s);
     }
     if (a.bits2) return main16 ? dispatch_m<V, XT, 16, 1>(a, s) : dispatch_m<V, XT, 0, 1>(a, s);

@@ -477,25 +477,33 @@ __device__ __forceinline__ void step6(const ProductArgs& a, Walk6& w, int chunks
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   // the chunk two ahead (past the end, an in-bounds row) in flight meanwhile
   fetch6<MT, RK, U>(a, min(w.row2, a.n - 1), w.c2, lane, dw1, dw2, k);
+  // all fields first, then all centroid reads, then the products: every LDS read of the
+  // chunk is in flight before the first product waits on one
+  uint32_t i1[U], i2[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const uint32_t jl = (uint32_t)(u * 64 + lane);
     const uint32_t b1 = jl * (uint32_t)a.bits1;
-    const uint32_t i1 = __builtin_amdgcn_alignbit(my1[(b1 >> 5) + 1], my1[b1 >> 5], b1 & 31u) & mask1;
-    const uint4 c1 = book1[i1];
-    uint4 c2;
+    i1[u] = __builtin_amdgcn_alignbit(my1[(b1 >> 5) + 1], my1[b1 >> 5], b1 & 31u) & mask1;
     if constexpr (RK != 0) {
       const uint32_t b2 = jl * (uint32_t)a.bits2;
-      const uint32_t i2 = __builtin_amdgcn_alignbit(my2[(b2 >> 5) + 1], my2[b2 >> 5], b2 & 31u) & mask2;
-      c2 = book2[i2];
-    }
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      float r = dot6(c1, xc[u][m], acc[m]);
-      if constexpr (RK != 0) r = dot6(c2, xc[u][m], r);
-      acc[m] = r;
+      i2[u] = __builtin_amdgcn_alignbit(my2[(b2 >> 5) + 1], my2[b2 >> 5], b2 & 31u) & mask2;
     }
   }
+  uint4 c1[U], c2[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    c1[u] = book1[i1[u]];
+    if constexpr (RK != 0) c2[u] = book2[i2[u]];
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      float r = dot6(c1[u], xc[u][m], acc[m]);
+      if constexpr (RK != 0) r = dot6(c2[u], xc[u][m], r);
+      acc[m] = r;
+    }
   __builtin_amdgcn_wave_barrier();  // this chunk's index reads stay before the next chunk's writes
   if (w.row < a.n && (w.row1 != w.row || w.row1 >= a.n)) {  // row finished
     const float sc = a.scale ? vqd::f16_to_f32((uint16_t)sc_raw) : 1.0f;
@@ -594,11 +602,8 @@ vq_status launch_gemv6(const ProductArgs& a, hipStream_t s) {
 
 template <int RK>
 vq_status dispatch_gemv6(const ProductArgs& a, hipStream_t s) {
-  // eight groups per chunk for one book where their index areas fit beside it (two books
-  // at eight would spill past 128 registers); two batch rows take two groups
-  if (a.m >= 2) return launch_gemv6<2, RK, 2>(a, s);
-  if (RK == 0 && gemv6_lds(8, a.bits1, a.bits2) <= 160u * 1024u) return launch_gemv6<1, RK, 8>(a, s);
-  return launch_gemv6<1, RK, 4>(a, s);
+  // four groups per chunk; two batch rows take two to stay within 128 registers
+  return a.m >= 2 ? launch_gemv6<2, RK, 2>(a, s) : launch_gemv6<1, RK, 4>(a, s);
 }
 
 template <int V, int MT, int XT, int IB1, int RK>

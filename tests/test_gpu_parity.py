@@ -172,6 +172,22 @@ def test_gemv_one_hot_columns_bit_exact(vq, n, i, v, b1, b2):
     assert np.array_equal(y, w32[:, cols].T)  # == comparison: +0 and -0 both accepted
 
 
+@pytest.mark.parametrize("n,i,b2,m", [(48, 96, 12, 1), (40, 4100, 0, 1), (33, 1538, 9, 2)])
+def test_gemv6_one_hot_columns_bit_exact(vq, n, i, b2, m):
+    """The v = 6 packed-dot kernel (fp16 x, M <= 2): a one-hot x still gives the exact fp32
+    W^ entry, main centroid added first."""
+    lay = synth.make_layer(n, i, 6, 12, b2, wid=76, copy=i)
+    dl = DeviceLayer(vq, lay)
+    w32 = oracle_w(lay)
+    cols = np.array([0, 1, 5, 6, i // 2 + 1, i - 2, i - 1])
+    for start in range(0, cols.size, m):
+        cs = cols[start:start + m]
+        xb = np.zeros((cs.size, i), dtype=np.uint16)
+        xb[np.arange(cs.size), cs] = 0x3C00  # 1.0
+        y = vq.gemv(*dl.args(), x_tensor(xb, "f16"), y_dtype=torch.float32).cpu().numpy()
+        assert np.array_equal(y, w32[:, cs].T), (start, cs)
+
+
 def test_gemv_edge_cases(vq):
     lay = synth.make_layer(40, 64, 8, 8, 0, wid=73, with_bias=True)
     dl = DeviceLayer(vq, lay)

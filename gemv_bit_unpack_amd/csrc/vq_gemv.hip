@@ -358,6 +358,7 @@ constexpr int kNumCU = 256;
 // add nothing.
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // Dwords of one wavefront's LDS area per index stream: a chunk of U groups holds 2 * U * bits
 // dwords per stream; the area rounds the wider stream up to whole 64-lane stores.
@@ -394,7 +395,7 @@ __device__ __forceinline__ uint32_t own_copy(uint32_t v) {
 // is masked off only when the chunk is used, so nothing waits on the loads before then.
 template <int MT, int U>
 struct Chunk6 {
-  uint32_t q1[U / 2], q2[U / 2], x[U][MT][3], sc, bi;
+  uint32_t q1[U / 2], q2[U / 2], x[U][MT][3];
 };
 
 // Raw buffer resource over n bytes at p (stride 0, dword data).  A buffer load returns
@@ -404,29 +405,31 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc6(const void* p, uint32_t 
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
 }
 
+template <int U>
+__device__ __forceinline__ void load_q6(__amdgpu_buffer_rsrc_t b, int voff, int soff, uint32_t (&q)[U / 2]) {
+  static_assert(U == 2 || U == 4, "one or two index dwords per lane");
+  if constexpr (U == 4) {
+    const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(b, voff, soff, 0);
+    q[0] = v.x;
+    q[1] = v.y;
+  } else {
+    q[0] = __builtin_amdgcn_raw_buffer_load_b32(b, voff, soff, 0);
+  }
+}
+
 // Loads of chunk cc of row r.  Buffer loads bounded by the row: index dwords and
 // activation pairs past the row's end read as zero, so a row's last chunk needs no masking
 // (its vectors past the end have zero indices and zero x) and the addresses stay scalar.
 template <int MT, int RK, int U>
 __device__ __forceinline__ void fetch6(const ProductArgs& a, int r, int cc, int lane, int dw1, int dw2,
                                        Chunk6<MT, U>& k) {
-  const uint32_t* r1 = a.packed1 + (size_t)r * a.s1_words;
-  // scale and bias first: the compiler may copy them between register sets where the loop
-  // turns, and that copy waits only for loads issued before them.  A missing scale or bias
-  // reads the row's first index halfword in its place (unused).
-  const uint16_t* sp = a.scale ? a.scale + r : (const uint16_t*)r1;
-  const uint16_t* bp = a.bias ? a.bias + r : (const uint16_t*)r1;
-  k.sc = *sp;
-  k.bi = *bp;
-  const __amdgpu_buffer_rsrc_t b1 = rsrc6(r1, 4u * (uint32_t)a.s1_words);
-#pragma unroll
-  for (int i = 0; i < U / 2; ++i)
-    k.q1[i] = __builtin_amdgcn_raw_buffer_load_b32(b1, 4 * (lane + 64 * i), 4 * cc * dw1, 0);
+  // index dwords: lane l takes dwords (U / 2) l .. (U / 2) l + U / 2 - 1 of the chunk in one
+  // load (a load instruction costs the texture data path about the same whatever its width)
+  const __amdgpu_buffer_rsrc_t b1 = rsrc6(a.packed1 + (size_t)r * a.s1_words, 4u * (uint32_t)a.s1_words);
+  load_q6<U>(b1, 4 * (U / 2) * lane, 4 * cc * dw1, k.q1);
   if constexpr (RK != 0) {
     const __amdgpu_buffer_rsrc_t b2 = rsrc6(a.packed2 + (size_t)r * a.s2_words, 4u * (uint32_t)a.s2_words);
-#pragma unroll
-    for (int i = 0; i < U / 2; ++i)
-      k.q2[i] = __builtin_amdgcn_raw_buffer_load_b32(b2, 4 * (lane + 64 * i), 4 * cc * dw2, 0);
+    load_q6<U>(b2, 4 * (U / 2) * lane, 4 * cc * dw2, k.q2);
   }
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
@@ -444,7 +447,7 @@ __device__ __forceinline__ void fetch6(const ProductArgs& a, int r, int cc, int 
 
 // Per-wavefront walk state: the chunk being multiplied and the two behind it.
 struct Walk6 {
-  int row, c, row1, c1, row2, c2;
+  int row, c, row1, c1, row2, c2, rk;  // rk: how many rows this wavefront finished before w.row
 };
 
 // Multiplies the chunk held in k (row w.row, chunk w.c), then refills k with the chunk two
@@ -454,14 +457,15 @@ template <int MT, int RK, int U>
 __device__ __forceinline__ void step6(const ProductArgs& a, Walk6& w, int chunks, int total_waves, int lane,
                                       int dw1, int dw2, uint32_t mask1, uint32_t mask2, const uint4* book1,
                                       const uint4* book2, uint32_t* my1, uint32_t* my2, int area, Chunk6<MT, U>& k,
-                                      float (&acc)[MT]) {
-  // this chunk's index dwords into the wavefront's LDS area, this lane's three x pairs per
-  // group into xc
+                                      uint32_t scv, uint32_t biv, float (&acc)[MT]) {
+  // this chunk's index dwords into the wavefront's LDS area (lane l's U / 2 dwords at
+  // (U / 2) l; the area ends on a whole store, or half of one), this lane's three x pairs
+  // per group into xc
+  if ((U / 2) * lane < area) {
 #pragma unroll
-  for (int i = 0; i < U / 2; ++i) {
-    if (64 * i < area) {  // uniform: the area ends on a whole store
-      my1[lane + 64 * i] = k.q1[i];
-      if constexpr (RK != 0) my2[lane + 64 * i] = k.q2[i];
+    for (int i = 0; i < U / 2; ++i) {
+      my1[(U / 2) * lane + i] = k.q1[i];
+      if constexpr (RK != 0) my2[(U / 2) * lane + i] = k.q2[i];
     }
   }
   uint32_t xc[U][MT][3];
@@ -471,7 +475,6 @@ __device__ __forceinline__ void step6(const ProductArgs& a, Walk6& w, int chunks
     for (int m = 0; m < MT; ++m)
 #pragma unroll
       for (int d = 0; d < 3; ++d) xc[u][m][d] = own_copy(k.x[u][m][d]);
-  const uint32_t sc_raw = k.sc, bi_raw = k.bi;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -506,8 +509,9 @@ __device__ __forceinline__ void step6(const ProductArgs& a, Walk6& w, int chunks
     }
   __builtin_amdgcn_wave_barrier();  // this chunk's index reads stay before the next chunk's writes
   if (w.row < a.n && (w.row1 != w.row || w.row1 >= a.n)) {  // row finished
-    const float sc = a.scale ? vqd::f16_to_f32((uint16_t)sc_raw) : 1.0f;
-    const float bi = a.bias ? vqd::f16_to_f32((uint16_t)bi_raw) : 0.0f;
+    // the row's scale and bias, loaded at the start into lane w.rk
+    const float sc = a.scale ? vqd::f16_to_f32((uint16_t)__builtin_amdgcn_readlane((int)scv, w.rk)) : 1.0f;
+    const float bi = a.bias ? vqd::f16_to_f32((uint16_t)__builtin_amdgcn_readlane((int)biv, w.rk)) : 0.0f;
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       if (m < a.m) {
@@ -521,6 +525,7 @@ __device__ __forceinline__ void step6(const ProductArgs& a, Walk6& w, int chunks
       acc[m] = 0.0f;
     }
   }
+  w.rk += w.row1 != w.row ? 1 : 0;
   w.row = w.row1;
   w.c = w.c1;
   w.row1 = w.row2;
@@ -553,6 +558,15 @@ __global__ __launch_bounds__(1024) void gemv6_kernel(ProductArgs a, int grid) {
   Walk6 w;
   w.row = blockIdx.x * 16 + wave;
   if (w.row >= a.n) return;
+  w.rk = 0;
+  // scale and bias of this wavefront's rows (at most 64: the launch checks), lane k
+  // holding those of its k-th row; a missing one reads the first index halfword (unused)
+  uint32_t scv, biv;
+  {
+    const int r = min(w.row + lane * total_waves, a.n - 1);
+    scv = *(a.scale ? a.scale + r : (const uint16_t*)a.packed1);
+    biv = *(a.bias ? a.bias + r : (const uint16_t*)a.packed1);
+  }
   w.c = 0;
   w.row1 = w.row;
   w.c1 = 1;
@@ -579,8 +593,8 @@ __global__ __launch_bounds__(1024) void gemv6_kernel(ProductArgs a, int grid) {
   // two steps per trip and one exit test: an exit between them leaves values undefined on
   // that path, and the compiler then reads them out of registers whose loads are in flight
   while (w.row < a.n) {
-    step6<MT, RK, U>(a, w, chunks, total_waves, lane, dw1, dw2, mask1, mask2, book1, book2, my1, my2, area, ka, acc);
-    step6<MT, RK, U>(a, w, chunks, total_waves, lane, dw1, dw2, mask1, mask2, book1, book2, my1, my2, area, kb, acc);
+    step6<MT, RK, U>(a, w, chunks, total_waves, lane, dw1, dw2, mask1, mask2, book1, book2, my1, my2, area, ka, scv, biv, acc);
+    step6<MT, RK, U>(a, w, chunks, total_waves, lane, dw1, dw2, mask1, mask2, book1, book2, my1, my2, area, kb, scv, biv, acc);
   }
 }
 
@@ -652,7 +666,8 @@ vq_status dispatch_books(const ProductArgs& a, hipStream_t s) {
   const bool main16 = a.bits1 == 16;
   if constexpr (V == 6) {
     // fp16 activations, decode batches, both books in LDS (with room for the index areas)
-    if (XT == 0 && a.m <= 2 && !main16 && a.in_features >= 6 && gemv6_lds(4, a.bits1, a.bits2) <= 160u * 1024u) {
+    if (XT == 0 && a.m <= 2 && !main16 && a.in_features >= 6 && a.n <= 64 * 16 * kNumCU &&
+        gemv6_lds(4, a.bits1, a.bits2) <= 160u * 1024u) {
       return a.bits2 ? dispatch_gemv6<1>(a, s) : dispatch_gemv6<0>(a, s);
     }
     if (a.bits2) return main16 ? dispatch_m<V, XT, 16, 1>(a, s) : dispatch_m<V, XT, 0, 1>(a, s);

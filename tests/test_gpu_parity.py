@@ -188,6 +188,22 @@ def test_gemv6_one_hot_columns_bit_exact(vq, n, i, b2, m):
         assert np.array_equal(y, w32[:, cs].T), (start, cs)
 
 
+@pytest.mark.parametrize("n", [262144, 262145])
+def test_gemv6_row_limit(vq, n):
+    """The v = 6 packed-dot kernel holds each wavefront's scales and biases in its lanes, one
+    row each: at 262144 rows (64 per wavefront) the last lane is used; one row more goes to
+    the general kernel.  Sampled rows, the last wavefront's rows included."""
+    lay = synth.make_layer(n, 12, 6, 12, 12, wid=77, with_scale=True, with_bias=True)
+    dl = DeviceLayer(vq, lay)
+    xb = synth.activations(np.random.default_rng(5), 1, 12, "f16")
+    rows = np.unique(np.concatenate([sample_rows(n, 40, seed=n), np.arange(n - 4100, n, 97), [n - 1]]))
+    y64 = oracle_y(lay, xb, "f16", rows)
+    y = vq.gemv(*dl.args(), x_tensor(xb, "f16"), y_dtype=torch.float32)
+    check_y(y[:, torch.from_numpy(rows).cuda()], y64, "f32")
+    yb = vq.gemv(*dl.args(), x_tensor(xb, "f16"), y_dtype=torch.bfloat16)
+    check_y(yb[:, torch.from_numpy(rows).cuda()], y64, "bf16")
+
+
 def test_gemv_edge_cases(vq):
     lay = synth.make_layer(40, 64, 8, 8, 0, wid=73, with_bias=True)
     dl = DeviceLayer(vq, lay)

@@ -307,7 +307,9 @@ __global__ __launch_bounds__(kThreads) void gemv_sliced_kernel(ProductArgs a, Sl
   }
 }
 
-// y[m][row] = scale[row] * 2^e[m] * (sum of the partials in a fixed order) + bias[row]
+// y[m][row] = scale[row] * 2^e[m] * (sum of the partials in a fixed order) + bias[row].
+// The exponent, scale and bias are loaded beside the partials (a missing one reads a
+// partial in its place, unused), so a thread waits for memory once.
 __global__ __launch_bounds__(256) void gemv_sliced_finalize(ProductArgs a, const float* __restrict__ part,
                                                             const int32_t* __restrict__ xexp, int nparts) {
   const int t = blockIdx.x * 256 + threadIdx.x;
@@ -316,6 +318,9 @@ __global__ __launch_bounds__(256) void gemv_sliced_finalize(ProductArgs a, const
   const int row = t - m * a.n;
   const float* p = part + (size_t)m * a.n + row;
   const size_t stride = (size_t)a.m * a.n;
+  const int32_t e = *(xexp ? xexp + m : (const int32_t*)p);
+  const uint16_t sc = *(a.scale ? a.scale + row : (const uint16_t*)p);
+  const uint16_t bi = *(a.bias ? a.bias + row : (const uint16_t*)p);
   float acc = 0.0f;
   int q = 0;
   for (; q + 8 <= nparts; q += 8) {  // eight loads in flight, added in order
@@ -326,14 +331,38 @@ __global__ __launch_bounds__(256) void gemv_sliced_finalize(ProductArgs a, const
     for (int k = 0; k < 8; ++k) acc += v[k];
   }
   for (; q < nparts; ++q) acc += p[(size_t)q * stride];
-  if (xexp) acc = ldexpf(acc, xexp[m]);
-  if (a.scale) acc = acc * vqd::f16_to_f32(a.scale[row]);
-  if (a.bias) acc = acc + vqd::f16_to_f32(a.bias[row]);
+  if (xexp) acc = ldexpf(acc, e);
+  if (a.scale) acc = acc * vqd::f16_to_f32(sc);
+  if (a.bias) acc = acc + vqd::f16_to_f32(bi);
   vqd::store_out(a.y, (size_t)m * a.n + row, acc, a.y_dtype);
 }
 
 // bf16 activations -> fp16 * 2^e, one workgroup per batch row: e is the smallest
 // exponent >= 0 that brings max |x| below 2^15, so every finite value stays finite.
+// Rows of up to 4 * 1024 * 8 values are read once into registers (all loads in flight
+// together) and converted from there; longer rows are walked in passes of that size.
+constexpr int kXprepHold = 4;  // 16-byte words per thread held in registers
+
+__device__ __forceinline__ uint32_t xprep_absmax(const uint4& v) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t mx = 0;
+#pragma unroll
+  for (int h = 0; h < 4; ++h) mx = max(mx, max(w[h] & 0x7FFFu, (w[h] >> 16) & 0x7FFFu));
+  return mx;
+}
+
+__device__ __forceinline__ uint4 xprep_convert(const uint4& v, int e) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    const uint32_t lo = vqd::f32_to_f16_rne(ldexpf(vqd::bf16_to_f32(w[h] & 0xFFFFu), -e));
+    const uint32_t hi = vqd::f32_to_f16_rne(ldexpf(vqd::bf16_to_f32(w[h] >> 16), -e));
+    o[h] = lo | (hi << 16);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 __global__ __launch_bounds__(1024) void xprep_kernel(const uint16_t* __restrict__ x, int in_features,
                                                      uint16_t* __restrict__ x16, int32_t* __restrict__ xexp) {
   __shared__ uint32_t wmax[16];
@@ -341,34 +370,30 @@ __global__ __launch_bounds__(1024) void xprep_kernel(const uint16_t* __restrict_
   const uint4* xr = (const uint4*)(x + (size_t)m * in_features);
   uint4* xo = (uint4*)(x16 + (size_t)m * in_features);
   const int n8 = in_features / 8;
-  uint32_t mx = 0;  // max of |x| as bits: orders like the values, NaN above infinity
-  for (int i = threadIdx.x; i < n8; i += 1024) {
-    const uint4 v = xr[i];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  const int tid = threadIdx.x;
+  // max of |x| as bits: orders like the values, NaN above infinity
+  uint32_t mx = 0;
+  uint4 held[kXprepHold];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) mx = max(mx, max(w[h] & 0x7FFFu, (w[h] >> 16) & 0x7FFFu));
-  }
+  for (int k = 0; k < kXprepHold; ++k) held[k] = xr[min(tid + k * 1024, n8 - 1)];  // clamped: no branch
+#pragma unroll
+  for (int k = 0; k < kXprepHold; ++k) mx = max(mx, tid + k * 1024 < n8 ? xprep_absmax(held[k]) : 0u);
+  for (int i = tid + kXprepHold * 1024; i < n8; i += 1024) mx = max(mx, xprep_absmax(xr[i]));
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
-  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = mx;
+  if ((tid & 63) == 0) wmax[tid >> 6] = mx;
   __syncthreads();
   mx = 0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) mx = max(mx, wmax[i]);
   const int e = max(0, (int)((mx >> 7) & 0xFFu) - 127 - 14);
-  for (int i = threadIdx.x; i < n8; i += 1024) {
-    const uint4 v = xr[i];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t o[4];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const uint32_t lo = vqd::f32_to_f16_rne(ldexpf(vqd::bf16_to_f32(w[h] & 0xFFFFu), -e));
-      const uint32_t hi = vqd::f32_to_f16_rne(ldexpf(vqd::bf16_to_f32(w[h] >> 16), -e));
-      o[h] = lo | (hi << 16);
-    }
-    xo[i] = make_uint4(o[0], o[1], o[2], o[3]);
+  for (int k = 0; k < kXprepHold; ++k) {
+    const int i = tid + k * 1024;
+    if (i < n8) xo[i] = xprep_convert(held[k], e);
   }
-  if (threadIdx.x == 0) xexp[m] = e;
+  for (int i = tid + kXprepHold * 1024; i < n8; i += 1024) xo[i] = xprep_convert(xr[i], e);
+  if (tid == 0) xexp[m] = e;
 }
 
 struct Plan {

@@ -507,7 +507,7 @@ def main():
         "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": "gemv_sliced_kernel<false>" if ring.sliced else "gemv_kernel<8,1,0,16,false,8>"},
+                     "kernel": "gemv_sliced_kernel<false>" if ring.sliced else "gemv_kernel<8,1,0,16,false,4>"},
         "gather": {"gathers_per_s": round(ring.desc.out_features * nv / sec, 1),
                    "effective_incl_gathered_centroids_GBps": round(g_cb, 2),
                    "note": "every 16-byte centroid lookup counted once: through L2 for the gather kernel, "

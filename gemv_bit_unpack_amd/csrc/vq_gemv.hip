@@ -334,7 +334,7 @@ constexpr int kNumCU = 256;
 #define VQ_GEMV_SMALL_PER_CU 8  // resident workgroups per CU assumed for the persistent grid
 #endif
 #ifndef VQ_GEMV_U1
-#define VQ_GEMV_U1 8  // vectors in flight per lane for M <= 2
+#define VQ_GEMV_U1 8  // vectors in flight per lane for M <= 2 (rows of up to 512 vectors: 4)
 #endif
 
 
@@ -620,10 +620,10 @@ vq_status dispatch_gemv6(const ProductArgs& a, hipStream_t s) {
   return a.m >= 2 ? launch_gemv6<2, RK, 2>(a, s) : launch_gemv6<1, RK, 4>(a, s);
 }
 
-template <int V, int MT, int XT, int IB1, int RK>
+template <int V, int MT, int XT, int IB1, int RK, int UQ>  // UQ: vectors per lane for MT <= 2
 vq_status launch_fast(const ProductArgs& a, hipStream_t s) {
   // vectors in flight per lane: fewer for wide centroids and large batches (registers)
-  constexpr int U0 = MT <= 2 ? VQ_GEMV_U1 : (MT <= 8 ? 4 : 2);
+  constexpr int U0 = MT <= 2 ? UQ : (MT <= 8 ? 4 : 2);
   constexpr int U = V > 8 ? (U0 > 4 ? 4 : (U0 > 1 ? U0 / 2 : 1)) : U0;
   constexpr bool kLds1 = IB1 != 16;
   const size_t lds_bytes =
@@ -651,11 +651,20 @@ vq_status launch_fast(const ProductArgs& a, hipStream_t s) {
 
 template <int V, int XT, int IB1, int RK>
 vq_status dispatch_m(const ProductArgs& a, hipStream_t s) {
-  if (a.m <= 1) return launch_fast<V, 1, XT, IB1, RK>(a, s);
-  if (a.m <= 2) return launch_fast<V, 2, XT, IB1, RK>(a, s);
-  if (a.m <= 4) return launch_fast<V, 4, XT, IB1, RK>(a, s);
-  if (a.m <= 8) return launch_fast<V, 8, XT, IB1, RK>(a, s);
-  return launch_fast<V, 16, XT, IB1, RK>(a, s);
+  // M <= 2: a row of at most 512 vectors takes four per lane, so that it runs in two
+  // steps with the second step's index loads in flight during the first one's gathers
+  // (4096-column layers: 14.6 -> 14.1 us with one global book, 18.3 -> 17.0 with a residual
+  // in LDS); longer rows, and two global books, keep eight (more gathers in flight)
+  if (a.m <= 2) {
+    if constexpr (V <= 8 && RK != 2)
+      if (a.nv <= 512)
+        return a.m <= 1 ? launch_fast<V, 1, XT, IB1, RK, 4>(a, s) : launch_fast<V, 2, XT, IB1, RK, 4>(a, s);
+    return a.m <= 1 ? launch_fast<V, 1, XT, IB1, RK, VQ_GEMV_U1>(a, s)
+                    : launch_fast<V, 2, XT, IB1, RK, VQ_GEMV_U1>(a, s);
+  }
+  if (a.m <= 4) return launch_fast<V, 4, XT, IB1, RK, 0>(a, s);
+  if (a.m <= 8) return launch_fast<V, 8, XT, IB1, RK, 0>(a, s);
+  return launch_fast<V, 16, XT, IB1, RK, 0>(a, s);
 }
 
 // Book placements with a fast kernel (checked by launch_gemv): main book global (16-bit)

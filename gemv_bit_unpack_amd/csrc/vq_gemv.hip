@@ -341,8 +341,8 @@ constexpr int kNumCU = 256;
 // ---------------------------------------------------------------------------------------
 // v = 6 decode kernel for fp16 activations with both books in LDS (the 8B-class MLP
 // layers: K1 = K2 = 4096, 12-bit indices).  The general kernel above spends ~97 VALU and
-// ~10 memory instructions per vector here (each lane extracts its own index fields from
-// global words and converts x and both centroids to fp32).  This one keeps the books'
+// ~10 memory instructions per 64 vectors here (each lane extracts its own index fields
+// from global words and converts x and both centroids to fp32).  This one keeps the books'
 // fp16 values and x in fp16 and multiplies them on the packed dot unit
 // (v_dot2_f32_f16: exact products, fp32 sums; the main book is added first, so a one-hot
 // x still yields fp32(c1 + c2)), and moves the index streams through LDS: per chunk of
@@ -361,7 +361,7 @@ typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // Dwords of one wavefront's LDS area per index stream: a chunk of U groups holds 2 * U * bits
-// dwords per stream; the area rounds the wider stream up to whole 64-lane stores.
+// dwords per stream; the area rounds the wider stream up to a multiple of 64 dwords.
 __host__ __device__ constexpr int area6(int u, int bits1, int bits2) {
   return 64 * ((u * (bits1 > bits2 ? bits1 : bits2) + 31) / 32);
 }
@@ -389,10 +389,8 @@ __device__ __forceinline__ uint32_t own_copy(uint32_t v) {
   return r;
 }
 
-// One chunk's loads, as loaded: U groups of 64 vectors.  q1/q2 hold this lane's share of
-// the index dwords, x the three dwords its vector's activation pairs sit in (per group and
-// batch row), sc/bi the raw fp16 scale and bias of the chunk's row.  What lies past the row
-// is masked off only when the chunk is used, so nothing waits on the loads before then.
+// One chunk's loads: U groups of 64 vectors.  q1/q2 hold this lane's share of the index
+// dwords, x the three dwords its vector's activation pairs sit in (per group and batch row).
 template <int MT, int U>
 struct Chunk6 {
   uint32_t q1[U / 2], q2[U / 2], x[U][MT][3];
@@ -423,8 +421,7 @@ __device__ __forceinline__ void load_q6(__amdgpu_buffer_rsrc_t b, int voff, int 
 template <int MT, int RK, int U>
 __device__ __forceinline__ void fetch6(const ProductArgs& a, int r, int cc, int lane, int dw1, int dw2,
                                        Chunk6<MT, U>& k) {
-  // index dwords: lane l takes dwords (U / 2) l .. (U / 2) l + U / 2 - 1 of the chunk in one
-  // load (a load instruction costs the texture data path about the same whatever its width)
+  // index dwords: lane l takes dwords (U / 2) l .. (U / 2) l + U / 2 - 1 of the chunk in one load
   const __amdgpu_buffer_rsrc_t b1 = rsrc6(a.packed1 + (size_t)r * a.s1_words, 4u * (uint32_t)a.s1_words);
   load_q6<U>(b1, 4 * (U / 2) * lane, 4 * cc * dw1, k.q1);
   if constexpr (RK != 0) {

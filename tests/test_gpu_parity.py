@@ -139,6 +139,9 @@ def test_gemv_parity_workloads(vq, key, layer, m):
     (65, 512, 8, 16, 16, 2, "f16", False, True),    # two global books (AQLM 2 x 2^16)
     (33, 1000, 8, 16, 16, 16, "bf16", True, True),
     (5, 104, 16, 12, 0, 2, "f16", True, False),     # v = 16 with an LDS main book: generic path
+    # the gather kernel takes 4 vectors per lane for rows of <= 512 vectors at M <= 2, else 8
+    (96, 4096, 8, 16, 8, 2, "f16", True, True),     # 512 vectors: two steps of 4 per lane
+    (96, 4104, 8, 16, 0, 1, "bf16", False, True),   # 513 vectors: 8 per lane, ragged last group
     # v = 6, fp16 x, M <= 2, books in LDS: the packed-dot kernel with LDS-staged index chunks
     (1000, 4100, 6, 12, 12, 1, "f16", True, True),  # last vector keeps 2 lanes
     (333, 1538, 6, 11, 9, 2, "f16", False, True),   # odd index widths; 257 vectors: two chunks

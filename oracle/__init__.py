@@ -52,9 +52,13 @@ def _load():
     with _lock:
         if _lib is not None:
             return _lib
-        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
-            build()
-        lib = ctypes.CDLL(_LIB_PATH)
+        # VQ_ORACLE_LIB names another build of vq_oracle.c (the sanitizer build of the tests)
+        path = os.environ.get("VQ_ORACLE_LIB")
+        if not path:
+            if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+                build()
+            path = _LIB_PATH
+        lib = ctypes.CDLL(path)
         i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
         lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
         lib.oracle_f16_to_f64.restype = ctypes.c_double
@@ -283,7 +287,8 @@ def rht(x, signs, transpose=False):
 
 def rvq_assign(w, v, cb1, cb2=None):
     """(idx1, idx2 or None) [n, in / v]: nearest main centroid, then nearest residual centroid of
-    the fp32 residual; ranking |c|^2 - 2 w.c in fp64, ties to the lowest index.  w: any float
+    the fp32 residual; nearest = the exact minimum of |w - c|^2 (decided in exact arithmetic),
+    ties to the lowest index; non-finite values as described in vq_oracle.h.  w: any float
     array [n, in] whose values are fp32-representable (fp16 / bf16 / fp32 weights)."""
     wd = np.ascontiguousarray(np.atleast_2d(np.asarray(w, dtype=np.float64)))
     n, i = wd.shape

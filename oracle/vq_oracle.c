@@ -535,56 +535,175 @@ int oracle_rht(int64_t M, int64_t n, const double* x, const uint8_t* signs, int 
 
 /* ---------------------------------------------------------------- residual VQ encode */
 
-/* Squared-distance ranking of centroid c (v fp16 values) against vector w (v doubles), the
- * quantity the assignment minimises: |c|^2 - 2 w.c (the constant |w|^2 dropped), in fp64,
- * each sum an ascending chain of fused multiply-adds, then fma(-2, w.c, |c|^2). */
-static double rank_distance(const double* w, const uint16_t* c, int v) {
-  double nc = 0.0, dot = 0.0;
-  for (int t = 0; t < v; ++t) {
-    const double ct = oracle_f16_to_f64(c[t]);
-    nc = fma(ct, ct, nc);
-    dot = fma(w[t], ct, dot);
+/*
+ * The encode picks, for each v-vector w, the centroid c_k of smallest squared Euclidean
+ * distance D_k = sum_t (w_t - c_t)^2 (VPTQ guide, "The Information-Theoretic Superiority of
+ * Vector Quantization": q(w) = argmin_k |w - c_k|^2; its "Step 2" quantizer takes
+ * torch.cdist and argmin, the first index among equal minima).  Here the minimum is the
+ * exact one: ties and near-ties are decided on exact values, never on a rounded distance.
+ *
+ * Exact values.  w_t is an fp32 value (fp16 / bf16 / fp32 weights, or an fp32 residual) and
+ * c_t an fp16 value, so each of w_t^2, w_t c_t and c_t^2 is exact in fp64 (at most 48, 35
+ * and 22 significant bits), and (w_t - c_t)^2 = w_t^2 - 2 w_t c_t + c_t^2 exactly.  D_k is
+ * therefore an exact sum of fp64 numbers, each an integer multiple of 2^-350 (the lowest
+ * bit of w_t^2 for the smallest fp32 subnormal is 2^-298, and a 53-bit significand reaches
+ * 52 bits below its leading bit) and below 2^257 in magnitude.  The sum is held as a
+ * two's-complement integer in units of 2^-350 in ten 64-bit limbs (640 bits).
+ */
+#define EXACT_LIMBS 10
+#define EXACT_UNIT_EXP (-350)
+typedef struct {
+  uint64_t limb[EXACT_LIMBS]; /* little-endian, two's complement */
+} exact_sum;
+
+/* acc += x (x finite, an integer multiple of 2^-350 below 2^257 in magnitude). */
+static void exact_add(exact_sum* acc, double x) {
+  if (x == 0.0) return;
+  int e;
+  const double f = frexp(fabs(x), &e);              /* |x| = f 2^e, 0.5 <= f < 1 */
+  uint64_t m = (uint64_t)ldexp(f, 53);              /* exact: f has at most 53 bits */
+  int shift = e - 53 - EXACT_UNIT_EXP;              /* |x| = m 2^(shift + unit exponent) */
+  while (shift < 0 && (m & 1u) == 0) {              /* drop trailing zero bits */
+    m >>= 1;
+    ++shift;
   }
-  return fma(-2.0, dot, nc);
+  if (shift < 0) abort();                           /* not a multiple of the unit */
+  const int li = shift / 64, off = shift % 64;
+  uint64_t part[EXACT_LIMBS] = {0};
+  const unsigned __int128 wide = (unsigned __int128)m << off;
+  part[li] = (uint64_t)wide;
+  if (li + 1 < EXACT_LIMBS) part[li + 1] = (uint64_t)(wide >> 64);
+  else if ((uint64_t)(wide >> 64) != 0) abort();
+  if (x < 0.0) { /* part = -part: complement and add one */
+    unsigned carry = 1;
+    for (int i = 0; i < EXACT_LIMBS; ++i) {
+      const uint64_t c = ~part[i] + carry;
+      carry = carry && c == 0;
+      part[i] = c;
+    }
+  }
+  unsigned carry = 0;
+  for (int i = 0; i < EXACT_LIMBS; ++i) {
+    const unsigned __int128 t = (unsigned __int128)acc->limb[i] + part[i] + carry;
+    acc->limb[i] = (uint64_t)t;
+    carry = (unsigned)(t >> 64);
+  }
 }
 
-/* Nearest centroid: the lowest index among those with the smallest ranking distance. */
-static uint32_t nearest(const double* w, const uint16_t* cb, int64_t k, int v) {
-  uint32_t best = 0;
-  double bd = INFINITY;
+/* Sign of a - b as signed integers: -1, 0 or 1. */
+static int exact_cmp(const exact_sum* a, const exact_sum* b) {
+  const int na = (int)(a->limb[EXACT_LIMBS - 1] >> 63), nb = (int)(b->limb[EXACT_LIMBS - 1] >> 63);
+  if (na != nb) return na ? -1 : 1;
+  for (int i = EXACT_LIMBS - 1; i >= 0; --i) {
+    if (a->limb[i] != b->limb[i]) return a->limb[i] < b->limb[i] ? -1 : 1;
+  }
+  return 0;
+}
+
+/* D = sum_t (w_t - c_t)^2 exactly, as w_t^2 - 2 w_t c_t + c_t^2 per coordinate. */
+static void exact_distance(const double* w, const uint16_t* c, int v, exact_sum* d) {
+  memset(d, 0, sizeof *d);
+  for (int t = 0; t < v; ++t) {
+    const double ct = oracle_f16_to_f64(c[t]);
+    exact_add(d, w[t] * w[t]);
+    exact_add(d, -2.0 * (w[t] * ct));
+    exact_add(d, ct * ct);
+  }
+}
+
+/* Kind of D_k under IEEE arithmetic on extended values: a NaN coordinate, or the same
+ * infinity in w and c at one coordinate (inf - inf), makes it NaN; otherwise any infinite
+ * coordinate makes it +inf; otherwise it is finite. */
+enum { DIST_FINITE = 0, DIST_INF = 1, DIST_NAN = 2 };
+static int distance_kind(const double* w, const uint16_t* c, int v) {
+  int inf = 0;
+  for (int t = 0; t < v; ++t) {
+    const double ct = oracle_f16_to_f64(c[t]);
+    if (isnan(w[t]) || isnan(ct)) return DIST_NAN;
+    if (isinf(w[t]) && isinf(ct) && (w[t] > 0) == (ct > 0)) return DIST_NAN;
+    if (isinf(w[t]) || isinf(ct)) inf = 1;
+  }
+  return inf ? DIST_INF : DIST_FINITE;
+}
+
+/* fp64 approximation of a finite D: fl(fl(w_t - c_t)^2) summed in ascending t.  Every term
+ * is >= 0 and none underflows or overflows (w_t - c_t is 0 or at least 2^-149 and below
+ * 2^129), so the result is D times a factor within (1 -+ u)^(v + 2), u = 2^-53: the
+ * difference, the square and at most v - 1 additions each round once. */
+static double approx_distance(const double* w, const uint16_t* c, int v) {
+  double d = 0.0;
+  for (int t = 0; t < v; ++t) {
+    const double diff = w[t] - oracle_f16_to_f64(c[t]);
+    d = d + diff * diff;
+  }
+  return d;
+}
+
+/* Nearest centroid of w among k, as defined above: the smallest exact D_k among finite
+ * distances, the lowest index among equal ones; with no finite distance the lowest index
+ * whose distance is +inf; with every distance NaN, index 0.  The fp64 approximations only
+ * select which centroids get an exact evaluation: with rho = 2 (v + 3) u, every exact D_k
+ * lies in [a_k (1 - rho), a_k (1 + rho)] (a_k the approximation), so the exact minimum is
+ * among the centroids whose lower end is at most the smallest upper end. */
+static uint32_t nearest(const double* w, const uint16_t* cb, int64_t k, int v, double* approx) {
+  const double rho = 2.0 * (v + 3) * 0x1p-53;
+  int64_t first_inf = -1;
+  double min_hi = INFINITY;
+  int any_finite = 0;
   for (int64_t i = 0; i < k; ++i) {
-    const double d = rank_distance(w, cb + i * v, v);
-    if (d < bd) {
+    const int kind = distance_kind(w, cb + i * v, v);
+    if (kind == DIST_FINITE) {
+      approx[i] = approx_distance(w, cb + i * v, v);
+      const double hi = approx[i] * (1.0 + rho);
+      if (hi < min_hi) min_hi = hi;
+      any_finite = 1;
+    } else {
+      approx[i] = NAN;
+      if (kind == DIST_INF && first_inf < 0) first_inf = i;
+    }
+  }
+  if (!any_finite) return first_inf >= 0 ? (uint32_t)first_inf : 0u;
+  uint32_t best = 0;
+  int have = 0;
+  exact_sum bd, d;
+  for (int64_t i = 0; i < k; ++i) {
+    if (!(approx[i] * (1.0 - rho) <= min_hi)) continue; /* also skips the NaN markers */
+    exact_distance(w, cb + i * v, v, &d);
+    if (!have || exact_cmp(&d, &bd) < 0) { /* increasing i: equal ones keep the lower index */
       bd = d;
       best = (uint32_t)i;
+      have = 1;
     }
   }
   return best;
 }
 
 /* Two-stage residual VQ encode (VPTQ guide, "Step 2: Multi-Stage Residual Vector Quantizer
- * (RVQ)": each v-vector of W takes the nearest main centroid, the residual
- * r = w - C1[idx1] (computed in fp32) takes the nearest residual centroid; the guide uses
- * Euclidean distances and argmin, which keeps the first of equal distances).  Codebooks
- * are given (the guide's random-sample initialisation and any k-means are outside this).
- * w: [n][in] as doubles holding fp32 values; in % v == 0; cb1 fp16 [k1][v]; cb2 fp16
- * [k2][v] or NULL when k2 == 0 (idx2 untouched). */
+ * (RVQ)"): each v-vector of W takes the nearest main centroid, the residual
+ * r = w - C1[idx1] (computed in fp32, as the guide's residuals are) takes the nearest
+ * residual centroid.  Codebooks are given (the guide's random-sample initialisation and
+ * any k-means are outside this).  w: [n][in] as doubles holding fp32 values; in % v == 0;
+ * cb1 fp16 [k1][v]; cb2 fp16 [k2][v] or NULL when k2 == 0 (idx2 untouched). */
 int oracle_rvq_assign(int64_t n, int64_t in_features, int v, int64_t k1, int64_t k2, const double* w,
                       const uint16_t* cb1, const uint16_t* cb2, uint32_t* idx1, uint32_t* idx2) {
   if (n < 0 || in_features < 0 || v < 1 || v > 16 || k1 < 1 || k2 < 0 || in_features % v != 0) return ORACLE_BAD_ARGS;
   if (n * in_features > 0 && (!w || !cb1 || !idx1 || (k2 > 0 && (!cb2 || !idx2)))) return ORACLE_BAD_ARGS;
   const int64_t nv = in_features / v;
+  if (n * nv == 0) return ORACLE_OK;
+  double* approx = (double*)malloc((size_t)(k1 > k2 ? k1 : k2) * sizeof(double));
+  if (!approx) return ORACLE_BAD_ARGS;
   for (int64_t o = 0; o < n; ++o) {
     for (int64_t j = 0; j < nv; ++j) {
       const double* wv = w + o * in_features + j * v;
-      const uint32_t i1 = nearest(wv, cb1, k1, v);
+      const uint32_t i1 = nearest(wv, cb1, k1, v, approx);
       idx1[o * nv + j] = i1;
       if (k2 > 0) {
         double r[16];
         for (int t = 0; t < v; ++t) r[t] = (double)((float)wv[t] - (float)oracle_f16_to_f64(cb1[(int64_t)i1 * v + t]));
-        idx2[o * nv + j] = nearest(r, cb2, k2, v);
+        idx2[o * nv + j] = nearest(r, cb2, k2, v, approx);
       }
     }
   }
+  free(approx);
   return ORACLE_OK;
 }

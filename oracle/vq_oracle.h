@@ -106,8 +106,11 @@ int oracle_rht(int64_t M, int64_t n, const double* x, const uint8_t* signs, int 
 /*
  * Two-stage residual VQ encode with given codebooks: idx1 = nearest main centroid of each
  * v-vector of w, idx2 = nearest residual centroid of r = fl32(w - C1[idx1]); "nearest" is the
- * lowest index minimising |c|^2 - 2 w.c in fp64 (fma chains).  w: [n][in] doubles holding
- * fp32 values, in % v == 0.
+ * lowest index of the exact minimum of |w - c|^2 (decided in exact arithmetic, not on a
+ * rounded distance).  Non-finite values: a distance is NaN when a coordinate is NaN or holds
+ * the same infinity in w and c, else +inf when a coordinate is infinite; finite distances
+ * win over +inf, NaN ones are never taken, and index 0 is returned when all are NaN.
+ * w: [n][in] doubles holding fp32 values, in % v == 0.
  */
 int oracle_rvq_assign(int64_t n, int64_t in_features, int v, int64_t k1, int64_t k2, const double* w,
                       const uint16_t* cb1, const uint16_t* cb2, uint32_t* idx1, uint32_t* idx2);

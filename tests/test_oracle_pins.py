@@ -18,6 +18,7 @@ import numpy as np
 import pytest
 import torch
 
+import neartie
 import synth
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -744,6 +745,45 @@ def test_rvq_scalar_levels_closed_form(oracle_mod):
     mids = (levels[1:] + levels[:-1]) / 2
     want = np.searchsorted(mids, w[0].astype(np.float64), side="left")
     assert np.array_equal(i1[0], want)
+
+
+@pytest.mark.parametrize("w_dtype,v,k,seed", [("f32", 8, 16, 21), ("f16", 8, 256, 22), ("f32", 4, 8, 23),
+                                           ("f16", 16, 64, 24), ("f32", 3, 2, 25)])
+def test_rvq_near_ties_decided_exactly(oracle_mod, w_dtype, v, k, seed):
+    """Pairs of centroids whose exact squared distances differ by ~2^-40 (fp32 weights) or
+    3 * 2^-36 (fp16 weights) beside terms of 2^45 / 2^31: only cases where an fp64 ranking
+    of |c|^2 - 2 w.c picks the other row are kept, so a rounded-distance encode fails here."""
+    for w, book, want in neartie.disagreeing_cases(seed, 6, v, w_dtype, k):
+        assert want == neartie.exact_pick(w.astype(np.float64), book.astype(np.float64))
+        i1, _ = oracle_mod.rvq_assign(w[None, :], v, book.view(np.uint16))
+        assert int(i1[0, 0]) == want
+        # the same decision in the residual stage: main book = the zero vector (row 0, nearest)
+        # and far rows, so the fp32 residual is w itself
+        c1 = np.zeros((4, v), np.float16)
+        c1[1:, 0] = np.float16(-65504.0)
+        j1, j2 = oracle_mod.rvq_assign(w[None, :], v, c1.view(np.uint16), book.view(np.uint16))
+        assert int(j1[0, 0]) == 0 and int(j2[0, 0]) == want
+
+
+def test_rvq_non_finite_reading(oracle_mod):
+    """Distances under IEEE arithmetic on extended values: NaN when a coordinate is NaN or the
+    same infinity sits in w and c; +inf when a coordinate is infinite; finite ones win, NaN
+    ones are never taken, all-NaN gives index 0."""
+    inf, nan = np.inf, np.nan
+    book = _f16v([[inf, 0], [1, 0], [0, nan], [-inf, 0], [0, 0]])
+    cases = [
+        ([nan, 0], 0),      # every distance NaN
+        ([inf, 0], 1),      # row 0: inf - inf = NaN; rows 1, 3, 4: +inf (row 2: NaN): first is 1
+        ([-inf, 0], 0),     # row 0: -inf - inf = -inf, squared +inf: row 0 first
+        ([0.5, 0], 1),      # finite rows 1 and 4 tie at 0.25: row 1; rows 0, 3 +inf, row 2 NaN
+        ([0.25, 0], 4),     # finite: row 4 (0.0625) beats row 1 (0.5625)
+    ]
+    for w, want in cases:
+        i1, _ = oracle_mod.rvq_assign(np.array([w], np.float32), 2, book)
+        assert int(i1[0, 0]) == want, (w, int(i1[0, 0]), want)
+    only_bad = _f16v([[nan, 0], [inf, 1], [0, -inf]])
+    i1, _ = oracle_mod.rvq_assign(np.array([[1.0, 1.0]], np.float32), 2, only_bad)
+    assert int(i1[0, 0]) == 1  # no finite distance: the first +inf one
 
 
 def test_rvq_permuting_the_book_permutes_the_indices(oracle_mod):

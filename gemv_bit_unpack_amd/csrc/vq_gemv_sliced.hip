@@ -27,7 +27,8 @@
 //     order and applies the channel scale and bias, so results do not depend on
 //     scheduling.
 // bf16 activations are first rewritten as fp16 times a power of two per batch row (a
-// small pass over x): exact for every bf16 value from 2^-16 to 65504 times that power.
+// small pass over x), chosen from the row's largest magnitude: exact for every value down
+// to 2^-31 of that magnitude, whether the row is large, small or in between.
 #include "vq_device.h"
 
 namespace {
@@ -337,8 +338,11 @@ __global__ __launch_bounds__(256) void gemv_sliced_finalize(ProductArgs a, const
   vqd::store_out(a.y, (size_t)m * a.n + row, acc, a.y_dtype);
 }
 
-// bf16 activations -> fp16 * 2^e, one workgroup per batch row: e is the smallest
-// exponent >= 0 that brings max |x| below 2^15, so every finite value stays finite.
+// bf16 activations -> fp16 * 2^e, one workgroup per batch row: e puts max |x| * 2^-e in
+// [2^14, 2^15), so every finite value stays finite and a row of small values is scaled up
+// into the normal fp16 range as a row of large ones is scaled down.  Every value at least
+// max |x| * 2^-31 converts exactly; smaller ones round with absolute error below
+// 2^-25 * 2^e.  An all-zero row takes e = -141 (its zeros stay zeros).
 // Rows of up to 4 * 1024 * 8 values are read once into registers (all loads in flight
 // together) and converted from there; longer rows are walked in passes of that size.
 constexpr int kXprepHold = 4;  // 16-byte words per thread held in registers
@@ -386,7 +390,7 @@ __global__ __launch_bounds__(1024) void xprep_kernel(const uint16_t* __restrict_
   mx = 0;
 #pragma unroll
   for (int i = 0; i < 16; ++i) mx = max(mx, wmax[i]);
-  const int e = max(0, (int)((mx >> 7) & 0xFFu) - 127 - 14);
+  const int e = (int)((mx >> 7) & 0xFFu) - 127 - 14;
 #pragma unroll
   for (int k = 0; k < kXprepHold; ++k) {
     const int i = tid + k * 1024;

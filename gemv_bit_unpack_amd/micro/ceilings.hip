@@ -3,7 +3,15 @@
 //   - random 16-byte gathers from a table in global memory (table sizes from L1-resident
 //     to larger than one XCD's L2), the operation behind every centroid lookup of a
 //     65536-entry codebook;
-//   - random 16-byte gathers from LDS tables (the small-codebook path).
+//   - random 16-byte gathers from LDS tables (the small-codebook path);
+//   - the LDS read rate with little VALU work per read (addresses held in registers,
+//     constant offsets), for four address patterns of a 64-lane 16-byte read: random,
+//     7 of 8 lanes on one address, 1 of 8 lanes active, and conflict-free;
+//   - the issue rate of the matrix instructions the products use (16x16x32, 32x32x16,
+//     4x4x4 with 16 blocks, fp16) and of the packed fp16 dot (v_dot2_f32_f16);
+//   - the rate at which 8 workgroups on one XCD can all read the same stream (each
+//     byte fetched once from HBM, then served 7 more times by the XCD's L2), against
+//     each workgroup reading its own stream.
 // Every index is masked into its table.  Prints one JSON object.
 #include <hip/hip_runtime.h>
 
@@ -68,6 +76,134 @@ __global__ void gather_lds(const uint4* __restrict__ tab, unsigned entries, int 
   if (acc == 0x12345678u) out[0] = acc;
 }
 
+// LDS read rate.  Each lane holds 8 table offsets in registers; the loop reads 4
+// consecutive entries from each (constant instruction offsets: no address VALU) and
+// folds the 16 bytes with two 3-input adds, so the SIMDs issue 2 VALU per read.
+//   MODE 0: random entries of a 128 KiB table;
+//   MODE 1: lanes 1..7 of every 8 read entry kLdsEntries - 4, lane 0 a random one;
+//   MODE 2: only lanes 0, 8, ..., 56 run the loop (7 of 8 lanes masked off);
+//   MODE 3: lane l reads entry l + 64 k (each group of 16 lanes covers all 64 banks).
+constexpr unsigned kLdsEntries = 8192;
+template <int MODE>
+__global__ __launch_bounds__(512) void lds_rate(const uint4* __restrict__ tab, int iters, unsigned* out) {
+  __shared__ uint4 t[kLdsEntries];
+  for (unsigned e = threadIdx.x; e < kLdsEntries; e += blockDim.x) t[e] = tab[e];
+  __syncthreads();
+  const unsigned lane = threadIdx.x & 63;
+  unsigned h = (blockIdx.x * blockDim.x + threadIdx.x) * 2654435761u + 12345u;
+  unsigned a[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    h = h * 1664525u + 1013904223u;
+    unsigned e = (h >> 9) % (kLdsEntries - 4);  // entries e .. e + 3 stay in the table
+    if (MODE == 1 && (lane & 7)) e = kLdsEntries - 4;
+    if (MODE == 3) e = lane + 64 * k;
+    a[k] = e;
+  }
+  unsigned acc0 = 0, acc1 = 0;
+  if (MODE != 2 || (lane & 7) == 0) {
+    for (int it = 0; it < iters; ++it) {
+      asm volatile("" ::: "memory");  // the table may have changed: read it again every pass
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const uint4 v = t[a[k] + j];
+          acc0 = acc0 + v.x + v.y;  // v_add3_u32
+          acc1 = acc1 + v.z + v.w;
+        }
+      }
+    }
+  }
+  if ((acc0 ^ acc1) == 0x12345678u) out[0] = acc0;
+}
+
+typedef _Float16 mr_half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 mr_half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 mr_half2 __attribute__((ext_vector_type(2)));
+typedef float mr_float4 __attribute__((ext_vector_type(4)));
+typedef float mr_float16 __attribute__((ext_vector_type(16)));
+
+// Matrix-instruction issue rate: 4 independent accumulator chains per wavefront.
+//   KIND 0: v_mfma_f32_16x16x32_f16; KIND 1: v_mfma_f32_32x32x16_f16;
+//   KIND 2: v_mfma_f32_4x4x4_16b_f16 (16 blocks).
+template <int KIND>
+__global__ __launch_bounds__(256) void mfma_rate(int iters, float* out) {
+  const float s = (float)(threadIdx.x & 7) * 0.001f;
+  float sum = 0.0f;
+  if constexpr (KIND == 0) {
+    const mr_half8 a = {(_Float16)s, 1, 2, 3, 4, 5, 6, 7}, b = {1, 1, 1, 1, 1, 1, 1, (_Float16)s};
+    mr_float4 c0 = {0, 0, 0, 0}, c1 = c0, c2 = c0, c3 = c0;
+    for (int it = 0; it < iters; ++it) {
+      c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c3, 0, 0, 0);
+    }
+    sum = c0[0] + c1[1] + c2[2] + c3[3];
+  } else if constexpr (KIND == 1) {
+    const mr_half8 a = {(_Float16)s, 1, 2, 3, 4, 5, 6, 7}, b = {1, 1, 1, 1, 1, 1, 1, (_Float16)s};
+    mr_float16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+    for (int it = 0; it < iters; ++it) {
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c3, 0, 0, 0);
+    }
+    sum = c0[0] + c1[5] + c2[10] + c3[15];
+  } else {
+    const mr_half4 a = {(_Float16)s, 1, 2, 3}, b = {1, 1, 1, (_Float16)s};
+    mr_float4 c0 = {0, 0, 0, 0}, c1 = c0, c2 = c0, c3 = c0;
+    for (int it = 0; it < iters; ++it) {
+      c0 = __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_f32_4x4x4f16(a, b, c3, 0, 0, 0);
+    }
+    sum = c0[0] + c1[1] + c2[2] + c3[3];
+  }
+  if (sum == 1234.5f) out[0] = sum;
+}
+
+// Packed fp16 dot (v_dot2_f32_f16) issue rate: 8 independent chains per lane.
+__global__ __launch_bounds__(256) void dot2_rate(int iters, float* out) {
+  const mr_half2 a = {(_Float16)((threadIdx.x & 7) * 0.001f), (_Float16)1}, b = {(_Float16)1, (_Float16)0.5f};
+  float c[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) c[k] = (float)k;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) c[k] = __builtin_amdgcn_fdot2(a, b, c[k], false);
+  }
+  float sum = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) sum += c[k];
+  if (sum == 1234.5f) out[0] = sum;
+}
+
+// Shared-stream read: 256 workgroups of 512 threads as 32 groups of 8 (the 8 workgroups of
+// a group have consecutive ids above the XCD bits, so they land on one XCD).  SHARED: the 8
+// read the same `per` bytes of their group's region; otherwise each reads its own.
+template <bool SHARED>
+__global__ __launch_bounds__(512) void group_stream(const uint4* __restrict__ p, size_t per16, unsigned* out) {
+  const int xcd = blockIdx.x & 7;
+  const int rest = blockIdx.x >> 3;
+  const int s = rest & 7;
+  const int grp = (rest >> 3) * 8 + xcd;
+  const uint4* q = p + (SHARED ? (size_t)grp : (size_t)grp * 8 + s) * per16;
+  unsigned acc = 0;
+  size_t i = threadIdx.x;
+  for (; i + 7 * 512 < per16; i += 8 * 512) {
+    uint4 v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = q[i + k * 512];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc ^= v[k].x ^ v[k].w;
+  }
+  for (; i < per16; i += 512) acc ^= q[i].x;
+  if (acc == 0x12345678u) out[0] = acc;
+}
+
 int main() {
   hipDeviceProp_t prop;
   CHECK(hipGetDeviceProperties(&prop, 0));
@@ -129,7 +265,64 @@ int main() {
            g, g / (ncu * clk));
     first = false;
   }
-  printf("}}\n");
+  printf("}");
+
+  // LDS read rate at 512 threads (one workgroup per CU: the 128 KiB table), 4 patterns.
+  printf(", \"lds_read_b128\": {");
+  const char* lds_modes[4] = {"random", "seven_of_eight_one_address", "one_of_eight_active", "conflict_free"};
+  for (int mode = 0; mode < 4; ++mode) {
+    const int grid = ncu, iters = 512;
+    auto launch = [&] {
+      switch (mode) {
+        case 0: hipLaunchKernelGGL(lds_rate<0>, dim3(grid), dim3(512), 0, 0, buf, iters, dout); break;
+        case 1: hipLaunchKernelGGL(lds_rate<1>, dim3(grid), dim3(512), 0, 0, buf, iters, dout); break;
+        case 2: hipLaunchKernelGGL(lds_rate<2>, dim3(grid), dim3(512), 0, 0, buf, iters, dout); break;
+        default: hipLaunchKernelGGL(lds_rate<3>, dim3(grid), dim3(512), 0, 0, buf, iters, dout); break;
+      }
+    };
+    const double t = timed(launch, 3);
+    const double instr = (double)grid * (512 / 64) * iters * 32;  // 64-lane read instructions
+    printf("%s\"%s\": {\"clk_per_instr_per_cu\": %.3f, \"active_lanes_per_clk_per_cu\": %.3f}", mode ? ", " : "",
+           lds_modes[mode], t * clk * ncu / instr, instr * (mode == 2 ? 8 : 64) / (t * clk * ncu));
+  }
+  printf("}");
+
+  // Matrix and dot instruction issue rates at 4 wavefronts per SIMD.
+  printf(", \"issue\": {");
+  const char* mnames[3] = {"mfma_f32_16x16x32_f16", "mfma_f32_32x32x16_f16", "mfma_f32_4x4x4_16b_f16"};
+  float* fout = (float*)dout;
+  for (int kind = 0; kind < 3; ++kind) {
+    const int grid = ncu * 4, iters = 4096;
+    auto launch = [&] {
+      if (kind == 0) hipLaunchKernelGGL(mfma_rate<0>, dim3(grid), dim3(256), 0, 0, iters, fout);
+      else if (kind == 1) hipLaunchKernelGGL(mfma_rate<1>, dim3(grid), dim3(256), 0, 0, iters, fout);
+      else hipLaunchKernelGGL(mfma_rate<2>, dim3(grid), dim3(256), 0, 0, iters, fout);
+    };
+    const double t = timed(launch, 3);
+    const double instr = (double)grid * 4 * iters * 4;  // per wavefront: 4 chains x iters
+    printf("%s\"%s\": {\"clk_per_instr_per_simd\": %.2f}", kind ? ", " : "", mnames[kind],
+           t * clk * ncu * 4 / instr);
+  }
+  {
+    const int grid = ncu * 4, iters = 4096;
+    const double t = timed([&] { hipLaunchKernelGGL(dot2_rate, dim3(grid), dim3(256), 0, 0, iters, fout); }, 3);
+    const double instr = (double)grid * 4 * iters * 8;
+    printf(", \"v_dot2_f32_f16\": {\"clk_per_instr_per_simd\": %.2f}", t * clk * ncu * 4 / instr);
+  }
+  printf("}");
+
+  // Eight workgroups of one XCD reading one stream vs their own streams.
+  {
+    const size_t per = (size_t)8 << 20;  // bytes per stream
+    const int grid = 256;
+    const double ts = timed([&] { hipLaunchKernelGGL(group_stream<true>, dim3(grid), dim3(512), 0, 0, buf, per / 16, dout); }, 3);
+    const double td = timed([&] { hipLaunchKernelGGL(group_stream<false>, dim3(grid), dim3(512), 0, 0, buf, per / 16, dout); }, 3);
+    const double delivered = (double)grid * per;
+    printf(", \"group_stream\": {\"bytes_per_workgroup\": %zu, \"shared_by_8_delivered_GBps\": %.1f, "
+           "\"shared_B_per_clk_per_cu\": %.2f, \"own_stream_GBps\": %.1f}",
+           per, delivered / ts / 1e9, delivered / ts / clk / grid, delivered / td / 1e9);
+  }
+  printf("}\n");
   CHECK(hipFree(buf));
   return 0;
 }

@@ -248,7 +248,7 @@ def test_gemv_and_gemm_on_side_stream(vq):
 
 GEMM_CASES = [("tiny", 0, 1), ("tiny", 0, 33), ("dec4k", 0, 32), ("dec4k_res", 0, 16), ("dec4k_res", 0, 40),
               ("mlp8b", 1, 32), ("mlp8b", 0, 4), ("l70b", 0, 32), ("l70b", 0, 128), ("l70b", 1, 128),
-              ("l70b", 0, 256), ("l70b", 1, 8)]
+              ("l70b", 0, 256), ("l70b", 1, 8), ("l70b", 1, 32), ("l70b", 1, 256)]
 
 
 @pytest.mark.parametrize("key,layer,m", GEMM_CASES)

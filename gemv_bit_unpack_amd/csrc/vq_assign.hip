@@ -1,20 +1,27 @@
 // vq_assign: two-stage residual VQ encode with given codebooks (VPTQ guide, "Step 2:
-// Multi-Stage Residual Vector Quantizer (RVQ)"; the distance and argmin of "1. Vector
-// Quantization Fundamentals"; the residual of "2. Multi-Stage Residual Vector
-// Quantization").  Each v-vector w of W takes
+// Multi-Stage Residual Vector Quantizer (RVQ)"; the nearest-centroid rule of "The
+// Information-Theoretic Superiority of Vector Quantization"; the residual of "2.
+// Multi-Stage Residual Vector Quantization").  Each v-vector w of W takes
 //
-//   idx1 = the lowest k minimising |C1[k]|^2 - 2 w . C1[k]
-//   idx2 = the lowest k minimising |C2[k]|^2 - 2 r . C2[k],   r = fp32(w - C1[idx1])
+//   idx1 = the lowest k of the exact minimum of |w - C1[k]|^2
+//   idx2 = the lowest k of the exact minimum of |r - C2[k]|^2,   r = fp32(w - C1[idx1])
 //
-// which ranks centroids as the squared Euclidean distance does (|w|^2 is common to all).
-// The ranking is evaluated in fp64 with one fused multiply-add per term, in ascending
-// coordinate order: the products of fp16 centroids with fp16 / bf16 / fp32 weights are
-// exact in fp64, and the index taken is the same on every conforming implementation of
-// that sequence of operations.
+// Centroids are ranked by d(c) = |c|^2 - 2 w . c, which orders them as the squared distance
+// does (|w|^2 is common to all), evaluated in fp64 with one fused multiply-add per term.
+// That value is within E = v 2^-53 (|c|^2 + 2 sum_t |w_t c_t|) of the exact one, so a
+// centroid whose fp64 value differs from the best one's by more than the two bounds is
+// ordered by it.  The fast kernels take only such certain decisions; a vector that meets a
+// closer pair (a near tie, or an exact one) is marked (top bit of its index) and the
+// fix-up kernel ranks it again with exact comparisons: for fp16 centroids and fp16 / bf16
+// / fp32 weights every product c_t^2 and 2 w_t c_t is exact in fp64, and `exact_order`
+// adds them exactly in 384-bit fixed point.  Vectors and books holding NaN or infinite
+// values are marked too; `nearest_general` ranks their IEEE distances: NaN ones never,
+// finite ones before +inf.
 //
 // Kernels:
 //   assign_table_kernel  one thread per centroid: the fp64 record {|c|^2, c_0 .. c_{v-1}}
-//                        of each fp16 centroid into the workspace.
+//                        of each fp16 centroid into the workspace, and per 256 centroids
+//                        the largest |c_t| and |c|^2 (infinite if any value is not finite).
 //   assign_mfma_table_kernel, assign_mfma_kernel<V>  the main stage for fp16 weights and
 //                        books of 256 or more centroids on the matrix cores (below).
 //   assign_kernel<V, R, WT, FIRST>  both stages (the residual stage only, after the
@@ -22,13 +29,16 @@
 //                        consecutive vectors), the vectors held in fp64 registers; every
 //                        wave walks the whole record table in index order with uniform
 //                        (scalar-unit) loads, so each centroid costs V + 1 fp64 FMAs and
-//                        one compare per vector, and the rare improvements take a branch
-//                        that the wave skips when none of its lanes improves.
+//                        one compare per vector, and the rare improvements or near ties
+//                        take a branch that the wave skips when none of its lanes needs it.
+//   assign_fixup_kernel<V, WT>  one thread per vector: marked vectors are ranked again by
+//                        nearest_general (both stages when the main index was marked).
 #include "vq_device.h"
 
 namespace {
 
 constexpr int kThreads = 256;
+constexpr uint32_t kMark = 0x80000000u;  // index needs the exact ranking (indices are < 2^16)
 
 template <int WT>  // VQ_F16, VQ_BF16, VQ_F32
 __device__ __forceinline__ double weight_at(const void* w, int64_t i) {
@@ -42,29 +52,170 @@ __device__ __forceinline__ double weight_at(const void* w, int64_t i) {
 }
 
 __global__ __launch_bounds__(kThreads) void assign_table_kernel(const uint16_t* __restrict__ cb, int32_t k, int32_t v,
-                                                                double* __restrict__ tab) {
+                                                                double* __restrict__ tab, double2* __restrict__ tmax) {
   const int32_t c = blockIdx.x * kThreads + threadIdx.x;
-  if (c >= k) return;
-  double* rec = tab + (size_t)c * (size_t)(v + 1);
-  double nc = 0.0;
-  for (int t = 0; t < v; ++t) {
-    const double ct = (double)vqd::f16_to_f32(cb[(size_t)c * v + t]);
-    nc = fma(ct, ct, nc);
-    rec[1 + t] = ct;
+  double cm = 0.0, nm = 0.0;
+  if (c < k) {
+    double* rec = tab + (size_t)c * (size_t)(v + 1);
+    double nc = 0.0;
+    bool fin = true;
+    for (int t = 0; t < v; ++t) {
+      const double ct = (double)vqd::f16_to_f32(cb[(size_t)c * v + t]);
+      nc = fma(ct, ct, nc);
+      rec[1 + t] = ct;
+      fin = fin && __builtin_isfinite(ct);
+      cm = fmax(cm, fabs(ct));
+    }
+    rec[0] = nc;
+    nm = nc;
+    if (!fin) cm = nm = __builtin_inf();
   }
-  rec[0] = nc;
+  __shared__ double2 red[kThreads / 64];
+  for (int o = 32; o > 0; o >>= 1) {
+    cm = fmax(cm, __shfl_xor(cm, o));
+    nm = fmax(nm, __shfl_xor(nm, o));
+  }
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = make_double2(cm, nm);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double2 m = red[0];
+    for (int i = 1; i < kThreads / 64; ++i) m = make_double2(fmax(m.x, red[i].x), fmax(m.y, red[i].y));
+    tmax[blockIdx.x] = m;
+  }
 }
 
-// Lowest index minimising the ranking distance, for each of the lane's R vectors.  The
-// record of centroid c + 1 is loaded while centroid c is ranked.
+// Book maxima {largest |c_t|, largest |c|^2} from the per-256-centroid table (uniform loads).
+__device__ __forceinline__ double2 book_max(const double2* __restrict__ tmax, int32_t k) {
+  const int nb = (k + kThreads - 1) / kThreads;
+  double2 m = make_double2(0.0, 0.0);
+  for (int i = 0; i < nb; ++i) {
+    const double2 b = tmax[i];
+    m = make_double2(fmax(m.x, b.x), fmax(m.y, b.y));
+  }
+  return m;
+}
+
+// Bound on |d~(c) - d(c) + d~(c') - d(c')| for every pair of centroids of a book, for one
+// vector (S_w = sum |w_t|): twice (V + 2) 2^-53 (|c|^2 + 2 sum_t |w_t c_t|), the latter at
+// most ncmax + 2 S_w cmax.  The margins over the V 2^-53 of the error analysis cover the
+// rounding of this expression.
+template <int V>
+__device__ __forceinline__ double pair_bound(double sw, double cmax, double ncmax) {
+  return 2.0 * (V + 2) * 0x1p-53 * (ncmax + 2.0 * sw * cmax) * (1.0 + 0x1p-20);
+}
+
+// Exact comparison of ranking distances.  For fp16 centroids and weights that are fp32
+// values, c_t^2 and 2 w_t c_t are exact fp64 numbers, each an integer multiple of 2^-226
+// (the lowest bit of an fp32 subnormal times an fp16 subnormal, times the 53-bit
+// significand's span) and below 2^146.  Positive and negative terms are added into two
+// unsigned 384-bit integers in units of 2^-226 (six 64-bit limbs; at most 4V <= 64 terms
+// stay below 2^152), which are then compared.
+constexpr int kUnitExp = -226;
+
+__device__ __forceinline__ void exact_acc(uint64_t (&a)[6], double x) {  // x > 0, as above
+  const uint64_t bits = __builtin_bit_cast(uint64_t, x);
+  const int sh = (int)(bits >> 52) - 1075 - kUnitExp;  // x = m 2^(sh + kUnitExp), 1 <= sh < 320
+  const uint64_t m = (bits & ((1ull << 52) - 1ull)) | (1ull << 52);
+  const int q = sh >> 6, r = sh & 63;
+  const uint64_t lo = m << r;
+  const uint64_t hi = r ? (m >> (64 - r)) : 0ull;
+  uint64_t carry = 0;
+#pragma unroll
+  for (int j = 0; j < 6; ++j) {
+    const uint64_t add = (j == q) ? lo : ((j == q + 1) ? hi : 0ull);
+    const uint64_t t = a[j] + add;
+    const uint64_t t2 = t + carry;
+    carry = (uint64_t)(t < add) | (uint64_t)(t2 < carry);
+    a[j] = t2;
+  }
+}
+
+// Sign of d(a) - d(b), d(c) = sum_t c_t^2 - 2 w_t c_t, all values finite: -1, 0 or 1.
+template <int V>
+__device__ __noinline__ int exact_order(const double* w, const double* ca, const double* cb) {
+  uint64_t pos[6] = {0, 0, 0, 0, 0, 0}, neg[6] = {0, 0, 0, 0, 0, 0};
+  auto put = [&](double x) {
+    if (x > 0.0) exact_acc(pos, x);
+    else if (x < 0.0) exact_acc(neg, -x);
+  };
+  for (int t = 0; t < V; ++t) {
+    const double a = ca[t], b = cb[t];
+    put(a * a);
+    put(-(b * b));
+    put(-2.0 * (w[t] * a));
+    put(2.0 * (w[t] * b));
+  }
+  for (int j = 5; j >= 0; --j) {
+    if (pos[j] != neg[j]) return pos[j] > neg[j] ? 1 : -1;
+  }
+  return 0;
+}
+
+// Nearest centroid for vectors or books with NaN or infinite values (or anything else):
+// the distance of a centroid is NaN when a coordinate is NaN or holds the same infinity in
+// w and c, +inf when a coordinate is infinite, finite otherwise.  The lowest index of the
+// exact smallest finite distance, else the lowest +inf one, else 0.  Finite distances are
+// ranked in fp64 with each centroid's own bound and near ones ordered exactly.
+template <int V>
+__device__ __noinline__ uint32_t nearest_general(const double* w, const double* __restrict__ tab, int32_t k) {
+  for (int t = 0; t < V; ++t) {
+    if (__builtin_isnan(w[t])) return 0u;
+  }
+  bool have = false;
+  double bd = 0.0, be = 0.0;
+  uint32_t bi = 0;
+  int32_t first_inf = -1;
+  for (int32_t c = 0; c < k; ++c) {
+    const double* rec = tab + (size_t)c * (V + 1);
+    bool nan = false, inf = false;
+    double dot = 0.0, sabs = 0.0;
+    for (int t = 0; t < V; ++t) {
+      const double ct = rec[1 + t];
+      const bool wi = __builtin_isinf(w[t]), ci = __builtin_isinf(ct);
+      nan = nan || __builtin_isnan(ct) || (wi && ci && ((w[t] > 0.0) == (ct > 0.0)));
+      inf = inf || wi || ci;
+      dot = fma(w[t], ct, dot);
+      sabs = fma(fabs(w[t]), fabs(ct), sabs);
+    }
+    if (nan) continue;
+    if (inf) {
+      if (first_inf < 0) first_inf = c;
+      continue;
+    }
+    const double d = fma(-2.0, dot, rec[0]);
+    const double e = (V + 2) * 0x1p-53 * (rec[0] + 2.0 * sabs) * (1.0 + 0x1p-20);
+    if (!have || d + e < bd - be) {
+      have = true;
+      bd = d;
+      be = e;
+      bi = (uint32_t)c;
+    } else if (d - e <= bd + be && exact_order<V>(w, rec + 1, tab + (size_t)bi * (V + 1) + 1) < 0) {
+      bd = d;
+      be = e;
+      bi = (uint32_t)c;
+    }
+  }
+  return have ? bi : (first_inf >= 0 ? (uint32_t)first_inf : 0u);
+}
+
+// Lowest index of the exact minimum, for each of the lane's R vectors whose values and
+// book are finite (the others are marked).  The record of centroid c + 1 is loaded while
+// centroid c is ranked.  Every decision taken is certain: a centroid replaces the best
+// only when its fp64 value is below the best's by more than the pair bound T; one within T
+// of the best marks the vector instead.  An unmarked result is therefore the exact
+// nearest.  The loop keeps lim = best + T (one compare per centroid); T is held in fp32,
+// rounded upwards, and is NaN for vectors that are marked from the start.
 template <int V, int R>
 __device__ __forceinline__ void nearest(const double (&w)[R][V], const double* __restrict__ tab, int32_t k,
-                                        uint32_t (&best_i)[R]) {
-  double best[R];
+                                        const float (&T)[R], uint32_t (&best_i)[R]) {
+  double lim[R];
+  uint32_t marks = 0;  // bit r: vector r needs the exact ranking
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    best[r] = __builtin_inf();
+    const bool ok = T[r] == T[r];
+    lim[r] = ok ? __builtin_inf() : -__builtin_inf();
     best_i[r] = 0;
+    marks |= ok ? 0u : 1u << r;
   }
   double cur[V + 1];
 #pragma unroll
@@ -75,35 +226,60 @@ __device__ __forceinline__ void nearest(const double (&w)[R][V], const double* _
 #pragma unroll
     for (int t = 0; t <= V; ++t) nxt[t] = nrec[t];
     double d[R];
-    bool better = false;
+    bool look = false;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       double dot = fma(w[r][0], cur[1], 0.0);
 #pragma unroll
       for (int t = 1; t < V; ++t) dot = fma(w[r][t], cur[1 + t], dot);
       d[r] = fma(-2.0, dot, cur[0]);
-      better |= d[r] < best[r];
+      look |= d[r] <= lim[r];
     }
-    if (__any(better)) {
+    if (__any(look)) {
 #pragma unroll
       for (int r = 0; r < R; ++r) {
-        if (d[r] < best[r]) {
-          best[r] = d[r];
-          best_i[r] = (uint32_t)c;
+        if (d[r] <= lim[r]) {
+          const double t = (double)T[r];
+          if (d[r] < lim[r] - 2.0 * t) {  // below best - T
+            lim[r] = d[r] + t;
+            best_i[r] = (uint32_t)c;
+          } else {
+            marks |= 1u << r;
+          }
         }
       }
     }
 #pragma unroll
     for (int t = 0; t <= V; ++t) cur[t] = nxt[t];
   }
+#pragma unroll
+  for (int r = 0; r < R; ++r) best_i[r] |= (marks >> r) & 1u ? kMark : 0u;
 }
 
-// FIRST: both stages (stage 2 skipped when k2 == 0); otherwise stage 1 has run already and
-// only the residual stage runs, on the idx1 it wrote.
+// Per-vector pair bound: NaN (marked from the start) for vectors or books with non-finite
+// values, else the bound of `pair_bound` rounded up to fp32.
+template <int V, int R>
+__device__ __forceinline__ void walk_setup(const double (&w)[R][V], double2 bm, float (&T)[R]) {
+  const bool book_ok = bm.x < __builtin_inf() && bm.y < __builtin_inf();
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    double sw = 0.0;
+    bool fin = book_ok;
+#pragma unroll
+    for (int t = 0; t < V; ++t) {
+      sw += fabs(w[r][t]);
+      fin = fin && __builtin_isfinite(w[r][t]);
+    }
+    T[r] = fin ? __double2float_ru(pair_bound<V>(sw, bm.x, bm.y)) : __builtin_nanf("");
+  }
+}
+
 template <int V, int R, int WT, bool FIRST>
 __global__ __launch_bounds__(kThreads) void assign_kernel(const void* __restrict__ w, int64_t nvec,
-                                                          const double* __restrict__ tab1, int32_t k1,
-                                                          const double* __restrict__ tab2, int32_t k2,
+                                                          const double* __restrict__ tab1,
+                                                          const double2* __restrict__ tmax1, int32_t k1,
+                                                          const double* __restrict__ tab2,
+                                                          const double2* __restrict__ tmax2, int32_t k2,
                                                           uint32_t* __restrict__ idx1, uint32_t* __restrict__ idx2) {
   const int64_t base = (int64_t)blockIdx.x * (kThreads * R) + threadIdx.x;
   double wv[R][V];
@@ -113,9 +289,11 @@ __global__ __launch_bounds__(kThreads) void assign_kernel(const void* __restrict
 #pragma unroll
     for (int t = 0; t < V; ++t) wv[r][t] = weight_at<WT>(w, g * V + t);
   }
+  float T[R];
   uint32_t i1[R];
   if constexpr (FIRST) {
-    nearest<V, R>(wv, tab1, k1, i1);
+    walk_setup<V, R>(wv, book_max(tmax1, k1), T);
+    nearest<V, R>(wv, tab1, k1, T, i1);
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int64_t g = base + (int64_t)r * kThreads;
@@ -126,15 +304,17 @@ __global__ __launch_bounds__(kThreads) void assign_kernel(const void* __restrict
 #pragma unroll
     for (int r = 0; r < R; ++r) i1[r] = idx1[min(base + (int64_t)r * kThreads, nvec - 1)];
   }
-  // residual in fp32, held exactly in fp64
+  // residual in fp32, held exactly in fp64 (a marked main index is ranked again, both
+  // stages, by the fix-up kernel; its residual here only has to be a valid one)
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const double* rec = tab1 + (size_t)i1[r] * (V + 1);
+    const double* rec = tab1 + (size_t)(i1[r] & ~kMark) * (V + 1);
 #pragma unroll
     for (int t = 0; t < V; ++t) wv[r][t] = (double)((float)wv[r][t] - (float)rec[1 + t]);
   }
+  walk_setup<V, R>(wv, book_max(tmax2, k2), T);
   uint32_t i2[R];
-  nearest<V, R>(wv, tab2, k2, i2);
+  nearest<V, R>(wv, tab2, k2, T, i2);
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int64_t g = base + (int64_t)r * kThreads;
@@ -146,21 +326,22 @@ __global__ __launch_bounds__(kThreads) void assign_kernel(const void* __restrict
 // Matrix-core pass for stage 1 with fp16 weights.  The matrix cores form, for 32 centroids
 // x 32 vectors at a time, the fp32 half-distance h = |c|^2 / 2 - w . c
 // (v_mfma_f32_32x32x16_f16 with A = -c, B = w, C = fl32(|c|^2 / 2), K = 16 holding v <= 16
-// coordinates and zeros).  Each product of two
-// fp16 values is exact in fp32, so h differs from the fp64 ranking above (halved) by at
-// most E = (v + 2) 2^-23 (S_w Cmax + NCmax / 2), with S_w = sum |w_t| and Cmax, NCmax
-// the largest |c_t| and |c|^2 of the book (the sum of v + 1 terms with at most 2^-23
-// relative error per addition, and the rounding of C).  If k* is the centroid the fp64
-// ranking picks and m the smallest h seen so far, then h(k*) <= m + 2E at every point
-// of the walk.  Each lane therefore keeps a threshold thr = min over seen tiles of
-// (tile minimum + delta), delta = 4 (v + 2) 2^-23 (S_w Cmax + NCmax / 2) (twice the bound,
-// which also covers the rounding of thr itself), and ranks in fp64, exactly as above,
-// every centroid with h <= thr; the lowest index of the smallest fp64 distance among them
-// is the answer.  A 32x32 block costs one MFMA, eight three-way minima and a compare;
-// the fp64 ranking runs only where a block holds a candidate (a new running minimum or a
-// near tie), about one block in eight for 65536 centroids.  NaN or infinite values make
-// delta infinite: every centroid is then ranked in fp64.  The matrix cores must multiply
-// fp16 subnormals exactly (they do on gfx950; a book of subnormals is among the tests).
+// coordinates and zeros).  Each product of two fp16 values is exact in fp32, so h differs
+// from the exact half-distance by at most E = (v + 2) 2^-23 (S_w Cmax + NCmax / 2), with
+// S_w = sum |w_t| and Cmax, NCmax the largest |c_t| and |c|^2 of the book (the sum of
+// v + 1 terms with at most 2^-23 relative error per addition, and the rounding of C).  If
+// k* is the exact nearest centroid and m the smallest h seen so far, then h(k*) <= m + 2E
+// at every point of the walk.  Each lane therefore keeps a threshold thr = min over seen
+// tiles of (tile minimum + delta), delta = 4 (v + 2) 2^-23 (S_w Cmax + NCmax / 2) (twice
+// the bound, which also covers the rounding of thr itself), and ranks every centroid with
+// h <= thr in fp64 with the same near-tie rule as the walk above (exact comparison within
+// the fp64 bound); k* is always among them.  A 32x32 block costs one MFMA, eight
+// three-way minima and a compare; the fp64 ranking runs only where a block holds a
+// candidate (a new running minimum or a near tie), about one block in eight for 65536
+// centroids.  Vectors with NaN or infinite values, and every vector of a book holding
+// such values, skip the candidates and take nearest_general on the fp64 records at the
+// end.  The matrix cores must multiply fp16 subnormals exactly (they do on gfx950; a
+// book of subnormals is among the tests).
 //
 // Work split: 256 threads = 4 wavefronts; a wavefront owns kGroups groups of 32 vectors
 // (B operands in registers for the whole walk); lanes l and l + 32 share vector l % 32
@@ -238,6 +419,25 @@ __global__ __launch_bounds__(kThreads) void assign_mfma_table_kernel(const uint1
   }
 }
 
+// The lane's whole vector in fp64: coordinates 8 h .. 8 h + 7 from its own B operand, the
+// others from the partner lane (l ^ 32).  Every lane of the wave must call this.
+template <int V>
+__device__ __forceinline__ void gather_vector(const half8_t& bv, int h, double (&wv)[V]) {
+  const uint4 own = __builtin_bit_cast(uint4, bv);
+  uint4 oth;
+  oth.x = (uint32_t)__shfl_xor((int)own.x, 32);
+  oth.y = (uint32_t)__shfl_xor((int)own.y, 32);
+  oth.z = (uint32_t)__shfl_xor((int)own.z, 32);
+  oth.w = (uint32_t)__shfl_xor((int)own.w, 32);
+#pragma unroll
+  for (int t = 0; t < V; ++t) {
+    const uint4 u = ((t >> 3) == h) ? own : oth;
+    const int e = t & 7;
+    const uint32_t word = e < 2 ? u.x : e < 4 ? u.y : e < 6 ? u.z : u.w;
+    wv[t] = (double)vqd::f16_to_f32((e & 1) ? (word >> 16) : (word & 0xFFFFu));
+  }
+}
+
 template <int V>
 __global__ __launch_bounds__(kThreads) void assign_mfma_kernel(const uint16_t* __restrict__ w, int64_t nvec,
                                                                const uint16_t* __restrict__ a16,
@@ -270,33 +470,48 @@ __global__ __launch_bounds__(kThreads) void assign_mfma_kernel(const uint16_t* _
   const int64_t vbase = (int64_t)blockIdx.x * kMfmaVectors + (int64_t)wave * (R * 32) + col;
   half8_t b[R];
   float swp[R];
+  bool fast[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const uint16_t* wp = w + min(vbase + r * 32, nvec - 1) * V;  // lanes past the end rank a copy
     float sw = 0.f;
+    bool fin = true;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int t = 8 * h + q;
       const uint16_t hv = t < V ? wp[t] : (uint16_t)0;
       b[r][q] = __builtin_bit_cast(_Float16, hv);
       sw += fabsf(vqd::f16_to_f32(hv));
+      fin = fin && (hv & 0x7C00u) != 0x7C00u;
     }
     swp[r] = sw + __shfl_xor(sw, 32);
+    fast[r] = fin && __shfl_xor((int)fin, 32);
   }
   __syncthreads();
   cmax = fmaxf(fmaxf(sred[0].x, sred[1].x), fmaxf(sred[2].x, sred[3].x));
   ncmax = fmaxf(fmaxf(sred[0].y, sred[1].y), fmaxf(sred[2].y, sred[3].y));
-  float thr[R], dl[R];
+  const bool book_ok = cmax < __builtin_inff() && ncmax < __builtin_inff();
+  float thr[R], tb[R];
   double best[R];
   uint32_t bi[R];
+  uint32_t marks = 0;  // bit r: vector r needs the exact ranking
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    float d = (4.f * (V + 2) * 0x1p-23f) * (swp[r] * cmax + 0.5f * ncmax) + 0x1p-100f;
-    dl[r] = (d <= __builtin_inff()) ? d : __builtin_inff();  // NaN -> rank everything
-    thr[r] = __builtin_inff();
+    // vectors or books with non-finite values are marked from the start; their threshold
+    // of -inf keeps them out of the candidate ranking (but for NaN / -inf entries, whose
+    // result is discarded anyway)
+    const bool ok = fast[r] && book_ok;
+    thr[r] = ok ? __builtin_inff() : -__builtin_inff();
     best[r] = __builtin_inf();
     bi[r] = 0;
+    marks |= ok ? 0u : 1u << r;
+    // the fp64 pair bound (|c_t| is exact in fp32; |c|^2 and the sum of |w_t| are rounded,
+    // hence the margins), held in fp32 rounded upwards
+    tb[r] = __double2float_ru(
+        pair_bound<V>((double)swp[r] * (1.0 + 0x1p-18), (double)cmax, (double)ncmax * (1.0 + 0x1p-20)));
   }
+  // the fp32 threshold margin, computed where used
+  auto delta = [&](int r) { return (4.f * (V + 2) * 0x1p-23f) * (swp[r] * cmax + 0.5f * ncmax) + 0x1p-100f; };
 
   // chunk staging: thread tid copies A words tid, tid + 256, ... and C quad tid (< kChunk / 4)
   constexpr int kAPer = kAWords / kThreads;
@@ -350,23 +565,11 @@ __global__ __launch_bounds__(kThreads) void assign_mfma_kernel(const uint16_t* _
           const bool trig = !(tmin[r] > thr[r]);
           if (__any(trig)) {
             const f32x16_t d = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b[r], cv, 0, 0, 0);
-            // the whole vector: coordinates 8 h .. 8 h + 7 here, the others in the partner lane
-            const uint4 own = __builtin_bit_cast(uint4, b[r]);
-            uint4 oth;
-            oth.x = (uint32_t)__shfl_xor((int)own.x, 32);
-            oth.y = (uint32_t)__shfl_xor((int)own.y, 32);
-            oth.z = (uint32_t)__shfl_xor((int)own.z, 32);
-            oth.w = (uint32_t)__shfl_xor((int)own.w, 32);
-            if (trig) {
-              thr[r] = fminf(thr[r], tmin[r] + dl[r]);
-              double wv[V];
-#pragma unroll
-              for (int t = 0; t < V; ++t) {
-                const uint4 u = ((t >> 3) == h) ? own : oth;
-                const int e = t & 7;
-                const uint32_t word = e < 2 ? u.x : e < 4 ? u.y : e < 6 ? u.z : u.w;
-                wv[t] = (double)vqd::f16_to_f32((e & 1) ? (word >> 16) : (word & 0xFFFFu));
-              }
+            double wv[V];
+            gather_vector<V>(b[r], h, wv);
+            if (trig) {  // (fp64 candidates ranked in increasing index order)
+              thr[r] = fminf(thr[r], tmin[r] + delta(r));
+              const double T = (double)tb[r];
               uint32_t cand = 0;
 #pragma unroll
               for (int q = 0; q < 16; ++q) cand |= (d[q] > thr[r] ? 0u : 1u) << q;
@@ -394,9 +597,11 @@ __global__ __launch_bounds__(kThreads) void assign_mfma_kernel(const uint16_t* _
                     }
                   }
                   const double dd = fma(-2.0, dot, nc);
-                  if (dd < best[r]) {  // a lane meets its centroids in increasing index order
+                  if (dd < best[r] - T) {  // certainly nearer
                     best[r] = dd;
                     bi[r] = (uint32_t)k;
+                  } else if (dd <= best[r] + T) {  // too close to tell in fp64
+                    marks |= 1u << r;
                   }
                 }
               }
@@ -414,20 +619,56 @@ __global__ __launch_bounds__(kThreads) void assign_mfma_kernel(const uint16_t* _
     if (tid < kChunk / 4) sc[buf ^ 1][tid] = rc;
     __syncthreads();
   }
-  // lanes l and l + 32 hold the same vector: smaller fp64 distance, then lower index
+  // lanes l and l + 32 hold the same vector: the certainly smaller distance, else a mark
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const double ob = __shfl_xor(best[r], 32);
     const uint32_t oi = (uint32_t)__shfl_xor((int)bi[r], 32);
-    if (ob < best[r] || (ob == best[r] && oi < bi[r])) bi[r] = oi;
+    const uint32_t om = (uint32_t)__shfl_xor((int)marks, 32);
+    const double T = (double)tb[r];
+    uint32_t pick = bi[r], m = ((marks | om) >> r) & 1u ? kMark : 0u;
+    if (ob < best[r] - T) {
+      pick = oi;
+    } else if (!(ob > best[r] + T)) {
+      m = kMark;
+    }
     const int64_t g = vbase + r * 32;
-    if (h == 0 && g < nvec) idx1[g] = bi[r];
+    if (h == 0 && g < nvec) idx1[g] = pick | m;
+  }
+}
+
+// Marked vectors ranked again with exact comparisons: the main stage when its index is
+// marked (then the residual stage too, from the new residual), else the residual stage
+// when that index is marked.
+template <int V, int WT>
+__global__ __launch_bounds__(kThreads) void assign_fixup_kernel(const void* __restrict__ w, int64_t nvec,
+                                                                const double* __restrict__ tab1, int32_t k1,
+                                                                const double* __restrict__ tab2, int32_t k2,
+                                                                uint32_t* __restrict__ idx1,
+                                                                uint32_t* __restrict__ idx2) {
+  const int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (g >= nvec) return;
+  uint32_t i1 = idx1[g];
+  uint32_t i2 = k2 ? idx2[g] : 0u;
+  if (!((i1 | i2) & kMark)) return;
+  double wv[V];
+  for (int t = 0; t < V; ++t) wv[t] = weight_at<WT>(w, g * V + t);
+  const bool redo1 = (i1 & kMark) != 0;
+  if (redo1) {
+    i1 = nearest_general<V>(wv, tab1, k1);
+    idx1[g] = i1;
+  }
+  if (k2 && (redo1 || (i2 & kMark))) {
+    const double* rec = tab1 + (size_t)i1 * (V + 1);
+    for (int t = 0; t < V; ++t) wv[t] = (double)((float)wv[t] - (float)rec[1 + t]);
+    idx2[g] = nearest_general<V>(wv, tab2, k2);
   }
 }
 
 template <int V>
-vq_status launch_v(const void* w, vq_dtype w_dtype, int64_t nvec, const double* tab1, int32_t k1, const double* tab2,
-                   int32_t k2, uint32_t* idx1, uint32_t* idx2, const MfmaTable* mt, hipStream_t s) {
+vq_status launch_v(const void* w, vq_dtype w_dtype, int64_t nvec, const double* tab1, const double2* tmax1, int32_t k1,
+                   const double* tab2, const double2* tmax2, int32_t k2, uint32_t* idx1, uint32_t* idx2,
+                   const MfmaTable* mt, hipStream_t s) {
   constexpr int R = V <= 4 ? 4 : 2;
   const int64_t blocks = (nvec + (int64_t)kThreads * R - 1) / ((int64_t)kThreads * R);
   if (blocks > 0x7FFFFFFF) return VQ_ERR_UNSUPPORTED;
@@ -438,18 +679,26 @@ vq_status launch_v(const void* w, vq_dtype w_dtype, int64_t nvec, const double* 
     hipLaunchKernelGGL((assign_mfma_kernel<V>), dim3((unsigned)mblocks), dim3(kThreads), 0, s, (const uint16_t*)w,
                        nvec, mt->a16, mt->cf, mt->bmax, mt->nbmax, mt->kp, k1, idx1);
     if (k2) {
-      hipLaunchKernelGGL((assign_kernel<V, R, VQ_F16, false>), grid, block, 0, s, w, nvec, tab1, k1, tab2, k2, idx1,
-                         idx2);
+      hipLaunchKernelGGL((assign_kernel<V, R, VQ_F16, false>), grid, block, 0, s, w, nvec, tab1, tmax1, k1, tab2, tmax2, k2,
+                         idx1, idx2);
     }
   } else if (w_dtype == VQ_F16) {
-    hipLaunchKernelGGL((assign_kernel<V, R, VQ_F16, true>), grid, block, 0, s, w, nvec, tab1, k1, tab2, k2, idx1,
-                       idx2);
+    hipLaunchKernelGGL((assign_kernel<V, R, VQ_F16, true>), grid, block, 0, s, w, nvec, tab1, tmax1, k1, tab2, tmax2, k2,
+                       idx1, idx2);
   } else if (w_dtype == VQ_BF16) {
-    hipLaunchKernelGGL((assign_kernel<V, R, VQ_BF16, true>), grid, block, 0, s, w, nvec, tab1, k1, tab2, k2, idx1,
-                       idx2);
+    hipLaunchKernelGGL((assign_kernel<V, R, VQ_BF16, true>), grid, block, 0, s, w, nvec, tab1, tmax1, k1, tab2, tmax2, k2,
+                       idx1, idx2);
   } else {
-    hipLaunchKernelGGL((assign_kernel<V, R, VQ_F32, true>), grid, block, 0, s, w, nvec, tab1, k1, tab2, k2, idx1,
-                       idx2);
+    hipLaunchKernelGGL((assign_kernel<V, R, VQ_F32, true>), grid, block, 0, s, w, nvec, tab1, tmax1, k1, tab2, tmax2, k2,
+                       idx1, idx2);
+  }
+  const dim3 fgrid((unsigned)((nvec + kThreads - 1) / kThreads));
+  if (w_dtype == VQ_F16) {
+    hipLaunchKernelGGL((assign_fixup_kernel<V, VQ_F16>), fgrid, block, 0, s, w, nvec, tab1, k1, tab2, k2, idx1, idx2);
+  } else if (w_dtype == VQ_BF16) {
+    hipLaunchKernelGGL((assign_fixup_kernel<V, VQ_BF16>), fgrid, block, 0, s, w, nvec, tab1, k1, tab2, k2, idx1, idx2);
+  } else {
+    hipLaunchKernelGGL((assign_fixup_kernel<V, VQ_F32>), fgrid, block, 0, s, w, nvec, tab1, k1, tab2, k2, idx1, idx2);
   }
   return VQ_OK;
 }
@@ -458,10 +707,10 @@ vq_status launch_v(const void* w, vq_dtype w_dtype, int64_t nvec, const double* 
 
 namespace {
 
-// Workspace layout: the fp64 records of both books, then (K1 >= 256) the matrix-core
-// tables of the main book, each part 256-byte aligned.
+// Workspace layout: the fp64 records of both books, their per-256-centroid maxima, then
+// (K1 >= 256) the matrix-core tables of the main book, each part 256-byte aligned.
 struct WsLayout {
-  size_t tab, a16, cf, bmax, total;
+  size_t tab, tmax1, tmax2, a16, cf, bmax, total;
   int32_t kp;
   bool mfma;
 };
@@ -473,6 +722,10 @@ WsLayout ws_layout(const vq_desc& d) {
   const size_t k1 = (size_t)1 << d.bits1, k2 = d.bits2 ? (size_t)1 << d.bits2 : 0;
   l.tab = 0;
   size_t off = up256((k1 + k2) * (size_t)(d.v + 1) * sizeof(double));
+  l.tmax1 = off;
+  off += up256((k1 + kThreads - 1) / kThreads * sizeof(double2));
+  l.tmax2 = off;
+  off += up256((k2 + kThreads - 1) / kThreads * sizeof(double2));
   l.mfma = d.bits1 >= 8;
   if (l.mfma) {
     const int kb = (d.v + 7) / 8;
@@ -502,11 +755,13 @@ vq_status launch_assign(const vq_desc& d, const void* w, vq_dtype w_dtype, const
   char* ws = (char*)workspace;
   double* tab1 = (double*)(ws + l.tab);
   double* tab2 = tab1 + (size_t)k1 * (d.v + 1);
+  double2* tmax1 = (double2*)(ws + l.tmax1);
+  double2* tmax2 = (double2*)(ws + l.tmax2);
   hipLaunchKernelGGL(assign_table_kernel, dim3((k1 + kThreads - 1) / kThreads), dim3(kThreads), 0, s, cb1, k1, d.v,
-                     tab1);
+                     tab1, tmax1);
   if (k2) {
     hipLaunchKernelGGL(assign_table_kernel, dim3((k2 + kThreads - 1) / kThreads), dim3(kThreads), 0, s, cb2, k2, d.v,
-                       tab2);
+                       tab2, tmax2);
   }
   MfmaTable mt{};
   const MfmaTable* mtp = nullptr;
@@ -530,7 +785,7 @@ vq_status launch_assign(const vq_desc& d, const void* w, vq_dtype w_dtype, const
   switch (d.v) {
 #define VQ_ASSIGN_CASE(V)                                                        \
   case V:                                                                        \
-    st = launch_v<V>(w, w_dtype, nvec, tab1, k1, tab2, k2, idx1, idx2, mtp, s); \
+    st = launch_v<V>(w, w_dtype, nvec, tab1, tmax1, k1, tab2, tmax2, k2, idx1, idx2, mtp, s); \
     break;
     VQ_ASSIGN_CASE(1)
     VQ_ASSIGN_CASE(2)

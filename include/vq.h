@@ -223,17 +223,20 @@ int32_t vq_rht_block(int32_t n);
 /*
  * Two-stage residual VQ encode with given codebooks (VPTQ guide, "Step 2: Multi-Stage
  * Residual Vector Quantizer (RVQ)": Euclidean distance and argmin, then the same on the
- * residuals; "2. Multi-Stage Residual Vector Quantization" for the residual).  W [N][IN]
- * is cut into nv = IN / v vectors per row; for each vector w
+ * residuals; the nearest-centroid rule q(w) = argmin_k |w - c_k|^2 of "The
+ * Information-Theoretic Superiority of Vector Quantization"; "2. Multi-Stage Residual
+ * Vector Quantization" for the residual).  W [N][IN] is cut into nv = IN / v vectors per
+ * row; for each vector w
  *
- *   idx1 = the lowest k minimising |C1[k]|^2 - 2 w . C1[k]
- *   idx2 = the lowest k minimising |C2[k]|^2 - 2 r . C2[k],    r = fp32(w - C1[idx1])
+ *   idx1 = the lowest k of the exact minimum of |w - C1[k]|^2
+ *   idx2 = the lowest k of the exact minimum of |r - C2[k]|^2,    r = fp32(w - C1[idx1])
  *
- * (the squared Euclidean distance less |w|^2, which all centroids share), evaluated in
- * fp64: |c|^2 as fma(c_t, c_t, .) over t = 0 .. v-1 from 0, w . c the same way, then
- * fma(-2, w . c, |c|^2).  Every product is exact, so the result is the same on any
- * machine that runs that sequence of IEEE operations.  Codebook initialisation (the
- * guide's random samples) and refinement are the caller's.
+ * decided on exact values (not on a rounded distance), so the result does not depend on
+ * an evaluation order.  NaN or infinite values: a distance is NaN when a coordinate is NaN
+ * or holds the same infinity in w and c, +inf when a coordinate is infinite; finite
+ * distances win over +inf, NaN ones are never taken, and index 0 is returned when all are
+ * NaN.  Codebook initialisation (the guide's random samples) and refinement are the
+ * caller's.
  * desc: N = out_features, IN = in_features (a multiple of v, else VQ_ERR_UNSUPPORTED),
  *   v, K1 = 2^bits1, K2 = 2^bits2 (bits2 = 0: one stage; idx2 and cb2 ignored), layout
  *   as for the other calls.

@@ -44,12 +44,20 @@ def exact_pick(w, book) -> int:
     return d.index(min(d))
 
 
+def _bf16(x: float) -> np.float32:
+    """x rounded to bfloat16 (nearest, ties to even), as a float32."""
+    u = np.array([x], np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32)[0]
+
+
 def _next_f16(x: np.float16) -> np.float16:
     return (np.array([x], np.float16).view(np.uint16) + 1).view(np.float16)[0]
 
 
 def near_tie_case(rng, v: int, w_dtype: str, k: int):
-    """One vector w (float32 values, fp16- or fp32-representable) and a fp16 book [k][v]
+    """One vector w (float32 values representable in w_dtype: "f16", "bf16" or "f32") and a
+    fp16 book [k][v]
     holding the pair a, b at two random rows; every other row is far away.  Returns
     (w [v] float32, book [k][v] float16, rows (ia, ib))."""
     assert v >= 3 and k >= 2
@@ -63,6 +71,14 @@ def near_tie_case(rng, v: int, w_dtype: str, k: int):
         w2 = lo if rng.integers(2) else _next_f16(cb2)
         w = np.zeros(v, np.float32)
         w[0], w[2] = np.float32(w0), np.float32(w2)
+    elif w_dtype == "bf16":
+        w0 = _bf16(rng.uniform(2.0 ** 29, 2.0 ** 30))  # w0 c0 ~ 2^45
+        ca2 = np.float16(rng.uniform(2.0 ** -4, 2.0 ** -3))
+        cb2 = _next_f16(ca2)
+        # a bf16 value near the pair (bf16 steps there are 2^-11, the pair 2^-14 apart)
+        w2 = _bf16(rng.uniform(float(ca2) - 2.0 ** -12, float(cb2) + 2.0 ** -12))
+        w = np.zeros(v, np.float32)
+        w[0], w[2] = w0, w2
     else:
         w0 = np.float32(rng.uniform(2.0 ** 29, 2.0 ** 30))  # w0 c0 ~ 2^45
         ca2 = np.float16(rng.uniform(2.0 ** -4, 2.0 ** -3))

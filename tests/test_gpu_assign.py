@@ -1,6 +1,6 @@
 """GPU parity of the residual VQ encode (vq_assign) against the CPU oracle through the C
-ABI: indices are compared element by element and must be equal (the ranking is one fixed
-sequence of fp64 operations on both sides, and ties go to the lowest index).
+ABI: indices are compared element by element and must be equal (both sides take the exact
+minimum of |w - c|^2, ties to the lowest index).
 
 - small shapes spanning several workgroups and a ragged tail of lanes, every v from 1 to
   16 among them, one and two stages, fp16 / bf16 / fp32 weights; with fp16 weights and
@@ -9,6 +9,8 @@ sequence of fp64 operations on both sides, and ties go to the lowest index).
 - books made of fp16 subnormals (the matrix cores must multiply them exactly) and
   infinite / NaN weights and centroids (every centroid is then re-ranked in fp64);
 - exact ties: duplicated centroids and vectors that equal a centroid;
+- near ties far below fp64 rounding (an fp64 ranking gets them wrong), both stages, every
+  weight type, the matrix-core stage among them, and the non-finite reading on hand cases;
 - the 4096 x 4096 layer with a 65536-entry main book and a 256-entry residual book (the
   weights of the benchmark) on sampled rows at full size, plus the index range at any
   size;
@@ -21,6 +23,7 @@ import functools
 import numpy as np
 import pytest
 
+import neartie
 import oracle
 import synth
 from vqtest import check_y, f16_tensor, x_tensor
@@ -186,6 +189,58 @@ def test_assign_exact_ties_take_the_lowest_index(vq):
     assert len(hits) > 100
     flat = g1.reshape(-1)
     assert all(flat[i] == k for i, k in hits)
+
+
+NEAR_TIE_CASES = [
+    # weights, v, book rows (2^bits), seed: fp16 with 256+ rows takes the matrix-core stage
+    ("f16", 8, 256, 31), ("f16", 16, 512, 32), ("f16", 4, 16, 33), ("bf16", 8, 32, 34), ("f32", 8, 16, 35),
+    ("f32", 5, 64, 36),
+]
+
+
+@pytest.mark.parametrize("wd,v,k,seed", NEAR_TIE_CASES)
+def test_assign_near_ties_decided_exactly(vq, wd, v, k, seed):
+    """Centroid pairs whose exact distances differ by ~2^-25 .. 2^-40 beside 2^31 .. 2^45
+    terms, kept only where an fp64 ranking picks the other row; main and residual stages."""
+    bits = int(np.log2(k))
+    for w, book, want in neartie.disagreeing_cases(seed, 6, v, wd, k):
+        wbits = w[None, :].astype(np.float16).view(np.uint16) if wd == "f16" else (
+            synth.f32_to_bf16_bits(w[None, :]) if wd == "bf16" else w[None, :])
+        wt = _w_tensor({"w": wbits, "w_dtype": wd})
+        d = vq.make_desc(1, v, v, bits, 0)
+        i1, _ = vq.assign(d, wt, f16_tensor(book.view(np.uint16)), None)
+        torch.cuda.synchronize()
+        o1, _ = oracle.rvq_assign(w[None, :], v, book.view(np.uint16))
+        assert int(o1[0, 0]) == want
+        assert int(i1.cpu().numpy().view(np.uint32)[0, 0]) == want
+        # residual stage: main book = the zero vector (row 0, nearest) and far rows
+        c1 = np.zeros((4, v), np.float16)
+        c1[1:, 0] = np.float16(-65504.0)
+        d2 = vq.make_desc(1, v, v, 2, bits)
+        j1, j2 = vq.assign(d2, wt, f16_tensor(c1.view(np.uint16)), f16_tensor(book.view(np.uint16)))
+        torch.cuda.synchronize()
+        assert int(j1.cpu().numpy().view(np.uint32)[0, 0]) == 0
+        assert int(j2.cpu().numpy().view(np.uint32)[0, 0]) == want
+
+
+@pytest.mark.parametrize("wd,rows", [("f32", 8), ("f16", 256)])
+def test_assign_non_finite_reading(vq, wd, rows):
+    """The IEEE reading on hand cases (NaN distances never taken, finite before +inf, all
+    NaN gives 0); rows past the first five are NaN centroids.  With 256 rows and fp16
+    weights the book is non-finite, so every vector takes the general exact path."""
+    inf, nan = np.inf, np.nan
+    book = np.full((rows, 2), np.nan, np.float16)
+    book[:5] = [[inf, 0], [1, 0], [0, nan], [-inf, 0], [0, 0]]
+    ws = np.array([[nan, 0], [inf, 0], [-inf, 0], [0.5, 0], [0.25, 0]], np.float32)
+    want = [0, 1, 0, 1, 4]
+    wbits = ws.astype(np.float16).view(np.uint16) if wd == "f16" else ws
+    d = vq.make_desc(5, 2, 2, int(np.log2(rows)), 0)
+    i1, _ = vq.assign(d, _w_tensor({"w": wbits, "w_dtype": wd}), f16_tensor(book.view(np.uint16)), None)
+    torch.cuda.synchronize()
+    got = i1.cpu().numpy().view(np.uint32).reshape(-1).tolist()
+    o1, _ = oracle.rvq_assign(ws, 2, book.view(np.uint16))
+    assert o1.reshape(-1).tolist() == want
+    assert got == want
 
 
 @functools.lru_cache(maxsize=1)

@@ -748,7 +748,7 @@ def test_rvq_scalar_levels_closed_form(oracle_mod):
 
 
 @pytest.mark.parametrize("w_dtype,v,k,seed", [("f32", 8, 16, 21), ("f16", 8, 256, 22), ("f32", 4, 8, 23),
-                                           ("f16", 16, 64, 24), ("f32", 3, 2, 25)])
+                                           ("f16", 16, 64, 24), ("f32", 3, 2, 25), ("bf16", 8, 32, 26)])
 def test_rvq_near_ties_decided_exactly(oracle_mod, w_dtype, v, k, seed):
     """Pairs of centroids whose exact squared distances differ by ~2^-40 (fp32 weights) or
     3 * 2^-36 (fp16 weights) beside terms of 2^45 / 2^31: only cases where an fp64 ranking

@@ -2,16 +2,21 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
-A step is one vq_gemv_ws call (vq_gemv with a caller-owned workspace, M = 1) on a
-4096 x 4096 layer with v = 8 and a 65536-entry main codebook (2 index bits per weight),
-fp16 x, fp16 y: the decode GEMV the metric is quoted on.  Steps rotate through a ring of distinct layer copies (own
-indices, codebook and scale each) totalling more than 1 GiB, so the 256 MB
-Infinity Cache cannot hold the stream and every step reads its indices from HBM.
+A step is one decode pass over the 70B-class MLP layer pair: vq_gemv_ws (vq_gemv with a
+caller-owned workspace, the call VQLinear makes for decode batches) at M = 1 on the
+28672 x 8192 "up" layer, then on the 8192 x 28672 "down" layer; v = 8, a 65536-entry main
+codebook plus a 256-entry residual codebook (3 index bits per weight), bf16 x and y.  Steps
+rotate through a ring of distinct layer copies (own indices, codebooks and scales each)
+totalling more than 1 GiB per layer, so the 256 MB Infinity Cache cannot hold the stream
+and every step reads its indices from HBM.  W warm-up steps run first; exactly K steps are
+captured in one HIP graph, replayed once untimed, then timed in 5 trials (median reported,
+minimum beside it).
 
-Printed: ONE JSON line with the throughput on algorithmic bytes (packed indices +
-each codebook once + scales + x + y), the roofline of the kernel, the prefill GEMM
-(vq_gemm at M = 128 on the 28672 x 8192 / 8192 x 28672 layers), the GEMV at M = 1 on
-every workload, and the CPU oracle timed on the host on a bounded sample.
+Printed: ONE JSON line with the throughput on algorithmic bytes (packed indices + each
+codebook once + scales + x + y), the roofline of the call, the cold single-call latency,
+the GEMV / GEMM crossover on the same layers, the prefill GEMM (vq_gemm at M = 128), the
+GEMV at M = 1 on every workload, the other legs, and the CPU oracle timed on the host's
+cores on every workload.
 
 Inputs are synthetic: uniform indices (a packed stream of uniform random bits),
 centroids 0.02*N(0,1) main and 0.005*N(0,1) residual in fp16, scales U(0.5, 1.5),
@@ -65,8 +70,11 @@ SVQ_DESCRIBE = {
     "svq4k": "4096x4096 affine lattice d=4 (2 bits/weight)",
     "svq70b": "70B-class pair 28672x8192 + 8192x28672 affine lattice d=4 (2 bits/weight)",
 }
-GEMV_SOURCES = ["gemv_bit_unpack_amd/csrc/vq_gemv.hip", "gemv_bit_unpack_amd/csrc/vq_device.h"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_vq_gemv_dec4k_m1.json")
+GEMV_SOURCES = ["gemv_bit_unpack_amd/csrc/vq_gemv_sliced.hip", "gemv_bit_unpack_amd/csrc/vq_device.h",
+                "gemv_bit_unpack_amd/csrc/vq_internal.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_vq_gemv_ws_l70b_m1.json")
+TRIALS = 5
+HEADLINE_KEY = "l70b"
 
 
 def log(msg):
@@ -362,35 +370,141 @@ def time_ring(torch, rings, steps, warmup, use_graph=True):
     return gpu_s / n_calls, n_calls, wall, ("hipgraph" if graph is not None else "eager")
 
 
+# ------------------------------------------------------------------ exact-step timing
+
+def time_steps(torch, rings, steps, warmup, trials=TRIALS):
+    """Time exactly `steps` steps, one call per ring per step (ring copy = step mod copies).
+
+    `warmup` eager steps first; the `steps` steps are then captured in one HIP graph,
+    replayed once untimed, and replayed `trials` times, each between two device
+    synchronisations and timed with events on the replay stream.  Returns per-step seconds
+    for every trial."""
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    for k in range(warmup):
+        for r in rings:
+            r.call(k, sp)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    ssp = ctypes.c_void_p(side.cuda_stream)
+    for r in rings:  # warm-up on the capture stream too
+        r.call(0, ssp)
+    side.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        gsp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for k in range(steps):
+            for r in rings:
+                r.call(k, gsp)
+    torch.cuda.synchronize()
+    graph.replay()  # untimed: uploads the graph
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(trials):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        graph.replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        out.append(start.elapsed_time(end) * 1e-3 / steps)
+    del graph
+    return out
+
+
+def cold_call_us(torch, ring, reps=5):
+    """One call after streaming a 1 GiB buffer through the caches (L2 and Infinity Cache
+    flushed of the layer), timed with events; median over `reps` different copies."""
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    times = []
+    for k in range(reps):
+        flush.add_(1.0)
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        ring.call(k, sp)
+        end.record(stream)
+        torch.cuda.synchronize()
+        times.append(start.elapsed_time(end) * 1e3)
+    del flush
+    return round(sorted(times)[len(times) // 2], 3)
+
+
+def stream_ceiling_gbps():
+    """HBM streaming-read rate measured by the ceiling microbenchmark (a separate process)."""
+    import subprocess
+
+    exe = os.path.join(ROOT, "gemv_bit_unpack_amd", "micro", "vq_ceilings")
+    try:
+        r = subprocess.run([exe, "--stream"], capture_output=True, text=True, timeout=120)
+        return float(json.loads(r.stdout)["stream_read_GBps"])
+    except Exception as e:  # the ratio is reported only when the measurement ran
+        log("stream ceiling not measured: %s" % e)
+        return None
+
+
 # ------------------------------------------------------------------ CPU baseline
 
-def cpu_baseline(budget_s=12.0):
-    """The oracle (unpack + fp32 dequant + fp64 product) on the host, 4096x4096 K=65536 M=1."""
+CPU_CONFIGS = [("tiny", 1), ("dec4k", 1), ("dec4k_res", 1), ("mlp8b", 1), ("l70b", 1)]
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(budget_s=30.0):
+    """The oracle (bit-by-bit unpack + fp32 dequant + fp64 product) on all host cores, on
+    every workload at M = 1 (both layers of a pair): wall-clock median of 3 per workload.
+    Workloads are taken smallest first and stop once `budget_s` of timed work has run."""
     import numpy as np
 
     import oracle
     import synth
 
     try:
-        threads = min(len(os.sched_getaffinity(0)), 16)
+        threads = len(os.sched_getaffinity(0))
     except AttributeError:
-        threads = min(os.cpu_count() or 1, 16)
-    lay = synth.workload_layer("dec4k", 0)
-    n, i = lay["n"], lay["in_features"]
-    packed = oracle.pack(n, i, 8, 16, 0, lay["idx1"])
-    xb = synth.workload_x("dec4k", 0, 1)
-    per = packed.size + (1 << 16) * 8 * 2 + 2 * n + 2 * i + 2 * n
-    calls, t0 = 0, time.perf_counter()
-    while True:
-        oracle.forward(n, i, 8, 16, 0, packed, lay["cb1"], None, lay["scale"], None, xb, False, 1, nthreads=threads)
-        calls += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
+        threads = os.cpu_count() or 1
+    per, spent = {}, 0.0
+    for key, m in CPU_CONFIGS:
+        w = synth.WORKLOADS[key]
+        layers = []
+        for li, (n, i) in enumerate(w.layers):
+            lay = synth.workload_layer(key, li)
+            packed = oracle.pack(n, i, w.v, w.bits1, w.bits2, lay["idx1"], lay["idx2"])
+            layers.append((lay, packed, synth.workload_x(key, li, m)))
+        t_runs = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            for lay, packed, xb in layers:
+                oracle.forward(lay["n"], lay["in_features"], w.v, w.bits1, w.bits2, packed, lay["cb1"], lay["cb2"],
+                               lay["scale"], None, xb, w.x_dtype == "bf16", m, nthreads=threads)
+            t_runs.append(time.perf_counter() - t0)
+        t = sorted(t_runs)[1]
+        spent += sum(t_runs)
+        nbytes = sum(packed.size + ((1 << w.bits1) + ((1 << w.bits2) if w.bits2 else 0)) * w.v * 2
+                     + 2 * lay["n"] + 2 * m * lay["in_features"] + 2 * m * lay["n"] for lay, packed, _ in layers)
+        per[key] = {"ms_per_step": round(t * 1e3, 3), "GBps": round(nbytes / t / 1e9, 4), "layers": len(layers)}
+        del layers
+        if spent > budget_s:
             break
-    return {"value": round(per * calls / el / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": "%d calls of the 4096x4096 K1=65536 M=1 layer (bit-by-bit unpack, fp32 dequant, fp64 "
-                      "product) in %.1f s; same algorithmic bytes per call as the GPU step" % (calls, el),
-            "ms_per_call": round(el / calls * 1e3, 3)}
+    head = per.get(HEADLINE_KEY)
+    return {"value": head["GBps"] if head else None, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "cpu": cpu_model(),
+            "sample": "one copy of each workload's layer(s) at M = 1, the whole layer (bit-by-bit unpack, fp32 "
+                      "dequant, fp64 product over all rows), wall-clock median of 3 on %d threads; value = the "
+                      "70B-class pair, the headline workload, on the same algorithmic bytes" % threads,
+            "per_workload": per}
 
 
 # ------------------------------------------------------------------ main
@@ -398,13 +512,13 @@ def cpu_baseline(budget_s=12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=100, help="timed steps (layer pairs) per trial")
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a HIP graph")
     ap.add_argument("--only-headline", action="store_true", help="skip the GEMM, per-workload and CPU legs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-gemm", action="store_true", help="run only the M=128 prefill GEMM leg (for profiling)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=30.0)
     ap.add_argument("--ceilings", action="store_true",
                     help="run only the hardware-ceiling microbenchmark (stream read, global and LDS gathers)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -474,60 +588,101 @@ def main():
                           "kernel": "codebook-sliced" if any(r.sliced for r in rings) else "gather",
                           "calls": calls, "launch": launch}))
         return
-    # Headline: vq_gemv_ws, 4096x4096, K1 = 65536, M = 1.
-    ring = Ring(vq, torch, "dec4k", 0, 1, shared_book=args.shared_book)
-    log("headline ring: %d copies of %s, %.2f MB per call" % (ring.copies, DESCRIBE["dec4k"],
-                                                              ring.bytes_per_call / 1e6))
-    sec, n_calls, wall, launch = time_ring(torch, [ring], args.steps, args.warmup, use_graph)
-    gbps = ring.bytes_per_call / sec / 1e9
-    g_cb = (ring.bytes_per_call + gathered_bytes(ring.desc)) / sec / 1e9
-    nv = (ring.desc.in_features + 7) // 8
+    # Headline: vq_gemv_ws at M = 1 on the 70B-class pair (up, then down, per step).
+    stream_gbps = stream_ceiling_gbps()
+    up = Ring(vq, torch, HEADLINE_KEY, 0, 1, shared_book=args.shared_book)
+    down = Ring(vq, torch, HEADLINE_KEY, 1, 1, shared_book=args.shared_book)
+    rings = [up, down]
+    log("headline: %d + %d copies of %s, %.2f MB per step" % (up.copies, down.copies, DESCRIBE[HEADLINE_KEY],
+                                                           (up.bytes_per_call + down.bytes_per_call) / 1e6))
+    t0 = time.perf_counter()
+    per_step = time_steps(torch, rings, args.steps, args.warmup)
+    wall = time.perf_counter() - t0
+    sec = sorted(per_step)[len(per_step) // 2]
+    step_bytes = up.bytes_per_call + down.bytes_per_call
+    gbps = step_bytes / sec / 1e9
+    nv = lambda r: (r.desc.in_features + 7) // 8
+    gathers = sum(r.desc.out_features * nv(r) for r in rings)
+    g_cb = (step_bytes + sum(gathered_bytes(r.desc) for r in rings)) / sec / 1e9
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        if not ring.sliced and tr.get("source_hash") == source_hash(GEMV_SOURCES):
-            traffic = tr.get("hbm_bytes_per_launch")
+        if tr.get("source_hash") == source_hash(GEMV_SOURCES):
+            traffic = tr.get("hbm_bytes_per_step")
     out = {
         "metric": "vq_gemv effective GB/s & % HBM peak at M=1; vq_gemm TFLOP/s at M=128",
         "value": round(gbps, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": n_calls,
+        "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(sec * 1e3, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "decode GEMV, " + DESCRIBE["dec4k"] + ", M=1, fp16 x and y", "global_batch": 1,
-                   "layer_copies_in_ring": ring.copies, "launch": launch,
-                   "bytes_per_step": ring.bytes_per_call},
+        "config": {"workload": "decode GEMV (vq_gemv_ws) over the 70B-class MLP layer pair, "
+                               + DESCRIBE[HEADLINE_KEY] + ", M=1, bf16 x and y; one step = the up then the down layer",
+                   "global_batch": 1, "layer_copies_in_ring": [up.copies, down.copies],
+                   "launch": "hipgraph of exactly `steps` steps", "trials": TRIALS,
+                   "bytes_per_step": step_bytes,
+                   "path": "codebook-sliced" if all(r.sliced for r in rings) else "gather"},
+        "trials_ms_per_step": [round(t * 1e3, 6) for t in per_step],
+        "ms_per_step_min": round(min(per_step) * 1e3, 6),
+        "value_at_min": round(step_bytes / min(per_step) / 1e9, 2),
         "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+        "pct_measured_stream_ceiling": round(100.0 * gbps / stream_gbps, 2) if stream_gbps else None,
+        "measured_stream_ceiling_GBps": stream_gbps,
         "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": "gemv_sliced_kernel<false>" if ring.sliced else "gemv_kernel<8,1,0,16,false,4>"},
-        "gather": {"gathers_per_s": round(ring.desc.out_features * nv / sec, 1),
+                     "kernel": "vq_gemv_ws call, timed whole: gemv_sliced_kernel<true, true> (the dominant kernel, "
+                               "which also converts the bf16 x) + gemv_sliced_finalize",
+                     "units": "algorithmic bytes of the pair per step / event-timed step"},
+        "cold_single_call_us": {"up": cold_call_us(torch, up), "down": cold_call_us(torch, down),
+                                "note": "one call after a 1 GiB buffer has been streamed through the caches"},
+        "gather": {"gathers_per_s": round(gathers / sec, 1),
                    "effective_incl_gathered_centroids_GBps": round(g_cb, 2),
                    "note": "every 16-byte centroid lookup counted once: through L2 for the gather kernel, "
                            "from the 128 KiB LDS slices for the codebook-sliced one"},
         "wall_s_timed": round(wall, 4),
     }
+    del up, down, rings
+    torch.cuda.empty_cache()
     if args.shared_book:
         out["config"]["diagnostic"] = "shared codebook across the ring (not the headline protocol)"
     if not args.only_headline and not args.shared_book:
         # Prefill GEMM at M = 128 on the 70B-class pair.
-        up = Ring(vq, torch, "l70b", 0, 128, copies=6, fn="vq_gemm")
-        down = Ring(vq, torch, "l70b", 1, 128, copies=6, fn="vq_gemm")
-        gsec, gcalls, _, glaunch = time_ring(torch, [up, down], 48, 12, use_graph)
+        up = Ring(vq, torch, HEADLINE_KEY, 0, 128, copies=4, fn="vq_gemm")
+        down = Ring(vq, torch, HEADLINE_KEY, 1, 128, copies=4, fn="vq_gemm")
+        gt = time_steps(torch, [up, down], 8, 2)
+        gsec = sorted(gt)[len(gt) // 2] / 2  # per layer call
         flops = (up.flops_per_call + down.flops_per_call) / 2
         tflops = flops / gsec / 1e12
-        out["gemm"] = {"workload": "prefill GEMM, " + DESCRIBE["l70b"] + ", M=128, bf16 x and y",
+        out["gemm"] = {"workload": "prefill GEMM, " + DESCRIBE[HEADLINE_KEY] + ", M=128, bf16 x and y",
                        "tflops": round(tflops, 2), "frac_mfma_peak": round(tflops / MFMA_PEAK_TFLOPS, 4),
-                       "ms_per_call": round(gsec * 1e3, 4), "calls": gcalls, "launch": glaunch}
+                       "ms_per_call": round(gsec * 1e3, 4), "trials_ms_per_call": [round(t * 500, 4) for t in gt],
+                       "launch": "hipgraph, 8 steps (up + down) per trial"}
         del up, down
         torch.cuda.empty_cache()
+        # GEMV / GEMM crossover on the same pair: vq_gemv_ws (M <= 16) against vq_gemm.
+        cross = {}
+        for m in (1, 8, 16, 32):
+            entry = {}
+            for fn in ("vq_gemv_ws", "vq_gemm"):
+                if fn == "vq_gemv_ws" and m > 16:
+                    entry[fn + "_us_per_call"] = None  # the GEMV takes M <= 16
+                    continue
+                rr = [Ring(vq, torch, HEADLINE_KEY, li, m, copies=6, fn=fn) for li in (0, 1)]
+                tt = time_steps(torch, rr, 12, 2)
+                entry[fn + "_us_per_call"] = round(sorted(tt)[len(tt) // 2] / 2 * 1e6, 3)
+                del rr
+                torch.cuda.empty_cache()
+            g_us, m_us = entry.get("vq_gemv_ws_us_per_call"), entry["vq_gemm_us_per_call"]
+            entry["faster"] = "vq_gemm" if g_us is None or m_us < g_us else "vq_gemv_ws"
+            cross["m%d" % m] = entry
+        out["gemv_gemm_crossover_l70b"] = cross
         per = {}
 
         def measure(rings):
@@ -571,8 +726,8 @@ def main():
         out["affine_lattice"] = svq_leg(vq, torch, use_graph)
         out["rht"] = rht_leg(vq, torch, use_graph)
         out["encode"] = encode_leg(vq, torch)
-        if not args.no_cpu_baseline:
-            out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    if not args.no_cpu_baseline and not args.shared_book and not args.only_headline:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

@@ -44,7 +44,8 @@ constexpr int kGroups = 32;              // workgroup groups: 8 x 32 = 256 workg
 constexpr int kRes = 256;                // residual centroids (8-bit indices)
 constexpr int kRT = 128;                 // rows per tile
 constexpr int kRG = kRT / 16;            // 16-row groups per tile
-constexpr int kRedFloats = 8 * 16 * 16;  // column-block sums of one row group, M <= 16
+constexpr int kRedFloats = 8 * 16 * 16;  // column-block sums of one row group (M <= 16), or of
+                                         // all 8 row groups for M <= 2
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
@@ -60,6 +61,7 @@ struct SlicedCfg {
   float* part;          // [8 * n_cs][M][N] partial sums
   const uint16_t* x16;  // fp16 activations [M][IN]
   const int32_t* xexp;  // [M] power of two taken out of each bf16 row, or nullptr
+  int32_t* xexp_out;    // M <= 2, bf16: where the product kernel writes those powers
 };
 
 __device__ __forceinline__ float4_t mfma16(const uint4& a, const uint4& b, const float4_t& c) {
@@ -84,13 +86,46 @@ __device__ __forceinline__ void slice_addrs(const uint4& w, uint32_t tag, uint32
   }
 }
 
-template <bool RES>
+// Raw buffer resource over n bytes at p (stride 0).  A buffer load returns zero for every
+// dword that does not lie wholly inside the n bytes (the vector, scalar and instruction
+// offsets all counted) and reads no memory for it.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t span(const void* p, uint32_t n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
+}
+__device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ uint2 ld8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0));
+}
+
+// LDS layout (one array, fixed at compile time): the residual book (256 entries and a zero
+// entry) first, so a residual read needs no base; then the slice (8192 entries and the
+// zero centroid), whose base fits the 16-bit offset field of ds_read_b128; then the
+// reduction area.
+template <bool RES, bool SM>
+struct SlicedLds {
+  static constexpr int kResEntries = RES ? kRes + 1 : 0;
+  static constexpr int kSliceAt = kResEntries;              // in 16-byte entries
+  static constexpr int kRedAt = kSliceAt + kSlice + 1;
+  static constexpr int kXAt = kRedAt + kRedFloats / 4;
+  // M <= 2: each wavefront's activations, [wave][2 buffers][2 batch rows][32 vectors]
+  static constexpr int kEntries = kXAt + (SM ? 8 * 2 * 2 * 32 : 0);
+};
+
+// SM: M <= 2, where every row group's column-block sums fit the reduction area at once and
+// the activations go through LDS: each wavefront loads its 32 vectors of x (8 bytes per
+// lane per batch row), converts bf16 to fp16 times 2^-e itself (e from the row's largest
+// magnitude, found by every workgroup at the start), and reads its MFMA operands back
+// from LDS; no separate pass over x.  Larger M reads fp16 x (converted by xprep_kernel for
+// bf16) straight into registers, one chunk ahead.
+template <bool RES, bool SM>
 __global__ __launch_bounds__(kThreads) void gemv_sliced_kernel(ProductArgs a, SlicedCfg g) {
-  // static LDS: the slice's base address is fixed when compiling, so a centroid read needs
-  // no base add on top of index * 16
-  __shared__ uint4 slice[kSlice + 1];
-  __shared__ uint4 resb[RES ? kRes + 1 : 1];
-  __shared__ float red[kRedFloats];
+  using L = SlicedLds<RES, SM>;
+  __shared__ uint4 lds[L::kEntries];
+  uint4* const slice = lds + L::kSliceAt;
+  float* const red = (float*)(lds + L::kRedAt);
+  uint4* const xs = lds + L::kXAt;
 
   const int tid = threadIdx.x;
   const int xcd = blockIdx.x & 7;
@@ -108,10 +143,21 @@ __global__ __launch_bounds__(kThreads) void gemv_sliced_kernel(ProductArgs a, Sl
   const uint32_t tag = ((uint32_t)s << kSliceBits) * 0x10001u;
   const uint32_t s1b = (uint32_t)a.s1_words * 4u;
   const uint32_t s2b = (uint32_t)a.s2_words * 4u;
-  const char* p1 = (const char*)a.packed1;
-  const char* p2 = (const char*)a.packed2;
-  const char* xbase = (const char*)g.x16;
   const uint32_t lane_col = (uint32_t)(cb * 32 + g4 * 8);  // the lane's first vector within a chunk
+  // One buffer per stream: rows past N and vectors past the end of the last row read as
+  // zero.  The lane's part of every offset is fixed; the rest (row block, row group, chunk)
+  // is uniform and goes in the scalar offset.
+  const __amdgpu_buffer_rsrc_t b1 = span(a.packed1, (uint32_t)N * s1b);
+  const __amdgpu_buffer_rsrc_t b2 = span(RES ? (const void*)a.packed2 : (const void*)a.packed1,
+                                         RES ? (uint32_t)N * s2b : 0u);
+  const __amdgpu_buffer_rsrc_t bx = span(SM ? (const void*)a.x : (const void*)g.x16,
+                                         (uint32_t)M * (uint32_t)a.in_features * 2u);
+  const uint32_t v_idx = (uint32_t)r16 * s1b + lane_col * 2u;
+  const uint32_t v_res = (uint32_t)r16 * s2b + lane_col;
+  const uint32_t v_x = (uint32_t)min(r16, M - 1) * (uint32_t)a.in_features * 2u + lane_col * 16u;
+  // M <= 2: lane l stages half l & 1 (4 values) of vector l >> 1 of the wavefront's 32
+  const uint32_t v_xs = (uint32_t)(cb * 32 + (lane >> 1)) * 16u + (uint32_t)(lane & 1) * 8u;
+  const bool xbf16 = a.x_dtype == VQ_BF16;
 
   // current tile u (row block rbk, column split cs) and chunk c
   int u = grp, rbk = u / g.n_cs, cs = u - rbk * g.n_cs;
@@ -132,32 +178,56 @@ __global__ __launch_bounds__(kThreads) void gemv_sliced_kernel(ProductArgs a, Sl
       }
     }
   };
-  // byte offsets of the lane's index words for row group q of row block rb, chunk cc
-  // (rows past N read row N - 1; vectors past the row end read chunk 0 or vector nv - 1)
-  auto idx_off = [&](int rb, int cc, int q) __attribute__((always_inline)) -> uint32_t {
-    const int row = min(rb * kRT + q * 16 + r16, N - 1);
-    const uint32_t j0 = (uint32_t)cc * kChunk + lane_col;
-    const uint32_t c16 = j0 < (uint32_t)nv ? (j0 >> 3) : 0u;
-    return (uint32_t)row * s1b + c16 * 16u;
+  // index words of row group q of row block rb, chunk cc; the lane's 8 residual indices
+  // (row group s); the activations of the lane's 8 vectors (lanes of batch rows >= M read
+  // row M - 1: they feed output columns that are dropped)
+  auto load_idx = [&](int rb, int cc, int q) __attribute__((always_inline)) -> uint4 {
+    return ld16(b1, v_idx, (uint32_t)(rb * kRT + q * 16) * s1b + (uint32_t)cc * (kChunk * 2));
   };
-  // byte offset of the lane's 8 residual indices (row group s of row block rb, chunk cc)
-  auto res_off = [&](int rb, int cc) __attribute__((always_inline)) -> uint32_t {
-    const int row = min(rb * kRT + s * 16 + r16, N - 1);
-    const uint32_t j0 = (uint32_t)cc * kChunk + lane_col;
-    return (uint32_t)row * s2b + (j0 < (uint32_t)nv ? j0 : 0u);
+  auto load_res = [&](int rb, int cc) __attribute__((always_inline)) -> uint2 {
+    return ld8(b2, v_res, (uint32_t)(rb * kRT + s * 16) * s2b + (uint32_t)cc * kChunk);
   };
-  // activations of the lane's 8 vectors; lanes of batch rows >= M load row M - 1 (they
-  // feed output columns that are dropped)
   auto load_x = [&](int cc, uint4 (&xr)[8]) __attribute__((always_inline)) {
-    const uint32_t j0 = (uint32_t)cc * kChunk + lane_col;
-    const char* row = xbase + (size_t)min(r16, M - 1) * a.in_features * 2;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) xr[k] = *(const uint4*)(row + (size_t)min(j0 + k, (uint32_t)nv - 1u) * 16u);
+    for (int k = 0; k < 8; ++k) xr[k] = ld16(bx, v_x + k * 16u, (uint32_t)cc * (kChunk * 16));
+  };
+  // M <= 2: raw activations of chunk cc (8 bytes per lane and batch row), and their
+  // conversion into the wavefront's LDS buffer followed by the operand reads
+  int xe[2] = {0, 0};  // power of two taken out of each bf16 batch row
+  auto load_xraw = [&](int cc, uint2 (&xw)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      xw[m] = m < M ? ld8(bx, v_xs, (uint32_t)cc * (kChunk * 16) + (uint32_t)m * (uint32_t)a.in_features * 2u)
+                    : make_uint2(0u, 0u);
+    }
+  };
+  auto stage_x = [&](int buf, const uint2 (&xw)[2], uint4 (&xr)[8]) __attribute__((always_inline)) {
+    char* wbase = (char*)(xs + (cb * 2 + buf) * 64);
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      uint2 h = xw[m];
+      if (xbf16) {
+        const uint32_t w2[2] = {h.x, h.y};
+        uint32_t o[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const uint32_t lo = vqd::f32_to_f16_rne(ldexpf(vqd::bf16_to_f32(w2[i] & 0xFFFFu), -xe[m]));
+          const uint32_t hi = vqd::f32_to_f16_rne(ldexpf(vqd::bf16_to_f32(w2[i] >> 16), -xe[m]));
+          o[i] = lo | (hi << 16);
+        }
+        h = make_uint2(o[0], o[1]);
+      }
+      *(uint2*)(wbase + m * 512 + v_xs - (uint32_t)cb * 512u) = h;
+    }
+    const uint4* rbase = (const uint4*)(wbase + min(r16, M - 1) * 512) + g4 * 8;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) xr[k] = rbase[k];
   };
 
   uint4 iw[kRG];  // index words of the current chunk, one per row group
   uint2 ir = make_uint2(0u, 0u);  // residual indices of row group s, one byte per vector
   uint4 xa[8], xb[8];
+  uint2 xw[2];    // M <= 2: raw activations of the next chunk
 
   // stage the slice (and the residual book): the 16 loads per thread first, then the
   // first chunk's indices and activations, then the LDS writes
@@ -172,9 +242,13 @@ __global__ __launch_bounds__(kThreads) void gemv_sliced_kernel(ProductArgs a, Sl
     u32x4 qr = {0u, 0u, 0u, 0u};
     if (RES && tid < kRes) qr = ((const u32x4*)a.cb2)[tid];
 #pragma unroll
-    for (int q = 0; q < kRG; ++q) iw[q] = *(const uint4*)(p1 + idx_off(rbk, c, q));
-    if constexpr (RES) ir = *(const uint2*)(p2 + res_off(rbk, c));
-    load_x(c, xa);
+    for (int q = 0; q < kRG; ++q) iw[q] = load_idx(rbk, c, q);
+    if constexpr (RES) ir = load_res(rbk, c);
+    if constexpr (SM) {
+      load_xraw(c, xw);
+    } else {
+      load_x(c, xa);
+    }
     dst[0 * kThreads] = q0;
     dst[1 * kThreads] = q1;
     dst[2 * kThreads] = q2;
@@ -192,10 +266,50 @@ __global__ __launch_bounds__(kThreads) void gemv_sliced_kernel(ProductArgs a, Sl
     dst[14 * kThreads] = q14;
     dst[15 * kThreads] = q15;
     if (tid == 0) slice[kSlice] = make_uint4(0u, 0u, 0u, 0u);
-    if (RES && tid <= kRes) ((u32x4*)resb)[tid] = qr;  // entry kRes stays zero
+    if (RES && tid <= kRes) ((u32x4*)lds)[tid] = qr;  // entry kRes stays zero
+  }
+  if constexpr (SM) {
+    // largest |x| of each bf16 batch row (as bits: they order like the values), reduced
+    // over the workgroup; e puts it in [2^14, 2^15) after scaling by 2^-e
+    if (xbf16) {
+      const __amdgpu_buffer_rsrc_t bxr = span(a.x, (uint32_t)M * (uint32_t)a.in_features * 2u);
+      const int n16 = a.in_features / 8;
+      uint32_t mx[2] = {0u, 0u};
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        if (m < M) {
+          for (int i = tid; i < n16; i += kThreads) {
+            const uint4 v = ld16(bxr, (uint32_t)i * 16u, (uint32_t)m * (uint32_t)a.in_features * 2u);
+            const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int h = 0; h < 4; ++h) mx[m] = max(mx[m], max(w4[h] & 0x7FFFu, (w4[h] >> 16) & 0x7FFFu));
+          }
+#pragma unroll
+          for (int off = 32; off > 0; off >>= 1) mx[m] = max(mx[m], (uint32_t)__shfl_xor((int)mx[m], off, 64));
+        }
+      }
+      if (lane == 0) {
+        ((uint32_t*)red)[cb] = mx[0];
+        ((uint32_t*)red)[8 + cb] = mx[1];
+      }
+    }
   }
   adv_pre();
   __syncthreads();
+  if constexpr (SM) {
+    if (xbf16) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        uint32_t mx = 0u;
+#pragma unroll
+        for (int w = 0; w < 8; ++w) mx = max(mx, ((const uint32_t*)red)[8 * m + w]);
+        xe[m] = (int)((mx >> 7) & 0xFFu) - 127 - 14;
+      }
+      if (blockIdx.x == 0 && tid < M) g.xexp_out[tid] = xe[tid];
+    }
+    __syncthreads();  // the reduction area is reused at the first tile end
+    stage_x(0, xw, xa);
+  }
 
   float4_t d[kRG];
 #pragma unroll
@@ -206,11 +320,16 @@ __global__ __launch_bounds__(kThreads) void gemv_sliced_kernel(ProductArgs a, Sl
   // refill of the row group's index slot with the next chunk, and the 8 products; row
   // group s also takes the 8 residual centroids.  In the ragged last chunk of a row the
   // vectors past its end get zero x and an index outside every slice (bit 13 set after
-  // the slice XOR), so they read the zero centroid; this fix-up is a uniform branch.
+  // the slice XOR), so they read the zero centroid; their residual centroids meet zero x.
+  // This fix-up is a uniform branch.
+  int xbuf = 0;  // M <= 2: the LDS buffer holding the current chunk's activations
   auto chunk = [&](uint4 (&xr)[8], uint4 (&xn)[8]) __attribute__((always_inline)) {
-    load_x(pc, xn);
+    if constexpr (SM) {
+      load_xraw(pc, xw);
+    } else {
+      load_x(pc, xn);
+    }
     const int nvalid = nv - (c * kChunk + (int)lane_col);
-    uint32_t rmask = 0u;  // residual slots past the row end
     if ((c + 1) * kChunk > nv) {
       // a 16-bit index (s ^ 7) << 13 gives 0xE000 after the slice XOR: the zero centroid
       const uint32_t fill = ((uint32_t)(s ^ 7) << 13) * 0x10001u;
@@ -226,7 +345,6 @@ __global__ __launch_bounds__(kThreads) void gemv_sliced_kernel(ProductArgs a, Sl
       }
 #pragma unroll
       for (int k = 0; k < 8; ++k) xr[k] = k < nvalid ? xr[k] : make_uint4(0u, 0u, 0u, 0u);
-      rmask = nvalid >= 8 ? 0u : (nvalid > 0 ? 0xFFu & ~((1u << nvalid) - 1u) : 0xFFu);
     }
     uint4 cv[2][8];
     auto reads = [&](int q, uint4 (&c8)[8]) __attribute__((always_inline)) {
@@ -239,34 +357,86 @@ __global__ __launch_bounds__(kThreads) void gemv_sliced_kernel(ProductArgs a, Sl
 #pragma unroll
     for (int q = 0; q < kRG; ++q) {
       if (q + 1 < kRG) reads(q + 1, cv[(q + 1) & 1]);
-      iw[q] = *(const uint4*)(p1 + idx_off(prb, pc, q));
+      iw[q] = load_idx(prb, pc, q);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int k = 0; k < 8; ++k) d[q] = mfma16(cv[q & 1][k], xr[k], d[q]);
       if constexpr (RES) {
         if (q == s) {  // uniform: this slice's residual row group
-          const uint32_t rw[2] = {ir.x, ir.y};
-          uint4 cr[8];
+          // byte k of the residual words, times 16: the entry's LDS address (the book is
+          // at address 0), one SDWA shift each
+          uint32_t ra[8];
+          asm("v_lshlrev_b32_sdwa %0, 4, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0"
+              : "=v"(ra[0]) : "v"(ir.x));
+          asm("v_lshlrev_b32_sdwa %0, 4, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1"
+              : "=v"(ra[1]) : "v"(ir.x));
+          asm("v_lshlrev_b32_sdwa %0, 4, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2"
+              : "=v"(ra[2]) : "v"(ir.x));
+          asm("v_lshlrev_b32_sdwa %0, 4, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3"
+              : "=v"(ra[3]) : "v"(ir.x));
+          asm("v_lshlrev_b32_sdwa %0, 4, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0"
+              : "=v"(ra[4]) : "v"(ir.y));
+          asm("v_lshlrev_b32_sdwa %0, 4, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1"
+              : "=v"(ra[5]) : "v"(ir.y));
+          asm("v_lshlrev_b32_sdwa %0, 4, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2"
+              : "=v"(ra[6]) : "v"(ir.y));
+          asm("v_lshlrev_b32_sdwa %0, 4, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3"
+              : "=v"(ra[7]) : "v"(ir.y));
+          // into the registers the 8 products just issued read from: their LDS latency
+          // hides behind those products
+          uint4 (&cr)[8] = cv[q & 1];
 #pragma unroll
-          for (int k = 0; k < 8; ++k) {
-            const uint32_t e = (rw[k >> 2] >> (8 * (k & 3))) & 0xFFu;
-            cr[k] = resb[(rmask >> k) & 1u ? (uint32_t)kRes : e];
-          }
-          ir = *(const uint2*)(p2 + res_off(prb, pc));
+          for (int k = 0; k < 8; ++k) cr[k] = *(const uint4*)((const char*)lds + ra[k]);
+          ir = load_res(prb, pc);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int k = 0; k < 8; ++k) d[q] = mfma16(cr[k], xr[k], d[q]);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    if constexpr (SM) {  // the next chunk's activations: converted, staged, read back
+      xbuf ^= 1;
+      stage_x(xbuf, xw, xr);
+    }
     adv_pre();
   };
 
   // End of a tile: per row group, the 8 column blocks are added in LDS (fixed order) and
   // one partial per (row, batch row) goes to the workspace.  Lane l of a wavefront holds
-  // rows 4 * (l / 16) + r of output column l % 16 in register r.
+  // rows 4 * (l / 16) + r of output column l % 16 in register r.  For M <= 2 every row
+  // group fits the reduction area at once (two barriers per tile); larger M takes the
+  // row groups one at a time.
+  auto store_part = [&](int q, int rl, int m, float v) __attribute__((always_inline)) {
+    const int row = rbk * kRT + q * 16 + rl;
+    if (row < N) g.part[((size_t)(cs * kSlices + s) * M + m) * N + row] = v;
+  };
   auto tile_end = [&]() __attribute__((always_inline)) {
+    if constexpr (SM) {
+      if (r16 < M) {
 #pragma unroll
+        for (int q = 0; q < kRG; ++q) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) red[((q * 8 + cb) * 16 + 4 * g4 + r) * 2 + r16] = d[q][r];
+        }
+      }
+      __syncthreads();
+      if (tid < kRT * M) {  // thread = (row group, row, batch row)
+        const int m = tid & (M - 1);
+        const int qr = tid / M;
+        const int q = qr >> 4, rl = qr & 15;
+        float v = 0.0f;
+#pragma unroll
+        for (int c2 = 0; c2 < 8; ++c2) v += red[((q * 8 + c2) * 16 + rl) * 2 + m];
+        store_part(q, rl, m, v);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < kRG; ++q) d[q] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      return;
+    }
+    // one row group at a time (few row groups' addresses held live: no unrolling)
+#pragma unroll 1
     for (int q = 0; q < kRG; ++q) {
       if (r16 < M) {
 #pragma unroll
@@ -279,8 +449,7 @@ __global__ __launch_bounds__(kThreads) void gemv_sliced_kernel(ProductArgs a, Sl
         float v = 0.0f;
 #pragma unroll
         for (int c2 = 0; c2 < 8; ++c2) v += red[(c2 * 16 + rl) * M + m];
-        const int row = rbk * kRT + q * 16 + rl;
-        if (row < N) g.part[((size_t)(cs * kSlices + s) * M + m) * N + row] = v;
+        store_part(q, rl, m, v);
       }
       __syncthreads();
       d[q] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -300,11 +469,18 @@ __global__ __launch_bounds__(kThreads) void gemv_sliced_kernel(ProductArgs a, Sl
     return true;
   };
 
-  for (;;) {  // activations alternate between two register sets
-    chunk(xa, xb);
-    if (!next()) break;
-    chunk(xb, xa);
-    if (!next()) break;
+  if constexpr (SM) {
+    for (;;) {  // one register set: refilled from LDS at the end of each chunk
+      chunk(xa, xa);
+      if (!next()) break;
+    }
+  } else {
+    for (;;) {  // activations alternate between two register sets
+      chunk(xa, xb);
+      if (!next()) break;
+      chunk(xb, xa);
+      if (!next()) break;
+    }
   }
 }
 
@@ -424,7 +600,8 @@ Plan make_plan(int32_t n, int32_t in_features, int32_t m, bool bf16) {
   g.groups = units < kGroups ? units : kGroups;
   p.part_off = 0;
   p.x16_off = round256((size_t)kSlices * g.n_cs * m * n * sizeof(float));
-  p.exp_off = p.x16_off + (bf16 ? round256((size_t)m * in_features * 2) : 0);
+  // the fp16 copy of x only where xprep_kernel runs (bf16, M > 2)
+  p.exp_off = p.x16_off + (bf16 && m > 2 ? round256((size_t)m * in_features * 2) : 0);
   p.bytes = p.exp_off + (bf16 ? round256((size_t)m * sizeof(int32_t)) : 0);
   return p;
 }
@@ -432,7 +609,7 @@ Plan make_plan(int32_t n, int32_t in_features, int32_t m, bool bf16) {
 
 template <bool RES>
 vq_status launch_res(const ProductArgs& a, const SlicedCfg& g, hipStream_t s) {
-  auto kern = gemv_sliced_kernel<RES>;
+  auto kern = a.m <= 2 ? gemv_sliced_kernel<RES, true> : gemv_sliced_kernel<RES, false>;
   const unsigned grid = 64u * (unsigned)((g.groups + 7) / 8);
   hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, s, a, g);
   if (hipGetLastError() != hipSuccess) return VQ_ERR_HIP;
@@ -474,13 +651,18 @@ vq_status launch_gemv_sliced(const ProductArgs& a, void* workspace, void* stream
   char* ws = (char*)workspace;
   p.cfg.part = (float*)(ws + p.part_off);
   hipStream_t s = (hipStream_t)stream;
-  if (bf16) {
+  p.cfg.xexp_out = nullptr;
+  if (bf16 && a.m > 2) {
     uint16_t* x16 = (uint16_t*)(ws + p.x16_off);
     int32_t* xexp = (int32_t*)(ws + p.exp_off);
     hipLaunchKernelGGL(xprep_kernel, dim3(a.m), dim3(1024), 0, s, a.x, a.in_features, x16, xexp);
     if (hipGetLastError() != hipSuccess) return VQ_ERR_HIP;
     p.cfg.x16 = x16;
     p.cfg.xexp = xexp;
+  } else if (bf16) {  // M <= 2: the product kernel converts x itself and writes the powers
+    p.cfg.x16 = a.x;
+    p.cfg.xexp_out = (int32_t*)(ws + p.exp_off);
+    p.cfg.xexp = p.cfg.xexp_out;
   } else {
     p.cfg.x16 = a.x;
     p.cfg.xexp = nullptr;

@@ -123,27 +123,39 @@ def test_gemv_ws_one_hot_columns_bit_exact(vq, b2):
     assert np.array_equal(y, w32.T)
 
 
-def test_gemv_ws_bf16_outside_fp16_range(vq):
+@functools.lru_cache(maxsize=1)
+def _range_layer():
+    import gemv_bit_unpack_amd as g
+
+    lay = synth.make_layer(4096, 8192, 8, 16, 8, wid=83, with_bias=False)  # 2^22 vectors: sliced from M = 1
+    return lay, DeviceLayer(g, lay)
+
+
+@pytest.mark.parametrize("pick", [[4], [0, 2], [3, 1], list(range(8))])
+def test_gemv_ws_bf16_outside_fp16_range(vq, pick):
     """Rows with values up to 3e5 (beyond fp16), rows of tiny values (4e-6 and 1e-12, the
-    second below the smallest fp16 subnormal), and a zero row.  No bias, so each batch row's
-    error is measured against its own product alone."""
-    n, i, m = 2048, 4096, 8
-    lay = synth.make_layer(n, i, 8, 16, 8, wid=83, with_bias=False)
-    dl = DeviceLayer(vq, lay)
+    second below the smallest fp16 subnormal), and a zero row; M = 1 and 2 convert x inside
+    the product kernel, M = 8 in the separate pass.  No bias, so each batch row's error is
+    measured against its own product alone."""
+    lay, dl = _range_layer()
+    i = lay["in_features"]
     g = np.random.default_rng(83)
-    xf = g.standard_normal((m, i)).astype(np.float32)
+    xf = g.standard_normal((8, i)).astype(np.float32)
     xf[0] *= 1e5
     xf[1, ::7] *= 3e5
     xf[2] *= 1e-6
     xf[3] = 0.0
     xf[4] *= 1e-12
+    xf = xf[pick]
+    m = len(pick)
     xb = synth.f32_to_bf16_bits(xf)
     y64 = oracle_y(lay, xb, "bf16")
     ws = _ws_for(vq, dl, m, "bf16")
     y = vq.gemv_ws(*dl.args(), x_tensor(xb, "bf16"), ws, y_dtype=torch.float32)
     for r in range(m):  # each batch row against its own scale
         check_y(y[r:r + 1], y64[r:r + 1], "f32", norm=max(float(np.abs(y64[r]).max()), 1e-37))
-    assert not torch.any(y[3] != 0)  # the zero row gives exact zeros
+        if pick[r] == 3:
+            assert not torch.any(y[r] != 0)  # the zero row gives exact zeros
 
 
 def test_gemv_ws_deterministic_and_reusable(vq):

@@ -86,6 +86,20 @@ __device__ __forceinline__ void slice_addrs(const uint4& w, uint32_t tag, uint32
   }
 }
 
+// The same for 4 indices in two words.
+__device__ __forceinline__ void slice_addrs4(uint32_t w0, uint32_t w1, uint32_t tag, uint32_t (&ad)[4]) {
+  const uint32_t wd[2] = {w0 ^ tag, w1 ^ tag};
+  const u16x2 lim = {(unsigned short)kSlice, (unsigned short)kSlice};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t v = __builtin_bit_cast(uint32_t, __builtin_elementwise_min(__builtin_bit_cast(u16x2, wd[h]), lim));
+    asm("v_lshlrev_b32_sdwa %0, 4, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:WORD_0"
+        : "=v"(ad[2 * h]) : "v"(v));
+    asm("v_lshlrev_b32_sdwa %0, 4, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:WORD_1"
+        : "=v"(ad[2 * h + 1]) : "v"(v));
+  }
+}
+
 // Raw buffer resource over n bytes at p (stride 0).  A buffer load returns zero for every
 // dword that does not lie wholly inside the n bytes (the vector, scalar and instruction
 // offsets all counted) and reads no memory for it.
@@ -346,23 +360,29 @@ __global__ __launch_bounds__(kThreads) void gemv_sliced_kernel(ProductArgs a, Sl
 #pragma unroll
       for (int k = 0; k < 8; ++k) xr[k] = k < nvalid ? xr[k] : make_uint4(0u, 0u, 0u, 0u);
     }
-    uint4 cv[2][8];
-    auto reads = [&](int q, uint4 (&c8)[8]) __attribute__((always_inline)) {
-      uint32_t ad[8];
-      slice_addrs(iw[q], tag, ad);
+    // 16 half steps: half h is row group h / 2, vectors 4 (h & 1) .. 4 (h & 1) + 3 of the
+    // lane's 8.  The centroid reads of half h + 2 are issued before the products of half h;
+    // three buffers of 4 centroids rotate.
+    uint4 cv[3][4];
+    auto reads = [&](int h, uint4 (&c4)[4]) __attribute__((always_inline)) {
+      const uint4& w = iw[h >> 1];
+      uint32_t ad[4];
+      slice_addrs4((h & 1) ? w.z : w.x, (h & 1) ? w.w : w.y, tag, ad);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) c8[k] = *(const uint4*)((const char*)slice + ad[k]);
+      for (int k = 0; k < 4; ++k) c4[k] = *(const uint4*)((const char*)slice + ad[k]);
     };
     reads(0, cv[0]);
+    reads(1, cv[1]);
 #pragma unroll
-    for (int q = 0; q < kRG; ++q) {
-      if (q + 1 < kRG) reads(q + 1, cv[(q + 1) & 1]);
-      iw[q] = load_idx(prb, pc, q);
+    for (int h = 0; h < 2 * kRG; ++h) {
+      const int q = h >> 1;
+      if (h + 2 < 2 * kRG) reads(h + 2, cv[(h + 2) % 3]);
+      if (h & 1) iw[q] = load_idx(prb, pc, q);  // both halves of row group q have been read
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) d[q] = mfma16(cv[q & 1][k], xr[k], d[q]);
+      for (int k = 0; k < 4; ++k) d[q] = mfma16(cv[h % 3][k], xr[4 * (h & 1) + k], d[q]);
       if constexpr (RES) {
-        if (q == s) {  // uniform: this slice's residual row group
+        if ((h & 1) && q == s) {  // uniform: this slice's residual row group
           // byte k of the residual words, times 16: the entry's LDS address (the book is
           // at address 0), one SDWA shift each
           uint32_t ra[8];
@@ -382,15 +402,20 @@ __global__ __launch_bounds__(kThreads) void gemv_sliced_kernel(ProductArgs a, Sl
               : "=v"(ra[6]) : "v"(ir.y));
           asm("v_lshlrev_b32_sdwa %0, 4, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3"
               : "=v"(ra[7]) : "v"(ir.y));
-          // into the registers the 8 products just issued read from: their LDS latency
-          // hides behind those products
-          uint4 (&cr)[8] = cv[q & 1];
+          // two groups of 4 into the buffer the products just issued read from: the first
+          // group's LDS latency hides behind those products
+          uint4 (&cr)[4] = cv[h % 3];
 #pragma unroll
-          for (int k = 0; k < 8; ++k) cr[k] = *(const uint4*)((const char*)lds + ra[k]);
+          for (int k = 0; k < 4; ++k) cr[k] = *(const uint4*)((const char*)lds + ra[k]);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) d[q] = mfma16(cr[k], xr[k], d[q]);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) cr[k] = *(const uint4*)((const char*)lds + ra[4 + k]);
           ir = load_res(prb, pc);
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int k = 0; k < 8; ++k) d[q] = mfma16(cr[k], xr[k], d[q]);
+          for (int k = 0; k < 4; ++k) d[q] = mfma16(cr[k], xr[4 + k], d[q]);
         }
       }
       __builtin_amdgcn_sched_barrier(0);

@@ -42,7 +42,7 @@ LAYOUT_ROWSTREAM = 1
 
 EXPORTED = ("vq_abi_version", "vq_status_string", "vq_packed_bytes", "vq_pack", "vq_dequant", "vq_gemv",
             "vq_gemv_workspace_bytes", "vq_gemv_ws", "vq_gemm", "vq_svq_dequant", "vq_svq_gemv", "vq_rht", "vq_rht_block",
-            "vq_assign_workspace_bytes", "vq_assign", "vq_svq_gemm")
+            "vq_assign_workspace_bytes", "vq_assign", "vq_svq_gemm", "vq_gemv_noalloc")
 
 
 class Desc(ctypes.Structure):
@@ -88,6 +88,8 @@ def _load():
     lib.vq_gemv_workspace_bytes.restype = ctypes.c_int
     lib.vq_gemv_ws.argtypes = [dp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i32, vp, ctypes.c_int, vp, sz, vp]
     lib.vq_gemv_ws.restype = ctypes.c_int
+    lib.vq_gemv_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i32, vp, ctypes.c_int, vp]
+    lib.vq_gemv_noalloc.restype = ctypes.c_int
     lib.vq_svq_dequant.argtypes = [dp, vp, vp, vp, vp, vp, ctypes.c_int, vp]
     lib.vq_svq_dequant.restype = ctypes.c_int
     lib.vq_svq_gemv.argtypes = [dp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i32, vp, ctypes.c_int, vp]
@@ -243,6 +245,13 @@ def gemv_ws(desc, packed, cb1, cb2, scale, bias, x, ws, y_dtype=None, out=None):
     Calls that share a workspace must be ordered (one stream)."""
     extra = (None, 0) if ws is None else (_dev_ptr(ws, "workspace"), ws.numel() * ws.element_size())
     return _product(lib().vq_gemv_ws, "vq_gemv_ws", desc, packed, cb1, cb2, scale, bias, x, y_dtype, out, extra)
+
+
+def gemv_noalloc(desc, packed, cb1, cb2, scale, bias, x, y_dtype=None, out=None):
+    """gemv_ws with the library's fixed per-GPU workspace: allocates nothing (``out`` given).
+
+    Calls on one GPU share that workspace and must not overlap."""
+    return _product(lib().vq_gemv_noalloc, "vq_gemv_noalloc", desc, packed, cb1, cb2, scale, bias, x, y_dtype, out)
 
 
 def gemm(desc, packed, cb1, cb2, scale, bias, x, y_dtype=None, out=None):

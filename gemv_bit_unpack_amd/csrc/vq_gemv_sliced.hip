@@ -29,6 +29,8 @@
 // bf16 activations are first rewritten as fp16 times a power of two per batch row (a
 // small pass over x), chosen from the row's largest magnitude: exact for every value down
 // to 2^-31 of that magnitude, whether the row is large, small or in between.
+#include <atomic>
+
 #include "vq_device.h"
 
 namespace {
@@ -644,9 +646,32 @@ vq_status launch_res(const ProductArgs& a, const SlicedCfg& g, hipStream_t s) {
   return hipGetLastError() == hipSuccess ? VQ_OK : VQ_ERR_HIP;
 }
 
+// Workspace for callers that cannot allocate (vq_gemv_noalloc): a fixed array in device
+// memory, one copy per GPU, held until the process ends.  In host code `scratch` names a
+// host-side stand-in, never the device memory: the device address of this GPU's copy is
+// looked up once per device, with that device current, and kept.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+
 }  // namespace
 
 namespace vqi {
+
+size_t static_scratch_bytes() { return kScratchBytes; }
+
+vq_status static_scratch(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return VQ_ERR_HIP;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {  // first call on this device (concurrent first calls find the same address)
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return VQ_ERR_HIP;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return VQ_OK;
+}
 
 bool sliced_gemv_shape_ok(const vq_desc& d, int32_t m, vq_dtype x_dtype) {
   if (d.v != 8 || d.bits1 != 16 || !(d.bits2 == 0 || d.bits2 == 8)) return false;

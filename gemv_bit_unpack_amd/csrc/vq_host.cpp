@@ -251,6 +251,22 @@ vq_status vq_gemv_ws(const vq_desc* desc, const void* packed, const void* cb1, c
   return launch_gemv(a, stream);
 }
 
+vq_status vq_gemv_noalloc(const vq_desc* desc, const void* packed, const void* cb1, const void* cb2,
+                          const void* scale, const void* bias, const void* x, vq_dtype x_dtype, int32_t M, void* y,
+                          vq_dtype y_dtype, void* stream) {
+  ProductArgs a;
+  vq_status st = prepare_product(desc, packed, cb1, cb2, scale, bias, x, x_dtype, M, y, y_dtype, 16, &a);
+  if (st != VQ_OK) return st;
+  if (a.n == 0 || a.m == 0) return VQ_OK;
+  const size_t need = sliced_gemv_workspace(*desc, a.m, a.x_dtype);
+  if (need == 0 || !sliced_gemv_pointers_ok(a)) return launch_gemv(a, stream);  // no workspace used
+  if (need > static_scratch_bytes()) return VQ_ERR_BUFFER_SIZE;
+  void* ws = nullptr;
+  st = static_scratch(&ws);
+  if (st != VQ_OK) return st;
+  return launch_gemv_sliced(a, ws, stream);
+}
+
 vq_status vq_svq_dequant(const vq_desc* desc, const void* packed, const void* a, const void* b, const void* scale,
                          void* w, vq_dtype w_dtype, void* stream) {
   SvqArgs p;

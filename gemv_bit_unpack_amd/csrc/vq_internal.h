@@ -63,6 +63,10 @@ bool sliced_gemv_shape_ok(const vq_desc& d, int32_t m, vq_dtype x_dtype);
 size_t sliced_gemv_workspace(const vq_desc& d, int32_t m, vq_dtype x_dtype);
 bool sliced_gemv_pointers_ok(const ProductArgs& a);
 vq_status launch_gemv_sliced(const ProductArgs& a, void* workspace, void* stream);
+// The fixed device workspace of vq_gemv_noalloc: its size, and this GPU's copy (looked up
+// on the first call on each device; no allocation).
+size_t static_scratch_bytes();
+vq_status static_scratch(void** ptr);
 vq_status launch_gemm(const ProductArgs& a, void* stream);
 
 // Affine-lattice layers (v = 4, one 8-bit field of four 2-bit codes per vector), after

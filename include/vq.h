@@ -142,6 +142,21 @@ vq_status vq_gemv_ws(const vq_desc* desc, const void* packed, const void* cb1, c
                      const void* bias, const void* x, vq_dtype x_dtype, int32_t M, void* y, vq_dtype y_dtype,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* vq_gemv_ws for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same operation,
+ * arguments (without the workspace) and errors as vq_gemv, and on the codebook-sliced path
+ * the same kernels and results as vq_gemv_ws, but the workspace is a fixed 16 MiB array in
+ * device memory that the library holds on each GPU it runs on until the process ends.
+ * It allocates nothing: the array's address is looked up on the first call on each
+ * device (with that device current).  Shapes whose sliced-path workspace
+ * (vq_gemv_workspace_bytes) exceeds 16 MiB return VQ_ERR_BUFFER_SIZE and launch
+ * nothing; shapes without the sliced path run the vq_gemv kernels, which use no
+ * workspace.  Every call on one GPU shares that GPU's array: calls that may run at the
+ * same time on one GPU (other streams, other threads) race and must not overlap. */
+vq_status vq_gemv_noalloc(const vq_desc* desc, const void* packed, const void* cb1, const void* cb2,
+                          const void* scale, const void* bias, const void* x, vq_dtype x_dtype, int32_t M, void* y,
+                          vq_dtype y_dtype, void* stream);
+
 /* Same operation and arguments as vq_gemv for any M >= 1 (M = 0: no-op), on the matrix
  * cores: rebuilt weight tiles are staged in LDS in the activation's 16-bit type and
  * multiplied with MFMA, fp32 accumulation.  Meant for prefill batches (M >= 32). */

@@ -221,6 +221,26 @@ def test_gemv_ws_validation_paths(vq):
     assert _gemv_ws(vq, d, ws=P, ws_bytes=0, m=0, y=None, x=None, packed=None) == vq.VQ_OK
 
 
+def test_gemv_noalloc_validation_paths(vq):
+    """vq_gemv_noalloc checks its arguments like vq_gemv, then rejects shapes whose sliced-path
+    workspace exceeds the library's fixed 16 MiB before touching the device."""
+    f = lambda d, m=1, xt=0, x=P: vq.lib().vq_gemv_noalloc(ctypes.byref(d) if d is not None else None, P, P, P,
+                                                           None, None, x, xt, m, P, 2, None)
+    d = vq.make_desc(8192, 4096, 8, 16, 0)
+    assert f(None) == vq.VQ_ERR_NULL
+    assert f(d, m=17) == vq.VQ_ERR_SHAPE
+    assert f(d, xt=2) == vq.VQ_ERR_UNSUPPORTED
+    assert f(d, x=ctypes.c_void_p(0x10001)) == vq.VQ_ERR_ALIGN
+    assert f(d, m=0) == vq.VQ_OK
+    # 2^19 rows of 8 vectors: 8 slices x 2^19 rows x 4 bytes of partials = 16 MiB + x exponents
+    huge = vq.make_desc(1 << 19, 64, 8, 16, 8)
+    assert _ws_bytes(vq, huge, 1, vq.VQ_BF16)[1] > 16 << 20
+    assert f(huge, xt=1) == vq.VQ_ERR_BUFFER_SIZE
+    m16 = vq.make_desc(1 << 16, 512, 8, 16, 0)  # fine at M = 1, too large at M = 16
+    assert _ws_bytes(vq, m16, 1, vq.VQ_F16)[1] <= 16 << 20 < _ws_bytes(vq, m16, 16, vq.VQ_F16)[1]
+    assert f(m16, m=16) == vq.VQ_ERR_BUFFER_SIZE
+
+
 def _svq(vq, desc, packed=P, a=P, b=P, scale=None, bias=None, x=P, xt=0, m=1, y=P, yt=2, fn=None):
     fn = fn or vq.lib().vq_svq_gemv
     return fn(ctypes.byref(desc) if desc is not None else None, packed, a, b, scale, bias, x, xt, m, y, yt, None)

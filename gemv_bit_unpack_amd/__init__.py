@@ -42,7 +42,7 @@ LAYOUT_ROWSTREAM = 1
 
 EXPORTED = ("vq_abi_version", "vq_status_string", "vq_packed_bytes", "vq_pack", "vq_dequant", "vq_gemv",
             "vq_gemv_workspace_bytes", "vq_gemv_ws", "vq_gemm", "vq_svq_dequant", "vq_svq_gemv", "vq_rht", "vq_rht_block",
-            "vq_assign_workspace_bytes", "vq_assign", "vq_svq_gemm", "vq_gemv_noalloc")
+            "vq_assign_workspace_bytes", "vq_assign", "vq_svq_gemm", "vq_gemv_noalloc", "vq_svq_pack")
 
 
 class Desc(ctypes.Structure):
@@ -77,6 +77,8 @@ def _load():
     lib.vq_packed_bytes.argtypes = [dp, ctypes.POINTER(sz)]
     lib.vq_packed_bytes.restype = ctypes.c_int
     lib.vq_pack.argtypes = [dp, vp, vp, vp, sz]
+    lib.vq_svq_pack.argtypes = [dp, vp, vp, sz]
+    lib.vq_svq_pack.restype = ctypes.c_int
     lib.vq_pack.restype = ctypes.c_int
     lib.vq_dequant.argtypes = [dp, vp, vp, vp, vp, vp, ctypes.c_int, vp]
     lib.vq_dequant.restype = ctypes.c_int
@@ -263,10 +265,18 @@ def svq_desc(out_features, in_features) -> Desc:
     return make_desc(out_features, in_features, 4, 8, 0)
 
 
-def svq_fields(q):
-    """Integer grid coordinates q [..., 4] (values 0..3) -> the 8-bit fields vq_pack takes."""
-    q = np.asarray(q, dtype=np.uint32)
-    return q[..., 0] | (q[..., 1] << 2) | (q[..., 2] << 4) | (q[..., 3] << 6)
+def svq_pack(desc: Desc, q) -> np.ndarray:
+    """Integer grid coordinates q [N, nv, 4] (values 0..3) of an affine-lattice layer -> its
+    packed row stream (host bytes), through vq_svq_pack."""
+    qa = np.ascontiguousarray(q, dtype=np.uint8)
+    nv = (desc.in_features + 3) // 4
+    if qa.shape != (desc.out_features, nv, 4):
+        raise ValueError("q must be [%d, %d, 4], got %s" % (desc.out_features, nv, qa.shape))
+    out = np.zeros(max(packed_bytes(desc), 1), dtype=np.uint8)
+    st = lib().vq_svq_pack(ctypes.byref(desc), qa.ctypes.data_as(ctypes.c_void_p), out.ctypes.data_as(ctypes.c_void_p),
+                           out.size)
+    _check(st, "vq_svq_pack")
+    return out[:packed_bytes(desc)]
 
 
 def svq_dequant(desc: Desc, packed, a, b, scale, w_dtype=None, out=None):

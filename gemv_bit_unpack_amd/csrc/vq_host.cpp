@@ -201,6 +201,31 @@ vq_status vq_pack(const vq_desc* desc, const uint32_t* idx1, const uint32_t* idx
   return VQ_OK;
 }
 
+vq_status vq_svq_pack(const vq_desc* desc, const uint8_t* q, void* packed, size_t nbytes) {
+  vq_status st = check_desc(desc);
+  if (st != VQ_OK) return st;
+  const vq_desc& d = *desc;
+  if (d.v != 4 || d.bits1 != 8 || d.bits2 != 0) return VQ_ERR_UNSUPPORTED;
+  const size_t need = packed_size(d);
+  const int64_t nv = num_vectors(d.in_features, 4);
+  const size_t count = (size_t)d.out_features * (size_t)nv * 4;
+  if ((need > 0 || count > 0) && (!packed || !q)) return VQ_ERR_NULL;
+  if (nbytes < need) return VQ_ERR_BUFFER_SIZE;
+  for (size_t i = 0; i < count; ++i)
+    if (q[i] > 3) return VQ_ERR_INDEX_RANGE;
+  if (need == 0) return VQ_OK;
+  uint8_t* out = (uint8_t*)packed;
+  std::memset(out, 0, need);
+  const int64_t stride = row_stride(d.in_features, 4, 8);  // one byte per vector
+  for (int64_t o = 0; o < d.out_features; ++o) {
+    for (int64_t j = 0; j < nv; ++j) {
+      const uint8_t* c = q + ((size_t)o * (size_t)nv + (size_t)j) * 4;
+      out[(size_t)o * (size_t)stride + (size_t)j] = (uint8_t)(c[0] | (c[1] << 2) | (c[2] << 4) | (c[3] << 6));
+    }
+  }
+  return VQ_OK;
+}
+
 vq_status vq_dequant(const vq_desc* desc, const void* packed, const void* cb1, const void* cb2, const void* scale,
                      void* w, vq_dtype w_dtype, void* stream) {
   vq_status st = check_desc(desc);

@@ -8,7 +8,8 @@
 //     constant offsets), for four address patterns of a 64-lane 16-byte read: random,
 //     7 of 8 lanes on one address, 1 of 8 lanes active, and conflict-free;
 //   - the issue rate of the matrix instructions the products use (16x16x32, 32x32x16,
-//     4x4x4 with 16 blocks, fp16) and of the packed fp16 dot (v_dot2_f32_f16);
+//     4x4x4 with 16 blocks, fp16) and of the packed fp16 dot (v_dot2_f32_f16), and whether
+//     VALU and matrix instructions overlap on one SIMD;
 //   - the rate at which 8 workgroups on one XCD can all read the same stream (each
 //     byte fetched once from HBM, then served 7 more times by the XCD's L2), against
 //     each workgroup reading its own stream.
@@ -183,6 +184,40 @@ __global__ __launch_bounds__(256) void dot2_rate(int iters, float* out) {
   if (sum == 1234.5f) out[0] = sum;
 }
 
+// Whether VALU and matrix instructions overlap on one SIMD: per iteration a wavefront
+// issues 4 independent v_mfma_f32_16x16x32_f16 (MODE 0), 16 independent v_dot2_f32_f16
+// (MODE 1), or both (MODE 2); 4 wavefronts per SIMD.  With full overlap MODE 2 would take
+// the longer of MODE 0 and MODE 1, without any the sum.
+template <int MODE>
+__global__ __launch_bounds__(256) void issue_overlap(int iters, float* out) {
+  const float s = (float)(threadIdx.x & 7) * 0.001f;
+  const mr_half8 a = {(_Float16)s, 1, 2, 3, 4, 5, 6, 7}, b = {1, 1, 1, 1, 1, 1, 1, (_Float16)s};
+  const mr_half2 p = {(_Float16)s, (_Float16)1}, q = {(_Float16)1, (_Float16)0.5f};
+  mr_float4 c0 = {0, 0, 0, 0}, c1 = c0, c2 = c0, c3 = c0;
+  float d[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) d[j] = (float)j;
+  for (int it = 0; it < iters; ++it) {
+    if constexpr (MODE != 1) {
+      c0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c3, 0, 0, 0);
+    }
+    if constexpr (MODE != 0) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) d[j] = __builtin_amdgcn_fdot2(p, q, d[j], false);
+      }
+    }
+  }
+  float sum = c0[0] + c1[1] + c2[2] + c3[3];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) sum += d[j];
+  if (sum == 1234.5f) out[0] = sum;
+}
+
 // Shared-stream read: 256 workgroups of 512 threads as 32 groups of 8 (the 8 workgroups of
 // a group have consecutive ids above the XCD bits, so they land on one XCD).  SHARED: the 8
 // read the same `per` bytes of their group's region; otherwise each reads its own.
@@ -316,6 +351,24 @@ int main(int argc, char** argv) {
     const double t = timed([&] { hipLaunchKernelGGL(dot2_rate, dim3(grid), dim3(256), 0, 0, iters, fout); }, 3);
     const double instr = (double)grid * 4 * iters * 8;
     printf(", \"v_dot2_f32_f16\": {\"clk_per_instr_per_simd\": %.2f}", t * clk * ncu * 4 / instr);
+  }
+  printf("}");
+
+  // VALU / matrix-core overlap on one SIMD.
+  printf(", \"valu_mfma_overlap\": {");
+  {
+    const char* onames[3] = {"mfma_only", "dot2_only", "both_in_one_wave"};
+    for (int mode = 0; mode < 3; ++mode) {
+      const int grid = ncu * 4, iters = 2048;
+      auto launch = [&] {
+        if (mode == 0) hipLaunchKernelGGL(issue_overlap<0>, dim3(grid), dim3(256), 0, 0, iters, fout);
+        else if (mode == 1) hipLaunchKernelGGL(issue_overlap<1>, dim3(grid), dim3(256), 0, 0, iters, fout);
+        else hipLaunchKernelGGL(issue_overlap<2>, dim3(grid), dim3(256), 0, 0, iters, fout);
+      };
+      const double t = timed(launch, 3);
+      printf("%s\"%s\": {\"simd_clk_per_iteration_4_waves\": %.1f}", mode ? ", " : "", onames[mode],
+             t * clk / iters);
+    }
   }
   printf("}");
 

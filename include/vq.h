@@ -35,8 +35,9 @@
  * (NULL = the default stream).  These three calls validate on the host, enqueue kernels
  * on `stream` and return without synchronising: inputs must stay unchanged until the
  * stream has run them, and y / w must not alias any input.  The library allocates no
- * memory (vq_gemv_ws takes its scratch space from the caller), keeps no pointer after
- * returning and is safe to call from several threads.
+ * memory (vq_gemv_ws and vq_assign take their scratch space from the caller;
+ * vq_gemv_noalloc uses a fixed array in device memory that the library holds), keeps no
+ * pointer after returning and is safe to call from several threads.
  * vq_packed_bytes and vq_pack work on HOST memory and are synchronous.
  *
  * Errors.  Every argument is checked before anything is enqueued; on error nothing is
@@ -94,18 +95,26 @@ vq_status vq_packed_bytes(const vq_desc* desc, size_t* nbytes);
 /* Pack idx1 [N][nv] (and idx2 [N][nv] when bits2 > 0; must be NULL-free then, ignored
  * otherwise) into `packed` (HOST memory, nbytes >= vq_packed_bytes).  Writes every byte
  * of the packed size, pad bits zero.  VQ_ERR_INDEX_RANGE if any index >= 2^bits, with
- * `packed` untouched. */
+ * `packed` untouched.  The pages fix no storage layout (the VPTQ guide's "Step 3" layer
+ * keeps whole uint8 / int16 index tensors); this one stores exactly the log2(K) bits per
+ * index per book that the guide's "3. Effective Bit-Width Calculation" counts, main and
+ * residual indices in separate streams as its residual pipeline keeps them ("2.
+ * Multi-Stage Residual Vector Quantization (RVQ)"). */
 vq_status vq_pack(const vq_desc* desc, const uint32_t* idx1, const uint32_t* idx2, void* packed, size_t nbytes);
 
 /* Rebuild W^ [N][IN] into `w` (device, row-major, w_dtype; fp16 / bf16 outputs are the
- * nearest-even rounding of the exact fp32 value).  packed: device, 4-byte aligned;
+ * nearest-even rounding of the exact fp32 value): the VPTQ guide's "Step 2" dequantize
+ * (gather both books, add, view as [out, in]) with the per-channel scale.  packed: device, 4-byte aligned;
  * cb1: fp16 [2^bits1][v]; cb2: fp16 [2^bits2][v] (NULL iff bits2 == 0);
  * scale: fp16 [N] or NULL (scale 1).  Codebook and scale pointers must be 2-byte
  * aligned, w aligned to its element size. */
 vq_status vq_dequant(const vq_desc* desc, const void* packed, const void* cb1, const void* cb2, const void* scale,
                      void* w, vq_dtype w_dtype, void* stream);
 
-/* Decode-batch product y [M][N] = x [M][IN] * W^T (+ bias), 1 <= M <= 16 (M = 0: no-op).
+/* Decode-batch product y [M][N] = x [M][IN] * W^T (+ bias), 1 <= M <= 16 (M = 0: no-op):
+ * the forward of the VPTQ guide's "Step 3: Fused Low-Bit VPTQ Linear Layer", fused so that
+ * W^ is never written, for the memory-bound decode regime of the production-VQ post's
+ * "1. Prefill vs. Decode Bottlenecks".
  * The VALU path: each wavefront reduces whole rows; accumulation in fp32.
  * x: device, x_dtype VQ_F16 or VQ_BF16, row-major [M][IN]; bias: fp16 [N] or NULL;
  * y: device, y_dtype VQ_F16, VQ_BF16 or VQ_F32, row-major [M][N].  Other pointers as
@@ -128,9 +137,9 @@ vq_status vq_gemv_workspace_bytes(const vq_desc* desc, int32_t M, vq_dtype x_dty
  * that serve it; the matrix cores form the dot products; per-slice fp32 partial sums
  * go to the workspace and a second kernel adds them in a fixed order, so results are
  * deterministic.  bf16 activations are rewritten as fp16 times a power of two per
- * batch row, which is exact for every value whose magnitude lies within
- * 2^-16 .. 65504 times that power; smaller values round with an absolute error below
- * 2^-25 times it.
+ * batch row, chosen so that the row's largest magnitude lands in [2^14, 2^15); every
+ * value down to 2^-31 of that magnitude converts exactly, smaller ones round with an
+ * absolute error below 2^-39 of it.
  * Same arguments, results (to the vq_gemv tolerance) and errors as vq_gemv, plus:
  *   workspace: NULL (then this is vq_gemv), or device memory, 256-byte aligned, of at
  *     least vq_gemv_workspace_bytes(desc, M, x_dtype) bytes (VQ_ERR_BUFFER_SIZE /
@@ -159,7 +168,9 @@ vq_status vq_gemv_noalloc(const vq_desc* desc, const void* packed, const void* c
 
 /* Same operation and arguments as vq_gemv for any M >= 1 (M = 0: no-op), on the matrix
  * cores: rebuilt weight tiles are staged in LDS in the activation's 16-bit type and
- * multiplied with MFMA, fp32 accumulation.  Meant for prefill batches (M >= 32). */
+ * multiplied with MFMA, fp32 accumulation.  Meant for prefill batches (M >= 32), where the
+ * production-VQ post ("1. Prefill vs. Decode Bottlenecks", "Throughput and Concurrency
+ * Trade-Offs") places the compute-bound regime and matrix-engine formats. */
 vq_status vq_gemm(const vq_desc* desc, const void* packed, const void* cb1, const void* cb2, const void* scale,
                   const void* bias, const void* x, vq_dtype x_dtype, int32_t M, void* y, vq_dtype y_dtype,
                   void* stream);
@@ -178,9 +189,21 @@ vq_status vq_gemm(const vq_desc* desc, const void* packed, const void* cb1, cons
  * as the row stream of a descriptor with v = 4, bits1 = 8, bits2 = 0: vector j's 8-bit
  * field holds code u in bits [2u, 2u + 2), so vq_pack packs them from idx1[o][j] =
  * q_0 | q_1 << 2 | q_2 << 4 | q_3 << 6, and a row takes 16 * ceil(nv / 16) bytes
- * (2 bits per weight).  Any other descriptor gives VQ_ERR_UNSUPPORTED.  As for the
- * codebook calls, lanes of the last vector past IN are dropped.
+ * (2 bits per weight); vq_svq_pack packs them from the coordinates directly.  Any other
+ * descriptor gives VQ_ERR_UNSUPPORTED.  As for the codebook calls, lanes of the last
+ * vector past IN are dropped.
  */
+
+/* Pack the integer grid coordinates q [N][nv][4] (uint8, each 0..3; nv = ceil(IN / 4),
+ * the last vector's lanes past IN included and ignored by the products) of an
+ * affine-lattice layer into its row stream (HOST memory, synchronous, nbytes >=
+ * vq_packed_bytes(desc)): vector j's byte in row o is q_0 | q_1 << 2 | q_2 << 4 | q_3 << 6,
+ * rows padded to 16 bytes with zeros.  desc must be the lattice descriptor (v = 4,
+ * bits1 = 8, bits2 = 0; else VQ_ERR_UNSUPPORTED); a coordinate above 3 gives
+ * VQ_ERR_INDEX_RANGE with `packed` untouched; other errors as for vq_pack.  The UniSVQ
+ * summary gives the grid (w̄ in Z^4, "Mathematical Formulation") and 2 bits per weight
+ * ("Efficiency") but no storage; this is the plainest packing of those 2-bit codes. */
+vq_status vq_svq_pack(const vq_desc* desc, const uint8_t* q, void* packed, size_t nbytes);
 
 /* Write W^ [N][IN] of an affine-lattice layer into `w` (device, w_dtype; fp16 / bf16 are
  * the nearest-even rounding of the exact fp32 value, which this call reproduces bit for

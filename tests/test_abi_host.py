@@ -302,14 +302,34 @@ def test_svq_dequant_validation_paths(vq):
     assert f(ctypes.byref(vq.svq_desc(64, 0)), None, None, None, None, None, 2, None) == vq.VQ_OK
 
 
-def test_svq_pack_fields_match_oracle(vq):
-    """The binding's svq_fields + vq_pack give the oracle's lattice stream."""
-    lay = synth.make_svq_layer(5, 37)
-    q = np.stack([(lay["codes"] >> (2 * u)) & 3 for u in range(4)], axis=-1)
-    fields = vq.svq_fields(q)
-    assert np.array_equal(fields, lay["codes"])
-    ours = vq.pack(vq.svq_desc(5, 37), fields)
-    assert np.array_equal(ours, oracle.pack(5, 37, 4, 8, 0, lay["codes"]))
+def test_svq_pack_through_the_abi(vq):
+    """vq_svq_pack on integer grid coordinates: the oracle's lattice decode with the identity
+    grid (A = I, B = 0) returns every coordinate, and the bytes equal the oracle's own packing
+    of the same layer; coordinates above 3, a codebook descriptor and a short buffer are
+    refused."""
+    g = np.random.default_rng(5)
+    n, i = 5, 37  # nv = 10, the last vector has one live lane
+    nv = (i + 3) // 4
+    q = g.integers(0, 4, size=(n, nv, 4), dtype=np.uint8)
+    d = vq.svq_desc(n, i)
+    packed = vq.svq_pack(d, q)
+    eye = np.eye(4, dtype=np.float16).view(np.uint16)
+    w = oracle.svq_dequant(n, i, packed, eye, np.zeros(4, np.uint16))
+    assert np.array_equal(w, q.reshape(n, nv * 4)[:, :i].astype(np.float32))
+    lay = synth.make_svq_layer(n, i)
+    q2 = np.stack([(lay["codes"] >> (2 * u)) & 3 for u in range(4)], axis=-1).astype(np.uint8)
+    assert np.array_equal(vq.svq_pack(d, q2), oracle.pack(n, i, 4, 8, 0, lay["codes"]))
+    f = vq.lib().vq_svq_pack
+    buf = np.zeros(vq.packed_bytes(d), dtype=np.uint8)
+    bad = q.copy()
+    bad[3, 4, 2] = 4
+    bp = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    assert f(ctypes.byref(d), bp(bad), bp(buf), buf.size) == vq.VQ_ERR_INDEX_RANGE
+    assert not buf.any()
+    assert f(ctypes.byref(vq.make_desc(n, i, 4, 8, 2)), bp(q), bp(buf), buf.size) == vq.VQ_ERR_UNSUPPORTED
+    assert f(ctypes.byref(d), bp(q), bp(buf), buf.size - 1) == vq.VQ_ERR_BUFFER_SIZE
+    assert f(ctypes.byref(d), None, bp(buf), buf.size) == vq.VQ_ERR_NULL
+    assert f(ctypes.byref(vq.svq_desc(0, 16)), None, None, 0) == vq.VQ_OK
 
 
 def test_rht_block_and_validation(vq):

@@ -14,9 +14,9 @@ minimum beside it).
 
 Printed: ONE JSON line with the throughput on algorithmic bytes (packed indices + each
 codebook once + scales + x + y), the roofline of the call, the cold single-call latency,
-the GEMV / GEMM crossover on the same layers, the prefill GEMM (vq_gemm at M = 128), the
-GEMV at M = 1 on every workload, the other legs, and the CPU oracle timed on the host's
-cores on every workload.
+the GEMV / GEMM crossover on the same layers, the prefill GEMM at M = 128 (vq_gemm_ws,
+with vq_gemm beside it), the GEMV at M = 1 on every workload, the other legs, and the CPU
+oracle timed on the host's cores on every workload.
 
 Inputs are synthetic: uniform indices (a packed stream of uniform random bits),
 centroids 0.02*N(0,1) main and 0.005*N(0,1) residual in fp16, scales U(0.5, 1.5),
@@ -131,10 +131,14 @@ class Ring:
         lib = vq.lib()
         self.fn = getattr(lib, fn)
         # one workspace for the whole ring: its calls run in order on one stream
-        self.ws = vq.workspace(self.desc, m, xdt, dev) if fn == "vq_gemv_ws" else None
-        self.sliced = self.ws is not None
-        extra = ()
+        self.ws = None
         if fn == "vq_gemv_ws":
+            self.ws = vq.workspace(self.desc, m, xdt, dev)
+        elif fn == "vq_gemm_ws":
+            self.ws = vq.gemm_workspace(self.desc, m, xdt, dev)
+        self.sliced = fn == "vq_gemv_ws" and self.ws is not None
+        extra = ()
+        if fn in ("vq_gemv_ws", "vq_gemm_ws"):
             extra = (None, 0) if self.ws is None else (ctypes.c_void_p(self.ws.data_ptr()), self.ws.numel())
         code = {torch.float16: vq.VQ_F16, torch.bfloat16: vq.VQ_BF16, torch.float32: vq.VQ_F32}
         self.tensors = []
@@ -563,12 +567,17 @@ def main():
         return
 
     if args.only_gemm:
-        up = Ring(vq, torch, "l70b", 0, 128, copies=6, fn="vq_gemm")
-        down = Ring(vq, torch, "l70b", 1, 128, copies=6, fn="vq_gemm")
-        gsec, gcalls, _, glaunch = time_ring(torch, [up, down], args.steps, args.warmup, use_graph)
-        flops = (up.flops_per_call + down.flops_per_call) / 2
-        print(json.dumps({"gemm_tflops": round(flops / gsec / 1e12, 2), "ms_per_call": round(gsec * 1e3, 4),
-                          "calls": gcalls, "launch": glaunch}))
+        res = {}
+        for fn in ("vq_gemm_ws", "vq_gemm"):
+            up = Ring(vq, torch, "l70b", 0, 128, copies=6, fn=fn)
+            down = Ring(vq, torch, "l70b", 1, 128, copies=6, fn=fn)
+            gsec, gcalls, _, glaunch = time_ring(torch, [up, down], args.steps, args.warmup, use_graph)
+            flops = (up.flops_per_call + down.flops_per_call) / 2
+            res[fn] = {"gemm_tflops": round(flops / gsec / 1e12, 2), "ms_per_call": round(gsec * 1e3, 4),
+                       "calls": gcalls, "launch": glaunch}
+            del up, down
+            torch.cuda.empty_cache()
+        print(json.dumps(res))
         return
     if args.only_rht:
         print(json.dumps({"rht": rht_leg(vq, torch, use_graph)}))
@@ -653,24 +662,32 @@ def main():
     if args.shared_book:
         out["config"]["diagnostic"] = "shared codebook across the ring (not the headline protocol)"
     if not args.only_headline and not args.shared_book:
-        # Prefill GEMM at M = 128 on the 70B-class pair.
-        up = Ring(vq, torch, HEADLINE_KEY, 0, 128, copies=4, fn="vq_gemm")
-        down = Ring(vq, torch, HEADLINE_KEY, 1, 128, copies=4, fn="vq_gemm")
-        gt = time_steps(torch, [up, down], 8, 2)
-        gsec = sorted(gt)[len(gt) // 2] / 2  # per layer call
-        flops = (up.flops_per_call + down.flops_per_call) / 2
-        tflops = flops / gsec / 1e12
-        out["gemm"] = {"workload": "prefill GEMM, " + DESCRIBE[HEADLINE_KEY] + ", M=128, bf16 x and y",
-                       "tflops": round(tflops, 2), "frac_mfma_peak": round(tflops / MFMA_PEAK_TFLOPS, 4),
-                       "ms_per_call": round(gsec * 1e3, 4), "trials_ms_per_call": [round(t * 500, 4) for t in gt],
-                       "launch": "hipgraph, 8 steps (up + down) per trial"}
-        del up, down
-        torch.cuda.empty_cache()
-        # GEMV / GEMM crossover on the same pair: vq_gemv_ws (M <= 16) against vq_gemm.
+        # Prefill GEMM at M = 128 on the 70B-class pair: vq_gemm_ws (the gather-fed matrix-core
+        # product) and, for comparison, vq_gemm (LDS weight tiles, no workspace).
+        gemm = {"workload": "prefill GEMM, " + DESCRIBE[HEADLINE_KEY] + ", M=128, bf16 x and y",
+                "launch": "hipgraph, 8 steps (up + down) per trial"}
+        for fn in ("vq_gemm_ws", "vq_gemm"):
+            up = Ring(vq, torch, HEADLINE_KEY, 0, 128, copies=4, fn=fn)
+            down = Ring(vq, torch, HEADLINE_KEY, 1, 128, copies=4, fn=fn)
+            gt = time_steps(torch, [up, down], 8, 2)
+            gsec = sorted(gt)[len(gt) // 2] / 2  # per layer call
+            flops = (up.flops_per_call + down.flops_per_call) / 2
+            tflops = flops / gsec / 1e12
+            entry = {"tflops": round(tflops, 2), "frac_mfma_peak": round(tflops / MFMA_PEAK_TFLOPS, 4),
+                     "ms_per_call": round(gsec * 1e3, 4), "trials_ms_per_call": [round(t * 500, 4) for t in gt]}
+            if fn == "vq_gemm_ws":
+                gemm.update(entry)
+                gemm["call"] = fn
+            else:
+                gemm["vq_gemm"] = entry
+            del up, down
+            torch.cuda.empty_cache()
+        out["gemm"] = gemm
+        # GEMV / GEMM crossover on the same pair: vq_gemv_ws (M <= 16) against vq_gemm_ws.
         cross = {}
         for m in (1, 8, 16, 32):
             entry = {}
-            for fn in ("vq_gemv_ws", "vq_gemm"):
+            for fn in ("vq_gemv_ws", "vq_gemm_ws"):
                 if fn == "vq_gemv_ws" and m > 16:
                     entry[fn + "_us_per_call"] = None  # the GEMV takes M <= 16
                     continue
@@ -679,8 +696,8 @@ def main():
                 entry[fn + "_us_per_call"] = round(sorted(tt)[len(tt) // 2] / 2 * 1e6, 3)
                 del rr
                 torch.cuda.empty_cache()
-            g_us, m_us = entry.get("vq_gemv_ws_us_per_call"), entry["vq_gemm_us_per_call"]
-            entry["faster"] = "vq_gemm" if g_us is None or m_us < g_us else "vq_gemv_ws"
+            g_us, m_us = entry.get("vq_gemv_ws_us_per_call"), entry["vq_gemm_ws_us_per_call"]
+            entry["faster"] = "vq_gemm_ws" if g_us is None or m_us < g_us else "vq_gemv_ws"
             cross["m%d" % m] = entry
         out["gemv_gemm_crossover_l70b"] = cross
         per = {}

@@ -13,9 +13,12 @@ Calls (same names as the C ABI):
     gemv_workspace_bytes(desc, m, x_dtype) -> int
     gemv_ws(desc, packed, cb1, cb2, scale, bias, x, workspace, y_dtype=None, out=None)
     gemm(desc, packed, cb1, cb2, scale, bias, x, y_dtype=None, out=None)  # any M, MFMA
-plus ``workspace(desc, m, x_dtype, device)``, a zero-filled device buffer for gemv_ws,
-and ``VQLinear``, a layer object holding the packed weights that picks gemv(_ws) or
-gemm by batch size, the analogue of the VPTQ guide's ``VPTQLinear`` module.
+    gemm_workspace_bytes(desc, m, x_dtype) -> int
+    gemm_ws(desc, packed, cb1, cb2, scale, bias, x, workspace, y_dtype=None, out=None)
+plus ``workspace(desc, m, x_dtype, device)`` and ``gemm_workspace(...)``, zero-filled
+device buffers for gemv_ws / gemm_ws, and ``VQLinear``, a layer object holding the packed
+weights that picks gemv_ws or gemm_ws by batch size, the analogue of the VPTQ guide's
+``VPTQLinear`` module.
 """
 from __future__ import annotations
 
@@ -42,7 +45,8 @@ LAYOUT_ROWSTREAM = 1
 
 EXPORTED = ("vq_abi_version", "vq_status_string", "vq_packed_bytes", "vq_pack", "vq_dequant", "vq_gemv",
             "vq_gemv_workspace_bytes", "vq_gemv_ws", "vq_gemm", "vq_svq_dequant", "vq_svq_gemv", "vq_rht", "vq_rht_block",
-            "vq_assign_workspace_bytes", "vq_assign", "vq_svq_gemm", "vq_gemv_noalloc", "vq_svq_pack")
+            "vq_assign_workspace_bytes", "vq_assign", "vq_svq_gemm", "vq_gemv_noalloc", "vq_svq_pack",
+            "vq_gemm_workspace_bytes", "vq_gemm_ws")
 
 
 class Desc(ctypes.Structure):
@@ -90,6 +94,10 @@ def _load():
     lib.vq_gemv_workspace_bytes.restype = ctypes.c_int
     lib.vq_gemv_ws.argtypes = [dp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i32, vp, ctypes.c_int, vp, sz, vp]
     lib.vq_gemv_ws.restype = ctypes.c_int
+    lib.vq_gemm_workspace_bytes.argtypes = [dp, i32, ctypes.c_int, ctypes.POINTER(sz)]
+    lib.vq_gemm_workspace_bytes.restype = ctypes.c_int
+    lib.vq_gemm_ws.argtypes = [dp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i32, vp, ctypes.c_int, vp, sz, vp]
+    lib.vq_gemm_ws.restype = ctypes.c_int
     lib.vq_gemv_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i32, vp, ctypes.c_int, vp]
     lib.vq_gemv_noalloc.restype = ctypes.c_int
     lib.vq_svq_dequant.argtypes = [dp, vp, vp, vp, vp, vp, ctypes.c_int, vp]
@@ -260,6 +268,30 @@ def gemm(desc, packed, cb1, cb2, scale, bias, x, y_dtype=None, out=None):
     return _product(lib().vq_gemm, "vq_gemm", desc, packed, cb1, cb2, scale, bias, x, y_dtype, out)
 
 
+def gemm_workspace_bytes(desc: Desc, m: int, x_dtype) -> int:
+    """Workspace bytes for gemm_ws at batch m with activations of torch dtype x_dtype (0: none used)."""
+    n = ctypes.c_size_t(0)
+    _check(lib().vq_gemm_workspace_bytes(ctypes.byref(desc), int(m), _dtype_code(x_dtype), ctypes.byref(n)),
+           "vq_gemm_workspace_bytes")
+    return int(n.value)
+
+
+def gemm_workspace(desc: Desc, m: int, x_dtype, device="cuda"):
+    """A zero-filled device workspace for gemm_ws (None when the shape needs none)."""
+    nbytes = gemm_workspace_bytes(desc, m, x_dtype)
+    if nbytes == 0:
+        return None
+    return _torch().zeros(nbytes, dtype=_torch().uint8, device=device)
+
+
+def gemm_ws(desc, packed, cb1, cb2, scale, bias, x, ws, y_dtype=None, out=None):
+    """gemm with a caller-owned workspace (from ``gemm_workspace``; None where none is needed).
+
+    Calls that share a workspace must be ordered (one stream)."""
+    extra = (None, 0) if ws is None else (_dev_ptr(ws, "workspace"), ws.numel() * ws.element_size())
+    return _product(lib().vq_gemm_ws, "vq_gemm_ws", desc, packed, cb1, cb2, scale, bias, x, y_dtype, out, extra)
+
+
 def svq_desc(out_features, in_features) -> Desc:
     """Descriptor of an affine-lattice layer: one 8-bit field of four 2-bit codes per 4-vector."""
     return make_desc(out_features, in_features, 4, 8, 0)
@@ -379,11 +411,12 @@ def assign(desc: Desc, w, cb1, cb2=None, ws=None, out1=None, out2=None):
 _stream_ws = {}
 
 
-def stream_workspace(desc: Desc, m: int, x_dtype, device):
+def stream_workspace(desc: Desc, m: int, x_dtype, device, gemm_path: bool = False):
     """A workspace kept per (device, current stream), grown on demand, for layers that run
-    their calls in stream order.  None when the shape needs none."""
+    their calls in stream order (gemv_ws, or gemm_ws with ``gemm_path``).  None when the
+    shape needs none."""
     torch = _torch()
-    nbytes = gemv_workspace_bytes(desc, m, x_dtype)
+    nbytes = (gemm_workspace_bytes if gemm_path else gemv_workspace_bytes)(desc, m, x_dtype)
     if nbytes == 0:
         return None
     dev = torch.device(device)
@@ -401,7 +434,8 @@ class VQLinear:
 
     ``forward(x)`` computes x W^T (+ bias) for x of shape [..., in_features]; batches of
     up to ``gemv_max_m`` rows take gemv_ws (the codebook-sliced kernel where the shape has
-    it, with a workspace kept per device and stream), larger ones the MFMA GEMM.
+    it), larger ones gemm_ws (the matrix-core product fed by the gathering lanes where the
+    shape has it); both with a workspace kept per device and stream.
     """
 
     def __init__(self, desc: Desc, packed, cb1, cb2=None, scale=None, bias=None, gemv_max_m: int = 16):
@@ -423,7 +457,8 @@ class VQLinear:
             ws = stream_workspace(self.desc, x2.shape[0], x2.dtype, x2.device)
             y = gemv_ws(*args, ws, y_dtype)
         else:
-            y = gemm(*args, y_dtype)
+            ws = stream_workspace(self.desc, x2.shape[0], x2.dtype, x2.device, gemm_path=True)
+            y = gemm_ws(*args, ws, y_dtype)
         return y.reshape(*lead, self.desc.out_features)
 
     __call__ = forward

@@ -673,6 +673,19 @@ vq_status static_scratch(void** ptr) {
   return VQ_OK;
 }
 
+vq_status launch_x_to_f16(const ProductArgs& a, uint16_t* x16, int32_t* xexp, void* stream) {
+  hipLaunchKernelGGL(xprep_kernel, dim3(a.m), dim3(1024), 0, (hipStream_t)stream, a.x, a.in_features, x16, xexp);
+  return hipGetLastError() == hipSuccess ? VQ_OK : VQ_ERR_HIP;
+}
+
+vq_status launch_partials_finalize(const ProductArgs& a, const float* part, const int32_t* xexp, int nparts,
+                                   void* stream) {
+  const int total = a.n * a.m;
+  hipLaunchKernelGGL(gemv_sliced_finalize, dim3((total + 255) / 256), dim3(256), 0, (hipStream_t)stream, a, part, xexp,
+                     nparts);
+  return hipGetLastError() == hipSuccess ? VQ_OK : VQ_ERR_HIP;
+}
+
 bool sliced_gemv_shape_ok(const vq_desc& d, int32_t m, vq_dtype x_dtype) {
   if (d.v != 8 || d.bits1 != 16 || !(d.bits2 == 0 || d.bits2 == 8)) return false;
   if (m < 1 || m > 16 || !(x_dtype == VQ_F16 || x_dtype == VQ_BF16)) return false;

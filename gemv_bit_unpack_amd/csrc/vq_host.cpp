@@ -373,4 +373,33 @@ vq_status vq_gemm(const vq_desc* desc, const void* packed, const void* cb1, cons
   return launch_gemm(a, stream);
 }
 
+vq_status vq_gemm_workspace_bytes(const vq_desc* desc, int32_t M, vq_dtype x_dtype, size_t* nbytes) {
+  if (!nbytes) return VQ_ERR_NULL;
+  vq_status st = check_desc(desc);
+  if (st != VQ_OK) return st;
+  if (M < 0) return VQ_ERR_SHAPE;
+  if (x_dtype != VQ_F16 && x_dtype != VQ_BF16) return VQ_ERR_UNSUPPORTED;
+  *nbytes = M == 0 ? 0 : gather_gemm_workspace(*desc, M, x_dtype);
+  return VQ_OK;
+}
+
+vq_status vq_gemm_ws(const vq_desc* desc, const void* packed, const void* cb1, const void* cb2, const void* scale,
+                     const void* bias, const void* x, vq_dtype x_dtype, int32_t M, void* y, vq_dtype y_dtype,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  ProductArgs a;
+  vq_status st = prepare_product(desc, packed, cb1, cb2, scale, bias, x, x_dtype, M, y, y_dtype, 0, &a);
+  if (st != VQ_OK) return st;
+  if (a.n == 0 || a.m == 0) return VQ_OK;
+  if (gather_gemm_shape_ok(*desc, a.m, a.x_dtype) && gather_gemm_pointers_ok(a)) {
+    const size_t need = gather_gemm_workspace(*desc, a.m, a.x_dtype);
+    if (need == 0) return launch_gemm_gather(a, nullptr, stream);
+    if (workspace) {
+      if (workspace_bytes < need) return VQ_ERR_BUFFER_SIZE;
+      if (!aligned(workspace, 256)) return VQ_ERR_ALIGN;
+      return launch_gemm_gather(a, workspace, stream);
+    }
+  }
+  return launch_gemm(a, stream);
+}
+
 }  // extern "C"

@@ -68,6 +68,18 @@ vq_status launch_gemv_sliced(const ProductArgs& a, void* workspace, void* stream
 size_t static_scratch_bytes();
 vq_status static_scratch(void** ptr);
 vq_status launch_gemm(const ProductArgs& a, void* stream);
+// The prefill product for the same 65536-entry book (vq_gemm_ws): shape test, workspace
+// bytes (0: none needed), pointer test and launch.
+bool gather_gemm_shape_ok(const vq_desc& d, int32_t m, vq_dtype x_dtype);
+size_t gather_gemm_workspace(const vq_desc& d, int32_t m, vq_dtype x_dtype);
+bool gather_gemm_pointers_ok(const ProductArgs& a);
+vq_status launch_gemm_gather(const ProductArgs& a, void* workspace, void* stream);
+// Passes shared by the workspace products: bf16 activations rewritten as fp16 times a
+// power of two per batch row (x16 [M][IN], xexp [M]); and y = 2^e * scale * (sum of
+// `nparts` fp32 partial sums [nparts][M][N], in order) + bias.
+vq_status launch_x_to_f16(const ProductArgs& a, uint16_t* x16, int32_t* xexp, void* stream);
+vq_status launch_partials_finalize(const ProductArgs& a, const float* part, const int32_t* xexp, int nparts,
+                                   void* stream);
 
 // Affine-lattice layers (v = 4, one 8-bit field of four 2-bit codes per vector), after
 // validation.

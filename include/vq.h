@@ -175,6 +175,34 @@ vq_status vq_gemm(const vq_desc* desc, const void* packed, const void* cb1, cons
                   const void* bias, const void* x, vq_dtype x_dtype, int32_t M, void* y, vq_dtype y_dtype,
                   void* stream);
 
+/* Bytes of device workspace with which vq_gemm_ws runs `desc` at batch M with activations
+ * of x_dtype on its gather path: the fp16 copy of bf16 activations with one power of two
+ * per batch row, and fp32 partial sums when the K range is split across workgroups.  0
+ * when the shape does not take that path or needs no workspace (fp16 activations, no
+ * split).  The path needs v = 8, bits1 = 16, bits2 = 0 or 8 and IN a multiple of 8
+ * (IN >= 8).  M = 0 gives 0. */
+vq_status vq_gemm_workspace_bytes(const vq_desc* desc, int32_t M, vq_dtype x_dtype, size_t* nbytes);
+
+/* vq_gemm with a caller-owned device workspace, for the 65536-entry main book (VPTQ
+ * guide, "Step 3: Fused Low-Bit VPTQ Linear Layer"; the production-VQ post, "1. Prefill
+ * vs. Decode Bottlenecks" and "Lookup Table (LUT) Overhead vs. Bit-Shifting").  Each
+ * lane gathers one weight vector's main centroid from L2, adds its residual centroid in
+ * fp16 (the exact sum rounded once to nearest even) and hands the vector to the matrix
+ * cores as one column of an fp16 operand; activations stay in LDS.  bf16 activations are
+ * first rewritten as fp16 times a power of two per batch row (as in vq_gemv_ws), so the
+ * product uses fp16 weights and activations with fp32 accumulation; partial sums of a
+ * split K range are added in a fixed order, so results are deterministic.
+ * Same arguments, results (to the vq_gemm tolerance) and errors as vq_gemm, plus:
+ *   workspace: device memory, 256-byte aligned, of at least
+ *     vq_gemm_workspace_bytes(desc, M, x_dtype) bytes (VQ_ERR_BUFFER_SIZE / VQ_ERR_ALIGN
+ *     otherwise), or NULL.  Its contents need no initialisation and are scratch after the
+ *     call; calls that may run at the same time need different workspaces.
+ * Shapes without the gather path, packed / cb1 / cb2 / x pointers that are not 16-byte
+ * aligned, or a NULL workspace where one is needed run the vq_gemm kernels. */
+vq_status vq_gemm_ws(const vq_desc* desc, const void* packed, const void* cb1, const void* cb2, const void* scale,
+                     const void* bias, const void* x, vq_dtype x_dtype, int32_t M, void* y, vq_dtype y_dtype,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * Affine-lattice layers (UniSVQ summary, gist.science, "Mathematical Formulation" and
  * "Efficiency"): instead of codebook entries, each 4-vector of W^ is a point of an affine

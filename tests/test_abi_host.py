@@ -221,6 +221,59 @@ def test_gemv_ws_validation_paths(vq):
     assert _gemv_ws(vq, d, ws=P, ws_bytes=0, m=0, y=None, x=None, packed=None) == vq.VQ_OK
 
 
+def _gemm_ws_bytes(vq, desc, m, xt):
+    n = ctypes.c_size_t(12345)
+    st = vq.lib().vq_gemm_workspace_bytes(ctypes.byref(desc) if desc is not None else None, m, xt, ctypes.byref(n))
+    return st, int(n.value)
+
+
+def _r256(b):
+    return (b + 255) // 256 * 256
+
+
+def test_gemm_workspace_bytes(vq):
+    """The workspace of vq_gemm_ws: for bf16 activations the fp16 copy [M][IN] and the M
+    powers of two, then fp32 partial sums [splits][M][N] when the K range is split (the
+    split count is chosen so that row blocks x splits cover about 192 of the 256 CUs)."""
+    down = vq.make_desc(8192, 28672, 8, 16, 8)  # 32 row blocks of 256: eight splits
+    st, nb = _gemm_ws_bytes(vq, down, 128, vq.VQ_BF16)
+    assert st == vq.VQ_OK
+    assert nb == _r256(128 * 28672 * 2) + _r256(128 * 4) + _r256(8 * 128 * 8192 * 4)
+    assert _gemm_ws_bytes(vq, down, 128, vq.VQ_F16)[1] == _r256(8 * 128 * 8192 * 4)
+    up = vq.make_desc(28672, 8192, 8, 16, 8)  # 112 row blocks: two splits
+    assert _gemm_ws_bytes(vq, up, 128, vq.VQ_F16)[1] == _r256(2 * 128 * 28672 * 4)
+    wide = vq.make_desc(50000, 512, 8, 16, 8)  # 196 row blocks: no split
+    assert _gemm_ws_bytes(vq, wide, 128, vq.VQ_F16) == (vq.VQ_OK, 0)
+    assert _gemm_ws_bytes(vq, wide, 128, vq.VQ_BF16)[1] == _r256(128 * 512 * 2) + _r256(128 * 4)
+    short = vq.make_desc(5000, 136, 8, 16, 8)  # two K-tiles of 128 columns: no split
+    assert _gemm_ws_bytes(vq, short, 7, vq.VQ_F16) == (vq.VQ_OK, 0)
+    # shapes without the gather path need none
+    for d in (vq.make_desc(14336, 4096, 6, 12, 12), vq.make_desc(4096, 4096, 8, 12, 0),
+              vq.make_desc(4096, 4096, 8, 16, 4), vq.make_desc(4096, 4100, 8, 16, 0),
+              vq.make_desc(4096, 0, 8, 16, 0), vq.make_desc(0, 4096, 8, 16, 0)):
+        assert _gemm_ws_bytes(vq, d, 64, vq.VQ_BF16) == (vq.VQ_OK, 0), d
+    assert _gemm_ws_bytes(vq, down, 0, vq.VQ_BF16) == (vq.VQ_OK, 0)
+    # errors leave the output alone
+    assert _gemm_ws_bytes(vq, down, -1, vq.VQ_F16) == (vq.VQ_ERR_SHAPE, 12345)
+    assert _gemm_ws_bytes(vq, down, 1, vq.VQ_F32) == (vq.VQ_ERR_UNSUPPORTED, 12345)
+    assert _gemm_ws_bytes(vq, None, 1, vq.VQ_F16) == (vq.VQ_ERR_NULL, 12345)
+    assert vq.lib().vq_gemm_workspace_bytes(ctypes.byref(down), 1, 0, None) == vq.VQ_ERR_NULL
+
+
+def test_gemm_ws_validation_paths(vq):
+    d = vq.make_desc(8192, 28672, 8, 16, 0)
+    need = _gemm_ws_bytes(vq, d, 64, vq.VQ_BF16)[1]
+    f = lambda d, ws=P, nbytes=need, m=64, xt=1, x=P: vq.lib().vq_gemm_ws(
+        ctypes.byref(d) if d is not None else None, P, P, P, None, None, x, xt, m, P, 2, ws, nbytes, None)
+    assert f(None) == vq.VQ_ERR_NULL
+    assert f(d, m=-1) == vq.VQ_ERR_SHAPE
+    assert f(d, xt=2) == vq.VQ_ERR_UNSUPPORTED
+    assert f(d, x=ctypes.c_void_p(0x10001)) == vq.VQ_ERR_ALIGN
+    assert f(d, nbytes=need - 1) == vq.VQ_ERR_BUFFER_SIZE
+    assert f(d, ws=ctypes.c_void_p(0x10010)) == vq.VQ_ERR_ALIGN
+    assert f(d, m=0) == vq.VQ_OK
+
+
 def test_gemv_noalloc_validation_paths(vq):
     """vq_gemv_noalloc checks its arguments like vq_gemv, then rejects shapes whose sliced-path
     workspace exceeds the library's fixed 16 MiB before touching the device."""

@@ -271,6 +271,63 @@ def rht_leg(vq, torch, use_graph):
     return out
 
 
+class RhtProductRing:
+    """A layer ring whose calls take the randomized Hadamard transform of x first: fused
+    (vq_gemv_ws_rht / vq_gemm_ws_rht) or separate (vq_rht into a buffer, then vq_gemv_ws /
+    vq_gemm_ws on it)."""
+
+    def __init__(self, vq, torch, key, layer, m, gemm, fused):
+        self.ring = Ring(vq, torch, key, layer, m, copies=6, fn="vq_gemm_ws" if gemm else "vq_gemv_ws")
+        self.copies = self.ring.copies
+        dev = torch.device("cuda")
+        n_in = self.ring.desc.in_features
+        g = torch.Generator(device=dev)
+        g.manual_seed(zlib.crc32(("%d/rhtp/%s/%d" % (42, key, layer)).encode()))
+        self.signs = torch.randint(0, 256, ((n_in + 7) // 8,), generator=g, device=dev, dtype=torch.uint8)
+        sp = ctypes.c_void_p(self.signs.data_ptr())
+        lib = vq.lib()
+        self.fused = fused
+        if fused:
+            self.fn = lib.vq_gemm_ws_rht if gemm else lib.vq_gemv_ws_rht
+            self.ws = torch.zeros(vq.rht_product_workspace_bytes(self.ring.desc, m, self.ring.x.dtype, gemm),
+                                  dtype=torch.uint8, device=dev)
+            wp = (ctypes.c_void_p(self.ws.data_ptr()), self.ws.numel())
+            self.items = [it[:9] + (sp,) + it[9:11] + wp for it in self.ring.items]
+        else:
+            self.fn = self.ring.fn
+            self.xt = torch.empty_like(self.ring.x)
+            xtp = ctypes.c_void_p(self.xt.data_ptr())
+            self.items = [it[:6] + (xtp,) + it[7:] for it in self.ring.items]
+            self.rht_args = (m, n_in, self.ring.items[0][6], self.ring.items[0][7], sp, 0, xtp, self.ring.items[0][7])
+            self.rht = lib.vq_rht
+
+    def call(self, k, stream_ptr):
+        if not self.fused:
+            st = self.rht(*self.rht_args, stream_ptr)
+            if st != 0:
+                raise RuntimeError("vq_rht failed with status %d" % st)
+        st = self.fn(*self.items[k % self.copies], stream_ptr)
+        if st != 0:
+            raise RuntimeError("%s failed with status %d" % (self.fn.__name__, st))
+
+
+def rht_fused_leg(vq, torch, use_graph):
+    """The 70B-class pair with the input transform: fused into the x pass against vq_rht
+    followed by the workspace product, per call (average of the two layers)."""
+    out = {}
+    for m, gemm in ((1, False), (8, False), (128, True)):
+        entry = {}
+        for fused in (True, False):
+            rings = [RhtProductRing(vq, torch, "l70b", li, m, gemm, fused) for li in (0, 1)]
+            sec, _, _, launch = time_ring(torch, rings, 240 if m < 128 else 48, 6, use_graph)
+            entry["fused_us_per_call" if fused else "separate_us_per_call"] = round(sec * 1e6, 3)
+            entry["launch"] = launch
+            del rings
+            torch.cuda.empty_cache()
+        out["l70b_m%d_%s" % (m, "vq_gemm_ws_rht" if gemm else "vq_gemv_ws_rht")] = entry
+    return out
+
+
 FP64_PEAK_TFLOPS = 78.6  # MI355X vector fp64 (FMA = 2 flops)
 
 
@@ -580,7 +637,7 @@ def main():
         print(json.dumps(res))
         return
     if args.only_rht:
-        print(json.dumps({"rht": rht_leg(vq, torch, use_graph)}))
+        print(json.dumps({"rht": rht_leg(vq, torch, use_graph), "rht_fused": rht_fused_leg(vq, torch, use_graph)}))
         return
     if args.only_encode:
         print(json.dumps({"encode": encode_leg(vq, torch)}))
@@ -742,6 +799,7 @@ def main():
         out["gemv_batched"] = batch
         out["affine_lattice"] = svq_leg(vq, torch, use_graph)
         out["rht"] = rht_leg(vq, torch, use_graph)
+        out["rht_fused"] = rht_fused_leg(vq, torch, use_graph)
         out["encode"] = encode_leg(vq, torch)
     if not args.no_cpu_baseline and not args.shared_book and not args.only_headline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

@@ -46,7 +46,8 @@ LAYOUT_ROWSTREAM = 1
 EXPORTED = ("vq_abi_version", "vq_status_string", "vq_packed_bytes", "vq_pack", "vq_dequant", "vq_gemv",
             "vq_gemv_workspace_bytes", "vq_gemv_ws", "vq_gemm", "vq_svq_dequant", "vq_svq_gemv", "vq_rht", "vq_rht_block",
             "vq_assign_workspace_bytes", "vq_assign", "vq_svq_gemm", "vq_gemv_noalloc", "vq_svq_pack",
-            "vq_gemm_workspace_bytes", "vq_gemm_ws")
+            "vq_gemm_workspace_bytes", "vq_gemm_ws", "vq_rht_product_workspace_bytes", "vq_gemv_ws_rht",
+            "vq_gemm_ws_rht")
 
 
 class Desc(ctypes.Structure):
@@ -98,6 +99,11 @@ def _load():
     lib.vq_gemm_workspace_bytes.restype = ctypes.c_int
     lib.vq_gemm_ws.argtypes = [dp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i32, vp, ctypes.c_int, vp, sz, vp]
     lib.vq_gemm_ws.restype = ctypes.c_int
+    lib.vq_rht_product_workspace_bytes.argtypes = [dp, i32, ctypes.c_int, i32, ctypes.POINTER(sz)]
+    lib.vq_rht_product_workspace_bytes.restype = ctypes.c_int
+    for name in ("vq_gemv_ws_rht", "vq_gemm_ws_rht"):
+        getattr(lib, name).argtypes = [dp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i32, vp, vp, ctypes.c_int, vp, sz, vp]
+        getattr(lib, name).restype = ctypes.c_int
     lib.vq_gemv_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, ctypes.c_int, i32, vp, ctypes.c_int, vp]
     lib.vq_gemv_noalloc.restype = ctypes.c_int
     lib.vq_svq_dequant.argtypes = [dp, vp, vp, vp, vp, vp, ctypes.c_int, vp]
@@ -409,6 +415,53 @@ def assign(desc: Desc, w, cb1, cb2=None, ws=None, out1=None, out2=None):
 
 
 _stream_ws = {}
+
+
+def rht_product_workspace_bytes(desc: Desc, m: int, x_dtype, gemm: bool) -> int:
+    """Workspace bytes for gemv_ws_rht (gemm False) or gemm_ws_rht (gemm True)."""
+    n = ctypes.c_size_t(0)
+    _check(lib().vq_rht_product_workspace_bytes(ctypes.byref(desc), int(m), _dtype_code(x_dtype), int(bool(gemm)),
+                                                ctypes.byref(n)), "vq_rht_product_workspace_bytes")
+    return int(n.value)
+
+
+def rht_workspace(desc: Desc, m: int, x_dtype, gemm: bool, device="cuda"):
+    """A zero-filled device workspace for gemv_ws_rht / gemm_ws_rht (None when none is needed)."""
+    nbytes = rht_product_workspace_bytes(desc, m, x_dtype, gemm)
+    if nbytes == 0:
+        return None
+    return _torch().zeros(nbytes, dtype=_torch().uint8, device=device)
+
+
+def _rht_product(gemm, desc, packed, cb1, cb2, scale, bias, x, signs, ws, y_dtype=None, out=None):
+    torch = _torch()
+    if x.dim() != 2 or x.shape[1] != desc.in_features:
+        raise ValueError("x must be [M, %d], got %s" % (desc.in_features, tuple(x.shape)))
+    m = x.shape[0]
+    y_dtype = y_dtype or x.dtype
+    if out is None:
+        out = torch.empty((m, desc.out_features), dtype=y_dtype, device=x.device)
+    f16 = (torch.float16,)
+    name = "vq_gemm_ws_rht" if gemm else "vq_gemv_ws_rht"
+    wsp, wsb = (None, 0) if ws is None else (_dev_ptr(ws, "workspace"), ws.numel() * ws.element_size())
+    st = getattr(lib(), name)(ctypes.byref(desc), _dev_ptr(packed, "packed"), _dev_ptr(cb1, "cb1", f16),
+                              _dev_ptr(cb2, "cb2", f16) if desc.bits2 else None, _dev_ptr(scale, "scale", f16),
+                              _dev_ptr(bias, "bias", f16), _dev_ptr(x, "x", (torch.float16, torch.bfloat16)),
+                              _dtype_code(x.dtype), m, _dev_ptr(signs, "signs", (torch.uint8,)), _dev_ptr(out, "out"),
+                              _dtype_code(out.dtype), wsp, wsb, _stream_ptr(x.device))
+    _check(st, name)
+    return out
+
+
+def gemv_ws_rht(desc, packed, cb1, cb2, scale, bias, x, signs, ws, y_dtype=None, out=None):
+    """gemv_ws on the randomized Hadamard transform of x (vq_rht forward, `signs` uint8 bits),
+    the transform fused into the x pass where the shape has the workspace path."""
+    return _rht_product(False, desc, packed, cb1, cb2, scale, bias, x, signs, ws, y_dtype, out)
+
+
+def gemm_ws_rht(desc, packed, cb1, cb2, scale, bias, x, signs, ws, y_dtype=None, out=None):
+    """gemm_ws on the randomized Hadamard transform of x, as gemv_ws_rht."""
+    return _rht_product(True, desc, packed, cb1, cb2, scale, bias, x, signs, ws, y_dtype, out)
 
 
 def stream_workspace(desc: Desc, m: int, x_dtype, device, gemm_path: bool = False):

@@ -291,7 +291,7 @@ size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 // 256-row blocks x batch chunks; the K range is split (into an even number of tiles per
 // split) until about three quarters of the CUs have a workgroup, keeping at least two
 // tiles per split.
-Plan make_plan(int32_t n, int32_t in_features, int32_t m, bool bf16) {
+Plan make_plan(int32_t n, int32_t in_features, int32_t m, bool bf16, bool rht = false) {
   Plan p{};
   GatherCfg& g = p.cfg;
   const int nv = in_features / 8;
@@ -308,8 +308,9 @@ Plan make_plan(int32_t n, int32_t in_features, int32_t m, bool bf16) {
   const int mr = m < kMC ? m : kMC;
   p.nb = (mr + 31) / 32;
   p.x16_off = 0;
-  p.exp_off = bf16 ? round256((size_t)m * in_features * 2) : 0;
-  p.part_off = p.exp_off + (bf16 ? round256((size_t)m * sizeof(int32_t)) : 0);
+  const bool pass = bf16 || rht;  // an x pass writes the fp16 copy and the powers of two
+  p.exp_off = pass ? round256((size_t)m * in_features * 2) : 0;
+  p.part_off = p.exp_off + (pass ? round256((size_t)m * sizeof(int32_t)) : 0);
   p.bytes = p.part_off + (g.ks > 1 ? round256((size_t)g.ks * m * n * sizeof(float)) : 0);
   return p;
 }
@@ -352,17 +353,23 @@ bool gather_gemm_pointers_ok(const ProductArgs& a) {
   return aligned(a.packed1, 16) && aligned(a.cb1, 16) && (a.bits2 == 0 || aligned(a.cb2, 16)) && aligned(a.x, 16);
 }
 
-vq_status launch_gemm_gather(const ProductArgs& a, void* workspace, void* stream) {
+size_t gather_gemm_rht_workspace(const vq_desc& d, int32_t m, vq_dtype x_dtype) {
+  if (!gather_gemm_shape_ok(d, m, x_dtype) || d.in_features > kFusedRhtMaxIn || d.in_features % 16 != 0) return 0;
+  return make_plan(d.out_features, d.in_features, m, x_dtype == VQ_BF16, true).bytes;
+}
+
+vq_status launch_gemm_gather(const ProductArgs& a, void* workspace, void* stream, const uint8_t* rht_signs) {
   const bool bf16 = a.x_dtype == VQ_BF16;
-  Plan p = make_plan(a.n, a.in_features, a.m, bf16);
+  Plan p = make_plan(a.n, a.in_features, a.m, bf16, rht_signs != nullptr);
   if (p.bytes > 0 && !workspace) return VQ_ERR_NULL;
   char* ws = (char*)workspace;
   hipStream_t s = (hipStream_t)stream;
   p.cfg.part = p.cfg.ks > 1 ? (float*)(ws + p.part_off) : nullptr;
-  if (bf16) {
+  if (bf16 || rht_signs) {
     uint16_t* x16 = (uint16_t*)(ws + p.x16_off);
     int32_t* xexp = (int32_t*)(ws + p.exp_off);
-    const vq_status st = launch_x_to_f16(a, x16, xexp, stream);
+    const vq_status st = rht_signs ? launch_x_rht_to_f16(a, rht_signs, x16, xexp, stream)
+                                   : launch_x_to_f16(a, x16, xexp, stream);
     if (st != VQ_OK) return st;
     p.cfg.x16 = x16;
     p.cfg.xexp = xexp;

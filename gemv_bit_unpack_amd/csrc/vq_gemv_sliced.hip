@@ -603,6 +603,149 @@ __global__ __launch_bounds__(1024) void xprep_kernel(const uint16_t* __restrict_
   if (tid == 0) xexp[m] = e;
 }
 
+// The x pass with the randomized Hadamard transform ahead of the rescale: per batch row,
+// x~ = H_b (s . x) / sqrt(b) for every block of b = rht_block(IN) columns (H_b in
+// Sylvester order, s_j = -1 where bit j of `signs` is set), in fp32, then the fp16 rewrite
+// times 2^-e.  One workgroup per (batch row, block), b / 8 threads with one 16-byte word
+// of x each.  The power of two comes from a bound every workgroup of the row computes the
+// same way, |x~_i| <= sqrt(b) max |x|: e puts that bound in [2^14, 2^15), so nothing
+// overflows, and since fp16 keeps 11 significant bits anywhere in its normal range the
+// values lose nothing to the bound's slack until they are 2^-20 or so of the largest.
+// The block sits in LDS; the butterflies run in phases of up to 4 index bits: a thread
+// takes the 2^ST values of a group (consecutive in the phase's bits, the other bits
+// fixed), transforms them in registers and writes them back; one barrier per phase.
+constexpr int kRhtMaxBlock = 16384;
+
+template <int ST>
+__device__ __forceinline__ void rht_phase(float* blk, int b, int lo_bits) {
+  constexpr int kLen = 1 << ST;
+  const int span = 1 << lo_bits;
+  const int groups = b >> ST;
+  for (int it = threadIdx.x; it < groups; it += blockDim.x) {
+    const int base = ((it >> lo_bits) << (lo_bits + ST)) | (it & (span - 1));
+    float v[kLen];
+#pragma unroll
+    for (int j = 0; j < kLen; ++j) v[j] = blk[base + j * span];
+#pragma unroll
+    for (int h = 1; h < kLen; h <<= 1) {
+#pragma unroll
+      for (int j = 0; j < kLen; ++j) {
+        if ((j & h) == 0) {
+          const float u = v[j], w = v[j + h];
+          v[j] = u + w;
+          v[j + h] = u - w;
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kLen; ++j) blk[base + j * span] = v[j];
+  }
+}
+
+// 16-point transform of v in registers (index bits 0..3).
+__device__ __forceinline__ void wht16(float (&v)[16]) {
+#pragma unroll
+  for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if ((j & h) == 0) {
+        const float u = v[j], w = v[j + h];
+        v[j] = u + w;
+        v[j + h] = u - w;
+      }
+    }
+  }
+}
+
+// block / 16 threads; thread t owns the block's values 16 t .. 16 t + 15.
+__global__ __launch_bounds__(1024) void xprep_rht_kernel(const uint16_t* __restrict__ x, int xbf16, int in_features,
+                                                         int block, float inv, float root_b,
+                                                         const uint8_t* __restrict__ signs,
+                                                         uint16_t* __restrict__ x16, int32_t* __restrict__ xexp) {
+  __shared__ float blk[kRhtMaxBlock];
+  __shared__ uint32_t smax;
+  const int nblk = in_features / block;
+  const int m = blockIdx.x / nblk;
+  const int bk = blockIdx.x - m * nblk;
+  const int tid = threadIdx.x;
+  const int nt = blockDim.x;
+  const int n8 = in_features / 8;
+  const uint4* xr = (const uint4*)(x + (size_t)m * in_features);
+  if (tid == 0) smax = 0;
+  // this thread's 16 values (two words, two sign bytes), then the whole row for the bound
+  const int w0 = bk * (block / 8) + 2 * tid;
+  const uint4 q0 = xr[w0], q1 = xr[w0 + 1];
+  const uint32_t sb = signs[w0] | ((uint32_t)signs[w0 + 1] << 8);
+  uint32_t mx = 0;  // largest |x| of the row, as bits of the 16-bit format (they order like the values)
+  for (int i0 = tid; i0 < n8; i0 += 8 * nt) {  // 8 loads in flight per thread (clamped, no branch)
+    uint4 q[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) q[k] = xr[min(i0 + k * nt, n8 - 1)];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t w[4] = {q[k].x, q[k].y, q[k].z, q[k].w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) mx = max(mx, max(w[h] & 0x7FFFu, (w[h] >> 16) & 0x7FFFu));
+    }
+  }
+  float v[16];
+  {
+    const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+    for (int h = 0; h < 16; ++h) {
+      const uint32_t b = (h & 1) ? (w[h >> 1] >> 16) : (w[h >> 1] & 0xFFFFu);
+      const float f = xbf16 ? vqd::bf16_to_f32(b) : vqd::f16_to_f32(b);
+      v[h] = ((sb >> h) & 1u) ? -f : f;
+    }
+  }
+  wht16(v);  // index bits 0..3 in registers
+  const int lb = 31 - __builtin_clz(block);  // block = 2^lb >= 16
+  if (lb > 4) {
+    float4* bp = (float4*)(blk + 16 * tid);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) bp[k] = make_float4(v[4 * k], v[4 * k + 1], v[4 * k + 2], v[4 * k + 3]);
+  }
+  __syncthreads();  // smax cleared, the block in LDS
+  atomicMax(&smax, mx);
+  for (int lo = 4; lo < lb; lo += 4) {
+    switch (min(4, lb - lo)) {
+      case 1: rht_phase<1>(blk, block, lo); break;
+      case 2: rht_phase<2>(blk, block, lo); break;
+      case 3: rht_phase<3>(blk, block, lo); break;
+      default: rht_phase<4>(blk, block, lo); break;
+    }
+    __syncthreads();
+  }
+  if (lb <= 4) __syncthreads();  // smax complete
+  mx = smax;
+  // bound = sqrt(b) max |x| (rounded up), e = its fp32 exponent less 141 - 127
+  const float xmax = xbf16 ? vqd::bf16_to_f32(mx) : vqd::f16_to_f32(mx);
+  const float bound = xmax * root_b * (1.0f + 0x1p-20f);
+  const int e = (int)((__builtin_bit_cast(uint32_t, bound) >> 23) & 0xFFu) - 141;
+  if (lb > 4) {
+    const float4* bp = (const float4*)(blk + 16 * tid);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float4 f = bp[k];
+      v[4 * k] = f.x;
+      v[4 * k + 1] = f.y;
+      v[4 * k + 2] = f.z;
+      v[4 * k + 3] = f.w;
+    }
+  }
+  uint32_t o[8];
+#pragma unroll
+  for (int h = 0; h < 8; ++h) {
+    const uint32_t l = vqd::f32_to_f16_rne(ldexpf(v[2 * h] * inv, -e));
+    const uint32_t u = vqd::f32_to_f16_rne(ldexpf(v[2 * h + 1] * inv, -e));
+    o[h] = l | (u << 16);
+  }
+  uint4* xo = (uint4*)(x16 + (size_t)m * in_features);
+  xo[w0] = make_uint4(o[0], o[1], o[2], o[3]);
+  xo[w0 + 1] = make_uint4(o[4], o[5], o[6], o[7]);
+  if (bk == 0 && tid == 0) xexp[m] = e;
+}
+
 struct Plan {
   SlicedCfg cfg;
   size_t part_off, x16_off, exp_off, bytes;
@@ -612,7 +755,7 @@ size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
 // Row blocks of 128 rows; the columns are split until every group has a tile (or the
 // chunks run out).
-Plan make_plan(int32_t n, int32_t in_features, int32_t m, bool bf16) {
+Plan make_plan(int32_t n, int32_t in_features, int32_t m, bool bf16, bool rht = false) {
   Plan p{};
   SlicedCfg& g = p.cfg;
   const int nv = in_features / 8;
@@ -627,9 +770,9 @@ Plan make_plan(int32_t n, int32_t in_features, int32_t m, bool bf16) {
   g.groups = units < kGroups ? units : kGroups;
   p.part_off = 0;
   p.x16_off = round256((size_t)kSlices * g.n_cs * m * n * sizeof(float));
-  // the fp16 copy of x only where xprep_kernel runs (bf16, M > 2)
-  p.exp_off = p.x16_off + (bf16 && m > 2 ? round256((size_t)m * in_features * 2) : 0);
-  p.bytes = p.exp_off + (bf16 ? round256((size_t)m * sizeof(int32_t)) : 0);
+  // the fp16 copy of x only where an x pass runs (bf16 at M > 2, or the transform)
+  p.exp_off = p.x16_off + ((bf16 && m > 2) || rht ? round256((size_t)m * in_features * 2) : 0);
+  p.bytes = p.exp_off + (bf16 || rht ? round256((size_t)m * sizeof(int32_t)) : 0);
   return p;
 }
 
@@ -690,6 +833,11 @@ bool sliced_gemv_shape_ok(const vq_desc& d, int32_t m, vq_dtype x_dtype) {
   if (d.v != 8 || d.bits1 != 16 || !(d.bits2 == 0 || d.bits2 == 8)) return false;
   if (m < 1 || m > 16 || !(x_dtype == VQ_F16 || x_dtype == VQ_BF16)) return false;
   if (d.in_features % 8 != 0 || d.out_features < 1) return false;
+  // 32-bit buffer offsets, the rows of the last row block included
+  const uint64_t rows = (uint64_t)d.out_features + 256;
+  if (rows * (uint64_t)row_stride(d.in_features, 8, 16) >= ((uint64_t)1 << 32)) return false;
+  if (rows * (uint64_t)row_stride(d.in_features, 8, d.bits2) >= ((uint64_t)1 << 32)) return false;
+  if ((uint64_t)m * (uint64_t)d.in_features * 2u >= ((uint64_t)1 << 32)) return false;
   // Filling 256 LDS slices costs a few microseconds per call: below about four million
   // vectors the L2-gather kernel is as fast up to M = 4.  From M = 8 the slices win from
   // half a million vectors, since one matrix instruction serves every batch row.
@@ -706,15 +854,46 @@ bool sliced_gemv_pointers_ok(const ProductArgs& a) {
   return aligned(a.packed1, 16) && aligned(a.cb1, 16) && (a.bits2 == 0 || aligned(a.cb2, 16)) && aligned(a.x, 16);
 }
 
-vq_status launch_gemv_sliced(const ProductArgs& a, void* workspace, void* stream) {
+vq_status launch_x_rht_to_f16(const ProductArgs& a, const uint8_t* signs, uint16_t* x16, int32_t* xexp,
+                              void* stream) {
+  if (a.in_features > vqi::kFusedRhtMaxIn || a.in_features % 16 != 0) return VQ_ERR_UNSUPPORTED;
+  const int b = rht_block(a.in_features);  // 16 <= b <= 16384
+  const float inv = (float)(1.0 / __builtin_sqrt((double)b));
+  const float root_b = (float)__builtin_sqrt((double)b);
+  const unsigned grid = (unsigned)a.m * (unsigned)(a.in_features / b);
+  // block / 16 threads, 16 values each (1 .. 1024 threads)
+  hipLaunchKernelGGL(xprep_rht_kernel, dim3(grid), dim3(b / 16), 0, (hipStream_t)stream, a.x,
+                     a.x_dtype == VQ_BF16 ? 1 : 0, a.in_features, b, inv, root_b, signs, x16, xexp);
+  return hipGetLastError() == hipSuccess ? VQ_OK : VQ_ERR_HIP;
+}
+
+size_t sliced_gemv_rht_workspace(const vq_desc& d, int32_t m, vq_dtype x_dtype) {
+  if (!sliced_gemv_shape_ok(d, m, x_dtype) || d.in_features > vqi::kFusedRhtMaxIn || d.in_features % 16 != 0) return 0;
+  return make_plan(d.out_features, d.in_features, m, x_dtype == VQ_BF16, true).bytes;
+}
+
+vq_status launch_gemv_sliced(const ProductArgs& a, void* workspace, void* stream, const uint8_t* rht_signs) {
   // the kernels store partial sums into the workspace: never launch without one
   if (!workspace) return VQ_ERR_NULL;
   const bool bf16 = a.x_dtype == VQ_BF16;
-  Plan p = make_plan(a.n, a.in_features, a.m, bf16);
+  Plan p = make_plan(a.n, a.in_features, a.m, bf16, rht_signs != nullptr);
   char* ws = (char*)workspace;
   p.cfg.part = (float*)(ws + p.part_off);
   hipStream_t s = (hipStream_t)stream;
   p.cfg.xexp_out = nullptr;
+  if (rht_signs) {
+    // the transform and the fp16 rewrite in one pass; the product then reads fp16 x
+    uint16_t* x16 = (uint16_t*)(ws + p.x16_off);
+    int32_t* xexp = (int32_t*)(ws + p.exp_off);
+    const vq_status st = launch_x_rht_to_f16(a, rht_signs, x16, xexp, stream);
+    if (st != VQ_OK) return st;
+    ProductArgs a16 = a;
+    a16.x = x16;
+    a16.x_dtype = VQ_F16;
+    p.cfg.x16 = x16;
+    p.cfg.xexp = xexp;
+    return a.bits2 == 8 ? launch_res<true>(a16, p.cfg, s) : launch_res<false>(a16, p.cfg, s);
+  }
   if (bf16 && a.m > 2) {
     uint16_t* x16 = (uint16_t*)(ws + p.x16_off);
     int32_t* xexp = (int32_t*)(ws + p.exp_off);

@@ -402,4 +402,71 @@ vq_status vq_gemm_ws(const vq_desc* desc, const void* packed, const void* cb1, c
   return launch_gemm(a, stream);
 }
 
+// Workspace of the transform-fused products: the fused path's (x pass, partial sums) or,
+// without it, the transformed activations [M][IN] for the separate transform.
+static size_t rht_product_bytes(const vq_desc& d, int32_t m, vq_dtype x_dtype, bool gemm) {
+  if (m <= 0 || d.in_features == 0) return 0;
+  const size_t fused = gemm ? gather_gemm_rht_workspace(d, m, x_dtype) : sliced_gemv_rht_workspace(d, m, x_dtype);
+  const size_t sep = ((size_t)m * (size_t)d.in_features * 2 + 255) / 256 * 256;
+  return fused > sep ? fused : sep;
+}
+
+vq_status vq_rht_product_workspace_bytes(const vq_desc* desc, int32_t M, vq_dtype x_dtype, int32_t gemm,
+                                         size_t* nbytes) {
+  if (!nbytes) return VQ_ERR_NULL;
+  vq_status st = check_desc(desc);
+  if (st != VQ_OK) return st;
+  if (gemm != 0 && gemm != 1) return VQ_ERR_UNSUPPORTED;
+  if (M < 0 || (!gemm && M > 16)) return VQ_ERR_SHAPE;
+  if (x_dtype != VQ_F16 && x_dtype != VQ_BF16) return VQ_ERR_UNSUPPORTED;
+  if (desc->in_features % 16 != 0) return VQ_ERR_UNSUPPORTED;
+  *nbytes = rht_product_bytes(*desc, M, x_dtype, gemm != 0);
+  return VQ_OK;
+}
+
+static vq_status rht_product(bool gemm, const vq_desc* desc, const void* packed, const void* cb1, const void* cb2,
+                             const void* scale, const void* bias, const void* x, vq_dtype x_dtype, int32_t M,
+                             const void* signs, void* y, vq_dtype y_dtype, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  ProductArgs a;
+  vq_status st = prepare_product(desc, packed, cb1, cb2, scale, bias, x, x_dtype, M, y, y_dtype, gemm ? 0 : 16, &a);
+  if (st != VQ_OK) return st;
+  if (a.in_features % 16 != 0) return VQ_ERR_UNSUPPORTED;
+  if (a.n == 0 || a.m == 0) return VQ_OK;
+  if (a.in_features == 0) return gemm ? launch_gemm(a, stream) : launch_gemv(a, stream);  // y = bias
+  if (!signs || !workspace) return VQ_ERR_NULL;
+  if (!aligned(x, 16)) return VQ_ERR_ALIGN;
+  const size_t need = rht_product_bytes(*desc, a.m, a.x_dtype, gemm);
+  if (workspace_bytes < need) return VQ_ERR_BUFFER_SIZE;
+  if (!aligned(workspace, 256)) return VQ_ERR_ALIGN;
+  const uint8_t* sg = (const uint8_t*)signs;
+  if (gemm) {
+    if (gather_gemm_rht_workspace(*desc, a.m, a.x_dtype) > 0 && gather_gemm_pointers_ok(a))
+      return launch_gemm_gather(a, workspace, stream, sg);
+  } else {
+    if (sliced_gemv_rht_workspace(*desc, a.m, a.x_dtype) > 0 && sliced_gemv_pointers_ok(a))
+      return launch_gemv_sliced(a, workspace, stream, sg);
+  }
+  // no fused path: the transform into the workspace, then the plain product on it
+  st = launch_rht(a.m, a.in_features, a.x, a.x_dtype, sg, 0, workspace, a.x_dtype, stream);
+  if (st != VQ_OK) return st;
+  ProductArgs at = a;
+  at.x = (const uint16_t*)workspace;
+  return gemm ? launch_gemm(at, stream) : launch_gemv(at, stream);
+}
+
+vq_status vq_gemv_ws_rht(const vq_desc* desc, const void* packed, const void* cb1, const void* cb2, const void* scale,
+                         const void* bias, const void* x, vq_dtype x_dtype, int32_t M, const void* signs, void* y,
+                         vq_dtype y_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return rht_product(false, desc, packed, cb1, cb2, scale, bias, x, x_dtype, M, signs, y, y_dtype, workspace,
+                     workspace_bytes, stream);
+}
+
+vq_status vq_gemm_ws_rht(const vq_desc* desc, const void* packed, const void* cb1, const void* cb2, const void* scale,
+                         const void* bias, const void* x, vq_dtype x_dtype, int32_t M, const void* signs, void* y,
+                         vq_dtype y_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  return rht_product(true, desc, packed, cb1, cb2, scale, bias, x, x_dtype, M, signs, y, y_dtype, workspace,
+                     workspace_bytes, stream);
+}
+
 }  // extern "C"

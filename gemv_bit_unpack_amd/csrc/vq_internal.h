@@ -62,7 +62,10 @@ vq_status launch_gemv(const ProductArgs& a, void* stream);
 bool sliced_gemv_shape_ok(const vq_desc& d, int32_t m, vq_dtype x_dtype);
 size_t sliced_gemv_workspace(const vq_desc& d, int32_t m, vq_dtype x_dtype);
 bool sliced_gemv_pointers_ok(const ProductArgs& a);
-vq_status launch_gemv_sliced(const ProductArgs& a, void* workspace, void* stream);
+// rht_signs: also the randomized Hadamard transform of x (forward, blocks of rht_block(IN))
+// in the x pass; then the workspace is sliced_gemv_rht_workspace(...) bytes.
+vq_status launch_gemv_sliced(const ProductArgs& a, void* workspace, void* stream, const uint8_t* rht_signs = nullptr);
+size_t sliced_gemv_rht_workspace(const vq_desc& d, int32_t m, vq_dtype x_dtype);
 // The fixed device workspace of vq_gemv_noalloc: its size, and this GPU's copy (looked up
 // on the first call on each device; no allocation).
 size_t static_scratch_bytes();
@@ -73,11 +76,16 @@ vq_status launch_gemm(const ProductArgs& a, void* stream);
 bool gather_gemm_shape_ok(const vq_desc& d, int32_t m, vq_dtype x_dtype);
 size_t gather_gemm_workspace(const vq_desc& d, int32_t m, vq_dtype x_dtype);
 bool gather_gemm_pointers_ok(const ProductArgs& a);
-vq_status launch_gemm_gather(const ProductArgs& a, void* workspace, void* stream);
+vq_status launch_gemm_gather(const ProductArgs& a, void* workspace, void* stream, const uint8_t* rht_signs = nullptr);
+size_t gather_gemm_rht_workspace(const vq_desc& d, int32_t m, vq_dtype x_dtype);
 // Passes shared by the workspace products: bf16 activations rewritten as fp16 times a
 // power of two per batch row (x16 [M][IN], xexp [M]); and y = 2^e * scale * (sum of
 // `nparts` fp32 partial sums [nparts][M][N], in order) + bias.
 vq_status launch_x_to_f16(const ProductArgs& a, uint16_t* x16, int32_t* xexp, void* stream);
+// The same pass with the forward randomized Hadamard transform first (IN a multiple of 16,
+// at most 32768; VQ_ERR_UNSUPPORTED otherwise).
+vq_status launch_x_rht_to_f16(const ProductArgs& a, const uint8_t* signs, uint16_t* x16, int32_t* xexp, void* stream);
+constexpr int32_t kFusedRhtMaxIn = 32768;
 vq_status launch_partials_finalize(const ProductArgs& a, const float* part, const int32_t* xexp, int nparts,
                                    void* stream);
 

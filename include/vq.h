@@ -286,6 +286,32 @@ vq_status vq_rht(int32_t M, int32_t n, const void* x, vq_dtype x_dtype, const vo
 /* The transform's block size for row length n (0 for n <= 0). */
 int32_t vq_rht_block(int32_t n);
 
+/* Products with the transform fused ahead of them: y = x~ W^T (+ bias), where x~ is
+ * vq_rht(x, signs, transpose = 0) row by row (the incoherence step on a layer's inputs:
+ * sub-4-bit lecture, "QuIP#: Incoherence Processing"; UniSVQ summary, "Preprocessing
+ * (Randomized Hadamard Transform - RHT)").  vq_gemv_ws_rht takes 1 <= M <= 16 as vq_gemv_ws,
+ * vq_gemm_ws_rht any M as vq_gemm_ws.  Where the shape has the workspace path of
+ * vq_gemv_ws / vq_gemm_ws (and IN <= 32768), the transform runs in that path's x pass: one
+ * workgroup per batch row transforms the row in LDS in fp32 and rewrites it as fp16 times a
+ * power of two, in place of vq_rht's own launch (and of the x pass bf16 activations take
+ * for M > 2 and in vq_gemm_ws).  Otherwise the call runs vq_rht into the workspace (x~
+ * rounded to x_dtype) and then vq_gemv / vq_gemm on it.
+ * Arguments as for vq_gemv_ws / vq_gemm_ws, plus signs (device, ceil(IN / 8) bytes, bit j
+ * of byte j / 8 set: s_j = -1).  IN must be a multiple of 16 (VQ_ERR_UNSUPPORTED); x must be
+ * 16-byte aligned (VQ_ERR_ALIGN).  The workspace is required (NULL: VQ_ERR_NULL): device
+ * memory, 256-byte aligned, of at least vq_rht_product_workspace_bytes(desc, M, x_dtype,
+ * gemm) bytes, gemm = 0 for vq_gemv_ws_rht and 1 for vq_gemm_ws_rht; contents need no
+ * initialisation, calls that may overlap need different workspaces.  Results match
+ * vq_gemv / vq_gemm on x~ to their tolerance. */
+vq_status vq_rht_product_workspace_bytes(const vq_desc* desc, int32_t M, vq_dtype x_dtype, int32_t gemm,
+                                         size_t* nbytes);
+vq_status vq_gemv_ws_rht(const vq_desc* desc, const void* packed, const void* cb1, const void* cb2, const void* scale,
+                         const void* bias, const void* x, vq_dtype x_dtype, int32_t M, const void* signs, void* y,
+                         vq_dtype y_dtype, void* workspace, size_t workspace_bytes, void* stream);
+vq_status vq_gemm_ws_rht(const vq_desc* desc, const void* packed, const void* cb1, const void* cb2, const void* scale,
+                         const void* bias, const void* x, vq_dtype x_dtype, int32_t M, const void* signs, void* y,
+                         vq_dtype y_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * Two-stage residual VQ encode with given codebooks (VPTQ guide, "Step 2: Multi-Stage
  * Residual Vector Quantizer (RVQ)": Euclidean distance and argmin, then the same on the

@@ -185,7 +185,8 @@ def test_gemv_workspace_bytes(vq):
     assert st == vq.VQ_OK and f16 > 0 and f16 % 256 == 0
     assert _ws_bytes(vq, big, 1, vq.VQ_BF16)[1] > f16          # + the fp16 copy of x
     assert _ws_bytes(vq, big, 16, vq.VQ_F16)[1] > f16          # partials per batch row
-    assert _ws_bytes(vq, vq.make_desc(16384, 4096, 8, 16, 8), 1, vq.VQ_F16)[1] > f16
+    # at least one fp32 partial per slice and row
+    assert _ws_bytes(vq, vq.make_desc(16384, 4096, 8, 16, 8), 1, vq.VQ_F16)[1] >= 8 * 16384 * 4
     dec = vq.make_desc(4096, 4096, 8, 16, 0)  # 2^21 vectors: sliced from M = 8 only
     assert _ws_bytes(vq, dec, 1, vq.VQ_F16) == (vq.VQ_OK, 0)
     assert _ws_bytes(vq, dec, 7, vq.VQ_F16) == (vq.VQ_OK, 0)
@@ -272,6 +273,56 @@ def test_gemm_ws_validation_paths(vq):
     assert f(d, nbytes=need - 1) == vq.VQ_ERR_BUFFER_SIZE
     assert f(d, ws=ctypes.c_void_p(0x10010)) == vq.VQ_ERR_ALIGN
     assert f(d, m=0) == vq.VQ_OK
+
+
+def _rht_ws(vq, desc, m, xt, gemm):
+    n = ctypes.c_size_t(12345)
+    st = vq.lib().vq_rht_product_workspace_bytes(ctypes.byref(desc) if desc is not None else None, m, xt, gemm,
+                                                 ctypes.byref(n))
+    return st, int(n.value)
+
+
+def test_rht_product_workspace_bytes(vq):
+    """Transform-fused products: the fused path's workspace (x pass and partial sums, never
+    less than the transformed activations) where the shape has it, else room for x~ [M][IN]."""
+    up = vq.make_desc(28672, 8192, 8, 16, 8)
+    st, nb = _rht_ws(vq, up, 1, vq.VQ_BF16, 0)
+    assert st == vq.VQ_OK and nb % 256 == 0
+    assert nb >= _ws_bytes(vq, up, 1, vq.VQ_BF16)[1] + 8192 * 2  # the sliced workspace plus the fp16 copy
+    st, nb = _rht_ws(vq, up, 128, vq.VQ_F16, 1)
+    assert st == vq.VQ_OK and nb >= _gemm_ws_bytes(vq, up, 128, vq.VQ_F16)[1] + 128 * 8192 * 2
+    dec = vq.make_desc(4096, 4096, 8, 16, 0)  # no sliced path at M = 1: x~ only
+    assert _rht_ws(vq, dec, 1, vq.VQ_F16, 0) == (vq.VQ_OK, _r256(4096 * 2))
+    v6 = vq.make_desc(300, 1024, 6, 12, 12)
+    assert _rht_ws(vq, v6, 48, vq.VQ_BF16, 1) == (vq.VQ_OK, _r256(48 * 1024 * 2))
+    wide = vq.make_desc(64, 65536, 8, 16, 0)  # beyond the fused pass's 32768 columns: x~ only
+    assert _rht_ws(vq, wide, 64, vq.VQ_F16, 1) == (vq.VQ_OK, _r256(64 * 65536 * 2))
+    assert _rht_ws(vq, up, 0, vq.VQ_F16, 0) == (vq.VQ_OK, 0)
+    # errors leave the output alone
+    assert _rht_ws(vq, up, 17, vq.VQ_F16, 0) == (vq.VQ_ERR_SHAPE, 12345)
+    assert _rht_ws(vq, up, -1, vq.VQ_F16, 1) == (vq.VQ_ERR_SHAPE, 12345)
+    assert _rht_ws(vq, up, 1, vq.VQ_F32, 0) == (vq.VQ_ERR_UNSUPPORTED, 12345)
+    assert _rht_ws(vq, up, 1, vq.VQ_F16, 2) == (vq.VQ_ERR_UNSUPPORTED, 12345)
+    assert _rht_ws(vq, vq.make_desc(64, 1000, 8, 16, 0), 1, vq.VQ_F16, 0) == (vq.VQ_ERR_UNSUPPORTED, 12345)
+    assert _rht_ws(vq, None, 1, vq.VQ_F16, 0) == (vq.VQ_ERR_NULL, 12345)
+
+
+def test_rht_product_validation_paths(vq):
+    d = vq.make_desc(28672, 8192, 8, 16, 8)
+    for gemm, fn in ((0, vq.lib().vq_gemv_ws_rht), (1, vq.lib().vq_gemm_ws_rht)):
+        need = _rht_ws(vq, d, 1, vq.VQ_BF16, gemm)[1]
+        f = lambda desc, ws=P, nbytes=need, x=P, sg=P, m=1: fn(ctypes.byref(desc) if desc is not None else None, P, P, P,
+                                                               None, None, x, 1, m, sg, P, 2, ws, nbytes, None)
+        assert f(None) == vq.VQ_ERR_NULL
+        assert f(vq.make_desc(64, 1000, 8, 16, 0)) == vq.VQ_ERR_UNSUPPORTED
+        assert f(d, sg=None) == vq.VQ_ERR_NULL
+        assert f(d, ws=None) == vq.VQ_ERR_NULL
+        assert f(d, x=ctypes.c_void_p(0x10008)) == vq.VQ_ERR_ALIGN
+        assert f(d, nbytes=need - 1) == vq.VQ_ERR_BUFFER_SIZE
+        assert f(d, ws=ctypes.c_void_p(0x10010)) == vq.VQ_ERR_ALIGN
+        assert f(d, m=0) == vq.VQ_OK
+    assert vq.lib().vq_gemv_ws_rht(ctypes.byref(d), P, P, P, None, None, P, 1, 17, P, P, 2, P, 1 << 30,
+                                   None) == vq.VQ_ERR_SHAPE
 
 
 def test_gemv_noalloc_validation_paths(vq):

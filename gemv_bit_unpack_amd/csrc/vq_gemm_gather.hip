@@ -9,9 +9,9 @@
 // same value as rounding the fp32 sum), and passes the vector to the matrix core: no
 // weight tile goes through LDS and each vector is rebuilt once per batch chunk of 128
 // rows.  The A operand is the activation tile (batch rows x 16 k), held in LDS and shared
-// by the workgroup's 8 wavefronts.
-//   - workgroup: 256 output rows (wavefront w owns rows 32w .. 32w + 31, lane l the row
-//     l % 32) x one batch chunk (<= 128 rows) x one range of K-tiles (a K split);
+// by the workgroup's 7 or 8 wavefronts.
+//   - workgroup: 224 or 256 output rows (wavefront w owns rows 32w .. 32w + 31, lane l the
+//     row l % 32) x one batch chunk (<= 128 rows) x one range of K-tiles (a K split);
 //   - K-tile: 16 vectors (128 columns) per row; lane l supplies vectors 8 (l / 32) ..
 //     8 (l / 32) + 7 of it, one per matrix step, so its 8 indices are one 16-byte load and
 //     its 8 residual indices one 8-byte load;
@@ -32,8 +32,7 @@ namespace {
 
 using vqi::ProductArgs;
 
-constexpr int kThreads = 512;  // 8 wavefronts
-constexpr int kRowsWG = 256;   // output rows per workgroup
+constexpr int kRowsWG = 256;   // output rows per workgroup at most (8 wavefronts)
 constexpr int kTileV = 16;     // vectors per K-tile
 constexpr int kMC = 128;       // batch rows per chunk
 constexpr int kXRow = 17;      // 16-byte units per batch row of an activation tile (16 + 1 pad)
@@ -44,7 +43,7 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 
 struct GatherCfg {
-  int32_t n_rb;         // row blocks of 256 rows
+  int32_t n_rb;         // row blocks of 32 * WV rows
   int32_t ks;           // K splits
   int32_t tps;          // K-tiles per split (even)
   int32_t n_kt;         // K-tiles of 16 vectors
@@ -112,8 +111,13 @@ __device__ __forceinline__ void gather8(__amdgpu_buffer_rsrc_t bc, const uint4& 
   c[7] = ld16(bc, word_x16<1>(iw.w), 0);
 }
 
-template <int NB, bool RES>
-__global__ __launch_bounds__(kThreads) void gemm_gather_kernel(ProductArgs a, GatherCfg g) {
+// WV wavefronts (7 or 8) per workgroup, one per 32 output rows: the host picks the count
+// that makes row blocks x K splits fill the CUs.
+template <int NB, bool RES, int WV>
+__global__ __launch_bounds__(512) void gemm_gather_kernel(ProductArgs a, GatherCfg g) {
+  constexpr int kThreadsW = 64 * WV;
+  constexpr int kXPass = kThreadsW / 16;                // activation rows staged per pass
+  constexpr int kXP = (32 * NB + kXPass - 1) / kXPass;  // passes over the chunk's 32 NB rows
   constexpr int kXBuf = 32 * NB * kXRow;  // 16-byte units per activation buffer
   constexpr int kResAt = 0;
   constexpr int kXAt = RES ? kRes : 0;
@@ -132,7 +136,7 @@ __global__ __launch_bounds__(kThreads) void gemm_gather_kernel(ProductArgs a, Ga
   const int mc = rest / g.n_rb;
   const int kt0 = split * g.tps;
   const int kt1 = min(kt0 + g.tps, g.n_kt);
-  const int row = rb * kRowsWG + wave * 32 + l32;
+  const int row = rb * 32 * WV + wave * 32 + l32;
   const int m0 = mc * kMC;
   const int M = a.m, N = a.n, IN = a.in_features;
   const uint32_t s1b = (uint32_t)a.s1_words * 4u;
@@ -146,25 +150,29 @@ __global__ __launch_bounds__(kThreads) void gemm_gather_kernel(ProductArgs a, Ga
   const __amdgpu_buffer_rsrc_t bx = span(g.x16, (uint32_t)M * (uint32_t)IN * 2u);
   const uint32_t v_idx = (uint32_t)row * s1b + (uint32_t)kg * 16u;
   const uint32_t v_res = (uint32_t)row * s2b + (uint32_t)kg * 8u;
-  // activation staging: thread tid moves 16-byte unit tid % 16 of batch rows tid / 16 + 32 h
+  // activation staging: thread tid moves 16-byte unit tid % 16 of batch rows
+  // tid / 16 + kXPass h (rows past the chunk's 32 NB are not stored)
   const int xr = tid >> 4, xu = tid & 15;
-  uint32_t v_x[NB];
+  uint32_t v_x[kXP];
 #pragma unroll
-  for (int h = 0; h < NB; ++h) v_x[h] = ((uint32_t)(m0 + xr + 32 * h) * (uint32_t)IN + (uint32_t)xu * 8u) * 2u;
+  for (int h = 0; h < kXP; ++h)
+    v_x[h] = ((uint32_t)(m0 + xr + kXPass * h) * (uint32_t)IN + (uint32_t)xu * 8u) * 2u;
 
-  auto load_x = [&](int kt, uint4 (&xs)[NB]) __attribute__((always_inline)) {
+  auto load_x = [&](int kt, uint4 (&xs)[kXP]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int h = 0; h < NB; ++h) xs[h] = ld16(bx, v_x[h], (uint32_t)kt * (kTileV * 16u));
+    for (int h = 0; h < kXP; ++h) xs[h] = ld16(bx, v_x[h], (uint32_t)kt * (kTileV * 16u));
   };
   // columns past IN (a ragged last tile) must be zero: they would read the next batch row.
   // A mask, not a select: a branch here would make the compiler wait for every load in
   // flight where the paths join.
-  auto store_x = [&](int kt, int buf, uint4 (&xs)[NB]) __attribute__((always_inline)) {
+  auto store_x = [&](int kt, int buf, uint4 (&xs)[kXP]) __attribute__((always_inline)) {
     const uint32_t keep = 0u - (uint32_t)(kt * (kTileV * 8) + xu * 8 < IN);
 #pragma unroll
-    for (int h = 0; h < NB; ++h) {
-      xt[buf * kXBuf + (xr + 32 * h) * kXRow + xu] =
-          make_uint4(xs[h].x & keep, xs[h].y & keep, xs[h].z & keep, xs[h].w & keep);
+    for (int h = 0; h < kXP; ++h) {
+      if (kXPass * kXP == 32 * NB || xr + kXPass * h < 32 * NB) {
+        xt[buf * kXBuf + (xr + kXPass * h) * kXRow + xu] =
+            make_uint4(xs[h].x & keep, xs[h].y & keep, xs[h].z & keep, xs[h].w & keep);
+      }
     }
   };
 
@@ -174,7 +182,7 @@ __global__ __launch_bounds__(kThreads) void gemm_gather_kernel(ProductArgs a, Ga
   const uint4 rbk = (RES && tid < kRes) ? ((const uint4*)a.cb2)[tid] : make_uint4(0u, 0u, 0u, 0u);
   const int32_t ex = (tid < kMC && g.xexp) ? g.xexp[min(m0 + tid, M - 1)] : 0;
   uint4 iwA = ld16(b1, v_idx, (uint32_t)kt0 * (kTileV * 2u));
-  uint4 xs[NB];
+  uint4 xs[kXP];
   load_x(kt0, xs);
   __builtin_amdgcn_sched_barrier(0);
   uint4 iwB = ld16(b1, v_idx, (uint32_t)min(kt0 + 1, kt1 - 1) * (kTileV * 2u));
@@ -282,29 +290,42 @@ __global__ __launch_bounds__(kThreads) void gemm_gather_kernel(ProductArgs a, Ga
 
 struct Plan {
   GatherCfg cfg;
-  int nb;
+  int nb, wv;
   size_t x16_off, exp_off, part_off, bytes;
 };
 
 size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
-// 256-row blocks x batch chunks; the K range is split (into an even number of tiles per
-// split) until about three quarters of the CUs have a workgroup, keeping at least two
-// tiles per split.
+// Row blocks of 32 WV rows x batch chunks; the K range is split (into an even number of
+// tiles per split) until about three quarters of the CUs have a workgroup, keeping at
+// least two tiles per split.  WV is 8, or 7 when that fills the 256 CUs in fewer rounds'
+// worth of idle CUs (the 28672-row layer: 128 blocks of 224 rows x 2 splits = 256
+// workgroups, against 112 x 2 = 224 with 8).
 Plan make_plan(int32_t n, int32_t in_features, int32_t m, bool bf16, bool rht = false) {
   Plan p{};
   GatherCfg& g = p.cfg;
   const int nv = in_features / 8;
   g.n_kt = (nv + kTileV - 1) / kTileV;
-  g.n_rb = (n + kRowsWG - 1) / kRowsWG;
   const int n_mc = (m + kMC - 1) / kMC;
-  const int base = g.n_rb * n_mc;
-  int ks = 1;
-  while (base * ks < 192 && ks < 16 && g.n_kt >= 4 * ks) ks *= 2;
-  int tps = (g.n_kt + ks - 1) / ks;
-  tps += tps & 1;
-  g.tps = tps;
-  g.ks = (g.n_kt + tps - 1) / tps;
+  long best_idle = -1;
+  for (int wv = 8; wv >= 7; --wv) {
+    const int n_rb = (n + 32 * wv - 1) / (32 * wv);
+    const int base = n_rb * n_mc;
+    int ks = 1;
+    while (base * ks < 192 && ks < 16 && g.n_kt >= 4 * ks) ks *= 2;
+    int tps = (g.n_kt + ks - 1) / ks;
+    tps += tps & 1;
+    const int ks_eff = (g.n_kt + tps - 1) / tps;
+    const long units = (long)base * ks_eff;
+    const long idle = (units + 255) / 256 * 256 - units;  // CU slots left empty in the last round
+    if (best_idle < 0 || idle < best_idle) {
+      best_idle = idle;
+      p.wv = wv;
+      g.n_rb = n_rb;
+      g.tps = tps;
+      g.ks = ks_eff;
+    }
+  }
   const int mr = m < kMC ? m : kMC;
   p.nb = (mr + 31) / 32;
   p.x16_off = 0;
@@ -315,14 +336,15 @@ Plan make_plan(int32_t n, int32_t in_features, int32_t m, bool bf16, bool rht = 
   return p;
 }
 
-template <bool RES>
+template <bool RES, int WV>
 vq_status launch_nb(const ProductArgs& a, const GatherCfg& g, int nb, int n_mc, hipStream_t s) {
   const unsigned grid = (unsigned)g.ks * (unsigned)g.n_rb * (unsigned)n_mc;
+  const dim3 block(64 * WV);
   switch (nb) {
-    case 1: hipLaunchKernelGGL((gemm_gather_kernel<1, RES>), dim3(grid), dim3(kThreads), 0, s, a, g); break;
-    case 2: hipLaunchKernelGGL((gemm_gather_kernel<2, RES>), dim3(grid), dim3(kThreads), 0, s, a, g); break;
-    case 3: hipLaunchKernelGGL((gemm_gather_kernel<3, RES>), dim3(grid), dim3(kThreads), 0, s, a, g); break;
-    default: hipLaunchKernelGGL((gemm_gather_kernel<4, RES>), dim3(grid), dim3(kThreads), 0, s, a, g); break;
+    case 1: hipLaunchKernelGGL((gemm_gather_kernel<1, RES, WV>), dim3(grid), block, 0, s, a, g); break;
+    case 2: hipLaunchKernelGGL((gemm_gather_kernel<2, RES, WV>), dim3(grid), block, 0, s, a, g); break;
+    case 3: hipLaunchKernelGGL((gemm_gather_kernel<3, RES, WV>), dim3(grid), block, 0, s, a, g); break;
+    default: hipLaunchKernelGGL((gemm_gather_kernel<4, RES, WV>), dim3(grid), block, 0, s, a, g); break;
   }
   return hipGetLastError() == hipSuccess ? VQ_OK : VQ_ERR_HIP;
 }
@@ -340,7 +362,7 @@ bool gather_gemm_shape_ok(const vq_desc& d, int32_t m, vq_dtype x_dtype) {
   const uint64_t s2 = (uint64_t)row_stride(d.in_features, 8, d.bits2);
   const uint64_t rows = (uint64_t)d.out_features + kRowsWG;
   if (rows * s1 >= ((uint64_t)1 << 32) || rows * s2 >= ((uint64_t)1 << 32)) return false;
-  if (((uint64_t)m + kMC) * (uint64_t)d.in_features * 2u >= ((uint64_t)1 << 32)) return false;
+  if (((uint64_t)m + kMC + 32) * (uint64_t)d.in_features * 2u >= ((uint64_t)1 << 32)) return false;
   return true;
 }
 
@@ -378,7 +400,10 @@ vq_status launch_gemm_gather(const ProductArgs& a, void* workspace, void* stream
     p.cfg.xexp = nullptr;
   }
   const int n_mc = (a.m + kMC - 1) / kMC;
-  const vq_status st = a.bits2 == 8 ? launch_nb<true>(a, p.cfg, p.nb, n_mc, s) : launch_nb<false>(a, p.cfg, p.nb, n_mc, s);
+  const vq_status st = a.bits2 == 8 ? (p.wv == 7 ? launch_nb<true, 7>(a, p.cfg, p.nb, n_mc, s)
+                                                  : launch_nb<true, 8>(a, p.cfg, p.nb, n_mc, s))
+                                     : (p.wv == 7 ? launch_nb<false, 7>(a, p.cfg, p.nb, n_mc, s)
+                                                  : launch_nb<false, 8>(a, p.cfg, p.nb, n_mc, s));
   if (st != VQ_OK || p.cfg.ks == 1) return st;
   return launch_partials_finalize(a, p.cfg.part, p.cfg.xexp, p.cfg.ks, stream);
 }

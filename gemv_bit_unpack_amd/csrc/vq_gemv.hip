@@ -359,6 +359,7 @@ constexpr int kNumCU = 256;
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // Dwords of one wavefront's LDS area per index stream: a chunk of U groups holds 2 * U * bits
 // dwords per stream; the area rounds the wider stream up to a multiple of 64 dwords.
@@ -617,6 +618,190 @@ vq_status dispatch_gemv6(const ProductArgs& a, hipStream_t s) {
   return a.m >= 2 ? launch_gemv6<2, RK, 2>(a, s) : launch_gemv6<1, RK, 4>(a, s);
 }
 
+// v = 6 with 12-bit fields, one fp16 batch row: both books and x in LDS, the index fields
+// taken straight from registers.
+//
+// Lane l takes the four consecutive vectors 4l .. 4l + 3 of a 256-vector chunk: its 48 bits
+// of each index stream are one 8-byte load (dword 3l / 2, shifted right by 16 (l & 1) bits),
+// its x slice three 16-byte LDS reads at a 48-byte lane stride (no bank conflicts), and the
+// only random LDS reads left are the two centroids per vector (16-byte entries, the residual
+// book 64 KiB above the main one).  Each workgroup owns a block of consecutive rows; its (row, chunk) items
+// are dealt evenly to the 16 wavefronts (a row may be shared by two or three), each
+// wavefront writes its partial sum of a row to an LDS slot, and after a barrier one thread
+// per row adds the slots in wavefront order, then applies the scale and bias.  Index loads
+// are buffer loads bounded by the row, so vectors past its end read index 0 (and meet zero
+// x): no masking.  kX6Depth chunks of index loads are in flight per wavefront.
+constexpr int kX6Chunk = 256;                 // vectors per chunk (4 per lane)
+constexpr int kX6ChunkBytes = kX6Chunk * 12;  // fp16 x bytes per chunk
+constexpr int kX6Depth = 4;                   // chunks of index loads in flight per wavefront
+constexpr int kX6Waves = 16;
+
+inline size_t gemv6x_lds(bool residual, int in_features, int rows_wg) {
+  const int chunks = (int)((vqi::num_vectors(in_features, 6) + kX6Chunk - 1) / kX6Chunk);
+  return (size_t)16 * (residual ? 8192 : 4096) + (size_t)chunks * kX6ChunkBytes + (size_t)rows_wg * kX6Waves * 4;
+}
+
+// Byte offsets in LDS of the four 12-bit fields of a lane's 48 bits (16-byte entries from
+// byte `at`): lo, hi are the dwords holding them, sh (0 or 16) where they start.
+__device__ __forceinline__ void fields12(uint32_t lo, uint32_t hi, uint32_t sh, uint32_t at, uint32_t (&ad)[4]) {
+  const uint32_t w0 = __builtin_amdgcn_alignbit(hi, lo, sh);  // bits sh .. sh + 31
+  const uint32_t w1 = hi >> sh;                               // bits sh + 32 ..
+  ad[0] = ((w0 & 0xFFFu) << 4) + at;
+  ad[1] = (((w0 >> 12) & 0xFFFu) << 4) + at;
+  ad[2] = ((__builtin_amdgcn_alignbit(w1, w0, 24) & 0xFFFu) << 4) + at;
+  ad[3] = (((w1 >> 4) & 0xFFFu) << 4) + at;
+}
+
+template <int RK>
+__global__ __launch_bounds__(1024) void gemv6x_kernel(ProductArgs a, int rows_wg, int chunks) {
+  extern __shared__ uint4 lds_x6[];
+  constexpr int kEntries = RK != 0 ? 8192 : 4096;
+  uint8_t* base = (uint8_t*)lds_x6;
+  const uint8_t* xl = base + (kEntries << 4);
+  float* part = (float*)(base + (kEntries << 4) + chunks * kX6ChunkBytes);
+  const int tid = threadIdx.x;
+  {  // books (all loads of a thread in flight, then the stores) and x, zero past IN
+    uint4 q[kEntries / 1024];
+#pragma unroll
+    for (int b = 0; b < kEntries / 1024; ++b) {
+      const int e = b * 1024 + tid;
+      q[b] = e < 4096 ? gather_global<6>(a.cb1, (uint32_t)e).q[0] : gather_global<6>(a.cb2, (uint32_t)(e - 4096)).q[0];
+    }
+#pragma unroll
+    for (int b = 0; b < kEntries / 1024; ++b) {
+      const int e = b * 1024 + tid;
+      *(uint4*)(base + 16 * e) = q[b];
+    }
+    const int units = chunks * (kX6ChunkBytes / 16), xunits = a.in_features / 8;
+    for (int u = tid; u < units; u += 1024) {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (u < xunits) v = ((const uint4*)a.x)[u];
+      ((uint4*)(base + (kEntries << 4)))[u] = v;
+    }
+  }
+  __syncthreads();
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int row0 = blockIdx.x * rows_wg;
+  const int nrows = min(rows_wg, a.n - row0);
+  const int items = nrows * chunks;
+  const int i0 = wave * items / kX6Waves, i1 = (wave + 1) * items / kX6Waves;
+  if (i1 > i0) {
+    const uint32_t sh = (uint32_t)(lane & 1) << 4;
+    const int voff = 4 * ((3 * lane) >> 1);
+    // consumed item (it, cr, cc) and prefetched item (pr, pc), uniform
+    int it = i0, cr = i0 / chunks, cc = i0 - cr * chunks;
+    int pr = cr, pc = cc;
+    auto fetch = [&](uint32_t (&q)[4]) __attribute__((always_inline)) {
+      const int row = row0 + min(pr, nrows - 1);
+      const __amdgpu_buffer_rsrc_t b1 = rsrc6(a.packed1 + (size_t)row * a.s1_words, 4u * (uint32_t)a.s1_words);
+      const u32x2_t v1 = __builtin_amdgcn_raw_buffer_load_b64(b1, voff, pc * 384, 0);
+      q[0] = v1.x;
+      q[1] = v1.y;
+      if constexpr (RK != 0) {
+        const __amdgpu_buffer_rsrc_t b2 = rsrc6(a.packed2 + (size_t)row * a.s2_words, 4u * (uint32_t)a.s2_words);
+        const u32x2_t v2 = __builtin_amdgcn_raw_buffer_load_b64(b2, voff, pc * 384, 0);
+        q[2] = v2.x;
+        q[3] = v2.y;
+      }
+      if (++pc == chunks) {
+        pc = 0;
+        ++pr;
+      }
+    };
+    // one accumulator per vector slot (each vector's main then residual terms stay in order)
+    float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    auto step = [&](uint32_t (&q)[4]) __attribute__((always_inline)) {
+      uint32_t ad1[4], ad2[4];
+      fields12(q[0], q[1], sh, 0u, ad1);
+      if constexpr (RK != 0) fields12(q[2], q[3], sh, 65536u, ad2);
+      fetch(q);  // the item kX6Depth ahead into the same registers
+      const uint4* xp = (const uint4*)(xl + cc * kX6ChunkBytes + 48 * lane);
+      const uint4 x0 = xp[0], x1 = xp[1], x2 = xp[2];
+      u32x4_t e1[4], e2[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        e1[u] = *(const u32x4_t*)(base + ad1[u]);
+        if constexpr (RK != 0) e2[u] = *(const u32x4_t*)(base + ad2[u]);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // every LDS read of the step in flight before the first product
+      const uint32_t xw[12] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w, x2.x, x2.y, x2.z, x2.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t xv[3] = {xw[3 * u], xw[3 * u + 1], xw[3 * u + 2]};
+        acc[u] = dot6(make_uint4(e1[u].x, e1[u].y, e1[u].z, 0u), xv, acc[u]);
+        if constexpr (RK != 0) acc[u] = dot6(make_uint4(e2[u].x, e2[u].y, e2[u].z, 0u), xv, acc[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {  // whole 16-byte entries read: ds_read_b128, not b96 + b32
+        asm volatile("" ::"v"(e1[u]));
+        if constexpr (RK != 0) asm volatile("" ::"v"(e2[u]));
+      }
+      if (it < i1 && (cc == chunks - 1 || it == i1 - 1)) {  // this wavefront's share of row cr ends
+        const float r = wave_sum((acc[0] + acc[1]) + (acc[2] + acc[3]));
+        if (lane == 0) part[cr * kX6Waves + wave] = r;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[u] = 0.0f;
+      }
+      ++it;
+      if (++cc == chunks) {
+        cc = 0;
+        ++cr;
+      }
+    };
+    uint32_t s0[4], s1[4], s2[4], s3[4];
+    static_assert(kX6Depth == 4, "four register sets in turn");
+    fetch(s0);
+    fetch(s1);
+    fetch(s2);
+    fetch(s3);
+    // four steps per trip, one exit test; past the wavefront's last item the steps run on
+    // in-bounds repeat data and record nothing
+    for (int t = i0; t < i1; t += kX6Depth) {
+      step(s0);
+      step(s1);
+      step(s2);
+      step(s3);
+    }
+  }
+  __syncthreads();
+  if (tid < nrows) {  // row tid: the slots of the wavefronts whose items cover it, in order
+    float r = 0.0f;
+    for (int w = 0; w < kX6Waves; ++w) {
+      const int w0 = w * items / kX6Waves, w1 = (w + 1) * items / kX6Waves;
+      if (w1 > w0 && w1 > tid * chunks && w0 < (tid + 1) * chunks) r += part[tid * kX6Waves + w];
+    }
+    const int row = row0 + tid;
+    if (a.scale) r = r * vqd::f16_to_f32(a.scale[row]);
+    if (a.bias) r = r + vqd::f16_to_f32(a.bias[row]);
+    vqd::store_out(a.y, (size_t)row, r, a.y_dtype);
+  }
+}
+
+// Rows per workgroup for the x-in-LDS kernel (0: the shape does not fit it).
+inline int gemv6x_rows(const ProductArgs& a) {
+  const int grid = a.n < kNumCU ? a.n : kNumCU;
+  const int rows = (a.n + grid - 1) / grid;
+  if (rows > 1024) return 0;  // one thread per row adds the slots
+  return gemv6x_lds(a.bits2 != 0, a.in_features, rows) <= 160u * 1024u ? rows : 0;
+}
+
+template <int RK>
+vq_status launch_gemv6x(const ProductArgs& a, int rows_wg, hipStream_t s) {
+  auto kern = gemv6x_kernel<RK>;
+  static std::once_flag once;
+  static hipError_t attr_err = hipSuccess;
+  std::call_once(once, [&] {
+    attr_err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+  });
+  if (attr_err != hipSuccess) return VQ_ERR_HIP;
+  const int chunks = (a.nv + kX6Chunk - 1) / kX6Chunk;
+  const unsigned grid = (unsigned)((a.n + rows_wg - 1) / rows_wg);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(1024), gemv6x_lds(RK != 0, a.in_features, rows_wg), s, a, rows_wg,
+                     chunks);
+  return hipGetLastError() == hipSuccess ? VQ_OK : VQ_ERR_HIP;
+}
+
 template <int V, int MT, int XT, int IB1, int RK, int UQ>  // UQ: vectors per lane for MT <= 2
 vq_status launch_fast(const ProductArgs& a, hipStream_t s) {
   // vectors in flight per lane: fewer for wide centroids and large batches (registers)
@@ -672,6 +857,12 @@ vq_status dispatch_books(const ProductArgs& a, hipStream_t s) {
   const bool main16 = a.bits1 == 16;
   if constexpr (V == 6) {
     // fp16 activations, decode batches, both books in LDS (with room for the index areas)
+    // one batch row, 12-bit fields, IN a multiple of 8 and a 16-byte aligned x: x in LDS too
+    if (XT == 0 && a.m == 1 && a.bits1 == 12 && (a.bits2 == 0 || a.bits2 == 12) && a.in_features % 8 == 0 &&
+        vqi::aligned(a.x, 16)) {
+      const int rows = gemv6x_rows(a);
+      if (rows > 0) return a.bits2 ? launch_gemv6x<1>(a, rows, s) : launch_gemv6x<0>(a, rows, s);
+    }
     if (XT == 0 && a.m <= 2 && !main16 && a.in_features >= 6 && a.n <= 64 * 16 * kNumCU &&
         gemv6_lds(4, a.bits1, a.bits2) <= 160u * 1024u) {
       return a.bits2 ? dispatch_gemv6<1>(a, s) : dispatch_gemv6<0>(a, s);

@@ -142,6 +142,10 @@ def test_gemv_parity_workloads(vq, key, layer, m):
     # the gather kernel takes 4 vectors per lane for rows of <= 512 vectors at M <= 2, else 8
     (96, 4096, 8, 16, 8, 2, "f16", True, True),     # 512 vectors: two steps of 4 per lane
     (96, 4104, 8, 16, 0, 1, "bf16", False, True),   # 513 vectors: 8 per lane, ragged last group
+    # v = 6, fp16 x, M = 1, 12-bit fields, IN % 8 == 0: books and x in LDS, fields from registers
+    (1000, 4104, 6, 12, 12, 1, "f16", True, True),  # 4 rows per workgroup, 12 items over 16 wavefronts
+    (3000, 2048, 6, 12, 0, 1, "f16", True, False),  # 12 rows per workgroup; no residual
+    (5, 48, 6, 12, 12, 1, "f16", False, True),      # five workgroups of one row, one chunk each
     # v = 6, fp16 x, M <= 2, books in LDS: the packed-dot kernel with LDS-staged index chunks
     (1000, 4100, 6, 12, 12, 1, "f16", True, True),  # last vector keeps 2 lanes
     (333, 1538, 6, 11, 9, 2, "f16", False, True),   # odd index widths; 257 vectors: two chunks
@@ -175,10 +179,12 @@ def test_gemv_one_hot_columns_bit_exact(vq, n, i, v, b1, b2):
     assert np.array_equal(y, w32[:, cols].T)  # == comparison: +0 and -0 both accepted
 
 
-@pytest.mark.parametrize("n,i,b2,m", [(48, 96, 12, 1), (40, 4100, 0, 1), (33, 1538, 9, 2)])
+@pytest.mark.parametrize("n,i,b2,m", [(48, 96, 12, 1), (40, 4100, 0, 1), (33, 1538, 9, 2), (300, 1544, 12, 1),
+                                      (20, 1544, 0, 1)])
 def test_gemv6_one_hot_columns_bit_exact(vq, n, i, b2, m):
-    """The v = 6 packed-dot kernel (fp16 x, M <= 2): a one-hot x still gives the exact fp32
-    W^ entry, main centroid added first."""
+    """The v = 6 packed-dot kernels (fp16 x, M <= 2; IN % 8 == 0 with 12-bit fields at M = 1
+    takes the x-in-LDS one): a one-hot x still gives the exact fp32 W^ entry, main centroid
+    added first."""
     lay = synth.make_layer(n, i, 6, 12, b2, wid=76, copy=i)
     dl = DeviceLayer(vq, lay)
     w32 = oracle_w(lay)

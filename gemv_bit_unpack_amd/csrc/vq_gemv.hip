@@ -641,20 +641,40 @@ inline size_t gemv6x_lds(bool residual, int in_features, int rows_wg) {
   return (size_t)16 * (residual ? 8192 : 4096) + (size_t)chunks * kX6ChunkBytes + (size_t)rows_wg * kX6Waves * 4;
 }
 
+// Sum over the wavefront without LDS traffic: within each row of 16 lanes by DPP (swap
+// neighbours, swap pairs, rotate by 4, rotate by 8), then the four row sums.  Uniform result.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v += dpp_f32<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp_f32<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp_f32<0x124>(v);  // row_ror 4
+  v += dpp_f32<0x128>(v);  // row_ror 8
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return (r0 + r1) + (r2 + r3);
+}
+
 // Byte offsets in LDS of the four 12-bit fields of a lane's 48 bits (16-byte entries from
 // byte `at`): lo, hi are the dwords holding them, sh (0 or 16) where they start.
 __device__ __forceinline__ void fields12(uint32_t lo, uint32_t hi, uint32_t sh, uint32_t at, uint32_t (&ad)[4]) {
   const uint32_t w0 = __builtin_amdgcn_alignbit(hi, lo, sh);  // bits sh .. sh + 31
   const uint32_t w1 = hi >> sh;                               // bits sh + 32 ..
-  ad[0] = ((w0 & 0xFFFu) << 4) + at;
-  ad[1] = (((w0 >> 12) & 0xFFFu) << 4) + at;
-  ad[2] = ((__builtin_amdgcn_alignbit(w1, w0, 24) & 0xFFFu) << 4) + at;
-  ad[3] = (((w1 >> 4) & 0xFFFu) << 4) + at;
+  ad[0] = ((w0 << 4) & 0xFFF0u) | at;
+  ad[1] = ((w0 >> 8) & 0xFFF0u) | at;
+  ad[2] = ((__builtin_amdgcn_alignbit(w1, w0, 24) << 4) & 0xFFF0u) | at;
+  ad[3] = (w1 & 0xFFF0u) | at;
 }
 
 template <int RK>
 __global__ __launch_bounds__(1024) void gemv6x_kernel(ProductArgs a, int rows_wg, int chunks) {
-  extern __shared__ uint4 lds_x6[];
+  // one workgroup per CU: all of the LDS, statically (addresses known when compiling)
+  __shared__ uint4 lds_x6[160 * 1024 / 16];
   constexpr int kEntries = RK != 0 ? 8192 : 4096;
   uint8_t* base = (uint8_t*)lds_x6;
   const uint8_t* xl = base + (kEntries << 4);
@@ -711,34 +731,46 @@ __global__ __launch_bounds__(1024) void gemv6x_kernel(ProductArgs a, int rows_wg
     };
     // one accumulator per vector slot (each vector's main then residual terms stay in order)
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    auto step = [&](uint32_t (&q)[4]) __attribute__((always_inline)) {
+    // An item's LDS reads (x slice, centroids) are issued one step before its products, so a
+    // wavefront always has the next item's reads in flight while it multiplies.
+    int nc = cc;  // chunk of the item whose reads are issued next
+    auto issue = [&](uint32_t (&q)[4], u32x4_t (&bx)[3], u32x4_t (&be1)[4], u32x4_t (&be2)[4])
+                     __attribute__((always_inline)) {
       uint32_t ad1[4], ad2[4];
       fields12(q[0], q[1], sh, 0u, ad1);
       if constexpr (RK != 0) fields12(q[2], q[3], sh, 65536u, ad2);
+      // the fields are out of q before its refill is issued, so the refill lands in the same
+      // registers (no copies where the loop turns, which would wait for the loads)
+      asm volatile("" ::"v"(ad1[0]), "v"(ad1[1]), "v"(ad1[2]), "v"(ad1[3]) : "memory");
+      if constexpr (RK != 0) asm volatile("" ::"v"(ad2[0]), "v"(ad2[1]), "v"(ad2[2]), "v"(ad2[3]) : "memory");
       fetch(q);  // the item kX6Depth ahead into the same registers
-      const uint4* xp = (const uint4*)(xl + cc * kX6ChunkBytes + 48 * lane);
-      const uint4 x0 = xp[0], x1 = xp[1], x2 = xp[2];
-      u32x4_t e1[4], e2[4];
+      const u32x4_t* xp = (const u32x4_t*)(xl + nc * kX6ChunkBytes + 48 * lane);
+      bx[0] = xp[0];
+      bx[1] = xp[1];
+      bx[2] = xp[2];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        e1[u] = *(const u32x4_t*)(base + ad1[u]);
-        if constexpr (RK != 0) e2[u] = *(const u32x4_t*)(base + ad2[u]);
+        be1[u] = *(const u32x4_t*)(base + ad1[u]);
+        if constexpr (RK != 0) be2[u] = *(const u32x4_t*)(base + ad2[u]);
       }
-      __builtin_amdgcn_sched_barrier(0);  // every LDS read of the step in flight before the first product
-      const uint32_t xw[12] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w, x2.x, x2.y, x2.z, x2.w};
+      if (++nc == chunks) nc = 0;
+    };
+    auto consume = [&](u32x4_t (&bx)[3], u32x4_t (&be1)[4], u32x4_t (&be2)[4]) __attribute__((always_inline)) {
+      const uint32_t xw[12] = {bx[0].x, bx[0].y, bx[0].z, bx[0].w, bx[1].x, bx[1].y,
+                               bx[1].z, bx[1].w, bx[2].x, bx[2].y, bx[2].z, bx[2].w};
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const uint32_t xv[3] = {xw[3 * u], xw[3 * u + 1], xw[3 * u + 2]};
-        acc[u] = dot6(make_uint4(e1[u].x, e1[u].y, e1[u].z, 0u), xv, acc[u]);
-        if constexpr (RK != 0) acc[u] = dot6(make_uint4(e2[u].x, e2[u].y, e2[u].z, 0u), xv, acc[u]);
+        acc[u] = dot6(make_uint4(be1[u].x, be1[u].y, be1[u].z, 0u), xv, acc[u]);
+        if constexpr (RK != 0) acc[u] = dot6(make_uint4(be2[u].x, be2[u].y, be2[u].z, 0u), xv, acc[u]);
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {  // whole 16-byte entries read: ds_read_b128, not b96 + b32
-        asm volatile("" ::"v"(e1[u]));
-        if constexpr (RK != 0) asm volatile("" ::"v"(e2[u]));
+        asm volatile("" ::"v"(be1[u]));
+        if constexpr (RK != 0) asm volatile("" ::"v"(be2[u]));
       }
       if (it < i1 && (cc == chunks - 1 || it == i1 - 1)) {  // this wavefront's share of row cr ends
-        const float r = wave_sum((acc[0] + acc[1]) + (acc[2] + acc[3]));
+        const float r = wave_sum_dpp((acc[0] + acc[1]) + (acc[2] + acc[3]));
         if (lane == 0) part[cr * kX6Waves + wave] = r;
 #pragma unroll
         for (int u = 0; u < 4; ++u) acc[u] = 0.0f;
@@ -755,13 +787,40 @@ __global__ __launch_bounds__(1024) void gemv6x_kernel(ProductArgs a, int rows_wg
     fetch(s1);
     fetch(s2);
     fetch(s3);
-    // four steps per trip, one exit test; past the wavefront's last item the steps run on
-    // in-bounds repeat data and record nothing
-    for (int t = i0; t < i1; t += kX6Depth) {
-      step(s0);
-      step(s1);
-      step(s2);
-      step(s3);
+    u32x4_t xa[3], a1[4], a2[4], xb[3], b1[4], b2[4];
+    issue(s0, xa, a1, a2);
+    // four steps per trip (the register sets in turn), then the last n % 4 items; the reads
+    // issued for the item after the wavefront's last run on in-bounds data and are dropped
+    const int n_w = i1 - i0;
+    for (int t = n_w / kX6Depth; t > 0; --t) {
+      issue(s1, xb, b1, b2);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(xa, a1, a2);
+      issue(s2, xa, a1, a2);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(xb, b1, b2);
+      issue(s3, xb, b1, b2);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(xa, a1, a2);
+      issue(s0, xa, a1, a2);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(xb, b1, b2);
+    }
+    const int rem = n_w % kX6Depth;
+    if (rem > 0) {
+      issue(s1, xb, b1, b2);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(xa, a1, a2);
+      if (rem > 1) {
+        issue(s2, xa, a1, a2);
+        __builtin_amdgcn_sched_barrier(0);
+        consume(xb, b1, b2);
+        if (rem > 2) {
+          issue(s3, xb, b1, b2);
+          __builtin_amdgcn_sched_barrier(0);
+          consume(xa, a1, a2);
+        }
+      }
     }
   }
   __syncthreads();
@@ -789,16 +848,9 @@ inline int gemv6x_rows(const ProductArgs& a) {
 template <int RK>
 vq_status launch_gemv6x(const ProductArgs& a, int rows_wg, hipStream_t s) {
   auto kern = gemv6x_kernel<RK>;
-  static std::once_flag once;
-  static hipError_t attr_err = hipSuccess;
-  std::call_once(once, [&] {
-    attr_err = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-  });
-  if (attr_err != hipSuccess) return VQ_ERR_HIP;
   const int chunks = (a.nv + kX6Chunk - 1) / kX6Chunk;
   const unsigned grid = (unsigned)((a.n + rows_wg - 1) / rows_wg);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(1024), gemv6x_lds(RK != 0, a.in_features, rows_wg), s, a, rows_wg,
-                     chunks);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(1024), 0, s, a, rows_wg, chunks);
   return hipGetLastError() == hipSuccess ? VQ_OK : VQ_ERR_HIP;
 }
 

@@ -252,6 +252,13 @@ __global__ __launch_bounds__(1024) void gemv_kernel(ProductArgs a, int block, in
           }
         }
       }
+      if constexpr (V == 6) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {  // whole 16-byte LDS entries read: ds_read_b128, not b96
+          if constexpr (kLds1) asm volatile("" ::"v"(c1[u].q[0].w));
+          if constexpr (RK == 1) asm volatile("" ::"v"(c2[u].q[0].w));
+        }
+      }
       if (ng == 0 || !has_next) {  // row finished
         const float s = a.scale ? vqd::f16_to_f32(a.scale[row]) : 1.0f;
         const float b = a.bias ? vqd::f16_to_f32(a.bias[row]) : 0.0f;
@@ -492,10 +499,15 @@ __device__ __forceinline__ void step6(const ProductArgs& a, Walk6& w, int chunks
     }
   }
   uint4 c1[U], c2[U];
+  u32x4_t e1[U], e2[U];  // whole 16-byte entries (ds_read_b128; the fourth word is padding)
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    c1[u] = book1[i1[u]];
-    if constexpr (RK != 0) c2[u] = book2[i2[u]];
+    e1[u] = *(const u32x4_t*)(book1 + i1[u]);
+    c1[u] = make_uint4(e1[u].x, e1[u].y, e1[u].z, 0u);
+    if constexpr (RK != 0) {
+      e2[u] = *(const u32x4_t*)(book2 + i2[u]);
+      c2[u] = make_uint4(e2[u].x, e2[u].y, e2[u].z, 0u);
+    }
   }
 #pragma unroll
   for (int u = 0; u < U; ++u)
@@ -505,6 +517,11 @@ __device__ __forceinline__ void step6(const ProductArgs& a, Walk6& w, int chunks
       if constexpr (RK != 0) r = dot6(c2[u], xc[u][m], r);
       acc[m] = r;
     }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {  // whole 16-byte LDS entries read: ds_read_b128, not b96
+    asm volatile("" ::"v"(e1[u]));
+    if constexpr (RK != 0) asm volatile("" ::"v"(e2[u]));
+  }
   __builtin_amdgcn_wave_barrier();  // this chunk's index reads stay before the next chunk's writes
   if (w.row < a.n && (w.row1 != w.row || w.row1 >= a.n)) {  // row finished
     // the row's scale and bias, loaded at the start into lane w.rk

@@ -652,6 +652,7 @@ constexpr int kX6Chunk = 256;                 // vectors per chunk (4 per lane)
 constexpr int kX6ChunkBytes = kX6Chunk * 12;  // fp16 x bytes per chunk
 constexpr int kX6Depth = 4;                   // chunks of index loads in flight per wavefront
 constexpr int kX6Waves = 16;
+constexpr int kX6Threads = 64 * kX6Waves;
 
 inline size_t gemv6x_lds(bool residual, int in_features, int rows_wg) {
   const int chunks = (int)((vqi::num_vectors(in_features, 6) + kX6Chunk - 1) / kX6Chunk);
@@ -682,14 +683,14 @@ __device__ __forceinline__ float wave_sum_dpp(float v) {
 __device__ __forceinline__ void fields12(uint32_t lo, uint32_t hi, uint32_t sh, uint32_t at, uint32_t (&ad)[4]) {
   const uint32_t w0 = __builtin_amdgcn_alignbit(hi, lo, sh);  // bits sh .. sh + 31
   const uint32_t w1 = hi >> sh;                               // bits sh + 32 ..
-  ad[0] = ((w0 << 4) & 0xFFF0u) | at;
-  ad[1] = ((w0 >> 8) & 0xFFF0u) | at;
-  ad[2] = ((__builtin_amdgcn_alignbit(w1, w0, 24) << 4) & 0xFFF0u) | at;
-  ad[3] = (w1 & 0xFFF0u) | at;
+  ad[0] = (__builtin_amdgcn_ubfe(w0, 0, 12) << 4) | at;
+  ad[1] = (__builtin_amdgcn_ubfe(w0, 12, 12) << 4) | at;
+  ad[2] = ((__builtin_amdgcn_alignbit(w1, w0, 24) & 0xFFFu) << 4) | at;
+  ad[3] = (__builtin_amdgcn_ubfe(w1, 4, 12) << 4) | at;
 }
 
 template <int RK>
-__global__ __launch_bounds__(1024) void gemv6x_kernel(ProductArgs a, int rows_wg, int chunks) {
+__global__ __launch_bounds__(kX6Threads) void gemv6x_kernel(ProductArgs a, int rows_wg, int chunks) {
   // one workgroup per CU: all of the LDS, statically (addresses known when compiling)
   __shared__ uint4 lds_x6[160 * 1024 / 16];
   constexpr int kEntries = RK != 0 ? 8192 : 4096;
@@ -698,19 +699,19 @@ __global__ __launch_bounds__(1024) void gemv6x_kernel(ProductArgs a, int rows_wg
   float* part = (float*)(base + (kEntries << 4) + chunks * kX6ChunkBytes);
   const int tid = threadIdx.x;
   {  // books (all loads of a thread in flight, then the stores) and x, zero past IN
-    uint4 q[kEntries / 1024];
+    uint4 q[kEntries / kX6Threads];
 #pragma unroll
-    for (int b = 0; b < kEntries / 1024; ++b) {
-      const int e = b * 1024 + tid;
+    for (int b = 0; b < kEntries / kX6Threads; ++b) {
+      const int e = b * kX6Threads + tid;
       q[b] = e < 4096 ? gather_global<6>(a.cb1, (uint32_t)e).q[0] : gather_global<6>(a.cb2, (uint32_t)(e - 4096)).q[0];
     }
 #pragma unroll
-    for (int b = 0; b < kEntries / 1024; ++b) {
-      const int e = b * 1024 + tid;
+    for (int b = 0; b < kEntries / kX6Threads; ++b) {
+      const int e = b * kX6Threads + tid;
       *(uint4*)(base + 16 * e) = q[b];
     }
     const int units = chunks * (kX6ChunkBytes / 16), xunits = a.in_features / 8;
-    for (int u = tid; u < units; u += 1024) {
+    for (int u = tid; u < units; u += kX6Threads) {
       uint4 v = make_uint4(0u, 0u, 0u, 0u);
       if (u < xunits) v = ((const uint4*)a.x)[u];
       ((uint4*)(base + (kEntries << 4)))[u] = v;
@@ -729,21 +730,28 @@ __global__ __launch_bounds__(1024) void gemv6x_kernel(ProductArgs a, int rows_wg
     // consumed item (it, cr, cc) and prefetched item (pr, pc), uniform
     int it = i0, cr = i0 / chunks, cc = i0 - cr * chunks;
     int pr = cr, pc = cc;
+    // the prefetched item's row (past the wavefront's rows: its last one, in-bounds repeat data)
+    const uint32_t* p1 = a.packed1 + (size_t)(row0 + pr) * a.s1_words;
+    const uint32_t* p2 = RK != 0 ? a.packed2 + (size_t)(row0 + pr) * a.s2_words : nullptr;
+    const uint32_t n1 = 4u * (uint32_t)a.s1_words, n2 = 4u * (uint32_t)a.s2_words;
+    int soff = pc * 384;  // the chunk's byte offset in each index stream's row
     auto fetch = [&](uint32_t (&q)[4]) __attribute__((always_inline)) {
-      const int row = row0 + min(pr, nrows - 1);
-      const __amdgpu_buffer_rsrc_t b1 = rsrc6(a.packed1 + (size_t)row * a.s1_words, 4u * (uint32_t)a.s1_words);
-      const u32x2_t v1 = __builtin_amdgcn_raw_buffer_load_b64(b1, voff, pc * 384, 0);
+      const u32x2_t v1 = __builtin_amdgcn_raw_buffer_load_b64(rsrc6(p1, n1), voff, soff, 0);
       q[0] = v1.x;
       q[1] = v1.y;
       if constexpr (RK != 0) {
-        const __amdgpu_buffer_rsrc_t b2 = rsrc6(a.packed2 + (size_t)row * a.s2_words, 4u * (uint32_t)a.s2_words);
-        const u32x2_t v2 = __builtin_amdgcn_raw_buffer_load_b64(b2, voff, pc * 384, 0);
+        const u32x2_t v2 = __builtin_amdgcn_raw_buffer_load_b64(rsrc6(p2, n2), voff, soff, 0);
         q[2] = v2.x;
         q[3] = v2.y;
       }
+      soff += 384;
       if (++pc == chunks) {
         pc = 0;
-        ++pr;
+        soff = 0;
+        if (++pr < nrows) {
+          p1 += a.s1_words;
+          if constexpr (RK != 0) p2 += a.s2_words;
+        }
       }
     };
     // one accumulator per vector slot (each vector's main then residual terms stay in order)
@@ -858,7 +866,7 @@ __global__ __launch_bounds__(1024) void gemv6x_kernel(ProductArgs a, int rows_wg
 inline int gemv6x_rows(const ProductArgs& a) {
   const int grid = a.n < kNumCU ? a.n : kNumCU;
   const int rows = (a.n + grid - 1) / grid;
-  if (rows > 1024) return 0;  // one thread per row adds the slots
+  if (rows > kX6Threads) return 0;  // one thread per row adds the slots
   return gemv6x_lds(a.bits2 != 0, a.in_features, rows) <= 160u * 1024u ? rows : 0;
 }
 
@@ -867,7 +875,7 @@ vq_status launch_gemv6x(const ProductArgs& a, int rows_wg, hipStream_t s) {
   auto kern = gemv6x_kernel<RK>;
   const int chunks = (a.nv + kX6Chunk - 1) / kX6Chunk;
   const unsigned grid = (unsigned)((a.n + rows_wg - 1) / rows_wg);
-  hipLaunchKernelGGL(kern, dim3(grid), dim3(1024), 0, s, a, rows_wg, chunks);
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kX6Threads), 0, s, a, rows_wg, chunks);
   return hipGetLastError() == hipSuccess ? VQ_OK : VQ_ERR_HIP;
 }
 

@@ -367,6 +367,8 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
 
 // Dwords of one wavefront's LDS area per index stream: a chunk of U groups holds 2 * U * bits
 // dwords per stream; the area rounds the wider stream up to a multiple of 64 dwords.
@@ -879,6 +881,252 @@ vq_status launch_gemv6x(const ProductArgs& a, int rows_wg, hipStream_t s) {
   return hipGetLastError() == hipSuccess ? VQ_OK : VQ_ERR_HIP;
 }
 
+// v = 6 with 12-bit fields, 2 <= M <= 16 fp16 batch rows: the same LDS books, the products
+// on the matrix cores.
+//
+// A 16-byte LDS entry is 6 centroid values and two zero halves, which is exactly one lane's
+// A operand of v_mfma_f32_16x16x32_f16 (8 consecutive k of one row): each vector takes 8
+// k slots, the last two multiplying zeros.  Lane l of a wavefront is row l % 16 of a
+// 16-row tile and takes vectors 4 (l / 16) .. + 3 of a 16-vector step, one per matrix
+// instruction, so its 48 bits of each index stream are one 8-byte load, as in the
+// one-row kernel.  Its B operand is x[l % 16][those 6 values] and two zeros: three 16-byte
+// loads per step cover its four vectors (rows past M read zeros, the x buffer ends there).
+// Main and residual entries go through two matrix instructions into the same fp32
+// accumulators: the products are exact and each vector's two terms are summed in fp32, so a
+// one-hot x still returns fp32(c1 + c2).  Lane l ends a tile with rows 4 (l / 16) .. + 3 of
+// output column (batch row) l % 16.
+// A workgroup owns whole tiles; its (tile, step) items are dealt evenly to the 16
+// wavefronts, each writes its partial tile to an LDS slot, and after a barrier the slots are
+// added in wavefront order.  The last step of a row may reach past IN: there the x values
+// past IN (the next batch row's, or zeros) are masked.
+constexpr int kM6Step = 16;  // vectors per step (4 per lane group)
+
+// LDS slots of partial tiles in a workgroup of nt tiles: a tile's slot k belongs to
+// wavefront first + k, first being the first wavefront whose items meet the tile; the most
+// any of the nt tiles needs.
+inline int gemv6m_slots(int nt, int steps) {
+  int most = 0;
+  const int items = nt * steps;
+  for (int t = 0; t < nt; ++t) {
+    int wf = 0;
+    while ((wf + 1) * items / kX6Waves <= t * steps) ++wf;
+    int wl = wf;
+    for (int w = wf; w < kX6Waves; ++w) {
+      const int w0 = w * items / kX6Waves, w1 = (w + 1) * items / kX6Waves;
+      if (w0 >= (t + 1) * steps) break;
+      if (w1 > w0) wl = w;
+    }
+    most = wl - wf + 1 > most ? wl - wf + 1 : most;
+  }
+  return most;
+}
+
+template <int RK>
+__global__ __launch_bounds__(kX6Threads) void gemv6m_kernel(ProductArgs a, int tiles_wg, int steps, int slots_full,
+                                                           int slots_last) {
+  __shared__ uint4 lds_m6[160 * 1024 / 16];
+  constexpr int kEntries = RK != 0 ? 8192 : 4096;
+  uint8_t* base = (uint8_t*)lds_m6;
+  float* part = (float*)(base + (kEntries << 4));  // [tile][slot][16 rows][16 columns]
+  const int tid = threadIdx.x;
+  {
+    uint4 q[kEntries / kX6Threads];
+#pragma unroll
+    for (int b = 0; b < kEntries / kX6Threads; ++b) {
+      const int e = b * kX6Threads + tid;
+      q[b] = e < 4096 ? gather_global<6>(a.cb1, (uint32_t)e).q[0] : gather_global<6>(a.cb2, (uint32_t)(e - 4096)).q[0];
+    }
+#pragma unroll
+    for (int b = 0; b < kEntries / kX6Threads; ++b) {
+      const int e = b * kX6Threads + tid;
+      *(uint4*)(base + 16 * e) = q[b];
+    }
+  }
+  __syncthreads();
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, g4 = lane >> 4;
+  const int tile0 = blockIdx.x * tiles_wg;
+  const int ntiles = min(tiles_wg, (a.n + 15) / 16 - tile0);
+  const int slots = ntiles == tiles_wg ? slots_full : slots_last;  // the last workgroup may hold fewer tiles
+  const int items = ntiles * steps;
+  const int i0 = wave * items / kX6Waves, i1 = (wave + 1) * items / kX6Waves;
+  const uint32_t s1b = 4u * (uint32_t)a.s1_words, s2b = 4u * (uint32_t)a.s2_words;
+  if (i1 > i0) {
+    // one buffer per index stream over all N rows (rows past N read zeros); the lane's row
+    // and window go in the vector offset, the tile and step in the scalar one
+    const __amdgpu_buffer_rsrc_t b1 = rsrc6(a.packed1, (uint32_t)a.n * s1b);
+    const __amdgpu_buffer_rsrc_t b2 = rsrc6(RK != 0 ? a.packed2 : a.packed1, RK != 0 ? (uint32_t)a.n * s2b : 0u);
+    const __amdgpu_buffer_rsrc_t bx = rsrc6(a.x, (uint32_t)a.m * (uint32_t)a.in_features * 2u);
+    const uint32_t row_l = (uint32_t)(tile0 * 16 + r16);
+    const int v1 = (int)(row_l * s1b) + 4 * ((3 * g4) >> 1);
+    const int v2 = (int)(row_l * s2b) + 4 * ((3 * g4) >> 1);
+    const int vx = r16 * a.in_features * 2 + 48 * g4;
+    const uint32_t sh = (uint32_t)(g4 & 1) << 4;
+    const int have_last = a.in_features - 6 * (kM6Step * (steps - 1) + 4 * g4);  // valid halves, last step
+    int it = i0, ct = i0 / steps, cs = i0 - ct * steps;  // consumed item (tile, step)
+    int pt = ct, ps = cs;                                 // prefetched item
+    // the prefetched item's scalar offsets (past the wavefront's tiles: its last one again)
+    int so1 = (int)((uint32_t)(16 * pt) * s1b) + 24 * ps, so2 = (int)((uint32_t)(16 * pt) * s2b) + 24 * ps;
+    int sox = 192 * ps;
+    auto fetch = [&](uint32_t (&q)[4], u32x4_t (&xq)[3]) __attribute__((always_inline)) {
+      const u32x2_t w1 = __builtin_amdgcn_raw_buffer_load_b64(b1, v1, so1, 0);
+      q[0] = w1.x;
+      q[1] = w1.y;
+      if constexpr (RK != 0) {
+        const u32x2_t w2 = __builtin_amdgcn_raw_buffer_load_b64(b2, v2, so2, 0);
+        q[2] = w2.x;
+        q[3] = w2.y;
+      }
+#pragma unroll
+      for (int h = 0; h < 3; ++h)
+        xq[h] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(bx, vx, sox + 16 * h, 0));
+      so1 += 24;
+      so2 += 24;
+      sox += 192;
+      if (++ps == steps) {
+        ps = 0;
+        sox = 0;
+        if (++pt < ntiles) {
+          so1 += (int)(16u * s1b) - 24 * steps;
+          so2 += (int)(16u * s2b) - 24 * steps;
+        } else {
+          so1 -= 24 * steps;
+          so2 -= 24 * steps;
+        }
+      }
+    };
+    float4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+    auto step = [&](uint32_t (&q)[4], u32x4_t (&xq)[3]) __attribute__((always_inline)) {
+      uint32_t ad1[4], ad2[4];
+      fields12(q[0], q[1], sh, 0u, ad1);
+      if constexpr (RK != 0) fields12(q[2], q[3], sh, 65536u, ad2);
+      // the row's last step: x past IN (the next batch row's values) reads as zero; selects
+      // on loop-invariant lane masks, no branch (a branch here makes the other path copy x,
+      // waiting for every load in flight)
+      const bool last = cs == steps - 1;
+      u32x4_t xs[3];
+#pragma unroll
+      for (int h = 0; h < 3; ++h) {
+        xs[h].x = last && 8 * h + 2 > have_last ? 0u : xq[h].x;
+        xs[h].y = last && 8 * h + 4 > have_last ? 0u : xq[h].y;
+        xs[h].z = last && 8 * h + 6 > have_last ? 0u : xq[h].z;
+        xs[h].w = last && 8 * h + 8 > have_last ? 0u : xq[h].w;
+      }
+      // fields and x out of the set before its refill is issued (same registers)
+      asm volatile("" ::"v"(ad1[0]), "v"(ad1[1]), "v"(ad1[2]), "v"(ad1[3]) : "memory");
+      if constexpr (RK != 0) asm volatile("" ::"v"(ad2[0]), "v"(ad2[1]), "v"(ad2[2]), "v"(ad2[3]) : "memory");
+      asm volatile("" ::"v"(xs[0]), "v"(xs[1]), "v"(xs[2]) : "memory");
+      fetch(q, xq);
+      u32x4_t e1[4], e2[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        e1[u] = *(const u32x4_t*)(base + ad1[u]);
+        if constexpr (RK != 0) e2[u] = *(const u32x4_t*)(base + ad2[u]);
+      }
+      const uint32_t xw[12] = {xs[0].x, xs[0].y, xs[0].z, xs[0].w, xs[1].x, xs[1].y,
+                               xs[1].z, xs[1].w, xs[2].x, xs[2].y, xs[2].z, xs[2].w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint4 bfrag = make_uint4(xw[3 * u], xw[3 * u + 1], xw[3 * u + 2], 0u);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, e1[u]),
+                                                   __builtin_bit_cast(half8_t, bfrag), d, 0, 0, 0);
+        if constexpr (RK != 0)
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, e2[u]),
+                                                     __builtin_bit_cast(half8_t, bfrag), d, 0, 0, 0);
+      }
+      if (it < i1 && (cs == steps - 1 || it == i1 - 1)) {  // this wavefront's share of tile ct ends
+        // slot: this wavefront less the first one whose items meet the tile
+        int w = (ct * steps) * kX6Waves / items;  // a lower bound on that first one
+        while ((w + 1) * items / kX6Waves <= ct * steps) ++w;
+        float* dst = part + ((size_t)(ct * slots + (wave - w)) * 256);
+        if (r16 < a.m) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) dst[(4 * g4 + q) * 16 + r16] = d[q];
+        }
+        d = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+      ++it;
+      if (++cs == steps) {
+        cs = 0;
+        ++ct;
+      }
+    };
+    uint32_t q0[4], q1[4], q2[4], q3[4];
+    u32x4_t x0[3], x1[3], x2[3], x3[3];
+    fetch(q0, x0);
+    fetch(q1, x1);
+    fetch(q2, x2);
+    fetch(q3, x3);
+    const int n_w = i1 - i0;
+    for (int t = n_w / 4; t > 0; --t) {
+      step(q0, x0);
+      step(q1, x1);
+      step(q2, x2);
+      step(q3, x3);
+    }
+    const int rem = n_w % 4;
+    if (rem > 0) {
+      step(q0, x0);
+      if (rem > 1) {
+        step(q1, x1);
+        if (rem > 2) step(q2, x2);
+      }
+    }
+  }
+  __syncthreads();
+  // (tile, row, batch row) outputs: the slots of the wavefronts whose items meet the tile,
+  // in wavefront order, then scale and bias
+  for (int o = tid; o < ntiles * 16 * a.m; o += kX6Threads) {
+    const int m = o % a.m, tr = o / a.m;
+    const int t = tr >> 4, rr = tr & 15;
+    const int row = (tile0 + t) * 16 + rr;
+    if (row >= a.n) continue;
+    float r = 0.0f;
+    int wf = (t * steps) * kX6Waves / items;  // the first wavefront whose items meet the tile
+    while ((wf + 1) * items / kX6Waves <= t * steps) ++wf;
+    for (int w = wf; w < kX6Waves; ++w) {
+      const int w0 = w * items / kX6Waves, w1 = (w + 1) * items / kX6Waves;
+      if (w0 >= (t + 1) * steps) break;
+      if (w1 > w0) r += part[(size_t)(t * slots + (w - wf)) * 256 + rr * 16 + m];
+    }
+    if (a.scale) r = r * vqd::f16_to_f32(a.scale[row]);
+    if (a.bias) r = r + vqd::f16_to_f32(a.bias[row]);
+    vqd::store_out(a.y, (size_t)m * a.n + row, r, a.y_dtype);
+  }
+}
+
+// Tiles per workgroup and partial-tile slots (full workgroups, the last one) for the
+// matrix-core v = 6 kernel (false: the shape does not fit it).
+inline bool gemv6m_plan(const ProductArgs& a, int* tiles_wg, int* steps, int* slots_full, int* slots_last) {
+  const int tiles = (a.n + 15) / 16;
+  const int grid = tiles < kNumCU ? tiles : kNumCU;
+  *tiles_wg = (tiles + grid - 1) / grid;
+  *steps = (a.nv + kM6Step - 1) / kM6Step;
+  const int last = tiles - (tiles - 1) / *tiles_wg * *tiles_wg;  // tiles of the last workgroup
+  *slots_full = gemv6m_slots(*tiles_wg, *steps);
+  *slots_last = gemv6m_slots(last, *steps);
+  const size_t books = (size_t)16 * (a.bits2 ? 8192 : 4096);
+  const size_t most = (size_t)*tiles_wg * *slots_full > (size_t)last * *slots_last ? (size_t)*tiles_wg * *slots_full
+                                                                                   : (size_t)last * *slots_last;
+  if (books + most * 1024 > 160u * 1024u) return false;
+  // 32-bit buffer offsets over the index streams and x
+  const uint64_t s1b = 4ull * (uint64_t)a.s1_words, s2b = 4ull * (uint64_t)a.s2_words;
+  const uint64_t rows = (uint64_t)(tiles + 1) * 16;
+  if (rows * s1b >= (1ull << 31) || rows * s2b >= (1ull << 31)) return false;
+  return (uint64_t)16 * (uint64_t)a.in_features * 2u + 192ull * (uint64_t)*steps < (1ull << 31);
+}
+
+template <int RK>
+vq_status launch_gemv6m(const ProductArgs& a, int tiles_wg, int steps, int slots_full, int slots_last,
+                        hipStream_t s) {
+  const int tiles = (a.n + 15) / 16;
+  const unsigned grid = (unsigned)((tiles + tiles_wg - 1) / tiles_wg);
+  hipLaunchKernelGGL(gemv6m_kernel<RK>, dim3(grid), dim3(kX6Threads), 0, s, a, tiles_wg, steps, slots_full,
+                     slots_last);
+  return hipGetLastError() == hipSuccess ? VQ_OK : VQ_ERR_HIP;
+}
+
 template <int V, int MT, int XT, int IB1, int RK, int UQ>  // UQ: vectors per lane for MT <= 2
 vq_status launch_fast(const ProductArgs& a, hipStream_t s) {
   // vectors in flight per lane: fewer for wide centroids and large batches (registers)
@@ -939,6 +1187,13 @@ vq_status dispatch_books(const ProductArgs& a, hipStream_t s) {
         vqi::aligned(a.x, 16)) {
       const int rows = gemv6x_rows(a);
       if (rows > 0) return a.bits2 ? launch_gemv6x<1>(a, rows, s) : launch_gemv6x<0>(a, rows, s);
+    }
+    // 2..16 batch rows, 12-bit fields, IN a multiple of 8 and a 16-byte aligned x: matrix cores
+    if (XT == 0 && a.m >= 2 && a.m <= 16 && a.bits1 == 12 && (a.bits2 == 0 || a.bits2 == 12) &&
+        a.in_features % 8 == 0 && vqi::aligned(a.x, 16)) {
+      int tw = 0, st = 0, sf = 0, sl = 0;
+      if (gemv6m_plan(a, &tw, &st, &sf, &sl))
+        return a.bits2 ? launch_gemv6m<1>(a, tw, st, sf, sl, s) : launch_gemv6m<0>(a, tw, st, sf, sl, s);
     }
     if (XT == 0 && a.m <= 2 && !main16 && a.in_features >= 6 && a.n <= 64 * 16 * kNumCU &&
         gemv6_lds(4, a.bits1, a.bits2) <= 160u * 1024u) {

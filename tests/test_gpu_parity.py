@@ -146,13 +146,19 @@ def test_gemv_parity_workloads(vq, key, layer, m):
     (1000, 4104, 6, 12, 12, 1, "f16", True, True),  # 4 rows per workgroup, 12 items over 16 wavefronts
     (3000, 2048, 6, 12, 0, 1, "f16", True, False),  # 12 rows per workgroup; no residual
     (5, 48, 6, 12, 12, 1, "f16", False, True),      # five workgroups of one row, one chunk each
+    # v = 6, fp16 x, 2 <= M <= 16, 12-bit fields, IN % 8 == 0: the matrix-core kernel
+    (1000, 4104, 6, 12, 12, 16, "f16", True, True),  # 63 tiles, 257-step rows over 16 wavefronts
+    (37, 48, 6, 12, 0, 5, "f16", False, True),       # 3 tiles of one step: most wavefronts idle
+    (5000, 2048, 6, 12, 12, 2, "f16", True, True),   # 2 tiles per workgroup; last tile ragged
+    (300, 4096, 6, 12, 12, 9, "f16", True, False),   # last vector keeps 4 lanes, odd M
     # v = 6, fp16 x, M <= 2, books in LDS: the packed-dot kernel with LDS-staged index chunks
     (1000, 4100, 6, 12, 12, 1, "f16", True, True),  # last vector keeps 2 lanes
     (333, 1538, 6, 11, 9, 2, "f16", False, True),   # odd index widths; 257 vectors: two chunks
     (17, 14336, 6, 12, 0, 1, "f16", True, False),   # no residual, ten chunks per row
     (4099, 96, 6, 12, 12, 2, "f16", True, True),    # more rows than wavefronts in the grid
     (5, 6, 6, 4, 3, 1, "f16", False, False),        # one vector per row
-    (40, 2000, 6, 12, 12, 3, "f16", True, True),    # M = 3: the general v = 6 kernel
+    (40, 2000, 6, 12, 12, 3, "f16", True, True),    # M = 3, IN % 8 == 0: the matrix-core kernel
+    (40, 2002, 6, 12, 12, 3, "f16", True, True),    # M = 3, IN % 8 == 2: the general v = 6 kernel
 ])
 def test_gemv_parity_shapes(vq, n, i, v, b1, b2, m, xd, bias, scale):
     lay = synth.make_layer(n, i, v, b1, b2, wid=71, copy=n, with_scale=scale, with_bias=bias)
@@ -180,11 +186,11 @@ def test_gemv_one_hot_columns_bit_exact(vq, n, i, v, b1, b2):
 
 
 @pytest.mark.parametrize("n,i,b2,m", [(48, 96, 12, 1), (40, 4100, 0, 1), (33, 1538, 9, 2), (300, 1544, 12, 1),
-                                      (20, 1544, 0, 1)])
+                                      (20, 1544, 0, 1), (64, 1544, 12, 4), (40, 200, 0, 16)])
 def test_gemv6_one_hot_columns_bit_exact(vq, n, i, b2, m):
-    """The v = 6 packed-dot kernels (fp16 x, M <= 2; IN % 8 == 0 with 12-bit fields at M = 1
-    takes the x-in-LDS one): a one-hot x still gives the exact fp32 W^ entry, main centroid
-    added first."""
+    """The v = 6 LDS-book kernels (fp16 x; with 12-bit fields and IN % 8 == 0 the x-in-LDS
+    one at M = 1 and the matrix-core one at 2 <= M <= 16): a one-hot x still gives the exact
+    fp32 W^ entry, main centroid added first."""
     lay = synth.make_layer(n, i, 6, 12, b2, wid=76, copy=i)
     dl = DeviceLayer(vq, lay)
     w32 = oracle_w(lay)

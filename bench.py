@@ -590,6 +590,7 @@ def main():
     ap.add_argument("--only-encode", action="store_true", help="run only the residual VQ encode leg (for profiling)")
     ap.add_argument("--only-svq", action="store_true",
                     help="run only the affine-lattice (vq_svq_gemv) leg (for profiling)")
+    ap.add_argument("--m", type=int, default=1, help="batch rows for --only-workload (1..16)")
     ap.add_argument("--only-workload", default=None, choices=sorted(WORKLOADS),
                     help="run only one workload's M=1 leg through vq_gemv_ws (for profiling)")
     args = ap.parse_args()
@@ -647,10 +648,10 @@ def main():
         return
     if args.only_workload:
         key = args.only_workload
-        rings = [Ring(vq, torch, key, li, 1) for li in range(len(WORKLOADS[key][0]))]
+        rings = [Ring(vq, torch, key, li, args.m) for li in range(len(WORKLOADS[key][0]))]
         sec, calls, _, launch = time_ring(torch, rings, args.steps, args.warmup, use_graph)
         b = sum(r.bytes_per_call for r in rings) / len(rings)
-        print(json.dumps({"workload": key, "us_per_call": round(sec * 1e6, 3), "GBps": round(b / sec / 1e9, 1),
+        print(json.dumps({"workload": key, "m": args.m, "us_per_call": round(sec * 1e6, 3), "GBps": round(b / sec / 1e9, 1),
                           "kernel": "codebook-sliced" if any(r.sliced for r in rings) else "gather",
                           "calls": calls, "launch": launch}))
         return
@@ -782,17 +783,20 @@ def main():
                 torch.cuda.empty_cache()
             per[key] = entry
         out["gemv_m1_per_workload"] = per
-        # Decode batches with the 65536-entry book: vq_gemv_ws against vq_gemv.
+        # Decode batches: the 65536-entry book (vq_gemv_ws against vq_gemv) and the v = 6
+        # LDS books (vq_gemv: the matrix-core kernel at 2..16 rows).
         batch = {}
-        for key, m in (("dec4k_res", 4), ("dec4k_res", 16), ("l70b", 8)):
+        for key, m in (("dec4k_res", 4), ("dec4k_res", 16), ("l70b", 8), ("mlp8b", 2), ("mlp8b", 4), ("mlp8b", 16)):
             n_layers = len(WORKLOADS[key][0])
             entry = {}
-            for fn in ("vq_gemv_ws", "vq_gemv"):
+            for fn in (("vq_gemv",) if key == "mlp8b" else ("vq_gemv_ws", "vq_gemv")):
                 rings = [Ring(vq, torch, key, li, m, fn=fn, copies=8) for li in range(n_layers)]
                 s, _, _, _ = time_ring(torch, rings, 64, 8, use_graph)
                 entry[fn + "_us_per_call"] = round(s * 1e6, 3)
                 if fn == "vq_gemv_ws":
                     entry["kernel"] = "codebook-sliced" if any(r.sliced for r in rings) else "gather"
+                elif key == "mlp8b":
+                    entry["kernel"] = "v6 matrix-core"
                 del rings
                 torch.cuda.empty_cache()
             batch["%s_m%d" % (key, m)] = entry

@@ -167,6 +167,26 @@ def test_gemm_ws_deterministic_and_reusable(vq):
     check_y(yb[:, torch.from_numpy(rows).cuda()], oracle_y(b, xbits, "bf16", rows), "f32")
 
 
+@pytest.mark.parametrize("xd", ["bf16", "f16"])
+def test_gemm_ws_two_splits_ragged_chunks(vq, xd):
+    """Two K splits over 90 row blocks of 224 rows (the last ragged) x two batch chunks
+    (128 + 72 rows), bf16 and fp16 activations; repeated calls on a workspace filled with
+    garbage give identical results (the partial sums are added in a fixed order)."""
+    c = synth.make_layer(20000, 2048, 8, 16, 8, wid=96, with_scale=True, with_bias=True)
+    dc = DeviceLayer(vq, c)
+    xc = synth.activations(np.random.default_rng(5), 200, 2048, xd)
+    need = vq.gemm_workspace_bytes(dc.desc, 200, _tdtype(xd))
+    assert need >= 2 * 200 * 20000 * 4
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")
+    y1 = vq.gemm_ws(*dc.args(), x_tensor(xc, xd), ws, y_dtype=torch.float32)
+    y2 = vq.gemm_ws(*dc.args(), x_tensor(xc, xd), ws, y_dtype=torch.float32)
+    ws.fill_(0xFF)
+    y3 = vq.gemm_ws(*dc.args(), x_tensor(xc, xd), ws, y_dtype=torch.float32)
+    assert torch.equal(y1, y2) and torch.equal(y1, y3)
+    rows = np.unique(np.concatenate([sample_rows(20000, 64, seed=6), [0, 223, 224, 19935, 19999]]))
+    check_y(y1[:, torch.from_numpy(rows).cuda()], oracle_y(c, xc, xd, rows), "f32")
+
+
 def test_gemm_ws_fallbacks(vq):
     lay = synth.make_layer(512, 4096, 8, 16, 8, wid=96, with_bias=True)
     dl = DeviceLayer(vq, lay)

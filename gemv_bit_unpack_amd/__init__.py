@@ -7,7 +7,7 @@ path, and nothing here computes.
 
 Calls (same names as the C ABI):
     packed_bytes(desc) -> int
-    pack(desc, idx1, idx2=None) -> numpy uint8 (host packing, layout of vq.h)
+    pack(desc, idx1, idx2=None) -> numpy uint8 (host packing in desc.layout, vq.h)
     dequant(desc, packed, cb1, cb2, scale, w_dtype=torch.float32, out=None) -> W^ [N, IN]
     gemv(desc, packed, cb1, cb2, scale, bias, x, y_dtype=None, out=None)  # 1 <= M <= 16
     gemv_workspace_bytes(desc, m, x_dtype) -> int
@@ -42,6 +42,7 @@ VQ_ERR_HIP = -8
 
 VQ_F16, VQ_BF16, VQ_F32 = 0, 1, 2
 LAYOUT_ROWSTREAM = 1
+LAYOUT_BUCKETED = 2  # slice-bucketed: the batch-1 decode layout of gemv_ws (v = 8, bits1 = 16)
 
 EXPORTED = ("vq_abi_version", "vq_status_string", "vq_packed_bytes", "vq_pack", "vq_dequant", "vq_gemv",
             "vq_gemv_workspace_bytes", "vq_gemv_ws", "vq_gemm", "vq_svq_dequant", "vq_svq_gemv", "vq_rht", "vq_rht_block",
@@ -55,8 +56,8 @@ class Desc(ctypes.Structure):
                 ("bits1", ctypes.c_int32), ("bits2", ctypes.c_int32), ("layout", ctypes.c_int32)]
 
     def __repr__(self):
-        return "Desc(N=%d, IN=%d, v=%d, bits1=%d, bits2=%d)" % (
-            self.out_features, self.in_features, self.v, self.bits1, self.bits2)
+        return "Desc(N=%d, IN=%d, v=%d, bits1=%d, bits2=%d, layout=%d)" % (
+            self.out_features, self.in_features, self.v, self.bits1, self.bits2, self.layout)
 
 
 def make_desc(out_features, in_features, v, bits1, bits2=0, layout=LAYOUT_ROWSTREAM) -> Desc:
@@ -155,7 +156,7 @@ def packed_bytes(desc: Desc) -> int:
 
 
 def pack(desc: Desc, idx1, idx2=None) -> np.ndarray:
-    """Host packing of uint32 indices [N, nv] into the row-stream layout."""
+    """Host packing of uint32 indices [N, nv] into desc.layout (row stream or slice-bucketed)."""
     nv = (desc.in_features + desc.v - 1) // desc.v
     i1 = np.ascontiguousarray(np.asarray(idx1, dtype=np.uint32).reshape(desc.out_features, nv))
     i2 = None
@@ -488,25 +489,40 @@ class VQLinear:
     ``forward(x)`` computes x W^T (+ bias) for x of shape [..., in_features]; batches of
     up to ``gemv_max_m`` rows take gemv_ws (the codebook-sliced kernel where the shape has
     it), larger ones gemm_ws (the matrix-core product fed by the gathering lanes where the
-    shape has it); both with a workspace kept per device and stream.
+    shape has it); both with a workspace kept per device and stream.  With
+    ``decode_packed`` (the same indices in the slice-bucketed layout, ``decode_desc``) a
+    batch of one row takes the bucketed decode product instead.
     """
 
-    def __init__(self, desc: Desc, packed, cb1, cb2=None, scale=None, bias=None, gemv_max_m: int = 16):
+    def __init__(self, desc: Desc, packed, cb1, cb2=None, scale=None, bias=None, gemv_max_m: int = 16,
+                 decode_desc: Desc | None = None, decode_packed=None):
         self.desc = desc
         self.packed, self.cb1, self.cb2, self.scale, self.bias = packed, cb1, cb2, scale, bias
         self.gemv_max_m = min(int(gemv_max_m), 16)
+        self.decode_desc, self.decode_packed = decode_desc, decode_packed
 
     @classmethod
-    def from_indices(cls, desc: Desc, idx1, idx2, cb1, cb2=None, scale=None, bias=None, device="cuda"):
+    def from_indices(cls, desc: Desc, idx1, idx2, cb1, cb2=None, scale=None, bias=None, device="cuda",
+                     decode_layout: bool = False):
+        """Packs the indices (and, with ``decode_layout``, their slice-bucketed copy for
+        batch-1 decode: 32 bits per vector) and uploads them."""
         torch = _torch()
         packed = torch.from_numpy(pack(desc, idx1, idx2)).to(device)
-        return cls(desc, packed, cb1, cb2, scale, bias)
+        ddesc = dpacked = None
+        if decode_layout:
+            ddesc = make_desc(desc.out_features, desc.in_features, desc.v, desc.bits1, desc.bits2, LAYOUT_BUCKETED)
+            dpacked = torch.from_numpy(pack(ddesc, idx1, idx2)).to(device)
+        return cls(desc, packed, cb1, cb2, scale, bias, decode_desc=ddesc, decode_packed=dpacked)
 
     def forward(self, x, y_dtype=None):
         lead = x.shape[:-1]
         x2 = x.reshape(-1, x.shape[-1]).contiguous()
         args = (self.desc, self.packed, self.cb1, self.cb2, self.scale, self.bias, x2)
-        if x2.shape[0] <= self.gemv_max_m:
+        if x2.shape[0] == 1 and self.decode_packed is not None:
+            dargs = (self.decode_desc, self.decode_packed, self.cb1, self.cb2, self.scale, self.bias, x2)
+            ws = stream_workspace(self.decode_desc, 1, x2.dtype, x2.device)
+            y = gemv_ws(*dargs, ws, y_dtype)
+        elif x2.shape[0] <= self.gemv_max_m:
             ws = stream_workspace(self.desc, x2.shape[0], x2.dtype, x2.device)
             y = gemv_ws(*args, ws, y_dtype)
         else:

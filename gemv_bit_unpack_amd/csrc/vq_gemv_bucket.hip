@@ -1,0 +1,403 @@
+// vq_gemv_ws over the slice-bucketed layout (VQ_LAYOUT_BUCKETED): the 65536-entry main
+// book (v = 8) at one batch row, with every weight vector read and used exactly once.
+//
+// The book does not fit one CU's LDS, so it is cut into 8 slices of 8192 centroids and
+// each workgroup holds one slice (the production-VQ post, "Lookup Table (LUT) Overhead vs.
+// Bit-Shifting": lookups must stay in fast memory).  In the row-stream layout every slice
+// workgroup has to look at every index to find its own; here the packer has already
+// sorted each row's vectors by slice: bucket (chunk c, slice s, row o) lists the vectors
+// j of row o with c*1024 <= j < (c+1)*1024 and idx1 >> 13 == s, one 32-bit word each:
+//   bits [0, 10)  j - c*1024      bits [10, 23) idx1 & 8191      bits [23, 31) idx2
+// behind a prefix table start[(c*8 + s)*N + o] of bucket offsets.
+//   - 256 persistent workgroups of 512 threads (8 wavefronts), one per CU; workgroup
+//     (slice s, group p); the 32 workgroups of slice s share one XCD (and its L2 copy of
+//     the slice's centroids);
+//   - a unit is (chunk c, tile of 64 rows); group p takes units p, p + 32, ... in
+//     chunk-major order; the chunk's 1024 activation vectors sit in LDS (reloaded when
+//     the chunk changes, bf16 rewritten as fp16 times 2^-e);
+//   - wavefront w takes rows 8w .. 8w + 7 of the tile; lane l handles words l, l + 64 and
+//     l + 128 of a row's bucket (lanes past its end read zero entries); the rare bucket
+//     longer than 192 words is finished by a loop after the tile's rows;
+//   - per word: three 16-byte LDS reads (x at the position, the main centroid, the
+//     residual centroid) and eight packed fp16 dot products into fp32;
+//   - the next unit's bucket words are loaded while the current unit runs (each row's
+//     words right after its own are consumed), the unit after that's prefix entries one
+//     unit earlier still;
+//   - the 8 rows' lane sums are reduced together (a butterfly that halves the rows held
+//     per lane at each of the first three exchanges) and stored as one fp32 partial per
+//     (chunk, slice, row); the shared finalize kernel adds the 8 * chunks partials of
+//     each output in a fixed order and applies 2^e, scale and bias.
+#include "vq_device.h"
+
+namespace {
+
+using vqi::ProductArgs;
+
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr int kRowsPerWave = 8;
+constexpr int kTileRows = kWaves * kRowsPerWave;  // 64
+constexpr int kSlices = 8;
+constexpr int kSlice = 8192;
+constexpr int kGroups = 32;
+constexpr int kChunk = vqi::kBucketChunk;  // 1024 vectors
+constexpr int kRes = 256;
+constexpr int kSteps = 3;  // bucket words per lane held in registers per row
+
+// LDS, in 16-byte entries: the residual book and a zero entry; the chunk's activations
+// and a zero entry; the slice and a zero entry.  Every base fits the 16-bit offset field
+// of ds_read_b128.
+constexpr int kResAt = 0;
+constexpr int kXAt = kRes + 1;
+constexpr int kSliceAt = kXAt + kChunk + 1;
+constexpr int kLdsEntries = kSliceAt + kSlice + 1;
+static_assert(kSliceAt * 16 < 65536, "slice base in the ds_read offset field");
+static_assert(kLdsEntries * 16 <= 160 * 1024 - 64, "fits one CU's LDS");
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+struct BucketCfg {
+  int32_t n_tiles;     // tiles of 64 rows
+  int32_t n_chunks;    // chunks of 1024 vectors
+  int32_t units;       // n_tiles * n_chunks
+  uint32_t n_starts;   // prefix entries: 8 * n_chunks * N + 1
+  uint32_t n_words;    // bucket words: N * nv
+  float* part;         // [8 * n_chunks][N] partial sums
+  int32_t* xexp_out;   // bf16: the power of two taken out of x (written by workgroup 0)
+};
+
+// Raw buffer resource over n bytes at p: a load whose offset (all in the vector operand
+// here) lies past the n bytes returns zero and reads no memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t span(const void* p, uint32_t n) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
+}
+__device__ __forceinline__ uint32_t ld4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+}
+__device__ __forceinline__ uint4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+
+__device__ __forceinline__ float dot8(const uint4& c, const uint4& x, float acc) {
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, c.x), __builtin_bit_cast(half2_t, x.x), acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, c.y), __builtin_bit_cast(half2_t, x.y), acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, c.z), __builtin_bit_cast(half2_t, x.z), acc, false);
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, c.w), __builtin_bit_cast(half2_t, x.w), acc, false);
+}
+
+// LDS byte addresses of one bucket word's operands; a lane past the bucket's end reads
+// the three zero entries.
+struct Addr {
+  uint32_t x, c, r;
+};
+__device__ __forceinline__ Addr word_addr(uint32_t wd, bool valid) {
+  Addr ad;
+  ad.x = valid ? (uint32_t)(kXAt * 16) + ((wd << 4) & 0x3FF0u) : (uint32_t)((kXAt + kChunk) * 16);
+  ad.c = valid ? (uint32_t)(kSliceAt * 16) + ((wd >> 6) & 0x1FFF0u) : (uint32_t)((kSliceAt + kSlice) * 16);
+  ad.r = valid ? (uint32_t)(kResAt * 16) + ((wd >> 19) & 0xFF0u) : (uint32_t)((kResAt + kRes) * 16);
+  return ad;
+}
+
+struct Ops {
+  uint4 x, c, r;
+};
+
+template <bool RES>
+__device__ __forceinline__ void read_ops(const char* lds, const Addr& ad, Ops& o) {
+  o.x = *(const uint4*)(lds + ad.x);
+  o.c = *(const uint4*)(lds + ad.c);
+  if constexpr (RES) o.r = *(const uint4*)(lds + ad.r);
+}
+
+template <bool RES>
+__device__ __forceinline__ void use_ops(const Ops& o, float& a0, float& a1) {
+  a0 = dot8(o.c, o.x, a0);
+  if constexpr (RES) a1 = dot8(o.r, o.x, a1);
+}
+
+// Sum of eight per-lane values r[0..7] over the wavefront: after the exchanges across 32,
+// 16 and 8 lanes each lane holds one row's partial, finished within its group of 8
+// lanes.  Lanes with (lane & 7) == 0 return row ((lane >> 5) & 1) * 4 + ((lane >> 4) &
+// 1) * 2 + ((lane >> 3) & 1).  A fixed order: deterministic.
+__device__ __forceinline__ float reduce8(const float (&r)[8], int lane) {
+  float t[4], u[2];
+  const bool h32 = lane & 32, h16 = lane & 16, h8 = lane & 8;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float keep = h32 ? r[4 + k] : r[k];
+    const float send = h32 ? r[k] : r[4 + k];
+    t[k] = keep + __shfl_xor(send, 32, 64);
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const float keep = h16 ? t[2 + k] : t[k];
+    const float send = h16 ? t[k] : t[2 + k];
+    u[k] = keep + __shfl_xor(send, 16, 64);
+  }
+  const float keep = h8 ? u[1] : u[0];
+  const float send = h8 ? u[0] : u[1];
+  float v = keep + __shfl_xor(send, 8, 64);
+  v += __shfl_xor(v, 4, 64);
+  v += __shfl_xor(v, 2, 64);
+  v += __shfl_xor(v, 1, 64);
+  return v;
+}
+
+template <bool RES>
+__global__ __launch_bounds__(kThreads) void gemv_bucket_kernel(ProductArgs a, BucketCfg g) {
+  __shared__ uint4 lds4[kLdsEntries];
+  __shared__ uint32_t wmax[kWaves];
+  const char* lds = (const char*)lds4;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: row offsets stay scalar
+  const int s = blockIdx.x & 7;
+  const int grp = blockIdx.x >> 3;
+  const int N = a.n, nv = a.nv;
+  const bool xbf16 = a.x_dtype == VQ_BF16;
+
+  const __amdgpu_buffer_rsrc_t bst = span(a.packed1, g.n_starts * 4u);
+  const __amdgpu_buffer_rsrc_t bw = span(a.packed2, g.n_words * 4u);
+  const __amdgpu_buffer_rsrc_t bx = span(a.x, (uint32_t)a.in_features * 2u);
+
+  // the unit cursor and the prefix entries of this wavefront's rows
+  int u = grp;
+  auto unit_rows = [&](int uu, int& c, int& row0) __attribute__((always_inline)) {
+    c = uu / g.n_tiles;
+    row0 = (uu - c * g.n_tiles) * kTileRows + w * kRowsPerWave;
+  };
+  auto load_starts = [&](int uu) __attribute__((always_inline)) -> uint32_t {
+    int c, row0;
+    unit_rows(min(uu, g.units - 1), c, row0);
+    const uint32_t b0 = (uint32_t)(c * kSlices + s) * (uint32_t)N + (uint32_t)row0;
+    return ld4(bst, (b0 + (uint32_t)min(lane, kRowsPerWave)) * 4u, 0u);
+  };
+
+  // stage the slice and the residual book (loads first), and the first unit's words
+  uint32_t ew[kRowsPerWave][kSteps];  // bucket words of the rows in flight
+  int nrow[kRowsPerWave];             // their lengths (0 past N)
+  uint32_t brow[kRowsPerWave];        // their first words
+  uint32_t st_next;                   // prefix entries of the next unit
+  {
+    const uint4* src = (const uint4*)a.cb1 + (size_t)s * kSlice + tid;
+    uint4* dst = lds4 + kSliceAt + tid;
+    uint4 q[kSlice / kThreads];
+#pragma unroll
+    for (int k = 0; k < kSlice / kThreads; ++k) q[k] = src[k * kThreads];
+    uint4 qr = make_uint4(0u, 0u, 0u, 0u);
+    if (RES && tid < kRes) qr = ((const uint4*)a.cb2)[tid];
+    const uint32_t st0 = load_starts(u);
+    st_next = load_starts(u + kGroups);
+    int c0, row0;
+    unit_rows(u, c0, row0);
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      const uint32_t beg = (uint32_t)__builtin_amdgcn_readlane((int)st0, i);
+      const uint32_t end = (uint32_t)__builtin_amdgcn_readlane((int)st0, i + 1);
+      nrow[i] = row0 + i < N ? (int)(end - beg) : 0;
+      brow[i] = beg;
+#pragma unroll
+      for (int k = 0; k < kSteps; ++k) ew[i][k] = ld4(bw, (beg + (uint32_t)(k * 64 + lane)) * 4u, 0u);
+    }
+#pragma unroll
+    for (int k = 0; k < kSlice / kThreads; ++k) dst[k * kThreads] = q[k];
+    if (RES && tid <= kRes) lds4[kResAt + tid] = qr;  // entry kRes stays zero
+    if (tid == 0) {
+      lds4[kSliceAt + kSlice] = make_uint4(0u, 0u, 0u, 0u);
+      lds4[kXAt + kChunk] = make_uint4(0u, 0u, 0u, 0u);
+      if (!RES) lds4[kResAt + kRes] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  // bf16: the largest |x| (as bits: they order like the values) over the row; e puts it
+  // in [2^14, 2^15) after scaling by 2^-e
+  int xe = 0;
+  if (xbf16) {
+    uint32_t mx = 0u;
+    const int n16 = a.in_features / 8;
+    for (int i = tid; i < n16; i += kThreads) {
+      const uint4 v = ld16(bx, (uint32_t)i * 16u, 0u);
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) mx = max(mx, max(w4[h] & 0x7FFFu, (w4[h] >> 16) & 0x7FFFu));
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, off, 64));
+    if (lane == 0) wmax[w] = mx;
+    __syncthreads();
+    mx = 0u;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) mx = max(mx, wmax[k]);
+    xe = (int)((mx >> 7) & 0xFFu) - 127 - 14;
+    if (blockIdx.x == 0 && tid == 0) g.xexp_out[0] = xe;
+  }
+
+  // the activations of chunk c into LDS (two 16-byte vectors per thread)
+  auto load_chunk = [&](int c) __attribute__((always_inline)) {
+    uint4 v[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int j = c * kChunk + tid + k * kThreads;
+      v[k] = j < nv ? ld16(bx, (uint32_t)j * 16u, 0u) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      if (xbf16) {
+        const uint32_t w4[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+        uint32_t o[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const uint32_t lo = vqd::f32_to_f16_rne(ldexpf(vqd::bf16_to_f32(w4[h] & 0xFFFFu), -xe));
+          const uint32_t hi = vqd::f32_to_f16_rne(ldexpf(vqd::bf16_to_f32(w4[h] >> 16), -xe));
+          o[h] = lo | (hi << 16);
+        }
+        v[k] = make_uint4(o[0], o[1], o[2], o[3]);
+      }
+      lds4[kXAt + tid + k * kThreads] = v[k];
+    }
+  };
+
+  int chunk_in_lds = -1;
+  while (u < g.units) {
+    int c, row0;
+    unit_rows(u, c, row0);
+    if (c != chunk_in_lds) {  // uniform over the workgroup: every wavefront walks the same units
+      __syncthreads();        // every wavefront is done with the previous chunk
+      load_chunk(c);
+      __syncthreads();
+      chunk_in_lds = c;
+    }
+    const int un = u + kGroups;
+    int cn, row0n;
+    unit_rows(min(un, g.units - 1), cn, row0n);
+    const uint32_t st_cur = st_next;
+    st_next = load_starts(un + kGroups);
+
+    // 24 steps (row i = k / 3, word k % 3 of the lane): the LDS reads of step k + 2 are
+    // issued before the products of step k, through three rotating operand sets; a row's
+    // words are replaced by the next unit's as soon as its last step's addresses are formed
+    float r[kRowsPerWave];
+    float a0[kRowsPerWave], a1[kRowsPerWave];
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) a0[i] = a1[i] = 0.0f;
+    Ops op[3];
+    int ncur[kRowsPerWave];
+    uint32_t bcur[kRowsPerWave];
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      ncur[i] = nrow[i];
+      bcur[i] = brow[i];
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = k / kSteps, q = k % kSteps;
+      read_ops<RES>(lds, word_addr(ew[i][q], q * 64 + lane < ncur[i]), op[k % 3]);
+    }
+#pragma unroll
+    for (int k = 0; k < kRowsPerWave * kSteps; ++k) {
+      const int kk = k + 2;
+      if (kk < kRowsPerWave * kSteps) {
+        const int i = kk / kSteps, q = kk % kSteps;
+        read_ops<RES>(lds, word_addr(ew[i][q], q * 64 + lane < ncur[i]), op[kk % 3]);
+        if (q == kSteps - 1) {  // (past the last unit these reads repeat it: unused, no branch)
+          const uint32_t beg = (uint32_t)__builtin_amdgcn_readlane((int)st_cur, i);
+          const uint32_t end = (uint32_t)__builtin_amdgcn_readlane((int)st_cur, i + 1);
+          nrow[i] = row0n + i < N ? (int)(end - beg) : 0;
+          brow[i] = beg;
+#pragma unroll
+          for (int q2 = 0; q2 < kSteps; ++q2)
+            ew[i][q2] = ld4(bw, (beg + (uint32_t)(q2 * 64 + lane)) * 4u, 0u);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      use_ops<RES>(op[k % 3], a0[k / kSteps], a1[k / kSteps]);
+      // the products happen here, not where their sums are first needed
+      asm volatile("" : "+v"(a0[k / kSteps]), "+v"(a1[k / kSteps]));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) r[i] = a0[i] + a1[i];
+
+    // buckets longer than the 192 words held in registers (uniform per row; rare for
+    // uniform indices, every word for a row whose indices all fall in one slice)
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      if (ncur[i] > kSteps * 64) {
+        float t0 = 0.0f, t1 = 0.0f;
+        for (int base = kSteps * 64; base < ncur[i]; base += 64) {
+          const uint32_t wd = ld4(bw, (bcur[i] + (uint32_t)(base + lane)) * 4u, 0u);
+          Ops o;
+          read_ops<RES>(lds, word_addr(wd, base + lane < ncur[i]), o);
+          use_ops<RES>(o, t0, t1);
+        }
+        r[i] += t0 + t1;
+      }
+    }
+
+    const float sum = reduce8(r, lane);
+    if ((lane & 7) == 0) {
+      const int rr = ((lane >> 5) & 1) * 4 + ((lane >> 4) & 1) * 2 + ((lane >> 3) & 1);
+      const int row = row0 + rr;
+      if (row < N) g.part[(size_t)(c * kSlices + s) * (size_t)N + (size_t)row] = sum;
+    }
+    u = un;
+  }
+}
+
+size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+BucketCfg make_cfg(const ProductArgs& a) {
+  BucketCfg g{};
+  g.n_tiles = (a.n + kTileRows - 1) / kTileRows;
+  g.n_chunks = (a.nv + kChunk - 1) / kChunk;
+  g.units = g.n_tiles * g.n_chunks;
+  g.n_starts = (uint32_t)(kSlices * g.n_chunks) * (uint32_t)a.n + 1u;
+  g.n_words = (uint32_t)a.n * (uint32_t)a.nv;
+  return g;
+}
+
+}  // namespace
+
+namespace vqi {
+
+bool bucketed_gemv_shape_ok(const vq_desc& d) {
+  if (d.v != 8 || d.bits1 != 16 || !(d.bits2 == 0 || d.bits2 == 8)) return false;
+  if (d.in_features % 8 != 0) return false;
+  // bucket words and prefix entries addressed with 32-bit byte offsets
+  const uint64_t nv = (uint64_t)d.in_features / 8;
+  const uint64_t chunks = (nv + kChunk - 1) / kChunk;
+  if ((uint64_t)d.out_features * nv * 4u >= ((uint64_t)1 << 31)) return false;
+  if (((uint64_t)kSlices * chunks * (uint64_t)d.out_features + 1u) * 4u >= ((uint64_t)1 << 31)) return false;
+  return true;
+}
+
+size_t bucketed_gemv_workspace(const vq_desc& d) {
+  const int64_t nv = d.in_features / 8;
+  const int64_t chunks = (nv + kChunk - 1) / kChunk;
+  return round256((size_t)kSlices * (size_t)chunks * (size_t)d.out_features * sizeof(float)) + 256;
+}
+
+vq_status launch_gemv_bucketed(const ProductArgs& a, void* workspace, void* stream) {
+  if (!workspace) return VQ_ERR_NULL;
+  hipStream_t st = (hipStream_t)stream;
+  BucketCfg g = make_cfg(a);
+  char* ws = (char*)workspace;
+  g.part = (float*)ws;
+  const size_t exp_off = round256((size_t)kSlices * (size_t)g.n_chunks * (size_t)a.n * sizeof(float));
+  g.xexp_out = (int32_t*)(ws + exp_off);
+  const int nparts = kSlices * g.n_chunks;
+  if (g.units > 0) {
+    const int groups = g.units < kGroups ? g.units : kGroups;
+    const unsigned grid = (unsigned)(kSlices * groups);
+    if (a.bits2 == 8) {
+      hipLaunchKernelGGL(gemv_bucket_kernel<true>, dim3(grid), dim3(kThreads), 0, st, a, g);
+    } else {
+      hipLaunchKernelGGL(gemv_bucket_kernel<false>, dim3(grid), dim3(kThreads), 0, st, a, g);
+    }
+    if (hipGetLastError() != hipSuccess) return VQ_ERR_HIP;
+  }
+  return launch_partials_finalize(a, g.part, a.x_dtype == VQ_BF16 && g.units > 0 ? g.xexp_out : nullptr,
+                                  g.units > 0 ? nparts : 0, stream);
+}
+
+}  // namespace vqi

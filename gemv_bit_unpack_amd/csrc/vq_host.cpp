@@ -19,6 +19,17 @@ vq_status check_desc(const vq_desc* d) {
   return VQ_OK;
 }
 
+vq_status check_desc_any(const vq_desc* d) {
+  if (d && d->layout == VQ_LAYOUT_BUCKETED) {
+    vq_desc rs = *d;
+    rs.layout = VQ_LAYOUT_ROWSTREAM;
+    const vq_status st = check_desc(&rs);
+    if (st != VQ_OK) return st;
+    return bucketed_gemv_shape_ok(*d) ? VQ_OK : VQ_ERR_UNSUPPORTED;
+  }
+  return check_desc(d);
+}
+
 static bool valid_x_dtype(vq_dtype t) { return t == VQ_F16 || t == VQ_BF16; }
 static bool valid_out_dtype(vq_dtype t) { return t == VQ_F16 || t == VQ_BF16 || t == VQ_F32; }
 static size_t dtype_size(vq_dtype t) { return t == VQ_F32 ? 4 : 2; }
@@ -64,6 +75,73 @@ vq_status prepare_product(const vq_desc* desc, const void* packed, const void* c
   a->x = (const uint16_t*)x;
   a->y = y;
   return VQ_OK;
+}
+
+// Products over the slice-bucketed layout (vq_gemv_ws, vq_gemv_noalloc): M = 1, 16-byte
+// aligned packed / cb1 / cb2 / x.  packed1 = the prefix table, packed2 = the bucket words.
+static vq_status prepare_bucketed(const vq_desc* desc, const void* packed, const void* cb1, const void* cb2,
+                                  const void* scale, const void* bias, const void* x, vq_dtype x_dtype, int32_t m,
+                                  void* y, vq_dtype y_dtype, ProductArgs* a) {
+  vq_status st = check_desc_any(desc);
+  if (st != VQ_OK) return st;
+  if (m < 0 || m > 16) return VQ_ERR_SHAPE;
+  if (!valid_x_dtype(x_dtype) || !valid_out_dtype(y_dtype)) return VQ_ERR_UNSUPPORTED;
+  const vq_desc& d = *desc;
+  std::memset(a, 0, sizeof *a);
+  a->n = d.out_features;
+  a->in_features = d.in_features;
+  a->v = d.v;
+  a->bits1 = d.bits1;
+  a->bits2 = d.bits2;
+  a->m = m;
+  a->x_dtype = x_dtype;
+  a->y_dtype = y_dtype;
+  if (d.out_features == 0 || m == 0) return VQ_OK;
+  if (m != 1) return VQ_ERR_UNSUPPORTED;
+  if (!y) return VQ_ERR_NULL;
+  if (!aligned(y, dtype_size(y_dtype))) return VQ_ERR_ALIGN;
+  if ((bias && !aligned(bias, 2)) || (scale && !aligned(scale, 2))) return VQ_ERR_ALIGN;
+  if (d.in_features > 0) {
+    if (!packed || !cb1 || !x || (d.bits2 > 0 && !cb2)) return VQ_ERR_NULL;
+    if (!aligned(packed, 16) || !aligned(cb1, 16) || !aligned(x, 16) || (d.bits2 > 0 && !aligned(cb2, 16)))
+      return VQ_ERR_ALIGN;
+  }
+  a->nv = (int32_t)(d.in_features / 8);
+  a->packed1 = (const uint32_t*)packed;
+  a->packed2 = packed ? (const uint32_t*)((const uint8_t*)packed + bucketed_header_bytes(d)) : nullptr;
+  a->cb1 = (const uint16_t*)cb1;
+  a->cb2 = d.bits2 > 0 ? (const uint16_t*)cb2 : nullptr;
+  a->scale = (const uint16_t*)scale;
+  a->bias = (const uint16_t*)bias;
+  a->x = (const uint16_t*)x;
+  a->y = y;
+  return VQ_OK;
+}
+
+// The slice-bucketed layout of idx1 / idx2 (vq.h): bucket sizes, their prefix table, then
+// each row's vectors in ascending j dropped into their buckets.
+static void pack_bucketed(const vq_desc& d, const uint32_t* idx1, const uint32_t* idx2, uint8_t* out) {
+  const int64_t n = d.out_features;
+  const int64_t nv = num_vectors(d.in_features, 8);
+  const int64_t chunks = bucketed_chunks(d);
+  const size_t nb = (size_t)(8 * chunks) * (size_t)n;
+  uint32_t* start = (uint32_t*)out;
+  uint32_t* words = (uint32_t*)(out + bucketed_header_bytes(d));
+  auto bucket = [&](int64_t o, int64_t j, uint32_t i1) {
+    return (size_t)((j / kBucketChunk) * 8 + (i1 >> 13)) * (size_t)n + (size_t)o;
+  };
+  std::vector<uint32_t> next(nb + 1, 0u);
+  for (int64_t o = 0; o < n; ++o)
+    for (int64_t j = 0; j < nv; ++j) ++next[bucket(o, j, idx1[o * nv + j]) + 1];
+  for (size_t b = 0; b < nb; ++b) next[b + 1] += next[b];
+  std::memcpy(start, next.data(), (nb + 1) * sizeof(uint32_t));
+  for (int64_t o = 0; o < n; ++o) {
+    for (int64_t j = 0; j < nv; ++j) {
+      const uint32_t i1 = idx1[o * nv + j];
+      const uint32_t i2 = d.bits2 > 0 ? idx2[o * nv + j] : 0u;
+      words[next[bucket(o, j, i1)]++] = (uint32_t)(j % kBucketChunk) | ((i1 & 8191u) << 10) | (i2 << 23);
+    }
+  }
 }
 
 // Affine-lattice calls: the descriptor must be the lattice stream (v = 4, bits1 = 8, no
@@ -154,7 +232,7 @@ const char* vq_status_string(vq_status status) {
 }
 
 vq_status vq_packed_bytes(const vq_desc* desc, size_t* nbytes) {
-  vq_status st = check_desc(desc);
+  vq_status st = check_desc_any(desc);
   if (st != VQ_OK) return st;
   if (!nbytes) return VQ_ERR_NULL;
   *nbytes = packed_size(*desc);
@@ -162,7 +240,7 @@ vq_status vq_packed_bytes(const vq_desc* desc, size_t* nbytes) {
 }
 
 vq_status vq_pack(const vq_desc* desc, const uint32_t* idx1, const uint32_t* idx2, void* packed, size_t nbytes) {
-  vq_status st = check_desc(desc);
+  vq_status st = check_desc_any(desc);
   if (st != VQ_OK) return st;
   const vq_desc& d = *desc;
   const size_t need = packed_size(d);
@@ -183,6 +261,14 @@ vq_status vq_pack(const vq_desc* desc, const uint32_t* idx1, const uint32_t* idx
   if (need == 0) return VQ_OK;
   uint8_t* out = (uint8_t*)packed;
   std::memset(out, 0, need);
+  if (d.layout == VQ_LAYOUT_BUCKETED) {
+    try {
+      pack_bucketed(d, idx1, idx2, out);
+    } catch (const std::bad_alloc&) {
+      return VQ_ERR_BUFFER_SIZE;
+    }
+    return VQ_OK;
+  }
   const int64_t s1 = row_stride(d.in_features, d.v, d.bits1);
   const int64_t s2 = row_stride(d.in_features, d.v, d.bits2);
   for (int stream = 0; stream < 2; ++stream) {
@@ -252,10 +338,15 @@ vq_status vq_gemv(const vq_desc* desc, const void* packed, const void* cb1, cons
 
 vq_status vq_gemv_workspace_bytes(const vq_desc* desc, int32_t M, vq_dtype x_dtype, size_t* nbytes) {
   if (!nbytes) return VQ_ERR_NULL;
-  vq_status st = check_desc(desc);
+  vq_status st = check_desc_any(desc);
   if (st != VQ_OK) return st;
   if (M < 0 || M > 16) return VQ_ERR_SHAPE;
   if (x_dtype != VQ_F16 && x_dtype != VQ_BF16) return VQ_ERR_UNSUPPORTED;
+  if (desc->layout == VQ_LAYOUT_BUCKETED) {
+    if (M > 1) return VQ_ERR_UNSUPPORTED;
+    *nbytes = (M == 0 || desc->in_features == 0 || desc->out_features == 0) ? 0 : bucketed_gemv_workspace(*desc);
+    return VQ_OK;
+  }
   *nbytes = sliced_gemv_workspace(*desc, M, x_dtype);
   return VQ_OK;
 }
@@ -264,6 +355,16 @@ vq_status vq_gemv_ws(const vq_desc* desc, const void* packed, const void* cb1, c
                      const void* bias, const void* x, vq_dtype x_dtype, int32_t M, void* y, vq_dtype y_dtype,
                      void* workspace, size_t workspace_bytes, void* stream) {
   ProductArgs a;
+  if (desc && desc->layout == VQ_LAYOUT_BUCKETED) {
+    vq_status st = prepare_bucketed(desc, packed, cb1, cb2, scale, bias, x, x_dtype, M, y, y_dtype, &a);
+    if (st != VQ_OK) return st;
+    if (a.n == 0 || a.m == 0) return VQ_OK;
+    if (a.in_features == 0) return launch_gemv(a, stream);  // y = bias or 0: no index is read
+    if (!workspace) return VQ_ERR_NULL;
+    if (workspace_bytes < bucketed_gemv_workspace(*desc)) return VQ_ERR_BUFFER_SIZE;
+    if (!aligned(workspace, 256)) return VQ_ERR_ALIGN;
+    return launch_gemv_bucketed(a, workspace, stream);
+  }
   vq_status st = prepare_product(desc, packed, cb1, cb2, scale, bias, x, x_dtype, M, y, y_dtype, 16, &a);
   if (st != VQ_OK) return st;
   if (a.n == 0 || a.m == 0) return VQ_OK;
@@ -280,6 +381,17 @@ vq_status vq_gemv_noalloc(const vq_desc* desc, const void* packed, const void* c
                           const void* scale, const void* bias, const void* x, vq_dtype x_dtype, int32_t M, void* y,
                           vq_dtype y_dtype, void* stream) {
   ProductArgs a;
+  if (desc && desc->layout == VQ_LAYOUT_BUCKETED) {
+    vq_status st = prepare_bucketed(desc, packed, cb1, cb2, scale, bias, x, x_dtype, M, y, y_dtype, &a);
+    if (st != VQ_OK) return st;
+    if (a.n == 0 || a.m == 0) return VQ_OK;
+    if (a.in_features == 0) return launch_gemv(a, stream);
+    if (bucketed_gemv_workspace(*desc) > static_scratch_bytes()) return VQ_ERR_BUFFER_SIZE;
+    void* ws = nullptr;
+    st = static_scratch(&ws);
+    if (st != VQ_OK) return st;
+    return launch_gemv_bucketed(a, ws, stream);
+  }
   vq_status st = prepare_product(desc, packed, cb1, cb2, scale, bias, x, x_dtype, M, y, y_dtype, 16, &a);
   if (st != VQ_OK) return st;
   if (a.n == 0 || a.m == 0) return VQ_OK;

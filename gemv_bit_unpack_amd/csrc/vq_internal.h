@@ -20,11 +20,28 @@ inline int64_t row_stride(int64_t in_features, int v, int bits) {
   return 16 * ((nbits + 127) / 128);
 }
 
-// Validates the descriptor fields (not pointers).  VQ_OK or the error code.
+// Validates the descriptor fields (not pointers) of a row-stream layer: VQ_OK or the error
+// code (any other layout is VQ_ERR_UNSUPPORTED).
 vq_status check_desc(const vq_desc* d);
+// The same, also accepting the slice-bucketed layout where it is defined (v = 8,
+// bits1 = 16, bits2 0 or 8, IN a multiple of 8, within the 32-bit offsets of its product).
+vq_status check_desc_any(const vq_desc* d);
+
+// Slice-bucketed layout: vectors per chunk, and the bytes of its prefix table (8 * chunks
+// * N + 1 uint32 bucket offsets, padded to 256 bytes) ahead of the 32-bit bucket words.
+constexpr int32_t kBucketChunk = 1024;
+inline int64_t bucketed_chunks(const vq_desc& d) {
+  return (num_vectors(d.in_features, 8) + kBucketChunk - 1) / kBucketChunk;
+}
+inline size_t bucketed_header_bytes(const vq_desc& d) {
+  const size_t starts = (size_t)(8 * bucketed_chunks(d)) * (size_t)d.out_features + 1;
+  return (starts * 4 + 255) / 256 * 256;
+}
 
 // Packed size in bytes of a validated descriptor.
 inline size_t packed_size(const vq_desc& d) {
+  if (d.layout == VQ_LAYOUT_BUCKETED)
+    return bucketed_header_bytes(d) + 4 * (size_t)d.out_features * (size_t)num_vectors(d.in_features, 8);
   return (size_t)d.out_features *
          (size_t)(row_stride(d.in_features, d.v, d.bits1) + row_stride(d.in_features, d.v, d.bits2));
 }
@@ -66,6 +83,12 @@ bool sliced_gemv_pointers_ok(const ProductArgs& a);
 // in the x pass; then the workspace is sliced_gemv_rht_workspace(...) bytes.
 vq_status launch_gemv_sliced(const ProductArgs& a, void* workspace, void* stream, const uint8_t* rht_signs = nullptr);
 size_t sliced_gemv_rht_workspace(const vq_desc& d, int32_t m, vq_dtype x_dtype);
+// The product over the slice-bucketed layout (M = 1): whether the descriptor's sizes fit
+// its 32-bit offsets, its workspace bytes, and the launch (packed1 = the prefix table,
+// packed2 = the bucket words, nv = IN / 8).
+bool bucketed_gemv_shape_ok(const vq_desc& d);
+size_t bucketed_gemv_workspace(const vq_desc& d);
+vq_status launch_gemv_bucketed(const ProductArgs& a, void* workspace, void* stream);
 // The fixed device workspace of vq_gemv_noalloc: its size, and this GPU's copy (looked up
 // on the first call on each device; no allocation).
 size_t static_scratch_bytes();

@@ -13,7 +13,7 @@
  * into a main codebook C1 of K1 = 2^bits1 fp16 centroids and an optional residual
  * codebook C2 of K2 = 2^bits2 fp16 centroids, each centroid a row of v fp16 values.
  *
- * Packed index layout (VQ_LAYOUT_ROWSTREAM, the only layout):
+ * Packed index layout (VQ_LAYOUT_ROWSTREAM, the layout every call takes):
  *   - row stride of stream b: S_b = 16 * ceil(nv * bits_b / 128) bytes (0 if bits_b == 0);
  *   - stream 1 (idx1) for rows 0..N-1 occupies bytes [0, N*S1), stream 2 (idx2) follows
  *     at [N*S1, N*(S1+S2));
@@ -22,6 +22,23 @@
  *   - pad bits are written as zero by vq_pack and ignored by the kernels.
  * When IN is not a multiple of v, the last vector's lanes t with j*v + t >= IN are
  * dropped (the centroid is stored in full, its tail is never used).
+ *
+ * Slice-bucketed layout (VQ_LAYOUT_BUCKETED): the same indices, regrouped once at load
+ * time for the batch-1 decode product of vq_gemv_ws / vq_gemv_noalloc, the only calls
+ * that take it.  Defined for v = 8, bits1 = 16 (K1 = 65536), bits2 = 0 or 8, IN a
+ * multiple of 8.  The main book is seen as 8 slices of 8192 centroids (slice s =
+ * idx1 >> 13); the vectors of row o are cut into chunks of 1024 (chunk c = j / 1024).
+ *   - bucket b = (c*8 + s)*N + o holds the vectors j of row o in chunk c whose idx1
+ *     lies in slice s, in ascending j, one 32-bit little-endian word each:
+ *       bits [0, 10) j - 1024*c,  bits [10, 23) idx1 & 8191,  bits [23, 31) idx2
+ *     (idx2 = 0 without a residual book), bit 31 zero;
+ *   - bytes [0, H) hold start[b], b = 0 .. 8*chunks*N, as uint32: bucket b is words
+ *     [start[b], start[b+1]); start[0] = 0; H = 4*(8*chunks*N + 1) rounded up to 256,
+ *     the rest of it zero;
+ *   - the words follow at byte H, buckets in order of b: N * IN/8 words in all.
+ * It stores 32 bits per vector where the row stream stores bits1 + bits2 (24 with the
+ * residual book): the position travels with each index, so that each slice's CUs read
+ * exactly the vectors whose centroids they hold.
  *
  * Numerics.  vq_dequant is exact: in fp32, w = fp32(C1) + fp32(C2) rounded to nearest
  * even, then w * fp32(scale[o]); without a residual book the add is skipped, without a
@@ -56,6 +73,7 @@ extern "C" {
 
 #define VQ_ABI_VERSION 1
 #define VQ_LAYOUT_ROWSTREAM 1
+#define VQ_LAYOUT_BUCKETED 2
 
 typedef enum vq_status {
   VQ_OK = 0,
@@ -72,7 +90,8 @@ typedef enum vq_status {
 typedef enum vq_dtype { VQ_F16 = 0, VQ_BF16 = 1, VQ_F32 = 2 } vq_dtype;
 
 /* W is [out_features][in_features]; vectors of v weights run along in_features.
- * bits1 in 1..16 (K1 = 2^bits1), bits2 in 0..16 (0: no residual book), layout = 1. */
+ * bits1 in 1..16 (K1 = 2^bits1), bits2 in 0..16 (0: no residual book); layout =
+ * VQ_LAYOUT_ROWSTREAM, or VQ_LAYOUT_BUCKETED where a call says it takes it. */
 typedef struct vq_desc {
   int32_t out_features;
   int32_t in_features;
@@ -89,7 +108,9 @@ int32_t vq_abi_version(void);
 const char* vq_status_string(vq_status status);
 
 /* Bytes of the packed index buffer for `desc` (bitrate log2(K)/v per book, VPTQ guide
- * "3. Effective Bit-Width Calculation", plus row padding to 16 bytes). */
+ * "3. Effective Bit-Width Calculation", plus row padding to 16 bytes).  For
+ * VQ_LAYOUT_BUCKETED: the prefix table plus 4 bytes per vector (VQ_ERR_UNSUPPORTED where
+ * that layout is not defined). */
 vq_status vq_packed_bytes(const vq_desc* desc, size_t* nbytes);
 
 /* Pack idx1 [N][nv] (and idx2 [N][nv] when bits2 > 0; must be NULL-free then, ignored
@@ -99,7 +120,9 @@ vq_status vq_packed_bytes(const vq_desc* desc, size_t* nbytes);
  * keeps whole uint8 / int16 index tensors); this one stores exactly the log2(K) bits per
  * index per book that the guide's "3. Effective Bit-Width Calculation" counts, main and
  * residual indices in separate streams as its residual pipeline keeps them ("2.
- * Multi-Stage Residual Vector Quantization (RVQ)"). */
+ * Multi-Stage Residual Vector Quantization (RVQ)").  With desc->layout ==
+ * VQ_LAYOUT_BUCKETED the same indices are written in the slice-bucketed layout above
+ * (VQ_ERR_UNSUPPORTED where it is not defined). */
 vq_status vq_pack(const vq_desc* desc, const uint32_t* idx1, const uint32_t* idx2, void* packed, size_t nbytes);
 
 /* Rebuild W^ [N][IN] into `w` (device, row-major, w_dtype; fp16 / bf16 outputs are the
@@ -127,7 +150,9 @@ vq_status vq_gemv(const vq_desc* desc, const void* packed, const void* cb1, cons
  * activations of x_dtype on its codebook-sliced path; 0 when the shape does not take
  * that path.  It needs v = 8, bits1 = 16, bits2 = 0 or 8, IN a multiple of 8, and at
  * least 2^22 weight vectors (N * IN / 8) for M < 8 or 2^19 for M >= 8: below that the
- * vq_gemv kernels are as fast.  M = 0 gives 0. */
+ * vq_gemv kernels are as fast.  M = 0 gives 0.  A VQ_LAYOUT_BUCKETED desc has no other
+ * path: M = 1 gives its workspace (8 * chunks * N floats and 256 bytes; 0 when IN == 0),
+ * M >= 2 VQ_ERR_UNSUPPORTED. */
 vq_status vq_gemv_workspace_bytes(const vq_desc* desc, int32_t M, vq_dtype x_dtype, size_t* nbytes);
 
 /* vq_gemv with a caller-owned device workspace, for the 65536-entry main book (VPTQ
@@ -146,7 +171,14 @@ vq_status vq_gemv_workspace_bytes(const vq_desc* desc, int32_t M, vq_dtype x_dty
  *     VQ_ERR_ALIGN otherwise).  Its contents need no initialisation and are scratch
  *     after the call; calls that may run at the same time need different workspaces.
  * Shapes without the sliced path, or packed / cb1 / cb2 / x pointers that are not
- * 16-byte aligned, run the vq_gemv kernels and leave the workspace untouched. */
+ * 16-byte aligned, run the vq_gemv kernels and leave the workspace untouched.
+ * A VQ_LAYOUT_BUCKETED desc (packed in that layout) runs the batch-1 decode product over
+ * it: each slice's workgroups read only their own buckets, so every index is read once;
+ * per word, the activation vector, the main and the residual centroid come from LDS and
+ * eight packed fp16 dot products accumulate in fp32; partial sums per (chunk, slice,
+ * row) are added in a fixed order by the same second kernel.  It takes M = 1 only (M >= 2:
+ * VQ_ERR_UNSUPPORTED), requires the workspace (NULL: VQ_ERR_NULL) and 16-byte aligned
+ * packed, cb1, cb2 and x (VQ_ERR_ALIGN): there is no other path for that layout. */
 vq_status vq_gemv_ws(const vq_desc* desc, const void* packed, const void* cb1, const void* cb2, const void* scale,
                      const void* bias, const void* x, vq_dtype x_dtype, int32_t M, void* y, vq_dtype y_dtype,
                      void* workspace, size_t workspace_bytes, void* stream);
@@ -160,8 +192,9 @@ vq_status vq_gemv_ws(const vq_desc* desc, const void* packed, const void* cb1, c
  * device (with that device current).  Shapes whose sliced-path workspace
  * (vq_gemv_workspace_bytes) exceeds 16 MiB return VQ_ERR_BUFFER_SIZE and launch
  * nothing; shapes without the sliced path run the vq_gemv kernels, which use no
- * workspace.  Every call on one GPU shares that GPU's array: calls that may run at the
- * same time on one GPU (other streams, other threads) race and must not overlap. */
+ * workspace.  A VQ_LAYOUT_BUCKETED desc runs its decode product as in vq_gemv_ws.  Every
+ * call on one GPU shares that GPU's array: calls that may run at the same time on one GPU
+ * (other streams, other threads) race and must not overlap. */
 vq_status vq_gemv_noalloc(const vq_desc* desc, const void* packed, const void* cb1, const void* cb2,
                           const void* scale, const void* bias, const void* x, vq_dtype x_dtype, int32_t M, void* y,
                           vq_dtype y_dtype, void* stream);

@@ -70,9 +70,9 @@ SVQ_DESCRIBE = {
     "svq4k": "4096x4096 affine lattice d=4 (2 bits/weight)",
     "svq70b": "70B-class pair 28672x8192 + 8192x28672 affine lattice d=4 (2 bits/weight)",
 }
-GEMV_SOURCES = ["gemv_bit_unpack_amd/csrc/vq_gemv_sliced.hip", "gemv_bit_unpack_amd/csrc/vq_device.h",
-                "gemv_bit_unpack_amd/csrc/vq_internal.h"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_vq_gemv_ws_l70b_m1.json")
+GEMV_SOURCES = ["gemv_bit_unpack_amd/csrc/vq_gemv_bucket.hip", "gemv_bit_unpack_amd/csrc/vq_gemv_sliced.hip",
+                "gemv_bit_unpack_amd/csrc/vq_device.h", "gemv_bit_unpack_amd/csrc/vq_internal.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_vq_gemv_ws_bucketed_l70b_m1.json")
 TRIALS = 5
 HEADLINE_KEY = "l70b"
 
@@ -113,17 +113,31 @@ def gathered_bytes(desc):
 class Ring:
     """Distinct copies of one workload layer on the device, plus ctypes argument tuples."""
 
-    def __init__(self, vq, torch, key, layer, m, copies=None, fn="vq_gemv_ws", y_dtype=None, shared_book=False):
+    def __init__(self, vq, torch, key, layer, m, copies=None, fn="vq_gemv_ws", y_dtype=None, shared_book=False,
+                 layout=1):
         layers, v, b1, b2, xd = WORKLOADS[key]
         n, i = layers[layer]
-        self.desc = vq.make_desc(n, i, v, b1, b2)
+        self.desc = vq.make_desc(n, i, v, b1, b2, layout)
+        rs_desc = vq.make_desc(n, i, v, b1, b2)  # algorithmic bytes: the row stream's log2(K) bits per index
         self.m = m
+        self.layout = layout
         dev = torch.device("cuda")
         per = layer_bytes(vq, self.desc, m)
         self.copies = copies or min(MAX_COPIES, max(1, -(-RING_BYTES // per)))
         g = torch.Generator(device=dev)
         g.manual_seed(zlib.crc32(("%d/%s/%d" % (42, key, layer)).encode()))
         nb = vq.packed_bytes(self.desc)
+        bucketed = None
+        if layout == vq.LAYOUT_BUCKETED:
+            # a valid bucketed buffer needs real indices: pack seeded ones once on the host, and
+            # give every copy its own device copy of it (the caches see distinct addresses)
+            import numpy as np
+
+            hr = np.random.default_rng(zlib.crc32(("%d/%s/%d/bucketed" % (42, key, layer)).encode()))
+            nvec = (i + v - 1) // v
+            idx1 = hr.integers(0, 1 << b1, (n, nvec), dtype=np.uint32)
+            idx2 = hr.integers(0, 1 << b2, (n, nvec), dtype=np.uint32) if b2 else None
+            bucketed = torch.from_numpy(vq.pack(self.desc, idx1, idx2)).to(dev)
         xdt = torch.bfloat16 if xd == "bf16" else torch.float16
         self.x = torch.randn((m, i), generator=g, device=dev, dtype=torch.float32).to(xdt)
         self.y_dtype = y_dtype or xdt
@@ -143,7 +157,10 @@ class Ring:
         code = {torch.float16: vq.VQ_F16, torch.bfloat16: vq.VQ_BF16, torch.float32: vq.VQ_F32}
         self.tensors = []
         for c in range(self.copies):
-            packed = torch.randint(0, 256, (nb,), generator=g, device=dev, dtype=torch.uint8)
+            if bucketed is not None:
+                packed = bucketed.clone()
+            else:
+                packed = torch.randint(0, 256, (nb,), generator=g, device=dev, dtype=torch.uint8)
             if shared_book and c > 0:
                 cb1, cb2 = self.tensors[0][1], self.tensors[0][2]
             else:
@@ -155,7 +172,9 @@ class Ring:
             p = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
             self.items.append((ctypes.byref(self.desc), p(packed), p(cb1), p(cb2), p(scale), None, p(self.x),
                                code[xdt], m, p(y), code[self.y_dtype]) + extra)
-        self.bytes_per_call = layer_bytes(vq, self.desc, m, 4 if self.y_dtype == torch.float32 else 2)
+        yb = 4 if self.y_dtype == torch.float32 else 2
+        self.bytes_per_call = layer_bytes(vq, rs_desc, m, yb)
+        self.stored_bytes_per_call = layer_bytes(vq, self.desc, m, yb)  # what the layout actually holds
         self.flops_per_call = 2.0 * m * n * i
 
     def call(self, k, stream_ptr):
@@ -591,6 +610,8 @@ def main():
     ap.add_argument("--only-svq", action="store_true",
                     help="run only the affine-lattice (vq_svq_gemv) leg (for profiling)")
     ap.add_argument("--m", type=int, default=1, help="batch rows for --only-workload (1..16)")
+    ap.add_argument("--layout", type=int, default=1, choices=(1, 2),
+                    help="packed layout for --only-workload: 1 row stream, 2 slice-bucketed (M = 1)")
     ap.add_argument("--only-workload", default=None, choices=sorted(WORKLOADS),
                     help="run only one workload's M=1 leg through vq_gemv_ws (for profiling)")
     args = ap.parse_args()
@@ -648,17 +669,29 @@ def main():
         return
     if args.only_workload:
         key = args.only_workload
-        rings = [Ring(vq, torch, key, li, args.m) for li in range(len(WORKLOADS[key][0]))]
+        rings = [Ring(vq, torch, key, li, args.m, layout=args.layout) for li in range(len(WORKLOADS[key][0]))]
         sec, calls, _, launch = time_ring(torch, rings, args.steps, args.warmup, use_graph)
         b = sum(r.bytes_per_call for r in rings) / len(rings)
+        kern = "slice-bucketed" if args.layout == 2 else (
+            "codebook-sliced" if any(r.sliced for r in rings) else "gather")
         print(json.dumps({"workload": key, "m": args.m, "us_per_call": round(sec * 1e6, 3), "GBps": round(b / sec / 1e9, 1),
-                          "kernel": "codebook-sliced" if any(r.sliced for r in rings) else "gather",
-                          "calls": calls, "launch": launch}))
+                          "kernel": kern, "calls": calls, "launch": launch}))
         return
-    # Headline: vq_gemv_ws at M = 1 on the 70B-class pair (up, then down, per step).
+    # Headline: vq_gemv_ws at M = 1 on the 70B-class pair (up, then down, per step), over the
+    # slice-bucketed decode layout; the row-stream (codebook-sliced) call is timed beside it.
     stream_gbps = stream_ceiling_gbps()
-    up = Ring(vq, torch, HEADLINE_KEY, 0, 1, shared_book=args.shared_book)
-    down = Ring(vq, torch, HEADLINE_KEY, 1, 1, shared_book=args.shared_book)
+    rs_up = Ring(vq, torch, HEADLINE_KEY, 0, 1, shared_book=args.shared_book)
+    rs_down = Ring(vq, torch, HEADLINE_KEY, 1, 1, shared_book=args.shared_book)
+    rs_steps = time_steps(torch, [rs_up, rs_down], args.steps, args.warmup)
+    rs_sec = sorted(rs_steps)[len(rs_steps) // 2]
+    rowstream = {"call": "vq_gemv_ws over the row-stream layout (codebook-sliced kernel)",
+                 "ms_per_step": round(rs_sec * 1e3, 6),
+                 "trials_ms_per_step": [round(t * 1e3, 6) for t in rs_steps],
+                 "GBps": round((rs_up.bytes_per_call + rs_down.bytes_per_call) / rs_sec / 1e9, 2)}
+    del rs_up, rs_down
+    torch.cuda.empty_cache()
+    up = Ring(vq, torch, HEADLINE_KEY, 0, 1, shared_book=args.shared_book, layout=vq.LAYOUT_BUCKETED)
+    down = Ring(vq, torch, HEADLINE_KEY, 1, 1, shared_book=args.shared_book, layout=vq.LAYOUT_BUCKETED)
     rings = [up, down]
     log("headline: %d + %d copies of %s, %.2f MB per step" % (up.copies, down.copies, DESCRIBE[HEADLINE_KEY],
                                                            (up.bytes_per_call + down.bytes_per_call) / 1e6))
@@ -695,7 +728,12 @@ def main():
                    "global_batch": 1, "layer_copies_in_ring": [up.copies, down.copies],
                    "launch": "hipgraph of exactly `steps` steps", "trials": TRIALS,
                    "bytes_per_step": step_bytes,
-                   "path": "codebook-sliced" if all(r.sliced for r in rings) else "gather"},
+                   "stored_bytes_per_step": up.stored_bytes_per_call + down.stored_bytes_per_call,
+                   "bytes_note": "value counts the row-stream bytes (16 + 8 bits per vector, 3 bits/weight); "
+                                 "the slice-bucketed layout the call reads stores 32 bits per vector "
+                                 "(stored_bytes_per_step)",
+                   "path": "slice-bucketed"},
+        "rowstream_codebook_sliced": rowstream,
         "trials_ms_per_step": [round(t * 1e3, 6) for t in per_step],
         "ms_per_step_min": round(min(per_step) * 1e3, 6),
         "value_at_min": round(step_bytes / min(per_step) / 1e9, 2),
@@ -704,15 +742,16 @@ def main():
         "measured_stream_ceiling_GBps": stream_gbps,
         "roofline": {"bound": "hbm", "achieved": round(gbps, 2), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "kernel": "vq_gemv_ws call, timed whole: gemv_sliced_kernel<true, true> (the dominant kernel, "
-                               "which also converts the bf16 x) + gemv_sliced_finalize",
+                     "kernel": "vq_gemv_ws call over the slice-bucketed layout, timed whole: "
+                               "gemv_bucket_kernel<true> (the dominant kernel, which also converts the bf16 x) "
+                               "+ gemv_sliced_finalize",
                      "units": "algorithmic bytes of the pair per step / event-timed step"},
         "cold_single_call_us": {"up": cold_call_us(torch, up), "down": cold_call_us(torch, down),
                                 "note": "one call after a 1 GiB buffer has been streamed through the caches"},
         "gather": {"gathers_per_s": round(gathers / sec, 1),
                    "effective_incl_gathered_centroids_GBps": round(g_cb, 2),
-                   "note": "every 16-byte centroid lookup counted once: through L2 for the gather kernel, "
-                           "from the 128 KiB LDS slices for the codebook-sliced one"},
+                   "note": "every 16-byte main-book centroid lookup counted once, from the 128 KiB LDS "
+                           "slices"},
         "wall_s_timed": round(wall, 4),
     }
     del up, down, rings
@@ -752,6 +791,12 @@ def main():
                 rr = [Ring(vq, torch, HEADLINE_KEY, li, m, copies=6, fn=fn) for li in (0, 1)]
                 tt = time_steps(torch, rr, 12, 2)
                 entry[fn + "_us_per_call"] = round(sorted(tt)[len(tt) // 2] / 2 * 1e6, 3)
+                del rr
+                torch.cuda.empty_cache()
+            if m == 1:  # the batch-1 decode product over the slice-bucketed layout
+                rr = [Ring(vq, torch, HEADLINE_KEY, li, 1, copies=6, layout=vq.LAYOUT_BUCKETED) for li in (0, 1)]
+                tt = time_steps(torch, rr, 12, 2)
+                entry["vq_gemv_ws_bucketed_us_per_call"] = round(sorted(tt)[len(tt) // 2] / 2 * 1e6, 3)
                 del rr
                 torch.cuda.empty_cache()
             g_us, m_us = entry.get("vq_gemv_ws_us_per_call"), entry["vq_gemm_ws_us_per_call"]

@@ -33,10 +33,10 @@ namespace {
 
 using vqi::ProductArgs;
 
-constexpr int kThreads = 512;
+constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr int kRowsPerWave = 8;
-constexpr int kTileRows = kWaves * kRowsPerWave;  // 64
+constexpr int kTileRows = kWaves * kRowsPerWave;  // 128
 constexpr int kSlices = 8;
 constexpr int kSlice = 8192;
 constexpr int kGroups = 32;
@@ -90,11 +90,13 @@ __device__ __forceinline__ float dot8(const uint4& c, const uint4& x, float acc)
 struct Addr {
   uint32_t x, c, r;
 };
+// Offsets within each region: the region bases are constants that the reads carry in
+// their instruction offset field.
 __device__ __forceinline__ Addr word_addr(uint32_t wd, bool valid) {
   Addr ad;
-  ad.x = valid ? (uint32_t)(kXAt * 16) + ((wd << 4) & 0x3FF0u) : (uint32_t)((kXAt + kChunk) * 16);
-  ad.c = valid ? (uint32_t)(kSliceAt * 16) + ((wd >> 6) & 0x1FFF0u) : (uint32_t)((kSliceAt + kSlice) * 16);
-  ad.r = valid ? (uint32_t)(kResAt * 16) + ((wd >> 19) & 0xFF0u) : (uint32_t)((kResAt + kRes) * 16);
+  ad.x = valid ? ((wd << 4) & 0x3FF0u) : (uint32_t)(kChunk * 16);
+  ad.c = valid ? ((wd >> 6) & 0x1FFF0u) : (uint32_t)(kSlice * 16);
+  ad.r = valid ? ((wd >> 19) & 0xFF0u) : (uint32_t)(kRes * 16);
   return ad;
 }
 
@@ -104,9 +106,9 @@ struct Ops {
 
 template <bool RES>
 __device__ __forceinline__ void read_ops(const char* lds, const Addr& ad, Ops& o) {
-  o.x = *(const uint4*)(lds + ad.x);
-  o.c = *(const uint4*)(lds + ad.c);
-  if constexpr (RES) o.r = *(const uint4*)(lds + ad.r);
+  o.x = *(const uint4*)(lds + kXAt * 16 + ad.x);
+  o.c = *(const uint4*)(lds + kSliceAt * 16 + ad.c);
+  if constexpr (RES) o.r = *(const uint4*)(lds + kResAt * 16 + ad.r);
 }
 
 template <bool RES>
@@ -233,15 +235,16 @@ __global__ __launch_bounds__(kThreads) void gemv_bucket_kernel(ProductArgs a, Bu
   }
 
   // the activations of chunk c into LDS (two 16-byte vectors per thread)
+  constexpr int kXPer = kChunk / kThreads;  // activation vectors per thread
   auto load_chunk = [&](int c) __attribute__((always_inline)) {
-    uint4 v[2];
+    uint4 v[kXPer];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < kXPer; ++k) {
       const int j = c * kChunk + tid + k * kThreads;
       v[k] = j < nv ? ld16(bx, (uint32_t)j * 16u, 0u) : make_uint4(0u, 0u, 0u, 0u);
     }
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < kXPer; ++k) {
       if (xbf16) {
         const uint32_t w4[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
         uint32_t o[4];
@@ -273,14 +276,12 @@ __global__ __launch_bounds__(kThreads) void gemv_bucket_kernel(ProductArgs a, Bu
     const uint32_t st_cur = st_next;
     st_next = load_starts(un + kGroups);
 
-    // 24 steps (row i = k / 3, word k % 3 of the lane): the LDS reads of step k + 2 are
-    // issued before the products of step k, through three rotating operand sets; a row's
-    // words are replaced by the next unit's as soon as its last step's addresses are formed
+    // Row by row: the reads of row i + 1's three steps are issued before row i's products
+    // (always issued, so the compiler counts them exactly; lanes past a bucket's end read
+    // the zero entries); the products of a row's second and third steps run only when its
+    // bucket reaches them (a uniform branch around VALU work only); a row's words are
+    // replaced by the next unit's as soon as its reads are issued.
     float r[kRowsPerWave];
-    float a0[kRowsPerWave], a1[kRowsPerWave];
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) a0[i] = a1[i] = 0.0f;
-    Ops op[3];
     int ncur[kRowsPerWave];
     uint32_t bcur[kRowsPerWave];
 #pragma unroll
@@ -288,35 +289,31 @@ __global__ __launch_bounds__(kThreads) void gemv_bucket_kernel(ProductArgs a, Bu
       ncur[i] = nrow[i];
       bcur[i] = brow[i];
     }
+    Ops op[2][kSteps];  // [row parity][step]
+    auto row_reads = [&](int i, Ops (&o)[kSteps]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
-      const int i = k / kSteps, q = k % kSteps;
-      read_ops<RES>(lds, word_addr(ew[i][q], q * 64 + lane < ncur[i]), op[k % 3]);
+      for (int q = 0; q < kSteps; ++q) read_ops<RES>(lds, word_addr(ew[i][q], q * 64 + lane < ncur[i]), o[q]);
+      // row i's words are consumed: fetch the next unit's row i (past the last unit these
+      // reads repeat it, unused: no branch)
+      const uint32_t beg = (uint32_t)__builtin_amdgcn_readlane((int)st_cur, i);
+      const uint32_t end = (uint32_t)__builtin_amdgcn_readlane((int)st_cur, i + 1);
+      nrow[i] = row0n + i < N ? (int)(end - beg) : 0;
+      brow[i] = beg;
+#pragma unroll
+      for (int q = 0; q < kSteps; ++q) ew[i][q] = ld4(bw, (beg + (uint32_t)(q * 64 + lane)) * 4u, 0u);
+    };
+    row_reads(0, op[0]);
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      if (i + 1 < kRowsPerWave) row_reads(i + 1, op[(i + 1) & 1]);
+      const Ops (&o)[kSteps] = op[i & 1];
+      float a0 = 0.0f, a1 = 0.0f;
+      if (ncur[i] > 0) use_ops<RES>(o[0], a0, a1);
+      if (ncur[i] > 64) use_ops<RES>(o[1], a0, a1);
+      if (ncur[i] > 128) use_ops<RES>(o[2], a0, a1);
+      r[i] = a0 + a1;
+      asm volatile("" : "+v"(r[i]));  // the products happen here
     }
-#pragma unroll
-    for (int k = 0; k < kRowsPerWave * kSteps; ++k) {
-      const int kk = k + 2;
-      if (kk < kRowsPerWave * kSteps) {
-        const int i = kk / kSteps, q = kk % kSteps;
-        read_ops<RES>(lds, word_addr(ew[i][q], q * 64 + lane < ncur[i]), op[kk % 3]);
-        if (q == kSteps - 1) {  // (past the last unit these reads repeat it: unused, no branch)
-          const uint32_t beg = (uint32_t)__builtin_amdgcn_readlane((int)st_cur, i);
-          const uint32_t end = (uint32_t)__builtin_amdgcn_readlane((int)st_cur, i + 1);
-          nrow[i] = row0n + i < N ? (int)(end - beg) : 0;
-          brow[i] = beg;
-#pragma unroll
-          for (int q2 = 0; q2 < kSteps; ++q2)
-            ew[i][q2] = ld4(bw, (beg + (uint32_t)(q2 * 64 + lane)) * 4u, 0u);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      use_ops<RES>(op[k % 3], a0[k / kSteps], a1[k / kSteps]);
-      // the products happen here, not where their sums are first needed
-      asm volatile("" : "+v"(a0[k / kSteps]), "+v"(a1[k / kSteps]));
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) r[i] = a0[i] + a1[i];
 
     // buckets longer than the 192 words held in registers (uniform per row; rare for
     // uniform indices, every word for a row whose indices all fall in one slice)

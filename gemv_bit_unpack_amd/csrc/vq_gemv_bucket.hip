@@ -45,14 +45,23 @@ constexpr int kRes = 256;
 constexpr int kSteps = 3;  // bucket words per lane held in registers per row
 
 // LDS, in 16-byte entries: the residual book and a zero entry; the chunk's activations
-// and a zero entry; the slice and a zero entry.  Every base fits the 16-bit offset field
-// of ds_read_b128.
+// and a zero entry; the slice (from an entry index that is a multiple of 16) and a zero
+// entry; the per-wavefront maxima of the bf16 pass.  Every base fits the 16-bit offset
+// field of ds_read_b128.
+//
+// A 16-byte read is served without extra passes when lanes 4q .. 4q + 3 of every 16-lane
+// group read entries in columns 4q .. 4q + 3 (column = entry mod 16; rows free, any order
+// inside the four).  The slice starting on a column-0 entry makes a main centroid's column
+// its index mod 16, and the packer places each bucket word where bits [2, 4) of its index
+// match bits [2, 4) of the lane (where the bucket's mix of indices allows).
 constexpr int kResAt = 0;
 constexpr int kXAt = kRes + 1;
-constexpr int kSliceAt = kXAt + kChunk + 1;
-constexpr int kLdsEntries = kSliceAt + kSlice + 1;
+constexpr int kSliceAt = (kXAt + kChunk + 1 + 15) / 16 * 16;
+constexpr int kMaxAt = kSliceAt + kSlice + 1;
+constexpr int kLdsEntries = kMaxAt + 4;  // 16 four-byte maxima
+static_assert(kSliceAt % 16 == 0, "slice on a column-0 entry");
 static_assert(kSliceAt * 16 < 65536, "slice base in the ds_read offset field");
-static_assert(kLdsEntries * 16 <= 160 * 1024 - 64, "fits one CU's LDS");
+static_assert(kLdsEntries * 16 <= 160 * 1024, "fits one CU's LDS");
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
@@ -147,8 +156,9 @@ __device__ __forceinline__ float reduce8(const float (&r)[8], int lane) {
 
 template <bool RES>
 __global__ __launch_bounds__(kThreads) void gemv_bucket_kernel(ProductArgs a, BucketCfg g) {
-  __shared__ uint4 lds4[kLdsEntries];
-  __shared__ uint32_t wmax[kWaves];
+  __shared__ uint4 lds4[kLdsEntries];  // the only LDS array: it starts at address 0
+  uint32_t* const wmax = (uint32_t*)(lds4 + kMaxAt);
+  static_assert(kWaves <= 16, "one maximum per wavefront");
   const char* lds = (const char*)lds4;
 
   const int tid = threadIdx.x;

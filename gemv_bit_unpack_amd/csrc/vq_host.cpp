@@ -1,8 +1,10 @@
 // Host side of libvq: descriptor and argument validation, the index packer and the
 // exported C entry points.  Everything here runs on the CPU; the kernels live in the
 // .hip units and are reached through the launch_* functions.
+#include <algorithm>
 #include <cstring>
 #include <new>
+#include <thread>
 #include <vector>
 
 #include "vq_internal.h"
@@ -118,8 +120,49 @@ static vq_status prepare_bucketed(const vq_desc* desc, const void* packed, const
   return VQ_OK;
 }
 
-// The slice-bucketed layout of idx1 / idx2 (vq.h): bucket sizes, their prefix table, then
-// each row's vectors in ascending j dropped into their buckets.
+// Order of the words inside one bucket.  The product hands word k of a bucket to lane
+// k mod 64, and each word costs three 16-byte LDS reads (the activation vector, the main
+// centroid, the residual centroid).  LDS serves such a read in one pass when lanes
+// 4q .. 4q + 3 of every 16-lane group read entries whose column (entry mod 16) lies in
+// 4q .. 4q + 3, rows free; the product's slice starts on a column-0 entry, so a main
+// centroid's column is idx1 mod 16.  The words are therefore dealt so that word k holds,
+// where the bucket's mix of indices allows, an index with idx1 mod 16 == k mod 16 (first
+// pass), else one in the same group of four columns (second pass), else any left over
+// (third pass), each pass in the words' order.  Only one of the three reads can be lined
+// up this way: the main-book read, from the largest table.
+namespace {
+void align_bucket(uint32_t* w, uint32_t n, std::vector<uint32_t>& tmp) {
+  if (n <= 1) return;
+  tmp.assign(w, w + n);
+  std::vector<uint32_t> q[16];
+  for (uint32_t i = 0; i < n; ++i) q[(tmp[i] >> 10) & 15u].push_back(tmp[i]);
+  uint32_t head[16] = {0};
+  auto take = [&](uint32_t col, uint32_t& out) {
+    if (head[col] < q[col].size()) {
+      out = q[col][head[col]++];
+      return true;
+    }
+    return false;
+  };
+  std::vector<uint8_t> filled(n, 0);
+  for (uint32_t k = 0; k < n; ++k) filled[k] = take(k & 15u, w[k]);
+  for (uint32_t k = 0; k < n; ++k) {
+    if (filled[k]) continue;
+    const uint32_t base = k & 12u;
+    for (uint32_t c = 0; c < 4 && !filled[k]; ++c) filled[k] = take(base + ((k + c) & 3u), w[k]);
+  }
+  uint32_t col = 0;
+  for (uint32_t k = 0; k < n; ++k) {
+    if (filled[k]) continue;
+    while (!take(col, w[k])) ++col;
+    filled[k] = 1;
+  }
+}
+}  // namespace
+
+// The slice-bucketed layout of idx1 / idx2 (vq.h): bucket sizes, their prefix table, each
+// row's vectors dropped into their buckets, then every bucket's words ordered for the LDS
+// (buckets in parallel threads; the result does not depend on their number).
 static void pack_bucketed(const vq_desc& d, const uint32_t* idx1, const uint32_t* idx2, uint8_t* out) {
   const int64_t n = d.out_features;
   const int64_t nv = num_vectors(d.in_features, 8);
@@ -142,6 +185,21 @@ static void pack_bucketed(const vq_desc& d, const uint32_t* idx1, const uint32_t
       words[next[bucket(o, j, i1)]++] = (uint32_t)(j % kBucketChunk) | ((i1 & 8191u) << 10) | (i2 << 23);
     }
   }
+  const unsigned hw = std::thread::hardware_concurrency();
+  const int64_t nthreads = std::max<int64_t>(1, std::min<int64_t>({(int64_t)(hw ? hw : 1), 16, (n + 63) / 64}));
+  auto work = [&](int64_t t0) {
+    std::vector<uint32_t> tmp;
+    for (size_t b = (size_t)t0; b < nb; b += (size_t)nthreads) align_bucket(words + start[b], start[b + 1] - start[b], tmp);
+  };
+  std::vector<std::thread> pool;
+  int64_t started = 1;  // work shares 1 .. started - 1 run in threads
+  try {
+    for (; started < nthreads; ++started) pool.emplace_back(work, started);
+  } catch (...) {  // no more threads: this one takes the shares that did not start
+  }
+  work(0);
+  for (int64_t t = started; t < nthreads; ++t) work(t);
+  for (auto& th : pool) th.join();
 }
 
 // Affine-lattice calls: the descriptor must be the lattice stream (v = 4, bits1 = 8, no

@@ -29,7 +29,10 @@
  * multiple of 8.  The main book is seen as 8 slices of 8192 centroids (slice s =
  * idx1 >> 13); the vectors of row o are cut into chunks of 1024 (chunk c = j / 1024).
  *   - bucket b = (c*8 + s)*N + o holds the vectors j of row o in chunk c whose idx1
- *     lies in slice s, in ascending j, one 32-bit little-endian word each:
+ *     lies in slice s, one 32-bit little-endian word each, in an order vq_pack chooses
+ *     (deterministically: word k preferably holds an idx1 whose bits [2, 4) equal those
+ *     of k, which lines the product's main-book reads up with the LDS banks); any order
+ *     gives the same y up to fp32 summation order:
  *       bits [0, 10) j - 1024*c,  bits [10, 23) idx1 & 8191,  bits [23, 31) idx2
  *     (idx2 = 0 without a residual book), bit 31 zero;
  *   - bytes [0, H) hold start[b], b = 0 .. 8*chunks*N, as uint32: bucket b is words

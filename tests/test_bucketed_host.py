@@ -4,8 +4,10 @@ validation of the calls that take it, with no GPU.
 The packer is checked by reading its output back with a decoder written here from the
 layout's definition in include/vq.h (prefix table of bucket offsets, one 32-bit word per
 vector: position in its 1024-vector chunk, idx1 & 8191, idx2), and recovering every
-index of the original tensors; ordering inside a bucket (ascending position), the
-zero padding and the prefix table's consistency are checked on the way.
+index of the original tensors; the zero padding and the prefix table's consistency are
+checked on the way.  The order of words inside a bucket is the packer's choice (it lines
+the main-book reads up with the LDS banks): checked to be deterministic and to place most
+words where the column group of their main index matches that of their lane.
 """
 import ctypes
 
@@ -61,7 +63,7 @@ def decode(packed: np.ndarray, n: int, i: int, b2: int):
                 b = (c * 8 + s) * n + o
                 wd = words[start[b]:start[b + 1]].astype(np.int64)
                 pos = wd & 0x3FF
-                assert (np.diff(pos) > 0).all(), "ascending positions in a bucket"
+                assert np.unique(pos).size == pos.size, "each position once in a bucket"
                 j = c * CHUNK + pos
                 assert (j < nv).all()
                 assert (idx1[o, j] == -1).all(), "each vector once"
@@ -207,3 +209,29 @@ def test_other_calls_refuse_the_bucketed_layout(vq):
     assert f.vq_rht_product_workspace_bytes(ctypes.byref(d), 1, 0, 0, ctypes.byref(n)) == vq.VQ_ERR_UNSUPPORTED
     assert f.vq_gemv_ws_rht(ctypes.byref(d), P, P, P, None, None, P, 0, 1, P, P, 2, P, 1 << 20,
                             None) == vq.VQ_ERR_UNSUPPORTED
+
+
+def _quad_match(words):
+    """Fraction of the words of a bucket whose main-index column group (bits [2, 4) of
+    idx1) equals that of their slot (bits [2, 4) of the word's place in the bucket)."""
+    k = np.arange(words.size)
+    return float(np.mean(((words.astype(np.int64) >> 12) & 3) == ((k >> 2) & 3))) if words.size else 1.0
+
+
+def test_bucketed_pack_lines_up_main_index_columns_deterministically(vq):
+    n, i = 64, 8192
+    lay = synth.make_layer(n, i, 8, 16, 8, wid=71)
+    d = _desc(vq, n, i, 8)
+    p1 = vq.pack(d, lay["idx1"], lay["idx2"])
+    p2 = vq.pack(d, lay["idx1"], lay["idx2"])
+    assert np.array_equal(p1, p2)
+    nb = 8 * n
+    start = p1[: 4 * (nb + 1)].view(np.uint32)
+    words = p1[_header_bytes(n, i):].view(np.uint32)
+    ours, plain = [], []
+    for b in range(nb):
+        wb = words[start[b]:start[b + 1]]
+        ours.append(_quad_match(wb))
+        plain.append(_quad_match(wb[np.argsort(wb & 0x3FF, kind="stable")]))  # ascending positions
+    # position order matches a quarter of the slots by chance; the packer's order most of them
+    assert np.mean(plain) < 0.35 and np.mean(ours) > 0.85, (np.mean(ours), np.mean(plain))

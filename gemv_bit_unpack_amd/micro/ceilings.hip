@@ -85,7 +85,13 @@ __global__ void gather_lds(const uint4* __restrict__ tab, unsigned entries, int 
 //   MODE 0: random entries of a 128 KiB table;
 //   MODE 1: lanes 1..7 of every 8 read entry kLdsEntries - 4, lane 0 a random one;
 //   MODE 2: only lanes 0, 8, ..., 56 run the loop (7 of 8 lanes masked off);
-//   MODE 3: lane l reads entry l + 64 k (each group of 16 lanes covers all 64 banks).
+//   MODE 3: lane l reads entry l + 64 k (each group of 16 lanes covers all 64 banks);
+//   MODE 4: lane l reads a random row of the table at column l mod 16 (column = entry
+//           mod 16), so lanes 4q .. 4q + 3 of each 16-lane group stay in columns
+//           4q .. 4q + 3;
+//   MODE 5: random rows at column 5 l mod 16: still 16 distinct columns per group of 16
+//           lanes, but a lane's column lies outside its group of four.
+// Modes 4 and 5 step the 4 reads of an offset by 16 entries (same column).
 constexpr unsigned kLdsEntries = 8192;
 template <int MODE>
 __global__ __launch_bounds__(512) void lds_rate(const uint4* __restrict__ tab, int iters, unsigned* out) {
@@ -101,8 +107,11 @@ __global__ __launch_bounds__(512) void lds_rate(const uint4* __restrict__ tab, i
     unsigned e = (h >> 9) % (kLdsEntries - 4);  // entries e .. e + 3 stay in the table
     if (MODE == 1 && (lane & 7)) e = kLdsEntries - 4;
     if (MODE == 3) e = lane + 64 * k;
+    if (MODE == 4) e = ((h >> 9) % (kLdsEntries / 16 - 4)) * 16 + (lane & 15);
+    if (MODE == 5) e = ((h >> 9) % (kLdsEntries / 16 - 4)) * 16 + ((lane * 5) & 15);
     a[k] = e;
   }
+  constexpr unsigned kStep = MODE >= 4 ? 16 : 1;
   unsigned acc0 = 0, acc1 = 0;
   if (MODE != 2 || (lane & 7) == 0) {
     for (int it = 0; it < iters; ++it) {
@@ -111,7 +120,7 @@ __global__ __launch_bounds__(512) void lds_rate(const uint4* __restrict__ tab, i
       for (int j = 0; j < 4; ++j) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          const uint4 v = t[a[k] + j];
+          const uint4 v = t[a[k] + j * kStep];
           acc0 = acc0 + v.x + v.y;  // v_add3_u32
           acc1 = acc1 + v.z + v.w;
         }
@@ -310,17 +319,20 @@ int main(int argc, char** argv) {
   }
   printf("}");
 
-  // LDS read rate at 512 threads (one workgroup per CU: the 128 KiB table), 4 patterns.
+  // LDS read rate at 512 threads (one workgroup per CU: the 128 KiB table), 6 patterns.
   printf(", \"lds_read_b128\": {");
-  const char* lds_modes[4] = {"random", "seven_of_eight_one_address", "one_of_eight_active", "conflict_free"};
-  for (int mode = 0; mode < 4; ++mode) {
+  const char* lds_modes[6] = {"random", "seven_of_eight_one_address", "one_of_eight_active", "conflict_free",
+                              "random_rows_column_in_lane_quad", "random_rows_distinct_columns_across_quads"};
+  for (int mode = 0; mode < 6; ++mode) {
     const int grid = ncu, iters = 512;
     auto launch = [&] {
       switch (mode) {
         case 0: hipLaunchKernelGGL(lds_rate<0>, dim3(grid), dim3(512), 0, 0, buf, iters, dout); break;
         case 1: hipLaunchKernelGGL(lds_rate<1>, dim3(grid), dim3(512), 0, 0, buf, iters, dout); break;
         case 2: hipLaunchKernelGGL(lds_rate<2>, dim3(grid), dim3(512), 0, 0, buf, iters, dout); break;
-        default: hipLaunchKernelGGL(lds_rate<3>, dim3(grid), dim3(512), 0, 0, buf, iters, dout); break;
+        case 3: hipLaunchKernelGGL(lds_rate<3>, dim3(grid), dim3(512), 0, 0, buf, iters, dout); break;
+        case 4: hipLaunchKernelGGL(lds_rate<4>, dim3(grid), dim3(512), 0, 0, buf, iters, dout); break;
+        default: hipLaunchKernelGGL(lds_rate<5>, dim3(grid), dim3(512), 0, 0, buf, iters, dout); break;
       }
     };
     const double t = timed(launch, 3);

@@ -826,6 +826,14 @@ def main():
                 entry["gather_kernel_us_per_call"] = measure(rings)["us_per_call"]
                 del rings
                 torch.cuda.empty_cache()
+            _, v_, b1_, b2_, _ = WORKLOADS[key]
+            if v_ == 8 and b1_ == 16 and b2_ in (0, 8):  # the slice-bucketed decode layout
+                rings = [Ring(vq, torch, key, li, 1, layout=vq.LAYOUT_BUCKETED) for li in range(n_layers)]
+                bk = measure(rings)
+                entry["bucketed_us_per_call"] = bk["us_per_call"]
+                entry["bucketed_GBps"] = bk["GBps"]
+                del rings
+                torch.cuda.empty_cache()
             per[key] = entry
         out["gemv_m1_per_workload"] = per
         # Decode batches: the 65536-entry book (vq_gemv_ws against vq_gemv) and the v = 6

@@ -12,7 +12,8 @@ reads); nothing the GPU computes reaches the oracle.
   one slice) and empty buckets;
 - one-hot x reproduces columns of W^ bit-exactly;
 - bf16 activations far outside the fp16 range and tiny ones;
-- determinism, vq_gemv_noalloc equal bit for bit, IN = 0, replays of a captured graph.
+- determinism, vq_gemv_noalloc equal bit for bit, IN = 0, replays of a captured graph;
+- VQLinear holding both layouts (one-row batches on the bucketed product).
 Tolerance: max |y - y64| <= 2e-3 * ||y64||_inf with fp32 outputs, plus half an output ulp
 for fp16 / bf16 outputs.
 """
@@ -203,3 +204,23 @@ def test_bucketed_graph_replays(vq):
         assert torch.equal(out, ref), k
         vq.gemv_ws(*bl.args(), x, ws, y_dtype=torch.float32)  # eager work between replays
         torch.cuda.synchronize()
+
+
+def test_vqlinear_with_decode_layout(vq):
+    """VQLinear keeping both layouts: one-row batches take the bucketed product, larger ones
+    the row-stream calls; every batch size matches the oracle, and the one-row result is the
+    bucketed call's exactly."""
+    n, i = 1536, 4096
+    lay = synth.make_layer(n, i, 8, 16, 8, wid=88, with_bias=True)
+    f = lambda b: f16_tensor(b)
+    layer = vq.VQLinear.from_indices(vq.make_desc(n, i, 8, 16, 8), lay["idx1"], lay["idx2"], f(lay["cb1"]),
+                                     f(lay["cb2"]), f(lay["scale"]), f(lay["bias"]), decode_layout=True)
+    assert layer.decode_desc.layout == vq.LAYOUT_BUCKETED
+    for m in (1, 3, 40):
+        xb = synth.activations(np.random.default_rng(m), m, i, "bf16")
+        x = x_tensor(xb, "bf16")
+        y = layer(x, y_dtype=torch.float32)
+        check_y(y, oracle_y(lay, xb, "bf16"), "f32")
+        if m == 1:
+            bl = BucketedLayer(vq, lay)
+            assert torch.equal(y, _run(vq, bl, x))

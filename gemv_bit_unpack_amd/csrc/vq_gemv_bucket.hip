@@ -9,10 +9,10 @@
 // j of row o with c*1024 <= j < (c+1)*1024 and idx1 >> 13 == s, one 32-bit word each:
 //   bits [0, 10)  j - c*1024      bits [10, 23) idx1 & 8191      bits [23, 31) idx2
 // behind a prefix table start[(c*8 + s)*N + o] of bucket offsets.
-//   - 256 persistent workgroups of 512 threads (8 wavefronts), one per CU; workgroup
+//   - 256 persistent workgroups of 1024 threads (16 wavefronts), one per CU; workgroup
 //     (slice s, group p); the 32 workgroups of slice s share one XCD (and its L2 copy of
 //     the slice's centroids);
-//   - a unit is (chunk c, tile of 64 rows); group p takes units p, p + 32, ... in
+//   - a unit is (chunk c, tile of 128 rows); group p takes units p, p + 32, ... in
 //     chunk-major order; the chunk's 1024 activation vectors sit in LDS (reloaded when
 //     the chunk changes, bf16 rewritten as fp16 times 2^-e);
 //   - wavefront w takes rows 8w .. 8w + 7 of the tile; lane l handles words l, l + 64 and
@@ -21,8 +21,9 @@
 //   - per word: three 16-byte LDS reads (x at the position, the main centroid, the
 //     residual centroid) and eight packed fp16 dot products into fp32;
 //   - the next unit's bucket words are loaded while the current unit runs (each row's
-//     words right after its own are consumed), the unit after that's prefix entries one
-//     unit earlier still;
+//     words as soon as its LDS reads are issued), the prefix entries of the unit after
+//     that one unit earlier still; all of row i + 1's LDS reads are issued before row i's
+//     products;
 //   - the 8 rows' lane sums are reduced together (a butterfly that halves the rows held
 //     per lane at each of the first three exchanges) and stored as one fp32 partial per
 //     (chunk, slice, row); the shared finalize kernel adds the 8 * chunks partials of
@@ -49,11 +50,12 @@ constexpr int kSteps = 3;  // bucket words per lane held in registers per row
 // entry; the per-wavefront maxima of the bf16 pass.  Every base fits the 16-bit offset
 // field of ds_read_b128.
 //
-// A 16-byte read is served without extra passes when lanes 4q .. 4q + 3 of every 16-lane
-// group read entries in columns 4q .. 4q + 3 (column = entry mod 16; rows free, any order
-// inside the four).  The slice starting on a column-0 entry makes a main centroid's column
-// its index mod 16, and the packer places each bucket word where bits [2, 4) of its index
-// match bits [2, 4) of the lane (where the bucket's mix of indices allows).
+// A 16-byte read is served as fast as a read of consecutive entries when lanes 4q .. 4q + 3
+// of every 16-lane group read entries in columns 4q .. 4q + 3 (column = entry mod 16; rows
+// free, any order inside the four), as measured; random columns cost about 2.5 times as
+// much.  The slice starting on a column-0 entry makes a main centroid's column its index
+// mod 16, and the packer places each bucket word where bits [2, 4) of its index match bits
+// [2, 4) of the lane (where the bucket's mix of indices allows).
 constexpr int kResAt = 0;
 constexpr int kXAt = kRes + 1;
 constexpr int kSliceAt = (kXAt + kChunk + 1 + 15) / 16 * 16;

@@ -2,6 +2,7 @@
 // exported C entry points.  Everything here runs on the CPU; the kernels live in the
 // .hip units and are reached through the launch_* functions.
 #include <algorithm>
+#include <atomic>
 #include <cstring>
 #include <new>
 #include <thread>
@@ -162,7 +163,8 @@ void align_bucket(uint32_t* w, uint32_t n, std::vector<uint32_t>& tmp) {
 
 // The slice-bucketed layout of idx1 / idx2 (vq.h): bucket sizes, their prefix table, each
 // row's vectors dropped into their buckets, then every bucket's words ordered for the LDS
-// (buckets in parallel threads; the result does not depend on their number).
+// (buckets in parallel threads; the result does not depend on their number).  Throws
+// std::bad_alloc when host memory runs out, in this thread or a worker.
 static void pack_bucketed(const vq_desc& d, const uint32_t* idx1, const uint32_t* idx2, uint8_t* out) {
   const int64_t n = d.out_features;
   const int64_t nv = num_vectors(d.in_features, 8);
@@ -187,9 +189,15 @@ static void pack_bucketed(const vq_desc& d, const uint32_t* idx1, const uint32_t
   }
   const unsigned hw = std::thread::hardware_concurrency();
   const int64_t nthreads = std::max<int64_t>(1, std::min<int64_t>({(int64_t)(hw ? hw : 1), 16, (n + 63) / 64}));
+  std::atomic<bool> failed{false};
   auto work = [&](int64_t t0) {
-    std::vector<uint32_t> tmp;
-    for (size_t b = (size_t)t0; b < nb; b += (size_t)nthreads) align_bucket(words + start[b], start[b + 1] - start[b], tmp);
+    try {  // an exception must not leave a worker thread
+      std::vector<uint32_t> tmp;
+      for (size_t b = (size_t)t0; b < nb; b += (size_t)nthreads)
+        align_bucket(words + start[b], start[b + 1] - start[b], tmp);
+    } catch (...) {
+      failed.store(true);
+    }
   };
   std::vector<std::thread> pool;
   int64_t started = 1;  // work shares 1 .. started - 1 run in threads
@@ -200,6 +208,7 @@ static void pack_bucketed(const vq_desc& d, const uint32_t* idx1, const uint32_t
   work(0);
   for (int64_t t = started; t < nthreads; ++t) work(t);
   for (auto& th : pool) th.join();
+  if (failed.load()) throw std::bad_alloc();
 }
 
 // Affine-lattice calls: the descriptor must be the lattice stream (v = 4, bits1 = 8, no
@@ -322,7 +331,7 @@ vq_status vq_pack(const vq_desc* desc, const uint32_t* idx1, const uint32_t* idx
   if (d.layout == VQ_LAYOUT_BUCKETED) {
     try {
       pack_bucketed(d, idx1, idx2, out);
-    } catch (const std::bad_alloc&) {
+    } catch (...) {  // host memory for the regrouping ran out: no exception crosses the ABI
       return VQ_ERR_BUFFER_SIZE;
     }
     return VQ_OK;

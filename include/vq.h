@@ -125,7 +125,8 @@ vq_status vq_packed_bytes(const vq_desc* desc, size_t* nbytes);
  * residual indices in separate streams as its residual pipeline keeps them ("2.
  * Multi-Stage Residual Vector Quantization (RVQ)").  With desc->layout ==
  * VQ_LAYOUT_BUCKETED the same indices are written in the slice-bucketed layout above
- * (VQ_ERR_UNSUPPORTED where it is not defined). */
+ * (VQ_ERR_UNSUPPORTED where it is not defined; VQ_ERR_BUFFER_SIZE also if the host runs
+ * out of memory for the regrouping, with `packed` then partly written). */
 vq_status vq_pack(const vq_desc* desc, const uint32_t* idx1, const uint32_t* idx2, void* packed, size_t nbytes);
 
 /* Rebuild W^ [N][IN] into `w` (device, row-major, w_dtype; fp16 / bf16 outputs are the

@@ -235,3 +235,15 @@ def test_bucketed_pack_lines_up_main_index_columns_deterministically(vq):
         plain.append(_quad_match(wb[np.argsort(wb & 0x3FF, kind="stable")]))  # ascending positions
     # position order matches a quarter of the slots by chance; the packer's order most of them
     assert np.mean(plain) < 0.35 and np.mean(ours) > 0.85, (np.mean(ours), np.mean(plain))
+
+
+def test_bucketed_layout_size_limits(vq):
+    """The product addresses the words and the prefix table with 32-bit offsets: a layer of
+    2^29 or more vectors is refused by every call that takes the layout."""
+    n = ctypes.c_size_t(77)
+    big = _desc(vq, 1 << 19, 8192)  # 2^19 rows x 1024 vectors = 2^29 vectors
+    assert vq.lib().vq_packed_bytes(ctypes.byref(big), ctypes.byref(n)) == vq.VQ_ERR_UNSUPPORTED
+    assert _ws_bytes(vq, big, 1, vq.VQ_F16) == (vq.VQ_ERR_UNSUPPORTED, 12345)
+    assert _call(vq, "vq_gemv_ws", big) == vq.VQ_ERR_UNSUPPORTED
+    ok = _desc(vq, (1 << 19) - 8, 8192)  # just below: accepted
+    assert vq.lib().vq_packed_bytes(ctypes.byref(ok), ctypes.byref(n)) == vq.VQ_OK
